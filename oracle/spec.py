@@ -1,0 +1,145 @@
+"""Speculative verification by rejection sampling (oracle; test infrastructure only).
+
+What it follows
+---------------
+"Accelerating Sonar through speculation" (Perplexity blog): a draft proposes n
+tokens and the target verifies them, so one step emits up to n + 1 tokens
+(section on speculative decoding); acceptance compares the full draft and target
+distributions and the target's logits after the accepted prefix are sampled for
+one extra token (section on target-draft decoding). Its reference list names
+"Fast inference from transformers via speculative decoding", the source of the
+rejection rule. SonicSampler's abstract puts verification inside the same
+batched sampler as the logit processing. The rule itself (a reading consistent
+with all of these):
+
+For request b, position j = 0 .. G-1 in order, with target row j processed by
+the full per-request pipeline (the penalty history of row j is the request's
+history followed by the draft tokens d_0 .. d_{j-1}, since row j is only reached
+if those were accepted; a per-position grammar mask is used when given):
+  * greedy (T == 0): accept iff d_j equals the greedy token of row j; otherwise
+    emit that greedy token and stop.
+  * T > 0: with pi_j the filtered target distribution and q_j the draft
+    probabilities, draw u = u24(Philox ACCEPT word at (seed, request, pos + j, 0))
+    and accept iff u < pi_j(d_j) / q_j(d_j) (if q_j(d_j) == 0: accept iff
+    pi_j(d_j) > 0). On the first rejection draw u' = u24(Philox RESIDUAL word at
+    (seed, request, pos + j, 0)) and emit the token of the normalised residual
+    r = max(0, pi_j - q_j) by inverse CDF in ascending token-id order (pi_j if
+    the residual sums to zero); then stop.
+  * If all G drafts are accepted, the bonus token is sampled from row G exactly
+    as the plain sampler would (SAMPLE word at (seed, request, pos + G, 0)).
+Output: tokens d_0 .. d_{n-1}, the final token, then -1 padding to G + 1;
+n_acc = n in [0, G].
+
+The residual CDF runs in token-id order (not by residual size) because the
+residual's values are binary64 here and binary32 on a GPU: an ordering by them
+could differ between the two sides by whole tokens, while an id-ordered CDF can
+only move its breakpoints by rounding.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import philox
+from .pipeline import BOUNDARY_EPS, boundary_draw, draw, filter_row, process_row
+
+
+@dataclass
+class SpecResult:
+    tokens: np.ndarray      # [G+1] int32, -1 padded
+    n_acc: int
+    flagged: bool           # a decision of this request lies on a boundary
+    accept_ratios: list     # per examined position: pi/q (sampling) or None
+
+
+def residual_draw(pi, q, u):
+    """Inverse CDF in token-id order over max(0, pi - q); returns (token, flagged)."""
+    r = np.maximum(0.0, np.asarray(pi, dtype=np.float64) - np.asarray(q, dtype=np.float64))
+    R = r.sum()
+    if not R > 0.0:
+        r = np.asarray(pi, dtype=np.float64).copy()
+        R = r.sum()
+    if not R > 0.0:
+        return -1, False
+    pos = np.nonzero(r > 0.0)[0]
+    cdf = np.cumsum(r[pos]) / R
+    i = int(np.searchsorted(cdf, u, side="right"))
+    i = min(i, pos.size - 1)
+    return int(pos[i]), boundary_draw(cdf, u)
+
+
+def verify_request(target_rows, draft_probs, draft_tokens, *, temperature, top_k=0,
+                   top_p=1.0, min_p=0.0, rep=1.0, freq=0.0, pres=0.0, hist=(),
+                   bias_ids=(), bias_vals=(), masks=None, seed=0, request=0, position=0,
+                   uniform=None):
+    """Verify one request's linear draft. target_rows: [G+1, V] float32.
+
+    uniform(domain, pos) -> u overrides the Philox uniforms (used by tests that
+    integrate over the uniforms); by default u = u24 of the Philox word at
+    (seed, request, pos, draw 0, domain).
+    """
+    if uniform is None:
+        def uniform(domain, pos):
+            return philox.uniform(seed, request, pos, 0, domain)
+    G = len(draft_tokens)
+    out = np.full(G + 1, -1, dtype=np.int32)
+    flagged = False
+    ratios = []
+    hist = [int(h) for h in hist]
+    for j in range(G + 1):
+        hj = hist + [int(d) for d in draft_tokens[:j]]
+        mj = None if masks is None else masks[j]
+        xp = process_row(target_rows[j], hj, rep, freq, pres, bias_ids, bias_vals, mj)
+        filt = filter_row(xp, temperature, top_k, top_p, min_p)
+        flagged = flagged or filt.flag_topp or filt.flag_minp
+        if j == G:
+            u = uniform(philox.SAMPLE, position + G)
+            res = draw(filt, u)
+            out[G] = res.token
+            return SpecResult(out, G, flagged or res.flag_draw, ratios)
+        d = int(draft_tokens[j])
+        if filt.greedy or filt.n_kept == 0:
+            g = filt.argmax if filt.n_kept else -1
+            ratios.append(None)
+            if g >= 0 and d == g:
+                out[j] = d
+                continue
+            out[j] = g
+            return SpecResult(out, j, flagged, ratios)
+        p = float(filt.probs[d]) if 0 <= d < len(filt.probs) else 0.0
+        q = float(draft_probs[j][d]) if 0 <= d < len(filt.probs) else 0.0
+        u = uniform(philox.ACCEPT, position + j)
+        if q > 0.0:
+            ratio = p / q
+            accept = u < ratio
+            if ratio < 1.0 and abs(u - ratio) < BOUNDARY_EPS:
+                flagged = True
+        else:
+            ratio = np.inf if p > 0.0 else 0.0
+            accept = p > 0.0
+        ratios.append(ratio)
+        if accept:
+            out[j] = d
+            continue
+        u2 = uniform(philox.RESIDUAL, position + j)
+        tok, fl = residual_draw(filt.probs, draft_probs[j], u2)
+        out[j] = tok
+        return SpecResult(out, j, flagged or fl, ratios)
+    raise AssertionError("unreachable")
+
+
+def verify_batch(target, draft_probs, draft_tokens, params):
+    """target [B, G+1, V] f32, draft_probs [B, G, V] f32, draft_tokens [B, G] int."""
+    res = []
+    for b in range(target.shape[0]):
+        pr = params.row(b)
+        masks = None if params.mask is None else params.mask[b]
+        res.append(verify_request(
+            target[b], draft_probs[b], draft_tokens[b],
+            temperature=float(params.temperature[b]), top_k=int(params.top_k[b]),
+            top_p=float(params.top_p[b]), min_p=float(params.min_p[b]),
+            rep=pr["rep"], freq=pr["freq"], pres=pr["pres"], hist=pr["hist"],
+            bias_ids=pr["bias_ids"], bias_vals=pr["bias_vals"], masks=masks,
+            seed=params.seed, request=pr["request"], position=pr["position"]))
+    return res
