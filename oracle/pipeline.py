@@ -38,8 +38,9 @@ open is a stated reading:
 
 Flags (counted, not compared): a draw is a boundary draw if u lies within 1e-6
 of any interior C_i; a top-p cut is flagged if a decisive exclusive cumulative
-sum lies within 1e-6 of top_p; a min-p cut is flagged if a surviving token's
-weight lies within 1e-6 of min_p. These are the cases a binary32 GPU cannot be
+sum after the first token lies within 1e-6 of top_p; a min-p cut is flagged if
+a surviving token after the first has a weight within 1e-6 of min_p (the first
+token's exclusive sum 0 and weight 1 are exact everywhere). These are the cases a binary32 GPU cannot be
 asked to decide the same way as this binary64 oracle.
 
 Binary32 steps use numpy float32 scalars: one rounding per operation, no fused
@@ -159,7 +160,9 @@ def filter_row(xp, temperature, top_k, top_p, min_p):
         excl = np.concatenate(([0.0], np.cumsum(P)[:-1]))
         tp = float(np.float32(top_p))
         n_topp = int(np.count_nonzero(excl < tp))
-        near = [excl[n_topp - 1]]
+        # the exclusive sum before the first token is exactly 0 on any
+        # implementation, so only later comparisons can be boundary cases
+        near = [excl[n_topp - 1]] if n_topp > 1 else []
         if n_topp < n_topk:
             near.append(excl[n_topp])
         flag_topp = any(abs(e - tp) < BOUNDARY_EPS for e in near)
@@ -169,7 +172,8 @@ def filter_row(xp, temperature, top_k, top_p, min_p):
     if float(min_p) > 0.0:
         mp = float(np.float32(min_p))
         n_kept = int(np.count_nonzero(w[:n_topp] >= mp))
-        flag_minp = bool(np.any(np.abs(w[:n_topp] - mp) < BOUNDARY_EPS))
+        # w of the first token is exactly 1 on any implementation
+        flag_minp = bool(np.any(np.abs(w[1:n_topp] - mp) < BOUNDARY_EPS))
     else:
         n_kept = n_topp
     pk = w[:n_kept] / w[:n_kept].sum()
