@@ -1,0 +1,187 @@
+/*
+ * ss_sampler.h -- C ABI of the MI355X (gfx950) batched sampling library.
+ *
+ * One library serves three hot paths that the source pages describe:
+ *
+ *  - ss_sample: per-request logit processing and token selection in one
+ *    batched, graph-capturable launch (SonicSampler abstract, arxivdaily page,
+ *    English abstract: grammar-constrained decoding; repetition, frequency and
+ *    presence penalties; logit bias; temperature; top-k / top-p / min-p
+ *    filtering; hierarchical two-stage top-k; per-request behaviour in one
+ *    batch).
+ *  - ss_spec_verify: verification of a linear draft by rejection sampling
+ *    ("Accelerating Sonar through speculation", Perplexity blog, sections on
+ *    speculative decoding and on target-draft decoding: up to n + 1 tokens per
+ *    step, acceptance compares the full distributions, the target supplies an
+ *    extra token; the accepted count is what the engine must read back).
+ *  - ss_lmhead_sample: LM-head GEMM fused with exact Gumbel-max sampling, the
+ *    logits never reaching memory (FlashSampling news item, meineki.news, body:
+ *    logits formed in on-chip tiles, Gumbel noise added, a per-row maximum per
+ *    vocabulary tile kept, a small cross-tile reduction; exact because argmax
+ *    decomposes over partitions).
+ *
+ * Conventions
+ *  - Every pointer passed to ss_sample, ss_spec_verify and ss_lmhead_sample
+ *    (inputs, outputs, parameter arrays) is a DEVICE pointer on the sampler's
+ *    device, except the ss_params / ss_debug structs themselves, which live in
+ *    host memory and are read during the call. The caller owns every buffer.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
+ *    stream) and return. They never allocate, copy to the host or synchronise,
+ *    so they may be captured in a HIP graph; the launch shape depends only on
+ *    (B, G, V, K), never on parameter values.
+ *  - Host-detectable argument errors are returned before anything is launched.
+ *    Values inside device parameter arrays cannot be checked without a
+ *    synchronisation; their ranges are a caller contract stated per field.
+ *  - Row-level degenerate data is encoded in the outputs: a row with no
+ *    finite processed logit yields token -1.
+ *  - Random numbers come from a counter-based Philox4x32-10 generator keyed by
+ *    (seed) with counter (request, position, draw >> 2, domain); a draw is
+ *    therefore a pure function of those values (domains: 0 sampling,
+ *    1 acceptance, 2 residual, 3 Gumbel noise).
+ *  - A sampler handle is not thread-safe; use one handle per concurrent stream.
+ */
+#ifndef SS_SAMPLER_H
+#define SS_SAMPLER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ss_sampler ss_sampler; /* opaque; owns its device workspace */
+
+typedef enum {
+    SS_OK = 0,
+    SS_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, size out of range */
+    SS_ERR_UNSUPPORTED = -2,   /* a valid request this build does not serve */
+    SS_ERR_OUT_OF_MEMORY = -3, /* workspace allocation failed (create only) */
+    SS_ERR_HIP = -4            /* a HIP runtime call or launch failed */
+} ss_status;
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+/* Host struct. Limits fixed for the handle's lifetime; workspace is sized from
+ * them once, in ss_sampler_create. */
+typedef struct {
+    int32_t max_batch;   /* max rows (ss_sample) / requests (spec, lmhead), >= 1 */
+    int32_t vocab_size;  /* V, 1 .. 262144 */
+    int32_t max_draft;   /* max G for ss_spec_verify, 0 .. 16 (0: verify unused) */
+    int32_t hidden_size; /* K for ss_lmhead_sample, 0 or a multiple of 64 (0: unused) */
+    int32_t device;      /* HIP device ordinal */
+} ss_sampler_config;
+
+/* Per-request parameters: a host struct holding DEVICE pointers, one entry per
+ * row (ss_sample) or per request (ss_spec_verify). NULL disables a feature and
+ * takes the stated default. */
+typedef struct {
+    const float* temperature;        /* [B] required; >= 0 and finite; 0 = greedy */
+    const int32_t* top_k;            /* [B]; <= 0 or >= V: off */
+    const float* top_p;              /* [B]; in (0, 1]; 1 = off (NULL: 1) */
+    const float* min_p;              /* [B]; in [0, 1]; 0 = off (NULL: 0) */
+    const float* repetition_penalty; /* [B]; > 0 (NULL: 1) */
+    const float* frequency_penalty;  /* [B] (NULL: 0) */
+    const float* presence_penalty;   /* [B] (NULL: 0) */
+    const int32_t* history_ids;      /* [B, history_stride]; ids outside [0,V) ignored */
+    const int32_t* history_len;      /* [B], each in [0, history_stride]; NULL: no history */
+    int32_t history_stride;          /* >= 0, <= 65535 */
+    const int32_t* bias_ids;         /* [B, bias_stride]; ids outside [0,V) ignored */
+    const float* bias_values;        /* [B, bias_stride]; applied in array order */
+    const int32_t* bias_len;         /* [B], each in [0, bias_stride]; NULL: no bias */
+    int32_t bias_stride;             /* >= 0 */
+    const uint32_t* grammar_mask;    /* [B, mask_stride] (verify: [B, G+1, mask_stride]);
+                                        bit (v & 31) of word (v >> 5), 1 = allowed */
+    int32_t mask_stride;             /* >= ceil(V / 32) when grammar_mask is set */
+    const int32_t* request_ids;      /* [B] Philox counter word 0 (NULL: row index) */
+    const int32_t* positions;        /* [B] Philox counter word 1 (NULL: 0) */
+    uint64_t seed;                   /* Philox key (host value) */
+} ss_params;
+
+/* Optional per-call debug outputs of ss_sample (DEVICE pointers, each may be
+ * NULL). They cost extra memory traffic; leave them NULL when timing. */
+typedef struct {
+    float* processed_logits; /* [B, V]: logits after penalties, bias and mask */
+    int32_t* topk_ids;       /* [B, topk_stride]: the top-k set (any order), -1 padded;
+                                all -1 for rows where top-k is off or T = 0 */
+    int32_t topk_stride;     /* columns of topk_ids; the set is cut at this many */
+    int32_t* kept_count;     /* [B]: size of the sampling support after all filters */
+    float* probs;            /* [B, V]: filtered probabilities (0 outside the support) */
+    int32_t* path;           /* [B]: 0 = resolved from the tile candidates,
+                                1 = resolved by the exact whole-row fallback */
+} ss_debug;
+
+/* Creates a sampler on cfg->device and allocates its workspace (the only call
+ * that allocates). Returns SS_ERR_INVALID_ARG for out-of-range limits,
+ * SS_ERR_OUT_OF_MEMORY if the workspace does not fit, SS_ERR_HIP otherwise. */
+ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out);
+
+/* Frees the workspace. The caller must ensure no enqueued call is pending. */
+void ss_sampler_destroy(ss_sampler* s);
+
+/* Static description of a status code. */
+const char* ss_status_string(ss_status st);
+
+/* Bytes of device workspace the handle holds. */
+int64_t ss_sampler_workspace_bytes(const ss_sampler* s);
+
+/* ss_sample -- sample one token per row of a [B, V] logits matrix.
+ *   logits      [B, row_stride] of dtype (SS_F32 or SS_BF16), element-aligned,
+ *               row_stride >= V. Rows whose start is 16-byte aligned are read
+ *               with 16-byte vector loads, others element by element.
+ *   B           0 .. max_batch (0 is a no-op).
+ *   params      per-row parameters (host struct of device pointers).
+ *   out_tokens  [B] int32: sampled token, or -1 when a row has no finite logit.
+ *   debug       NULL or optional debug outputs.
+ * Per row: penalties -> bias -> grammar mask -> temperature (T = 0: greedy,
+ * lowest id among the maxima) -> top-k -> top-p -> min-p -> inverse-CDF draw in
+ * (z descending, id ascending) order with u = u24(Philox(seed; request,
+ * position, 0, domain 0)). Ties always go to the lower token id. */
+ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t row_stride,
+                    int32_t B, const ss_params* params, int32_t* out_tokens,
+                    const ss_debug* debug, void* stream);
+
+/* ss_spec_verify -- verify a linear draft of G tokens per request.
+ *   target_logits [B, G+1, row_stride] of dtype: target logits at the G draft
+ *                 positions and the bonus position (same layout rules as above).
+ *   draft_probs   [B, G, draft_stride] float32 draft probabilities (draft_stride >= V).
+ *   draft_tokens  [B, G] int32 draft tokens.
+ *   B, G          0 .. max_batch, 1 .. max_draft.
+ *   out_tokens    [B, G+1] int32: accepted drafts, then the final (corrected or
+ *                 bonus) token, then -1 padding.
+ *   out_num_accepted [B] int32 in [0, G]; stays on the device (reading it back
+ *                 is the caller's synchronisation point).
+ * Row j of a request uses the request's parameters and, as penalty history, the
+ * request history followed by draft tokens 0 .. j-1. Greedy requests (T = 0)
+ * accept on exact match with the greedy token; others accept draft j with
+ * probability min(1, p/q) (u from domain 1 at position + j), on rejection
+ * resample from the normalised max(0, p - q) in token-id order (domain 2), and
+ * after full acceptance draw the bonus token as ss_sample would at position + G.
+ * Launches two kernels (the residual pass only does work for rejected rows). */
+ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtype,
+                         int64_t row_stride, const float* draft_probs, int64_t draft_stride,
+                         const int32_t* draft_tokens, int32_t B, int32_t G,
+                         const ss_params* params, int32_t* out_tokens,
+                         int32_t* out_num_accepted, void* stream);
+
+/* ss_lmhead_sample -- fused LM-head GEMM + Gumbel-max sampling.
+ *   hidden        [B, K] bfloat16 bits (row-major), 16-byte aligned.
+ *   weight        [V, K] bfloat16 bits (row-major), 16-byte aligned.
+ *   B             1 .. min(max_batch, 64); K = hidden_size of the handle.
+ *   temperature   [B] float32 (>= 0; 0 = argmax of the logits, no noise).
+ *   request_ids, positions  [B] int32 Philox counter words (NULL: row index / 0).
+ *   out_tokens    [B] int32.
+ *   debug_logits  NULL, or [B, V] float32 to receive the unscaled logits.
+ * Token = lowest v attaining max_v (z[b,v] / T_b + g(Philox(seed; request,
+ * position, v >> 2, domain 3)[v & 3])), g = -ln(-ln U), U = 1 - (w + 0.5) 2^-32.
+ * Per 256-column vocabulary tile the kernel keeps only a (max, argmax) pair per
+ * row; the last workgroup reduces the pairs. */
+ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t* weight,
+                           int32_t B, const float* temperature, const int32_t* request_ids,
+                           const int32_t* positions, uint64_t seed, int32_t* out_tokens,
+                           float* debug_logits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_SAMPLER_H */

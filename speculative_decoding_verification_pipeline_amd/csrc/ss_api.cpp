@@ -1,0 +1,274 @@
+// Host side of the C ABI: handle lifetime, workspace, argument validation and
+// kernel launches. Nothing here allocates or synchronises after create.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "ss_device.h"
+#include "ss_internal.h"
+
+struct ss_sampler {
+    ss_sampler_config cfg;
+    int n_tiles;       // 8192-entry tiles per row
+    int n_vtiles;      // 256-column LM-head tiles
+    int max_rows;      // rows of the row kernels (verification: B * (G + 1))
+    void* ws_base;
+    int64_t ws_bytes;
+    ss::Workspace ws;
+    float2* lm_partials;
+    uint32_t* lm_counter;
+};
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ss::ParamPtrs to_ptrs(const ss_params* p) {
+    ss::ParamPtrs q;
+    q.temperature = p->temperature;
+    q.top_k = p->top_k;
+    q.top_p = p->top_p;
+    q.min_p = p->min_p;
+    q.rep = p->repetition_penalty;
+    q.freq = p->frequency_penalty;
+    q.pres = p->presence_penalty;
+    q.hist_ids = p->history_ids;
+    q.hist_len = p->history_len;
+    q.hist_stride = p->history_stride;
+    q.bias_ids = p->bias_ids;
+    q.bias_vals = p->bias_values;
+    q.bias_len = p->bias_len;
+    q.bias_stride = p->bias_stride;
+    q.mask = p->grammar_mask;
+    q.mask_stride = p->mask_stride;
+    q.request_ids = p->request_ids;
+    q.positions = p->positions;
+    q.seed = p->seed;
+    return q;
+}
+
+ss_status check_params(const ss_sampler* s, const ss_params* p) {
+    if (!p || !p->temperature) return SS_ERR_INVALID_ARG;
+    const int V = s->cfg.vocab_size;
+    if (p->history_len) {
+        if (!p->history_ids || p->history_stride < 0 || p->history_stride > 65000)
+            return SS_ERR_INVALID_ARG;
+    }
+    if (p->bias_len) {
+        if (!p->bias_ids || !p->bias_values || p->bias_stride < 0) return SS_ERR_INVALID_ARG;
+    }
+    if (p->grammar_mask) {
+        if (p->mask_stride < (V + 31) / 32) return SS_ERR_INVALID_ARG;
+    }
+    return SS_OK;
+}
+
+ss_status check_logits(const ss_sampler* s, const void* logits, ss_dtype dtype, int64_t row_stride) {
+    if (!logits) return SS_ERR_INVALID_ARG;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_INVALID_ARG;
+    if (row_stride < s->cfg.vocab_size) return SS_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(logits) & (dtype == SS_F32 ? 3u : 1u)) != 0)
+        return SS_ERR_INVALID_ARG;  // not even element-aligned
+    return SS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ss_status_string(ss_status st) {
+    switch (st) {
+        case SS_OK: return "ok";
+        case SS_ERR_INVALID_ARG: return "invalid argument";
+        case SS_ERR_UNSUPPORTED: return "unsupported argument";
+        case SS_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case SS_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
+    if (!cfg || !out) return SS_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (cfg->max_batch < 1 || cfg->vocab_size < 1 || cfg->vocab_size > ss::MAX_VOCAB ||
+        cfg->max_draft < 0 || cfg->max_draft > 16 || cfg->hidden_size < 0 ||
+        cfg->hidden_size % 64 != 0 || cfg->device < 0)
+        return SS_ERR_INVALID_ARG;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device >= ndev) return SS_ERR_HIP;
+    if (hipSetDevice(cfg->device) != hipSuccess) return SS_ERR_HIP;
+
+    ss_sampler* s = new (std::nothrow) ss_sampler();
+    if (!s) return SS_ERR_OUT_OF_MEMORY;
+    s->cfg = *cfg;
+    const int V = cfg->vocab_size;
+    const int B = cfg->max_batch;
+    s->n_tiles = (V + ss::TILE - 1) / ss::TILE;
+    s->n_vtiles = (V + 255) / 256;
+    s->max_rows = B * (cfg->max_draft + 1);
+    const int64_t R = s->max_rows;
+    const int64_t nt = s->n_tiles;
+
+    // carve one allocation; counters first so a single memset clears them
+    int64_t off = 0;
+    auto take = [&off](int64_t bytes) {
+        const int64_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    const int64_t o_rowc = take(R * 4);
+    const int64_t o_reqc = take((int64_t)B * 4);
+    const int64_t o_resc = take((int64_t)B * 4);
+    const int64_t o_lmc = take(4);
+    const int64_t counters_end = off;
+    const int64_t o_stats = take(R * nt * (int64_t)sizeof(ss::TileStat));
+    const int64_t o_cand = take(R * nt * ss::CW * (int64_t)sizeof(float2));
+    const int64_t o_info = take(R * (int64_t)sizeof(ss::RowInfo));
+    const int64_t o_acc = take(R * 4);
+    const int64_t o_resrow = take((int64_t)B * 4);
+    const int64_t o_restile = take((int64_t)B * nt * (int64_t)sizeof(double2));
+    const int64_t o_scratch = take(R * (int64_t)V * 4);
+    const int64_t o_lmpart = cfg->hidden_size > 0 ? take(64 * (int64_t)s->n_vtiles * sizeof(float2)) : 0;
+    s->ws_bytes = off;
+    if (hipMalloc(&s->ws_base, (size_t)off) != hipSuccess) {
+        (void)hipGetLastError();
+        delete s;
+        return SS_ERR_OUT_OF_MEMORY;
+    }
+    if (hipMemset(s->ws_base, 0, (size_t)counters_end) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(s->ws_base);
+        delete s;
+        return SS_ERR_HIP;
+    }
+    char* b = static_cast<char*>(s->ws_base);
+    ss::Workspace& w = s->ws;
+    w.row_counter = reinterpret_cast<uint32_t*>(b + o_rowc);
+    w.req_counter = reinterpret_cast<uint32_t*>(b + o_reqc);
+    w.resid_counter = reinterpret_cast<uint32_t*>(b + o_resc);
+    w.stats = reinterpret_cast<ss::TileStat*>(b + o_stats);
+    w.cand = reinterpret_cast<float2*>(b + o_cand);
+    w.rowinfo = reinterpret_cast<ss::RowInfo*>(b + o_info);
+    w.row_accept = reinterpret_cast<int32_t*>(b + o_acc);
+    w.resid_row = reinterpret_cast<int32_t*>(b + o_resrow);
+    w.resid_tile = reinterpret_cast<double2*>(b + o_restile);
+    w.scratch_z = reinterpret_cast<float*>(b + o_scratch);
+    w.n_tiles = s->n_tiles;
+    w.V = V;
+    s->lm_counter = reinterpret_cast<uint32_t*>(b + o_lmc);
+    s->lm_partials = cfg->hidden_size > 0 ? reinterpret_cast<float2*>(b + o_lmpart) : nullptr;
+    *out = s;
+    return SS_OK;
+}
+
+void ss_sampler_destroy(ss_sampler* s) {
+    if (!s) return;
+    (void)hipSetDevice(s->cfg.device);
+    (void)hipFree(s->ws_base);
+    delete s;
+}
+
+int64_t ss_sampler_workspace_bytes(const ss_sampler* s) { return s ? s->ws_bytes : 0; }
+
+ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t row_stride,
+                    int32_t B, const ss_params* params, int32_t* out_tokens, const ss_debug* debug,
+                    void* stream) {
+    if (!s || B < 0 || B > s->cfg.max_batch) return SS_ERR_INVALID_ARG;
+    if (B == 0) return SS_OK;
+    if (!out_tokens) return SS_ERR_INVALID_ARG;
+    ss_status st = check_logits(s, logits, dtype, row_stride);
+    if (st != SS_OK) return st;
+    st = check_params(s, params);
+    if (st != SS_OK) return st;
+    if (debug && debug->topk_ids && debug->topk_stride < 1) return SS_ERR_INVALID_ARG;
+    ss::SampleArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.logits = logits;
+    a.row_stride = row_stride;
+    a.B = B;
+    a.V = s->cfg.vocab_size;
+    a.p = to_ptrs(params);
+    a.out_tokens = out_tokens;
+    if (debug) {
+        a.dbg_processed = debug->processed_logits;
+        a.dbg_topk = debug->topk_ids;
+        a.dbg_topk_stride = debug->topk_ids ? debug->topk_stride : 0;
+        a.dbg_kept = debug->kept_count;
+        a.dbg_probs = debug->probs;
+        a.dbg_path = debug->path;
+    }
+    a.ws = s->ws;
+    if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
+    return ss::launch_sample(a, dtype, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK
+                                                                                       : SS_ERR_HIP;
+}
+
+ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtype,
+                         int64_t row_stride, const float* draft_probs, int64_t draft_stride,
+                         const int32_t* draft_tokens, int32_t B, int32_t G,
+                         const ss_params* params, int32_t* out_tokens,
+                         int32_t* out_num_accepted, void* stream) {
+    if (!s || B < 0 || B > s->cfg.max_batch) return SS_ERR_INVALID_ARG;
+    if (G < 1 || G > s->cfg.max_draft) return SS_ERR_INVALID_ARG;
+    if (B == 0) return SS_OK;
+    if (!draft_probs || !draft_tokens || !out_tokens || !out_num_accepted) return SS_ERR_INVALID_ARG;
+    if (draft_stride < s->cfg.vocab_size) return SS_ERR_INVALID_ARG;
+    ss_status st = check_logits(s, target_logits, dtype, row_stride);
+    if (st != SS_OK) return st;
+    st = check_params(s, params);
+    if (st != SS_OK) return st;
+    ss::SpecArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.target = target_logits;
+    a.row_stride = row_stride;
+    a.draft_probs = draft_probs;
+    a.draft_stride = draft_stride;
+    a.draft_tokens = draft_tokens;
+    a.B = B;
+    a.G = G;
+    a.V = s->cfg.vocab_size;
+    a.p = to_ptrs(params);
+    a.out_tokens = out_tokens;
+    a.out_num_accepted = out_num_accepted;
+    a.ws = s->ws;
+    if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
+    return ss::launch_spec(a, dtype, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK
+                                                                                     : SS_ERR_HIP;
+}
+
+ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t* weight,
+                           int32_t B, const float* temperature, const int32_t* request_ids,
+                           const int32_t* positions, uint64_t seed, int32_t* out_tokens,
+                           float* debug_logits, void* stream) {
+    if (!s || s->cfg.hidden_size <= 0) return SS_ERR_INVALID_ARG;
+    if (B < 1 || B > s->cfg.max_batch || B > 64) return SS_ERR_INVALID_ARG;
+    if (!hidden || !weight || !temperature || !out_tokens) return SS_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(weight)) return SS_ERR_UNSUPPORTED;
+    ss::LmheadArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.hidden = hidden;
+    a.weight = weight;
+    a.B = B;
+    a.K = s->cfg.hidden_size;
+    a.V = s->cfg.vocab_size;
+    a.temperature = temperature;
+    a.request_ids = request_ids;
+    a.positions = positions;
+    a.seed = seed;
+    a.out_tokens = out_tokens;
+    a.debug_logits = debug_logits;
+    a.partials = s->lm_partials;
+    a.counter = s->lm_counter;
+    a.n_vtiles = s->n_vtiles;
+    if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
+    return ss::launch_lmhead(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK
+                                                                                : SS_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Internal structures shared by the host side of the library and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ss_sampler.h"
+
+namespace ss {
+
+// Stage-1 summary of one 8192-entry vocabulary tile of one row.
+struct TileStat {
+    float m;        // max processed logit in the tile (-inf if none finite)
+    int argmax;     // lowest id attaining m (greedy rows), else -1
+    double s;       // sum of exp((x' - m) / T) over the tile (T > 0 rows)
+    float beta;     // largest processed logit NOT among the candidates (-inf: all are)
+    int ncand;      // candidates written for the tile
+    int nfinite;    // finite processed logits in the tile
+    int pad;
+};
+static_assert(sizeof(TileStat) == 32, "TileStat layout");
+
+// What the row finaliser knows about one row's filtered distribution.
+// kept(v) <=> key64(z_v, v) >= kappa and (min_p <= 0 or exp(z_v - zmax) >= min_p),
+// pi(v) = kept(v) ? exp(z_v - zmax) / W : 0.
+struct RowInfo {
+    unsigned long long kappa;
+    double W;
+    float zmax;
+    float min_p;
+    int n_kept;
+    int token;      // sampled token (ss_sample and the bonus row), greedy token for T = 0
+    int argmax;     // lowest id among the maxima of x'
+    int path;       // 0 tile candidates, 1 whole-row fallback
+    int pad[2];
+};
+static_assert(sizeof(RowInfo) == 48, "RowInfo layout");
+
+// Per-row view of the caller's parameters, as device pointers (host-built).
+struct ParamPtrs {
+    const float* temperature;
+    const int32_t* top_k;
+    const float* top_p;
+    const float* min_p;
+    const float* rep;
+    const float* freq;
+    const float* pres;
+    const int32_t* hist_ids;
+    const int32_t* hist_len;
+    int32_t hist_stride;
+    const int32_t* bias_ids;
+    const float* bias_vals;
+    const int32_t* bias_len;
+    int32_t bias_stride;
+    const uint32_t* mask;
+    int32_t mask_stride;
+    const int32_t* request_ids;
+    const int32_t* positions;
+    uint64_t seed;
+};
+
+struct Workspace {
+    uint32_t* row_counter;   // [max_rows], zero between calls
+    uint32_t* req_counter;   // [max_batch], zero between calls
+    TileStat* stats;         // [max_rows * n_tiles]
+    float2* cand;            // [max_rows * n_tiles * CW]  (x', id bits)
+    RowInfo* rowinfo;        // [max_rows]
+    int32_t* row_accept;     // [max_rows]: spec decision per draft row
+    int32_t* resid_row;      // [max_batch]: position awaiting a residual draw, or -1
+    double2* resid_tile;     // [max_batch * n_tiles]: residual / target mass per tile
+    uint32_t* resid_counter; // [max_batch]
+    float* scratch_z;        // [max_rows * V] fallback rows
+    int n_tiles;
+    int V;
+};
+
+struct SampleArgs {
+    const void* logits;
+    int64_t row_stride;
+    int B;
+    int V;
+    ParamPtrs p;
+    int32_t* out_tokens;
+    float* dbg_processed;
+    int32_t* dbg_topk;
+    int32_t dbg_topk_stride;
+    int32_t* dbg_kept;
+    float* dbg_probs;
+    int32_t* dbg_path;
+    Workspace ws;
+};
+
+struct SpecArgs {
+    const void* target;
+    int64_t row_stride;
+    const float* draft_probs;
+    int64_t draft_stride;
+    const int32_t* draft_tokens;
+    int B;
+    int G;
+    int V;
+    ParamPtrs p;
+    int32_t* out_tokens;
+    int32_t* out_num_accepted;
+    Workspace ws;
+};
+
+struct LmheadArgs {
+    const uint16_t* hidden;
+    const uint16_t* weight;
+    int B;
+    int K;
+    int V;
+    const float* temperature;
+    const int32_t* request_ids;
+    const int32_t* positions;
+    uint64_t seed;
+    int32_t* out_tokens;
+    float* debug_logits;
+    float2* partials;        // [64 * n_vtiles] (score, id bits)
+    uint32_t* counter;       // [1], zero between calls
+    int n_vtiles;
+};
+
+hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st);
+hipError_t launch_spec(const SpecArgs& a, ss_dtype dt, hipStream_t st);
+hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st);
+
+}  // namespace ss

@@ -1,0 +1,190 @@
+"""GPU parity of ss_sample against the oracle (through the C ABI).
+
+Workloads: the low-entropy (B=4, V=32000 f32), heterogeneous (B=64, V=128256
+f32, penalties + bias + mixed filters) and grammar (B=256, V=152064 bf16 + mask)
+configurations at full size, each over >= 10^4 draws (seeds swept), plus ragged
+and degenerate cases that exercise the exact whole-row fallback."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import philox
+from oracle import pipeline as P
+from speculative_decoding_verification_pipeline_amd import workloads as W
+from tests.gpu_support import (Tally, compare_debug, device, log, logits_tensor, oracle_filtered,
+                               sampling_params)
+
+pytestmark = pytest.mark.gpu
+
+
+def make_sampler(B, V, **kw):
+    from speculative_decoding_verification_pipeline_amd.sampler import Sampler
+    return Sampler(B, V, device=0, **kw)
+
+
+def run_debug(s, w, seed=None):
+    from speculative_decoding_verification_pipeline_amd.sampler import Debug
+    dev = device()
+    x = logits_tensor(w, dev)
+    prm = sampling_params(w, dev, seed=seed)
+    dbg = Debug.full(w.B, w.V, dev)
+    toks = s.sample(x, prm, debug=dbg)
+    torch.cuda.synchronize()
+    return toks, dbg
+
+
+def seed_sweep(s, w, filts, seeds, tally):
+    dev = device()
+    x = logits_tensor(w, dev)
+    outs = []
+    for sd in seeds:
+        prm = sampling_params(w, dev, seed=sd)
+        outs.append(s.sample(x, prm))
+    torch.cuda.synchronize()
+    for sd, t in zip(seeds, outs):
+        t = t.cpu().numpy()
+        for b in range(w.B):
+            u = philox.uniform(sd, int(w.request_ids[b]), int(w.positions[b]), 0, philox.SAMPLE)
+            r = P.draw(filts[b], u)
+            tally.add(int(t[b]) == r.token, r.flagged, (sd, b, int(t[b]), r.token))
+
+
+@pytest.mark.parametrize("name,n_seeds", [("low_entropy", 2500), ("heterogeneous", 160),
+                                          ("grammar", 40)])
+def test_config_parity(name, n_seeds):
+    w = getattr(W, name)()
+    log(f"[{name}] B={w.B} V={w.V} dtype={w.dtype}")
+    xs, filts = oracle_filtered(w)
+    s = make_sampler(w.B, w.V)
+    tally = Tally(name)
+    toks, dbg = run_debug(s, w)
+    compare_debug(w, xs, filts, toks, dbg, w.seed, tally)
+    paths = dbg.path.cpu().numpy()
+    log(f"[{name}] fallback rows: {int((paths == 1).sum())}/{w.B}")
+    seed_sweep(s, w, filts, range(1, n_seeds + 1), tally)
+    tally.check()
+
+
+def random_workload(rng, B, V, dtype="f32", entropy="mixed", mask=False, extras=True):
+    x = np.empty((B, V), np.float32)
+    for b in range(B):
+        kind = entropy if entropy != "mixed" else rng.choice(["zipf", "normal", "flat"])
+        if kind == "zipf":
+            x[b] = W.zipf_rows(rng, 1, V)[0]
+        elif kind == "normal":
+            x[b] = rng.standard_normal(V).astype(np.float32) * rng.uniform(0.5, 3.0)
+        else:
+            x[b] = np.round(rng.standard_normal(V) * 2).astype(np.float32)  # heavy ties
+    logits = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    T = rng.choice(np.array([0.0, 0.5, 1.0, 1.3], np.float32), B)
+    top_k = rng.choice(np.array([0, 1, 7, 50, 1000, 1024, V + 3], np.int32), B)
+    top_p = rng.choice(np.array([1.0, 0.9, 0.3, 1e-6], np.float32), B)
+    min_p = rng.choice(np.array([0.0, 0.05, 0.5], np.float32), B)
+    kw = {}
+    if extras:
+        H = 64
+        kw = dict(rep=rng.uniform(0.8, 1.5, B).astype(np.float32),
+                  freq=rng.uniform(0, 0.5, B).astype(np.float32),
+                  pres=rng.uniform(0, 0.5, B).astype(np.float32),
+                  hist=rng.integers(-3, V + 3, (B, H)).astype(np.int32),
+                  bias_ids=rng.integers(-2, V + 2, (B, 6)).astype(np.int32),
+                  bias_vals=rng.uniform(-5, 5, (B, 6)).astype(np.float32))
+        kw["bias_ids"][:, 1] = kw["bias_ids"][:, 0]  # duplicate ids accumulate in order
+    if mask:
+        allowed = rng.random((B, V)) < rng.uniform(0.001, 0.9, (B, 1))
+        allowed[0] = False  # an all-masked row
+        if B > 1:
+            allowed[1] = False
+            allowed[1, rng.integers(0, V)] = True  # a single allowed token
+        kw["mask"] = W.pack_mask(allowed)
+    return W.SampleWorkload("random", logits, dtype, T, top_k, top_p, min_p,
+                            request_ids=rng.integers(0, 1 << 30, B).astype(np.int32),
+                            positions=rng.integers(0, 1 << 20, B).astype(np.int32),
+                            seed=int(rng.integers(0, 1 << 62)), **kw)
+
+
+@pytest.mark.parametrize("V,dtype,mask,entropy", [
+    (1, "f32", False, "normal"), (37, "f32", True, "mixed"), (1000, "bf16", True, "mixed"),
+    (8191, "f32", False, "mixed"), (8193, "bf16", False, "flat"), (20001, "f32", True, "mixed"),
+    (32000, "f32", False, "normal"), (50000, "bf16", True, "zipf")])
+def test_ragged_and_degenerate(V, dtype, mask, entropy):
+    rng = np.random.default_rng(V * 7 + len(dtype))
+    B = 6
+    w = random_workload(rng, B, V, dtype, entropy, mask)
+    log(f"[ragged] V={V} {dtype} mask={mask} {entropy}")
+    xs, filts = oracle_filtered(w)
+    s = make_sampler(B, V)
+    tally = Tally(f"ragged V={V}")
+    for sd in (w.seed, w.seed + 1, 12345):
+        toks, dbg = run_debug(s, w, seed=sd)
+        compare_debug(w, xs, filts, toks, dbg, sd, tally)
+    tally.check()
+
+
+def test_high_entropy_rows_take_the_exact_fallback():
+    rng = np.random.default_rng(5)
+    B, V = 4, 128256
+    x = rng.standard_normal((B, V)).astype(np.float32)
+    w = W.SampleWorkload("highent", x, "f32", np.ones(B, np.float32),
+                         np.array([0, 1024, 5000, 0], np.int32),
+                         np.array([1.0, 1.0, 0.95, 0.5], np.float32),
+                         np.zeros(B, np.float32), request_ids=np.arange(B, dtype=np.int32),
+                         positions=np.zeros(B, np.int32), seed=3)
+    xs, filts = oracle_filtered(w)
+    s = make_sampler(B, V)
+    tally = Tally("high-entropy")
+    toks, dbg = run_debug(s, w)
+    compare_debug(w, xs, filts, toks, dbg, w.seed, tally)
+    paths = dbg.path.cpu().numpy()
+    log(f"[high-entropy] paths {paths.tolist()}")
+    # top_k = 5000 and top_p = 0.5 over N(0,1) logits reach far past any tile's candidates
+    assert paths[2] == 1 and paths[3] == 1
+    seed_sweep(s, w, filts, range(10, 60), tally)
+    tally.check()
+
+
+def test_empty_batch_is_a_noop():
+    s = make_sampler(4, 100)
+    dev = device()
+    x = torch.zeros(0, 100, device=dev)
+    out = torch.full((1,), 7, dtype=torch.int32, device=dev)
+    from speculative_decoding_verification_pipeline_amd.sampler import SamplingParams
+    prm = SamplingParams(temperature=torch.ones(1, device=dev))
+    s.sample(x, prm, out=out[:0])
+    torch.cuda.synchronize()
+    assert int(out[0]) == 7
+
+
+def test_graph_replay_with_changed_parameters():
+    w = W.heterogeneous(B=16, V=50000)
+    dev = device()
+    s = make_sampler(w.B, w.V)
+    x = logits_tensor(w, dev)
+    prm = sampling_params(w, dev)
+    out = torch.empty(w.B, dtype=torch.int32, device=dev)
+    s.sample(x, prm, out=out)  # warm up outside the graph
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s.sample(x, prm, out=out)
+    tally = Tally("graph")
+    rng = np.random.default_rng(9)
+    for rep in range(6):
+        T = rng.choice(np.array([0.0, 0.7, 1.0], np.float32), w.B)
+        pos = rng.integers(0, 1000, w.B).astype(np.int32)
+        prm.temperature.copy_(torch.from_numpy(T))
+        prm.positions.copy_(torch.from_numpy(pos))
+        w.temperature = T
+        w.positions = pos
+        g.replay()
+        torch.cuda.synchronize()
+        eager = s.sample(x, prm)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got, eager.cpu().numpy())
+        _, filts = oracle_filtered(w)
+        for b in range(w.B):
+            u = philox.uniform(w.seed, int(w.request_ids[b]), int(pos[b]), 0, philox.SAMPLE)
+            r = P.draw(filts[b], u)
+            tally.add(int(got[b]) == r.token, r.flagged, (rep, b))
+    tally.check()

@@ -1,0 +1,118 @@
+"""GPU parity of ss_spec_verify against the oracle (through the C ABI).
+
+The speculative configuration (32 requests, linear draft of 4, V=128256 f32,
+half greedy) at full size over several positions, and small vocabularies over
+many positions with penalties, bias and per-position masks (which exercise the
+draft-prefix history and the residual pass)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pipeline as P
+from oracle import spec as S
+from speculative_decoding_verification_pipeline_amd import workloads as W
+from tests.gpu_support import Tally, device, log
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device(), dtype=dt)
+
+
+def run(s, sw, positions, extra=None):
+    from speculative_decoding_verification_pipeline_amd.sampler import SamplingParams
+    extra = extra or {}
+    B = sw.B
+    kw = {}
+    if "hist" in extra:
+        kw["history_ids"] = to_dev(extra["hist"], torch.int32)
+        kw["history_len"] = to_dev(np.full(B, extra["hist"].shape[1], np.int32), torch.int32)
+    if "bias_ids" in extra:
+        kw["bias_ids"] = to_dev(extra["bias_ids"], torch.int32)
+        kw["bias_values"] = to_dev(extra["bias_vals"], torch.float32)
+        kw["bias_len"] = to_dev(np.full(B, extra["bias_ids"].shape[1], np.int32), torch.int32)
+    for k in ("rep", "freq", "pres"):
+        if k in extra:
+            name = {"rep": "repetition_penalty", "freq": "frequency_penalty",
+                    "pres": "presence_penalty"}[k]
+            kw[name] = to_dev(extra[k], torch.float32)
+    if "mask" in extra:
+        kw["grammar_mask"] = to_dev(extra["mask"].view(np.int32), torch.int32)
+    prm = SamplingParams(temperature=to_dev(sw.temperature, torch.float32),
+                         top_k=to_dev(sw.top_k, torch.int32), top_p=to_dev(sw.top_p, torch.float32),
+                         min_p=to_dev(sw.min_p, torch.float32),
+                         request_ids=to_dev(sw.request_ids, torch.int32),
+                         positions=to_dev(positions, torch.int32), seed=sw.seed, **kw)
+    toks, nacc = s.spec_verify(to_dev(sw.target, torch.float32), to_dev(sw.draft_probs, torch.float32),
+                               to_dev(sw.draft_tokens, torch.int32), prm)
+    torch.cuda.synchronize()
+    return toks.cpu().numpy(), nacc.cpu().numpy()
+
+
+def oracle(sw, positions, extra=None):
+    extra = extra or {}
+    B = sw.B
+    prm = P.Params(temperature=sw.temperature, top_k=sw.top_k, top_p=sw.top_p, min_p=sw.min_p,
+                   rep=extra.get("rep"), freq=extra.get("freq"), pres=extra.get("pres"),
+                   hist=None if "hist" not in extra else list(extra["hist"]),
+                   bias_ids=None if "bias_ids" not in extra else list(extra["bias_ids"]),
+                   bias_vals=None if "bias_vals" not in extra else list(extra["bias_vals"]),
+                   mask=extra.get("mask"), request_ids=sw.request_ids, positions=positions,
+                   seed=sw.seed)
+    return S.verify_batch(sw.target, sw.draft_probs, sw.draft_tokens, prm)
+
+
+def compare(sw, positions, toks, nacc, tally, extra=None):
+    res = oracle(sw, positions, extra)
+    for b, r in enumerate(res):
+        ok = int(nacc[b]) == r.n_acc and np.array_equal(toks[b], r.tokens)
+        tally.add(ok, r.flagged, (b, toks[b].tolist(), r.tokens.tolist(), int(nacc[b]), r.n_acc))
+        emitted = int(np.count_nonzero(toks[b] >= 0))
+        assert emitted <= sw.G + 1
+
+
+def test_speculative_config_parity():
+    from speculative_decoding_verification_pipeline_amd.sampler import Sampler
+    sw = W.speculative()
+    log(f"[spec] B={sw.B} G={sw.G} V={sw.V}")
+    s = Sampler(sw.B, sw.V, max_draft=sw.G, device=0)
+    tally = Tally("speculative")
+    accepted = []
+    for p in range(6):
+        pos = np.full(sw.B, 100 * p, np.int32)
+        toks, nacc = run(s, sw, pos)
+        compare(sw, pos, toks, nacc, tally)
+        accepted.append(nacc)
+    tally.check()
+    log(f"[spec] mean accepted {np.mean(accepted):.3f}")
+
+
+@pytest.mark.parametrize("V,G,with_extras", [(64, 3, False), (200, 2, True), (9000, 4, True)])
+def test_small_vocab_many_positions(V, G, with_extras):
+    from speculative_decoding_verification_pipeline_amd.sampler import Sampler
+    rng = np.random.default_rng(V + G)
+    B = 16
+    sw = W.speculative(B=B, G=G, V=V, seed=V, draft_seed=V + 1)
+    sw.top_k = rng.choice(np.array([0, 5, V + 1], np.int32), B)
+    sw.top_p = rng.choice(np.array([1.0, 0.9], np.float32), B)
+    sw.min_p = rng.choice(np.array([0.0, 0.02], np.float32), B)
+    sw.temperature = rng.choice(np.array([0.0, 0.8, 1.0, 1.5], np.float32), B)
+    sw.request_ids = rng.integers(0, 1 << 20, B).astype(np.int32)
+    extra = None
+    if with_extras:
+        allowed = rng.random((B, G + 1, V)) < 0.7
+        allowed[..., :3] = True
+        extra = dict(hist=rng.integers(0, V, (B, 10)).astype(np.int32),
+                     bias_ids=rng.integers(0, V, (B, 3)).astype(np.int32),
+                     bias_vals=rng.uniform(-2, 2, (B, 3)).astype(np.float32),
+                     rep=np.full(B, 1.2, np.float32), freq=np.full(B, 0.3, np.float32),
+                     pres=np.full(B, 0.2, np.float32), mask=W.pack_mask(allowed))
+    s = Sampler(B, V, max_draft=G, device=0)
+    tally = Tally(f"spec V={V}")
+    n_pos = 40 if V < 1000 else 10
+    for p in range(n_pos):
+        pos = rng.integers(0, 1 << 16, B).astype(np.int32)
+        toks, nacc = run(s, sw, pos, extra)
+        compare(sw, pos, toks, nacc, tally, extra)
+    tally.check()
