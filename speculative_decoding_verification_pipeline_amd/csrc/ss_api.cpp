@@ -18,7 +18,6 @@ struct ss_sampler {
     int64_t ws_bytes;
     ss::Workspace ws;
     float2* lm_partials;
-    uint32_t* lm_counter;
 };
 
 namespace {
@@ -115,23 +114,17 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     const int64_t R = s->max_rows;
     const int64_t nt = s->n_tiles;
 
-    // carve one allocation; counters first so a single memset clears them
+    // carve one allocation; nothing in it needs clearing between calls
     int64_t off = 0;
     auto take = [&off](int64_t bytes) {
         const int64_t o = off;
         off = align_up(off + bytes);
         return o;
     };
-    const int64_t o_rowc = take(R * 4);
-    const int64_t o_reqc = take((int64_t)B * 4);
-    const int64_t o_resc = take((int64_t)B * 4);
-    const int64_t o_lmc = take(4);
-    const int64_t counters_end = off;
     const int64_t o_stats = take(R * nt * (int64_t)sizeof(ss::TileStat));
     const int64_t o_cand = take(R * nt * ss::CW * (int64_t)sizeof(float2));
     const int64_t o_info = take(R * (int64_t)sizeof(ss::RowInfo));
     const int64_t o_acc = take(R * 4);
-    const int64_t o_resrow = take((int64_t)B * 4);
     const int64_t o_restile = take((int64_t)B * nt * (int64_t)sizeof(double2));
     const int64_t o_scratch = take(R * (int64_t)V * 4);
     const int64_t o_lmpart = cfg->hidden_size > 0 ? take(64 * (int64_t)s->n_vtiles * sizeof(float2)) : 0;
@@ -141,27 +134,16 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
         delete s;
         return SS_ERR_OUT_OF_MEMORY;
     }
-    if (hipMemset(s->ws_base, 0, (size_t)counters_end) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
-        (void)hipFree(s->ws_base);
-        delete s;
-        return SS_ERR_HIP;
-    }
     char* b = static_cast<char*>(s->ws_base);
     ss::Workspace& w = s->ws;
-    w.row_counter = reinterpret_cast<uint32_t*>(b + o_rowc);
-    w.req_counter = reinterpret_cast<uint32_t*>(b + o_reqc);
-    w.resid_counter = reinterpret_cast<uint32_t*>(b + o_resc);
     w.stats = reinterpret_cast<ss::TileStat*>(b + o_stats);
     w.cand = reinterpret_cast<float2*>(b + o_cand);
     w.rowinfo = reinterpret_cast<ss::RowInfo*>(b + o_info);
     w.row_accept = reinterpret_cast<int32_t*>(b + o_acc);
-    w.resid_row = reinterpret_cast<int32_t*>(b + o_resrow);
     w.resid_tile = reinterpret_cast<double2*>(b + o_restile);
     w.scratch_z = reinterpret_cast<float*>(b + o_scratch);
     w.n_tiles = s->n_tiles;
     w.V = V;
-    s->lm_counter = reinterpret_cast<uint32_t*>(b + o_lmc);
     s->lm_partials = cfg->hidden_size > 0 ? reinterpret_cast<float2*>(b + o_lmpart) : nullptr;
     *out = s;
     return SS_OK;
@@ -264,7 +246,6 @@ ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t
     a.out_tokens = out_tokens;
     a.debug_logits = debug_logits;
     a.partials = s->lm_partials;
-    a.counter = s->lm_counter;
     a.n_vtiles = s->n_vtiles;
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
     return ss::launch_lmhead(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK

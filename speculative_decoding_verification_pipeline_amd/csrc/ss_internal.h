@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/ss_sampler.h"
+#include "ss_sampler.h"
 
 namespace ss {
 
@@ -60,15 +60,11 @@ struct ParamPtrs {
 };
 
 struct Workspace {
-    uint32_t* row_counter;   // [max_rows], zero between calls
-    uint32_t* req_counter;   // [max_batch], zero between calls
     TileStat* stats;         // [max_rows * n_tiles]
     float2* cand;            // [max_rows * n_tiles * CW]  (x', id bits)
     RowInfo* rowinfo;        // [max_rows]
     int32_t* row_accept;     // [max_rows]: spec decision per draft row
-    int32_t* resid_row;      // [max_batch]: position awaiting a residual draw, or -1
     double2* resid_tile;     // [max_batch * n_tiles]: residual / target mass per tile
-    uint32_t* resid_counter; // [max_batch]
     float* scratch_z;        // [max_rows * V] fallback rows
     int n_tiles;
     int V;
@@ -118,7 +114,6 @@ struct LmheadArgs {
     int32_t* out_tokens;
     float* debug_logits;
     float2* partials;        // [64 * n_vtiles] (score, id bits)
-    uint32_t* counter;       // [1], zero between calls
     int n_vtiles;
 };
 

@@ -21,8 +21,8 @@
 //    double buffering) to keep the W stream in flight; W is read once from HBM
 //    and never written back, and the logits never leave registers.
 //  * Epilogue: s = z / T + g, per-row (max, lowest index) over the tile, written
-//    as one pair per row per tile; the last workgroup to finish (agent-scope
-//    counter) reduces the pairs of every row.
+//    as one pair per row per tile; a second, single-workgroup launch reduces
+//    the pairs of every row.
 #include <float.h>
 #include <limits.h>
 
@@ -81,7 +81,6 @@ __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
 __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
     __shared__ float s_score[LM_NT / WAVE][LM_MAXB];
     __shared__ int s_idx[LM_NT / WAVE][LM_MAXB];
-    __shared__ int s_last;
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
     const int wave = tid / WAVE;
@@ -184,19 +183,14 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
             }
         a.partials[(size_t)tid * a.n_vtiles + tile] = make_float2(bs, __int_as_float(bi));
     }
-    // cross-tile reduction by the last workgroup
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(a.counter, 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == (uint32_t)gridDim.x - 1;
-        if (s_last) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    // 4 threads per batch row, each over a strided quarter of the tiles
+}
+
+// Cross-tile reduction: 4 threads per batch row, each over a strided quarter of
+// the tiles, then the lowest index among equal maxima.
+__global__ __launch_bounds__(LM_NT) void k_lmhead_reduce(LmheadArgs a) {
+    __shared__ float s_score[LM_NT / LM_MAXB][LM_MAXB];
+    __shared__ int s_idx[LM_NT / LM_MAXB][LM_MAXB];
+    const int tid = threadIdx.x;
     const int j = tid & (LM_MAXB - 1);
     const int part = tid / LM_MAXB;
     float bs = -FLT_MAX;
@@ -230,6 +224,7 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
 
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_lmhead, dim3(a.n_vtiles), dim3(LM_NT), 0, st, a);
+    hipLaunchKernelGGL(k_lmhead_reduce, dim3(1), dim3(LM_NT), 0, st, a);
     return hipGetLastError();
 }
 

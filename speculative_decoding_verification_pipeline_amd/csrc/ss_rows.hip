@@ -11,21 +11,26 @@
 //  * One workgroup (256 threads, 4 wave64s) per 8192-entry vocabulary tile of a
 //    row; the grid is rows x tiles and depends only on (B, V), so one launch
 //    serves any mix of per-request parameters and can be graph-captured.
-//  * Stage 1 streams the tile once with 16-byte loads (float4 / 8 x bf16),
-//    applies penalties (multiplicities counted in LDS), bias and the packed
-//    mask in registers, and reduces: tile max, softmax partial sum, and a
+//  * Stage 1 streams the tile once with 16-byte global loads (float4 / 8 x
+//    bf16), applies penalties (multiplicities counted in LDS), bias and the
+//    packed mask in registers, and reduces: tile max, softmax partial sum, and a
 //    candidate list -- every entry above a threshold taken from the sorted
 //    per-thread maxima, so the list is always an exact prefix of the tile in
-//    key order, capped at CW entries. Low-entropy rows leave only a handful of
-//    entries near the top of each tile, which keeps the lists short.
-//  * The last workgroup to finish a row (agent-scope release/acquire on a
-//    per-row counter, reset for the next launch) merges the tiles: the union of
-//    candidates above the highest tile threshold is an exact prefix of the
-//    whole row; it is sorted in LDS and top-k / top-p / min-p and the
-//    inverse-CDF draw are resolved on it with binary64 prefix sums. When a
-//    request needs more of the row than the prefix holds, the same workgroup
-//    runs an exact whole-row fallback (radix selection by count or by mass over
-//    the row's recomputed z), so results never depend on the fast path's reach.
+//    key order. Its length is capped per request: greedy rows need none, a
+//    top-k row never more than k from one tile, other rows a short head (the
+//    low-entropy structure of LLM logits puts nearly all mass there).
+//  * A second launch, one workgroup per row, merges (the kernel boundary is the
+//    only synchronisation, so stage 1 carries no fences and only its own
+//    registers): candidates above the highest tile threshold form an exact
+//    prefix of the whole row (the pool, in LDS). Its first 256 entries are
+//    sorted across the workgroup with a bitonic network in registers; the
+//    top-k boundary deeper than that comes from a radix selection over the
+//    pool; top-p, min-p and the inverse-CDF draw are ballots over binary64
+//    prefix sums of the sorted head. Requests that reach
+//    past the head sort the whole pool ("deep" path), and requests that reach
+//    past the pool run an exact whole-row fallback (radix selection by count
+//    and by mass over the row's recomputed z). Results never depend on which
+//    path resolved them.
 #include <float.h>
 #include <limits.h>
 
@@ -38,6 +43,27 @@ namespace ss {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr double MASS_SCALE = 17592186044416.0;  // 2^44 fixed-point weights in the fallback
+constexpr int CAP_FREE = 32;   // candidates per tile for rows without top-k
+constexpr int CAP_MIN = 8;     // smallest cap for a top-k row
+
+// Loads through the global address space (16-byte vector loads, no flat path).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <class T>
+__device__ __forceinline__ T gld(const T* p) {
+    return *(const __attribute__((address_space(1))) T*)p;
+}
+template <>
+__device__ __forceinline__ uint4 gld<uint4>(const uint4* p) {
+    const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <>
+__device__ __forceinline__ float2 gld<float2>(const float2* p) {
+    const f32x2_t v = *(const __attribute__((address_space(1))) f32x2_t*)p;
+    return make_float2(v.x, v.y);
+}
 
 struct RowCtx {
     const void* logits;
@@ -98,8 +124,11 @@ struct SmemTile {
 };
 
 struct SmemPool {
-    float z[POOL];
+    float z[POOL];            // trusted candidates (unsorted; sorted by the deep path)
     int id[POOL];
+    float hz[NT];             // head gather / sort exchange
+    int hid[NT];
+    uint32_t hc[256];         // radix histogram over the pool
     TileStat st[MAX_TILES];
 };
 
@@ -117,11 +146,14 @@ union SmemU {
 struct SmemS {
     RedScratch red;
     int npool;
-    int is_last;
+    int nhead;
     int sel;
     int take_last;
+    int cnt;
     unsigned long long rem;
-    int flag;
+    unsigned long long key;
+    float fz;
+    int fid;
 };
 
 // ---------------------------------------------------------------------------
@@ -142,46 +174,53 @@ __device__ __forceinline__ int slot_id(int tb, int s) {
 
 template <int DT>
 __device__ __forceinline__ float read_logit(const void* row, int id) {
-    if (DT == SS_F32) return ((const float*)row)[id];
-    const uint32_t b = ((const uint16_t*)row)[id];
+    if (DT == SS_F32) return gld((const float*)row + id);
+    const uint32_t b = gld((const uint16_t*)row + id);
     return __uint_as_float(b << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_group(const uint4 q, float* out) {
+    if constexpr (DT == SS_F32) {
+        out[0] = __uint_as_float(q.x);
+        out[1] = __uint_as_float(q.y);
+        out[2] = __uint_as_float(q.z);
+        out[3] = __uint_as_float(q.w);
+    } else {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            out[2 * k] = __uint_as_float(w[k] << 16);
+            out[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    }
 }
 
 template <int DT>
 __device__ __forceinline__ void load_tile(const RowCtx& c, int tb, float v[EPT]) {
     using L = Lay<DT>;
-    // 16-byte loads need a 16-byte aligned row; other rows take element loads
-    const bool vec = ((uintptr_t)c.logits & 15u) == 0;
+    constexpr int ES = DT == SS_F32 ? 4 : 2;
+    const char* row = (const char*)c.logits;
+    // 16-byte loads need a 16-byte aligned row; a full tile needs no bounds checks
+    const bool vec = ((uintptr_t)row & 15u) == 0;
+    if (vec && tb + TILE <= c.V) {
+        uint4 q[L::NG];
+#pragma unroll
+        for (int g = 0; g < L::NG; ++g)
+            q[g] = gld((const uint4*)(row + (size_t)(tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC) * ES));
+#pragma unroll
+        for (int g = 0; g < L::NG; ++g) unpack_group<DT>(q[g], v + g * L::VEC);
+        return;
+    }
 #pragma unroll
     for (int g = 0; g < L::NG; ++g) {
         const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
-        if (DT == SS_F32) {
-            const float* p = (const float*)c.logits + e0;
-            if (vec && e0 + 4 <= c.V) {
-                const float4 q = *(const float4*)p;
-                v[g * 4 + 0] = q.x;
-                v[g * 4 + 1] = q.y;
-                v[g * 4 + 2] = q.z;
-                v[g * 4 + 3] = q.w;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[g * 4 + j] = (e0 + j < c.V) ? p[j] : NEG_INF;
-            }
+        if (vec && e0 + L::VEC <= c.V) {
+            unpack_group<DT>(gld((const uint4*)(row + (size_t)e0 * ES)), v + g * L::VEC);
         } else {
-            const uint16_t* p = (const uint16_t*)c.logits + e0;
-            if (vec && e0 + 8 <= c.V) {
-                const uint4 q = *(const uint4*)p;
-                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    v[g * 8 + 2 * k] = __uint_as_float(w[k] << 16);
-                    v[g * 8 + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    v[g * 8 + j] = (e0 + j < c.V) ? __uint_as_float((uint32_t)p[j] << 16) : NEG_INF;
-            }
+            for (int j = 0; j < L::VEC; ++j)
+                v[g * L::VEC + j] = (e0 + j < c.V) ? read_logit<DT>(row, e0 + j) : NEG_INF;
         }
     }
 }
@@ -198,13 +237,15 @@ __device__ __forceinline__ float process_entry(const RowCtx& c, int id, float x,
     }
     if (bias_hit) {
         for (int k = 0; k < c.bias_len; ++k)
-            if (c.bias_ids[k] == id) x = x + c.bias_vals[k];
+            if (gld(c.bias_ids + k) == id) x = x + gld(c.bias_vals + k);
     }
     return allowed ? x : NEG_INF;
 }
 
 // Builds the tile's multiplicity counts and bias bitmap in LDS (two barriers).
-__device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& t) {
+// pre, if given, holds this thread's first two history ids, already loaded.
+__device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& t,
+                                             const int* pre = nullptr) {
     const int tid = threadIdx.x;
     const bool has_cnt = (c.hist_len + c.extra_len) > 0;
     if (has_cnt) {
@@ -215,15 +256,25 @@ __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& 
     if (c.bias_len > 0) t.bias[tid] = 0;
     __syncthreads();
     if (has_cnt) {
-        for (int i = tid; i < c.hist_len + c.extra_len; i += NT) {
-            const int id = i < c.hist_len ? c.hist[i] : c.extra[i - c.hist_len];
+        const int i0 = pre ? tid + 2 * NT : tid;
+        if (pre) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int id = pre[k];
+                const int l = id - tb;
+                if (id >= 0 && id < c.V && l >= 0 && l < TILE)
+                    atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
+            }
+        }
+        for (int i = i0; i < c.hist_len + c.extra_len; i += NT) {
+            const int id = i < c.hist_len ? gld(c.hist + i) : gld(c.extra + (i - c.hist_len));
             const int l = id - tb;
             if (id >= 0 && id < c.V && l >= 0 && l < TILE)
                 atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
         }
     }
     for (int i = tid; i < c.bias_len; i += NT) {
-        const int id = c.bias_ids[i];
+        const int id = gld(c.bias_ids + i);
         const int l = id - tb;
         if (id >= 0 && id < c.V && l >= 0 && l < TILE) atomicOr(&t.bias[l >> 5], 1u << (l & 31));
     }
@@ -235,6 +286,7 @@ __device__ __forceinline__ void process_tile(const RowCtx& c, int tb, float v[EP
     using L = Lay<DT>;
     const bool has_cnt = (c.hist_len + c.extra_len) > 0;
     const bool has_bias = c.bias_len > 0;
+    if (!has_cnt && !has_bias && !c.mask) return;
 #pragma unroll
     for (int g = 0; g < L::NG; ++g) {
         const int l0 = g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
@@ -257,7 +309,7 @@ __device__ __forceinline__ void process_tile(const RowCtx& c, int tb, float v[EP
             for (int k = 0; k < L::VEC / 2; ++k) cw[k] = 0;
         }
         const uint32_t bb = has_bias ? (t.bias[l0 >> 5] >> (l0 & 31)) : 0u;
-        const uint32_t mw = (c.mask && e0 < c.V) ? (c.mask[e0 >> 5] >> (e0 & 31)) : 0xFFFFFFFFu;
+        const uint32_t mw = (c.mask && e0 < c.V) ? (gld(c.mask + (e0 >> 5)) >> (e0 & 31)) : 0xFFFFFFFFu;
 #pragma unroll
         for (int j = 0; j < L::VEC; ++j) {
             const int id = e0 + j;
@@ -277,29 +329,50 @@ template <int DT>
 __device__ float single_entry(const RowCtx& c, int id, SmemS& sh) {
     int cnt = 0;
     for (int i = threadIdx.x; i < c.hist_len + c.extra_len; i += NT) {
-        const int h = i < c.hist_len ? c.hist[i] : c.extra[i - c.hist_len];
+        const int h = i < c.hist_len ? gld(c.hist + i) : gld(c.extra + (i - c.hist_len));
         cnt += (h == id);
     }
     cnt = block_sum_i(cnt, sh.red);
     bool hit = false;
-    for (int k = 0; k < c.bias_len; ++k) hit |= (c.bias_ids[k] == id);
-    const bool allowed = c.mask ? ((c.mask[id >> 5] >> (id & 31)) & 1u) : true;
+    for (int k = 0; k < c.bias_len; ++k) hit |= (gld(c.bias_ids + k) == id);
+    const bool allowed = c.mask ? ((gld(c.mask + (id >> 5)) >> (id & 31)) & 1u) : true;
     const float x = read_logit<DT>(c.logits, id);
     return process_entry(c, id, x, (uint32_t)cnt, hit, allowed);
+}
+
+// Candidate cap of one tile for this request: no tile can hold more than k of a
+// row's top-k; rows without top-k keep a short head.
+__device__ __forceinline__ int row_cap(const RowCtx& c) {
+    if (c.T == 0.0f) return 0;
+    if (c.top_k > 0 && c.top_k < c.V) return min(CW, max(c.top_k, CAP_MIN));
+    return CAP_FREE;
 }
 
 // ---------------------------------------------------------------------------
 // stage 1: one tile of one row
 
 template <int DT>
-__device__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace& ws, SmemU& su,
+__device__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace& ws, SmemTile& tt,
                             SmemS& sh, float* dbg_proc_row, float* dbg_probs_row) {
     const int tid = threadIdx.x;
     const int tb = tile * TILE;
     float v[EPT];
-    load_tile<DT>(c, tb, v);
-    build_tables(c, tb, su.t);
-    process_tile<DT>(c, tb, v, su.t);
+    if (c.hist_len + c.extra_len + c.bias_len > 0) {
+        // the row's history and bias lists are small and shared by all its
+        // tiles: fetch them first so the LDS tables build while the tile streams
+        int pre[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int i = (int)threadIdx.x + k * NT;
+            pre[k] = i < c.hist_len ? gld(c.hist + i)
+                     : (i < c.hist_len + c.extra_len ? gld(c.extra + (i - c.hist_len)) : -1);
+        }
+        load_tile<DT>(c, tb, v);
+        build_tables(c, tb, tt, pre);
+    } else {
+        load_tile<DT>(c, tb, v);
+    }
+    process_tile<DT>(c, tb, v, tt);
 
     if (dbg_proc_row || dbg_probs_row) {
 #pragma unroll
@@ -321,7 +394,8 @@ __device__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace&
     }
     TileStat st;
     st.pad = 0;
-    if (c.T == 0.0f) {
+    const int cap = row_cap(c);
+    if (cap == 0) {
         const float m = block_max(lm, sh.red);
         int am = INT_MAX;
         if (m > NEG_INF) {
@@ -338,26 +412,27 @@ __device__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace&
         st.ncand = 0;
         st.nfinite = nf;
     } else {
-        const float srt = block_sort_desc(lm, su.t.sorted);
-        su.t.sorted[tid] = srt;
+        const float srt = block_sort_desc(lm, tt.sorted);
+        tt.sorted[tid] = srt;
         __syncthreads();
-        const float m = su.t.sorted[0];
+        const float m = tt.sorted[0];
         nf = block_sum_i(nf, sh.red);
         float theta = NEG_INF;
         int ncand = nf;
-        if (nf > CW) {
-            int L = LTARGET;
+        if (nf > cap) {
+            const int step = max(1, cap / 8);
+            int L = cap - step;
             for (;;) {
-                theta = su.t.sorted[L];
+                theta = tt.sorted[L];
                 int cnt = 0;
 #pragma unroll
                 for (int s = 0; s < EPT; ++s) cnt += v[s] > theta;
                 cnt = block_sum_i(cnt, sh.red);
-                if (cnt <= CW) {
+                if (cnt <= cap) {
                     ncand = cnt;
                     break;
                 }
-                L = L > 16 ? L - 16 : 0;  // L = 0 puts theta at the tile max: no candidates
+                L = L > step ? L - step : 0;  // L = 0 puts theta at the tile max: no candidates
             }
         }
         double ssum = 0.0;
@@ -390,25 +465,6 @@ __device__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace&
         st.nfinite = nf;
     }
     if (tid == 0) ws.stats[(size_t)row * ws.n_tiles + tile] = st;
-}
-
-// Release this workgroup's stage-1 writes and count it in; true for the last
-// workgroup of the group (which then sees every other workgroup's writes and
-// leaves the counter at zero for the next launch or graph replay).
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, SmemS& sh) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        sh.is_last = (prev == expected - 1);
-        if (sh.is_last)
-            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    const bool last = sh.is_last != 0;
-    if (last) __threadfence();
-    return last;
 }
 
 // ---------------------------------------------------------------------------
@@ -555,16 +611,17 @@ __device__ void count_and_mass(const float* zr, int V, float zmax, Pred pred, in
 // Exact whole-row resolution: recompute z for the whole row into scratch, then
 // select by count (top-k) and by mass (top-p, the draw) with radix passes.
 template <int DT>
-__device__ void finalize_slow(const RowCtx& c, int row, const Workspace& ws, int n_tiles,
-                              const RowSummary& rs, float u, SmemU& su, SmemS& sh, RowInfo& info,
-                              const RowDbg& dbg) {
+__device__ __noinline__ void finalize_slow(const RowCtx& c, int row, const Workspace& ws,
+                                           int n_tiles, const RowSummary& rs, float u, SmemU& su,
+                                           SmemS& sh, RowInfo& info, const RowDbg& dbg) {
     const int tid = threadIdx.x;
     const int V = c.V;
     float* zr = ws.scratch_z + (size_t)row * V;
+    __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
         float v[EPT];
         load_tile<DT>(c, t * TILE, v);
-        build_tables(c, t * TILE, su.t);
+        if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, t * TILE, su.t);
         process_tile<DT>(c, t * TILE, v, su.t);
 #pragma unroll
         for (int s = 0; s < EPT; ++s) {
@@ -643,18 +700,133 @@ __device__ void finalize_slow(const RowCtx& c, int row, const Workspace& ws, int
     __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// pool helpers
+
+// Appends the lanes whose pred is true to an LDS list: one atomic per wave.
+__device__ __forceinline__ int wave_append(bool pred, int* counter) {
+    const unsigned long long m = __ballot(pred);
+    const int lane = threadIdx.x & (WAVE - 1);
+    int base = 0;
+    if (m) {
+        const int leader = __ffsll((long long)m) - 1;
+        if (lane == leader) base = atomicAdd(counter, __popcll(m));
+        base = __shfl(base, leader);
+    }
+    return base + __popcll(m & __lanemask_lt());
+}
+
+// Key of the rank-th (1-based) pool entry in key order: radix passes over the
+// 64-bit key (z then id), stopping as soon as the target's bucket is a single
+// entry.
+__device__ unsigned long long pool_select(const float* pz, const int* pid, int n, int rank,
+                                          uint32_t* hc, SmemS& sh) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    unsigned long long prefix = 0, pmask = 0;
+    int rem = rank;
+    for (int d = 7; d >= 0; --d) {
+        const int sft = d * 8;
+        if (tid < 256) hc[tid] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += NT) {
+            const unsigned long long k = key64(pz[i], pid[i]);
+            if ((k & pmask) == prefix) atomicAdd(&hc[(k >> sft) & 255ull], 1u);
+        }
+        __syncthreads();
+        if (tid < WAVE) {
+            // lane l holds buckets 255-4l .. 252-4l, i.e. descending key order
+            uint32_t cb[4];
+            int s = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                cb[j] = hc[255 - 4 * lane - j];
+                s += (int)cb[j];
+            }
+            const int inc = wave_incl_scan_i(s);
+            const int exc = inc - s;
+            const bool hit = exc < rem && rem <= inc;
+            if (hit) {
+                int r = rem - exc;
+                for (int j = 0; j < 4; ++j) {
+                    if (r <= (int)cb[j]) {
+                        sh.sel = 255 - 4 * lane - j;
+                        sh.cnt = (int)cb[j];
+                        sh.rem = (unsigned long long)r;
+                        break;
+                    }
+                    r -= (int)cb[j];
+                }
+            }
+        }
+        __syncthreads();
+        prefix |= (unsigned long long)sh.sel << sft;
+        pmask |= 255ull << sft;
+        rem = (int)sh.rem;
+        const int cnt = sh.cnt;
+        __syncthreads();
+        if (cnt == 1 || d == 0) {
+            if (d > 0) {
+                for (int i = tid; i < n; i += NT) {
+                    const unsigned long long k = key64(pz[i], pid[i]);
+                    if ((k & pmask) == prefix) sh.key = k;
+                }
+                __syncthreads();
+                prefix = sh.key;
+                __syncthreads();
+            }
+            return prefix;
+        }
+    }
+    return prefix;
+}
+
+// Sorts one (z, id) pair per thread into key order across the workgroup.
+__device__ __forceinline__ void block_sort_pairs(float& z, int& id, float* tz, int* ti) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 2; k <= NT; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            float oz;
+            int oi;
+            if (j >= WAVE) {
+                tz[tid] = z;
+                ti[tid] = id;
+                __syncthreads();
+                oz = tz[tid ^ j];
+                oi = ti[tid ^ j];
+                __syncthreads();
+            } else {
+                oz = __shfl_xor(z, j);
+                oi = __shfl_xor(id, j);
+            }
+            const bool desc = (tid & k) == 0;
+            const bool lower = (tid & j) == 0;
+            const bool mine_first = key_before(z, id, oz, oi);
+            const bool keep = (lower == desc) ? mine_first : !mine_first;
+            if (!keep) {
+                z = oz;
+                id = oi;
+            }
+        }
+    }
+}
+
 // Finds the first index i in [0, lim) of the sorted pool satisfying pred(i, excl,
-// incl, w), scanning each thread's chunk in order with binary64 prefix sums.
+// incl, w), scanning each thread's contiguous chunk with binary64 prefix sums.
 template <class Pred>
-__device__ int pool_first(int lim, int cs, const float* wl, double base, Pred pred, SmemS& sh) {
+__device__ int pool_first(int lim, int cs, const SmemPool& p, float zmax, double base, Pred pred,
+                          SmemS& sh) {
     int found = INT_MAX;
     double run = base;
     const int i0 = (int)threadIdx.x * cs;
     for (int k = 0; k < cs; ++k) {
         const int i = i0 + k;
         if (i >= lim) break;
-        const double w = (double)wl[k];
-        if (pred(i, run, run + w, wl[k])) {
+        const float wf = expf(p.z[i] - zmax);
+        const double w = (double)wf;
+        if (pred(i, run, run + w, wf)) {
             found = i;
             break;
         }
@@ -663,8 +835,114 @@ __device__ int pool_first(int lim, int cs, const float* wl, double base, Pred pr
     return block_min_i(found, sh.red);
 }
 
+__device__ __forceinline__ double pool_prefix_sum(int lim, int cs, const SmemPool& p, float zmax) {
+    double s = 0.0;
+    const int i0 = (int)threadIdx.x * cs;
+    for (int k = 0; k < cs; ++k) {
+        const int i = i0 + k;
+        if (i >= lim) break;
+        s += (double)expf(p.z[i] - zmax);
+    }
+    return s;
+}
+
+// The deep path: sort the whole pool (bitonic in LDS) and resolve on it.
+// Returns false if the request reaches past the pool (then the caller runs the
+// whole-row fallback).
+__device__ __noinline__ bool finalize_deep(const RowCtx& c, int n, const RowSummary& rs, float zmax,
+                                           float u, SmemPool& p, SmemS& sh, RowInfo& info,
+                                           const RowDbg& dbg) {
+    const int tid = threadIdx.x;
+    const int V = c.V;
+    int n_pad = 1;
+    while (n_pad < n) n_pad <<= 1;
+    for (int i = n + tid; i < n_pad; i += NT) {
+        p.z[i] = NEG_INF;
+        p.id[i] = INT_MAX;
+    }
+    __syncthreads();
+    for (int k = 2; k <= n_pad; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < n_pad; i += NT) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const float za = p.z[i], zb = p.z[ixj];
+                    const int ia = p.id[i], ib = p.id[ixj];
+                    const bool a_first = key_before(za, ia, zb, ib);
+                    const bool desc = (i & k) == 0;
+                    if (desc ? !a_first : a_first) {
+                        p.z[i] = zb;
+                        p.z[ixj] = za;
+                        p.id[i] = ib;
+                        p.id[ixj] = ia;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    const int cs = n_pad > NT ? n_pad / NT : 1;
+    double totw;
+    const double base = block_excl_scan_d(pool_prefix_sum(n, cs, p, zmax), sh.red, totw);
+    const int total = rs.nfinite;
+    const bool topk_on = c.top_k > 0 && c.top_k < V;
+    const int K_eff = topk_on ? min(c.top_k, total) : total;
+    const bool cut_k = topk_on && K_eff < total;
+    if ((cut_k && K_eff > n) || (dbg.topk && topk_on && !cut_k && total > n)) return false;
+    double WK = rs.W;
+    if (cut_k) WK = block_sum_d(pool_prefix_sum(K_eff, cs, p, zmax), sh.red);
+    int n_topp = cut_k ? K_eff : total;
+    if (c.top_p < 1.0f) {
+        const double thr = (double)c.top_p * WK;
+        const int f = pool_first(min(n, n_topp), cs, p, zmax, base,
+                                 [thr](int, double ex, double, float) { return ex >= thr; }, sh);
+        if (f != INT_MAX) n_topp = f;
+        else if (n_topp > n) return false;
+    }
+    int n_kept = n_topp;
+    if (c.min_p > 0.0f) {
+        const float mp = c.min_p;
+        const int f = pool_first(min(n, n_topp), cs, p, zmax, base,
+                                 [mp](int, double, double, float w) { return w < mp; }, sh);
+        if (f != INT_MAX) n_kept = f;
+        else if (n_topp > n) return false;
+    }
+    if (dbg.probs && n_kept > n) return false;
+    double Wk = rs.W;
+    if (n_kept < total) Wk = block_sum_d(pool_prefix_sum(n_kept, cs, p, zmax), sh.red);
+    const double tgt = (double)u * Wk;
+    const int f = pool_first(min(n, n_kept), cs, p, zmax, base,
+                             [tgt](int, double, double in, float) { return in > tgt; }, sh);
+    int token;
+    if (f != INT_MAX) token = p.id[f];
+    else if (n_kept <= n) token = p.id[n_kept - 1];
+    else return false;
+    if (tid == 0) {
+        info.kappa = n_kept < total ? key64(p.z[n_kept - 1], p.id[n_kept - 1]) : 0ull;
+        info.W = Wk;
+        info.zmax = zmax;
+        info.min_p = 0.0f;
+        info.n_kept = n_kept;
+        info.token = token;
+        info.argmax = -1;
+        info.path = 0;
+        if (dbg.kept) *dbg.kept = n_kept;
+        if (dbg.path) *dbg.path = 0;
+    }
+    if (dbg.probs)
+        for (int i = tid; i < n_kept; i += NT)
+            dbg.probs[p.id[i]] = (float)((double)expf(p.z[i] - zmax) / Wk);
+    if (dbg.topk) {
+        const int lim = cut_k ? K_eff : (topk_on ? total : 0);
+        for (int i = tid; i < dbg.topk_stride; i += NT)
+            dbg.topk[i] = (i < lim && i < n) ? p.id[i] : -1;
+    }
+    __syncthreads();
+    return true;
+}
+
 template <int DT>
-__device__ void finalize_row(const RowCtx& c, int row, const Workspace& ws, float u, SmemU& su,
+__device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Workspace& ws, float u, SmemU& su,
                              SmemS& sh, const RowDbg& dbg, RowInfo& info_out) {
     const int tid = threadIdx.x;
     const int n_tiles = ws.n_tiles;
@@ -676,10 +954,10 @@ __device__ void finalize_row(const RowCtx& c, int row, const Workspace& ws, floa
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int g = tid + k * NT;
-        cv[k] = g < n_tiles * CW ? cand[g] : make_float2(NEG_INF, 0.0f);
+        cv[k] = g < n_tiles * CW ? gld(cand + g) : make_float2(NEG_INF, 0.0f);
     }
     if (tid < n_tiles) su.p.st[tid] = ws.stats[(size_t)row * n_tiles + tid];
-    if (tid == 0) sh.npool = 0;
+    if (tid == 0) sh.nhead = 0;
     __syncthreads();
     const RowSummary rs = summarize_tiles(su.p.st, n_tiles, c.T);
 
@@ -707,156 +985,196 @@ __device__ void finalize_row(const RowCtx& c, int row, const Workspace& ws, floa
         info_out = info;
         return;
     }
-    // the union of candidates above the highest tile threshold is exact
+    // the union of candidates above the highest tile threshold is exact: gather
+    // it into LDS in slot order with one scan
     const float zmax = canon_zero(rs.m / c.T);
     const float zb = rs.beta > NEG_INF ? canon_zero(rs.beta / c.T) : NEG_INF;
+    uint32_t keepm = 0;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int g = tid + k * NT;
-        const int t = g / CW;
-        if (g < n_tiles * CW && (g % CW) < su.p.st[t].ncand) {
+        if (g < n_tiles * CW && (g % CW) < su.p.st[g / CW].ncand) {
             const float z = canon_zero(cv[k].x / c.T);
             if (z > zb) {
-                const int pos = atomicAdd(&sh.npool, 1);
-                su.p.z[pos] = z;
-                su.p.id[pos] = __float_as_int(cv[k].y);
+                keepm |= 1u << k;
+                cv[k].x = z;
             }
         }
     }
-    __syncthreads();
-    const int n = sh.npool;
-    int n_pad = 1;
-    while (n_pad < n) n_pad <<= 1;
-    for (int i = n + tid; i < n_pad; i += NT) {
-        su.p.z[i] = NEG_INF;
-        su.p.id[i] = INT_MAX;
-    }
-    __syncthreads();
-    // bitonic sort of the pool into key order (z descending, id ascending)
-    for (int k = 2; k <= n_pad; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < n_pad; i += NT) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const float za = su.p.z[i], zb2 = su.p.z[ixj];
-                    const int ia = su.p.id[i], ib = su.p.id[ixj];
-                    const bool a_first = key_before(za, ia, zb2, ib);
-                    const bool desc = (i & k) == 0;
-                    if (desc ? !a_first : a_first) {
-                        su.p.z[i] = zb2;
-                        su.p.z[ixj] = za;
-                        su.p.id[i] = ib;
-                        su.p.id[ixj] = ia;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-    // per-thread contiguous chunks, weights, binary64 exclusive prefix
-    const int cs = n_pad > NT ? n_pad / NT : 1;
-    float wl[POOL / NT];
-    double loc = 0.0;
+    int n;
+    {
+        int off = block_excl_scan_i(__popc(keepm), sh.red, n);
 #pragma unroll
-    for (int k = 0; k < POOL / NT; ++k) {
-        const int i = tid * cs + k;
-        wl[k] = (k < cs && i < n) ? expf(su.p.z[i] - zmax) : 0.0f;
-        loc += (double)wl[k];
+        for (int k = 0; k < PER; ++k) {
+            if (keepm & (1u << k)) {
+                su.p.z[off] = cv[k].x;
+                su.p.id[off] = __float_as_int(cv[k].y);
+                ++off;
+            }
+        }
     }
-    double totw;
-    const double base = block_excl_scan_d(loc, sh.red, totw);
-
+    __syncthreads();
     const int total = rs.nfinite;
     const bool topk_on = c.top_k > 0 && c.top_k < V;
     const int K_eff = topk_on ? min(c.top_k, total) : total;
     const bool cut_k = topk_on && K_eff < total;
-    // the debug top-k list needs the whole set when top-k keeps every finite entry
-    bool fallback = n == 0 || (cut_k && K_eff > n) || (dbg.topk && topk_on && !cut_k && total > n);
-    double WK = rs.W;
-    int n_topp = cut_k ? K_eff : total;
-    int n_kept = n_topp;
-    int token = -1;
+    bool slow = n == 0 || (cut_k && K_eff > n);
+    bool deep = false;
+    int n_kept = 0, token = -1;
     double Wk = rs.W;
-    if (!fallback && cut_k) {
-        double part = 0.0;
-#pragma unroll
-        for (int k = 0; k < POOL / NT; ++k)
-            if (tid * cs + k < K_eff) part += (double)wl[k];
-        WK = block_sum_d(part, sh.red);
-    }
-    if (!fallback && c.top_p < 1.0f) {
-        const double thr = (double)c.top_p * WK;
-        const int lim = min(n, n_topp);
-        const int f = pool_first(lim, cs, wl, base,
-                                 [thr](int, double ex, double, float) { return ex >= thr; }, sh);
-        if (f != INT_MAX) n_topp = f;
-        else if (n_topp > n) fallback = true;
-        n_kept = n_topp;
-    }
-    if (!fallback && c.min_p > 0.0f) {
-        const float mp = c.min_p;
-        const int lim = min(n, n_topp);
-        const int f = pool_first(lim, cs, wl, base,
-                                 [mp](int, double, double, float w) { return w < mp; }, sh);
-        if (f != INT_MAX) n_kept = f;
-        else if (n_topp > n) fallback = true;
-        else n_kept = n_topp;
-    }
-    if (!fallback && dbg.probs && n_kept > n) fallback = true;
-    if (!fallback) {
-        if (n_kept < total) {
-            double part = 0.0;
-#pragma unroll
-            for (int k = 0; k < POOL / NT; ++k)
-                if (tid * cs + k < n_kept) part += (double)wl[k];
-            Wk = block_sum_d(part, sh.red);
+    unsigned long long kappa = 0, kK = 0;
+    int nh = 0;
+    if (!slow) {
+        // head: the first min(n, 256) pool entries in key order, one per thread
+        unsigned long long khead = 0;
+        if (n > NT) khead = pool_select(su.p.z, su.p.id, n, NT, su.p.hc, sh);
+        for (int i0 = 0; i0 < n; i0 += NT) {
+            const int i = i0 + tid;
+            const bool in = i < n && key64(su.p.z[i], su.p.id[i]) >= khead;
+            const int pos = wave_append(in, &sh.nhead);
+            if (in) {
+                su.p.hz[pos] = su.p.z[i];
+                su.p.hid[pos] = su.p.id[i];
+            }
         }
-        const double tgt = (double)u * Wk;
-        const int lim = min(n, n_kept);
-        const int f = pool_first(lim, cs, wl, base,
-                                 [tgt](int, double, double in, float) { return in > tgt; }, sh);
-        if (f != INT_MAX) token = su.p.id[f];
-        else if (n_kept <= n) token = su.p.id[n_kept - 1];
-        else fallback = true;
-    }
-    if (fallback) {
         __syncthreads();
-        finalize_slow<DT>(c, row, ws, n_tiles, rs, u, su, sh, info, dbg);
+        nh = sh.nhead;
+        float hz = tid < nh ? su.p.hz[tid] : NEG_INF;
+        int hid = tid < nh ? su.p.hid[tid] : INT_MAX;
         __syncthreads();
-        info_out = info;
-        return;
+        block_sort_pairs(hz, hid, su.p.hz, su.p.hid);
+        const float w = tid < nh ? expf(hz - zmax) : 0.0f;
+        double toth;
+        const double excl = block_excl_scan_d((double)w, sh.red, toth);
+        const double incl = excl + (double)w;
+        // top-k boundary and its mass
+        double WK = rs.W;
+        if (cut_k) {
+            if (K_eff <= nh) {
+                WK = block_sum_d(tid < K_eff ? (double)w : 0.0, sh.red);
+                if (tid == K_eff - 1) sh.key = key64(hz, hid);
+                __syncthreads();
+                kK = sh.key;
+            } else {
+                kK = pool_select(su.p.z, su.p.id, n, K_eff, su.p.hc, sh);
+                double part = 0.0;
+                for (int i = tid; i < n; i += NT)
+                    if (key64(su.p.z[i], su.p.id[i]) >= kK) part += (double)expf(su.p.z[i] - zmax);
+                WK = block_sum_d(part, sh.red);
+            }
+        }
+        int n_topp = cut_k ? K_eff : total;
+        if (c.top_p < 1.0f) {
+            const double thr = (double)c.top_p * WK;
+            const int lim = min(nh, n_topp);
+            const int f = block_min_i(tid < lim && excl >= thr ? tid : INT_MAX, sh.red);
+            if (f != INT_MAX) n_topp = f;
+            else if (n_topp > nh) deep = true;
+        }
+        n_kept = n_topp;
+        if (!deep && c.min_p > 0.0f) {
+            const int lim = min(nh, n_topp);
+            const int cnt = block_sum_i(tid < lim && w >= c.min_p ? 1 : 0, sh.red);
+            if (cnt < lim) n_kept = cnt;
+            else if (n_topp > nh) deep = true;
+        }
+        if (!deep) {
+            if (n_kept == total) {
+                Wk = rs.W;
+                kappa = 0;
+            } else if (cut_k && n_kept == K_eff) {
+                Wk = WK;
+                kappa = kK;
+            } else {
+                Wk = block_sum_d(tid < n_kept ? (double)w : 0.0, sh.red);
+                if (tid == n_kept - 1) sh.key = key64(hz, hid);
+                __syncthreads();
+                kappa = sh.key;
+            }
+            const double tgt = (double)u * Wk;
+            const int lim = min(nh, n_kept);
+            const int f = block_min_i(tid < lim && incl > tgt ? tid : INT_MAX, sh.red);
+            const int pick = f != INT_MAX ? f : (n_kept <= nh ? n_kept - 1 : -1);
+            if (pick < 0) deep = true;
+            else {
+                if (tid == pick) sh.fid = hid;
+                __syncthreads();
+                token = sh.fid;
+            }
+        }
+        if (!deep) {
+            // debug outputs need the kept / top-k sets listed in full
+            const bool kept_listed = n_kept <= nh || (cut_k && n_kept == K_eff) || total <= n;
+            const bool topk_listed = !topk_on || (cut_k ? true : total <= n);
+            if ((dbg.probs && !kept_listed) || (dbg.topk && !topk_listed)) slow = true;
+            else {
+                if (tid == 0) {
+                    info.kappa = kappa;
+                    info.W = Wk;
+                    info.zmax = zmax;
+                    info.min_p = 0.0f;
+                    info.n_kept = n_kept;
+                    info.token = token;
+                    info.argmax = -1;
+                    info.path = 0;
+                    if (dbg.kept) *dbg.kept = n_kept;
+                    if (dbg.path) *dbg.path = 0;
+                }
+                if (dbg.probs) {
+                    if (n_kept <= nh) {
+                        if (tid < n_kept) dbg.probs[hid] = (float)((double)w / Wk);
+                    } else {
+                        for (int i = tid; i < n; i += NT) {
+                            if (key64(su.p.z[i], su.p.id[i]) >= kappa)
+                                dbg.probs[su.p.id[i]] = (float)((double)expf(su.p.z[i] - zmax) / Wk);
+                        }
+                    }
+                }
+                if (dbg.topk) {
+                    const int lim = cut_k ? K_eff : (topk_on ? total : 0);
+                    __syncthreads();
+                    if (tid == 0) sh.cnt = 0;
+                    __syncthreads();
+                    for (int i0 = 0; i0 < n; i0 += NT) {
+                        const int i = i0 + tid;
+                        const bool in = lim > 0 && i < n &&
+                                        (cut_k ? key64(su.p.z[i], su.p.id[i]) >= kK : true);
+                        const int pos = wave_append(in, &sh.cnt);
+                        if (in && pos < dbg.topk_stride) dbg.topk[pos] = su.p.id[i];
+                    }
+                    __syncthreads();
+                    for (int i = min(lim, dbg.topk_stride) + tid; i < dbg.topk_stride; i += NT)
+                        dbg.topk[i] = -1;
+                }
+                __syncthreads();
+                info_out = info;
+                return;
+            }
+        }
     }
-    if (tid == 0) {
-        info.kappa = n_kept < total ? key64(su.p.z[n_kept - 1], su.p.id[n_kept - 1]) : 0ull;
-        info.W = Wk;
-        info.zmax = zmax;
-        info.min_p = 0.0f;
-        info.n_kept = n_kept;
-        info.token = token;
-        info.argmax = -1;
-        info.path = 0;
-        if (dbg.kept) *dbg.kept = n_kept;
-        if (dbg.path) *dbg.path = 0;
+    __syncthreads();
+    if (!slow && deep) {
+        if (finalize_deep(c, n, rs, zmax, u, su.p, sh, info, dbg)) {
+            __syncthreads();
+            info_out = info;
+            return;
+        }
     }
-    if (dbg.probs) {
-        for (int i = tid; i < n_kept; i += NT)
-            dbg.probs[su.p.id[i]] = (float)((double)expf(su.p.z[i] - zmax) / Wk);
-    }
-    if (dbg.topk) {
-        const int lim = cut_k ? K_eff : (topk_on ? total : 0);
-        for (int i = tid; i < dbg.topk_stride; i += NT)
-            dbg.topk[i] = (i < lim && i < n) ? su.p.id[i] : -1;
-    }
+    finalize_slow<DT>(c, row, ws, n_tiles, rs, u, su, sh, info, dbg);
     __syncthreads();
     info_out = info;
 }
 
 // ---------------------------------------------------------------------------
 // kernels
+//
+// Each pass is a short chain of launches on one stream: the kernel boundary is
+// the only synchronisation between stages (no cross-workgroup fences or
+// counters), and each kernel carries only the registers and LDS of its stage.
 
-// Maps the linear workgroup index to a (row, tile) pair so that the tiles of a
-// row run on the same XCD (dispatch places workgroup i on XCD i mod 8), which
-// keeps the last-block merge's reads in that XCD's L2.
+// Workgroup i runs on XCD i mod 8. Stage 1 and the row merge both map their
+// linear index so that a row's tiles and its merge land on the same XCD, which
+// keeps the merge's reads of the stage-1 results in that XCD's L2.
 __device__ __forceinline__ int xcd_linear(int n) {
     const int i = blockIdx.x;
     if ((n & 7) != 0) return i;
@@ -864,20 +1182,42 @@ __device__ __forceinline__ int xcd_linear(int n) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(NT) void k_sample(SampleArgs a) {
-    __shared__ SmemU su;
+__device__ __forceinline__ RowCtx sample_ctx(const SampleArgs& a, int row) {
+    const void* logits = (const char*)a.logits + (size_t)row * a.row_stride * (DT == SS_F32 ? 4 : 2);
+    const uint32_t* mrow = a.p.mask ? a.p.mask + (size_t)row * a.p.mask_stride : nullptr;
+    return make_ctx(a.p, row, logits, a.V, nullptr, 0, mrow, 0);
+}
+
+// Target row j of request b is scored after the draft tokens d_0..d_{j-1}: they
+// extend the penalty history and the position.
+template <int DT>
+__device__ __forceinline__ RowCtx spec_ctx(const SpecArgs& a, int b, int j) {
+    const int row = b * (a.G + 1) + j;
+    const void* logits = (const char*)a.target + (size_t)row * a.row_stride * (DT == SS_F32 ? 4 : 2);
+    const uint32_t* mrow = a.p.mask ? a.p.mask + (size_t)row * a.p.mask_stride : nullptr;
+    return make_ctx(a.p, b, logits, a.V, a.draft_tokens + (size_t)b * a.G, j, mrow, (uint32_t)j);
+}
+
+template <int DT>
+__global__ __launch_bounds__(NT) void k_sample_tiles(SampleArgs a) {
+    __shared__ SmemTile tt;
     __shared__ SmemS sh;
     const int n_tiles = a.ws.n_tiles;
     const int lin = xcd_linear(a.B * n_tiles);
     const int row = lin / n_tiles;
     const int tile = lin % n_tiles;
-    const void* logits = (const char*)a.logits + (size_t)row * a.row_stride * (DT == SS_F32 ? 4 : 2);
-    const uint32_t* mrow = a.p.mask ? a.p.mask + (size_t)row * a.p.mask_stride : nullptr;
-    const RowCtx c = make_ctx(a.p, row, logits, a.V, nullptr, 0, mrow, 0);
-    tile_stage1<DT>(c, row, tile, a.ws, su, sh,
+    const RowCtx c = sample_ctx<DT>(a, row);
+    tile_stage1<DT>(c, row, tile, a.ws, tt, sh,
                     a.dbg_processed ? a.dbg_processed + (size_t)row * a.V : nullptr,
                     a.dbg_probs ? a.dbg_probs + (size_t)row * a.V : nullptr);
-    if (!arrive_last(a.ws.row_counter + row, (uint32_t)n_tiles, sh)) return;
+}
+
+template <int DT>
+__global__ __launch_bounds__(NT) void k_sample_rows(SampleArgs a) {
+    __shared__ SmemU su;
+    __shared__ SmemS sh;
+    const int row = xcd_linear(a.B);
+    const RowCtx c = sample_ctx<DT>(a, row);
     const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
     RowDbg dbg;
     dbg.topk = a.dbg_topk ? a.dbg_topk + (size_t)row * a.dbg_topk_stride : nullptr;
@@ -890,32 +1230,38 @@ __global__ __launch_bounds__(NT) void k_sample(SampleArgs a) {
     if (threadIdx.x == 0) a.out_tokens[row] = info.token;
 }
 
-// Verification, kernel 1: every target row of every request runs stage 1 and
-// the row finaliser; each draft row then takes its accept decision, the bonus
-// row samples its token, and the last row of a request assembles the output.
+// Verification, stage 1 over every target row of every request.
 template <int DT>
-__global__ __launch_bounds__(NT) void k_spec_rows(SpecArgs a) {
-    __shared__ SmemU su;
+__global__ __launch_bounds__(NT) void k_spec_tiles(SpecArgs a) {
+    __shared__ SmemTile tt;
     __shared__ SmemS sh;
     const int n_tiles = a.ws.n_tiles;
     const int G1 = a.G + 1;
     const int lin = xcd_linear(a.B * G1 * n_tiles);
     const int row = lin / n_tiles;
     const int tile = lin % n_tiles;
+    const RowCtx c = spec_ctx<DT>(a, row / G1, row % G1);
+    tile_stage1<DT>(c, row, tile, a.ws, tt, sh, nullptr, nullptr);
+}
+
+// Verification, per target row: the filtered distribution, then the accept
+// test of the draft token at that position (draft rows) or the bonus token
+// (last row).
+template <int DT>
+__global__ __launch_bounds__(NT) void k_spec_rows(SpecArgs a) {
+    __shared__ SmemU su;
+    __shared__ SmemS sh;
+    const int G1 = a.G + 1;
+    const int row = xcd_linear(a.B * G1);
     const int b = row / G1;
     const int j = row % G1;
-    const void* logits = (const char*)a.target + (size_t)row * a.row_stride * (DT == SS_F32 ? 4 : 2);
-    const uint32_t* mrow = a.p.mask ? a.p.mask + (size_t)row * a.p.mask_stride : nullptr;
-    const int32_t* drafts = a.draft_tokens + (size_t)b * a.G;
-    const RowCtx c = make_ctx(a.p, b, logits, a.V, drafts, j, mrow, (uint32_t)j);
-    tile_stage1<DT>(c, row, tile, a.ws, su, sh, nullptr, nullptr);
-    if (!arrive_last(a.ws.row_counter + row, (uint32_t)n_tiles, sh)) return;
+    const RowCtx c = spec_ctx<DT>(a, b, j);
     RowDbg dbg = {nullptr, 0, nullptr, nullptr, nullptr};
     const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
     RowInfo info;
     finalize_row<DT>(c, row, a.ws, u, su, sh, dbg, info);
     if (j < a.G) {
-        const int d = drafts[j];
+        const int d = a.draft_tokens[(size_t)b * a.G + j];
         int acc;
         if (c.T == 0.0f || info.n_kept == 0) {
             acc = (info.argmax >= 0 && d == info.argmax) ? 1 : 0;
@@ -937,93 +1283,115 @@ __global__ __launch_bounds__(NT) void k_spec_rows(SpecArgs a) {
         if (threadIdx.x == 0) a.ws.row_accept[row] = acc;
     }
     if (threadIdx.x == 0) a.ws.rowinfo[row] = info;
-    if (!arrive_last(a.ws.req_counter + b, (uint32_t)G1, sh)) return;
-    if (threadIdx.x == 0) {
-        int n = a.G;
-        for (int k = 0; k < a.G; ++k)
-            if (!a.ws.row_accept[(size_t)b * G1 + k]) {
-                n = k;
-                break;
-            }
-        int32_t* out = a.out_tokens + (size_t)b * G1;
-        for (int k = 0; k < n; ++k) out[k] = drafts[k];
-        const RowInfo ri = a.ws.rowinfo[(size_t)b * G1 + n];
-        int resid = -1;
-        if (n == a.G) out[n] = ri.token;
-        else if (c.T == 0.0f || ri.n_kept == 0) out[n] = ri.argmax;
-        else {
-            out[n] = -1;
-            resid = n;
-        }
-        for (int k = n + 1; k < G1; ++k) out[k] = -1;
-        a.out_num_accepted[b] = n;
-        a.ws.resid_row[b] = resid;
-    }
+}
+
+// Accepted draft count of request b: the first rejected position, or G.
+__device__ __forceinline__ int accepted_prefix(const SpecArgs& a, int b) {
+    const int G1 = a.G + 1;
+    int n = a.G;
+    for (int k = a.G - 1; k >= 0; --k)
+        if (!a.ws.row_accept[(size_t)b * G1 + k]) n = k;
+    return n;
+}
+
+// Position of request b whose token comes from the residual distribution, or -1.
+__device__ __forceinline__ int residual_position(const SpecArgs& a, int b, RowInfo& ri) {
+    const int n = accepted_prefix(a, b);
+    ri = a.ws.rowinfo[(size_t)b * (a.G + 1) + n];
+    if (n == a.G || a.p.temperature[b] == 0.0f || ri.n_kept == 0) return -1;
+    return n;
+}
+
+// pi(v) of the filtered distribution described by ri, for processed logit x.
+__device__ __forceinline__ float filtered_prob(const RowCtx& c, const RowInfo& ri, int id, float x) {
+    if (!(x > NEG_INF)) return 0.0f;
+    const float z = canon_zero(x / c.T);
+    const float w = expf(z - ri.zmax);
+    const bool kept = key64(z, id) >= ri.kappa && (ri.min_p <= 0.0f || w >= ri.min_p);
+    return kept ? (float)((double)w / ri.W) : 0.0f;
 }
 
 // Residual mass of one tile of a rejected row: r = max(0, pi - q) per entry (or
 // pi itself when use_pi), in token-id order within each thread group.
 template <int DT>
 __device__ void residual_values(const RowCtx& c, const RowInfo& ri, const float* q, int tb,
-                                bool use_pi, SmemU& su, double r[EPT]) {
+                                bool use_pi, SmemTile& tt, double r[EPT]) {
     float v[EPT];
     load_tile<DT>(c, tb, v);
-    build_tables(c, tb, su.t);
-    process_tile<DT>(c, tb, v, su.t);
+    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt);
+    process_tile<DT>(c, tb, v, tt);
 #pragma unroll
     for (int s = 0; s < EPT; ++s) {
         const int id = slot_id<DT>(tb, s);
         double val = 0.0;
-        if (id < c.V && v[s] > NEG_INF) {
-            const float z = canon_zero(v[s] / c.T);
-            const float w = expf(z - ri.zmax);
-            const bool kept = key64(z, id) >= ri.kappa && (ri.min_p <= 0.0f || w >= ri.min_p);
-            const float pi = kept ? (float)((double)w / ri.W) : 0.0f;
-            val = use_pi ? (double)pi : (double)fmaxf(0.0f, pi - q[id]);
+        if (id < c.V) {
+            const float pi = filtered_prob(c, ri, id, v[s]);
+            val = use_pi ? (double)pi : (double)fmaxf(0.0f, pi - gld(q + id));
         }
         r[s] = val;
     }
 }
 
+// Verification, residual stage 1: per tile of each rejected row, the sums of the
+// residual max(0, pi - q) and of pi (the fallback when the residual is zero).
 template <int DT>
-__global__ __launch_bounds__(NT) void k_spec_residual(SpecArgs a) {
-    __shared__ SmemU su;
+__global__ __launch_bounds__(NT) void k_spec_resid_tiles(SpecArgs a) {
+    __shared__ SmemTile tt;
     __shared__ SmemS sh;
     const int n_tiles = a.ws.n_tiles;
     const int b = blockIdx.x / n_tiles;
     const int tile = blockIdx.x % n_tiles;
-    const int j = a.ws.resid_row[b];
+    RowInfo ri;
+    const int j = residual_position(a, b, ri);
     if (j < 0) return;
-    const int G1 = a.G + 1;
-    const int row = b * G1 + j;
-    const void* logits = (const char*)a.target + (size_t)row * a.row_stride * (DT == SS_F32 ? 4 : 2);
-    const uint32_t* mrow = a.p.mask ? a.p.mask + (size_t)row * a.p.mask_stride : nullptr;
-    const int32_t* drafts = a.draft_tokens + (size_t)b * a.G;
-    const RowCtx c = make_ctx(a.p, b, logits, a.V, drafts, j, mrow, (uint32_t)j);
-    const RowInfo ri = a.ws.rowinfo[row];
+    const RowCtx c = spec_ctx<DT>(a, b, j);
     const float* q = a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride;
-    double r[EPT];
-    {
-        residual_values<DT>(c, ri, q, tile * TILE, false, su, r);
-        double sr = 0.0;
+    const int tb = tile * TILE;
+    float v[EPT];
+    load_tile<DT>(c, tb, v);
+    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt);
+    process_tile<DT>(c, tb, v, tt);
+    double sr = 0.0, sp = 0.0;
 #pragma unroll
-        for (int s = 0; s < EPT; ++s) sr += r[s];
-        sr = block_sum_d(sr, sh.red);
-        __syncthreads();
-        // pi alone, for a residual that sums to zero
-        double rp[EPT];
-        residual_values<DT>(c, ri, q, tile * TILE, true, su, rp);
-        double sp = 0.0;
-#pragma unroll
-        for (int s = 0; s < EPT; ++s) sp += rp[s];
-        sp = block_sum_d(sp, sh.red);
-        if (threadIdx.x == 0) a.ws.resid_tile[(size_t)b * n_tiles + tile] = make_double2(sr, sp);
+    for (int s = 0; s < EPT; ++s) {
+        const int id = slot_id<DT>(tb, s);
+        if (id < c.V) {
+            const float pi = filtered_prob(c, ri, id, v[s]);
+            sr += (double)fmaxf(0.0f, pi - gld(q + id));
+            sp += (double)pi;
+        }
     }
-    if (!arrive_last(a.ws.resid_counter + b, (uint32_t)n_tiles, sh)) return;
-    // last tile of this request: locate the tile, then the entry, in id order
+    sr = block_sum_d(sr, sh.red);
+    sp = block_sum_d(sp, sh.red);
+    if (threadIdx.x == 0) a.ws.resid_tile[(size_t)b * n_tiles + tile] = make_double2(sr, sp);
+}
+
+// Verification, per request: the output row. Accepted drafts, then the bonus
+// token, the greedy target token, or a draw from the residual distribution in
+// token-id order (tile by the per-tile sums, then the entry within the tile).
+template <int DT>
+__global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
+    __shared__ SmemTile tt;
+    __shared__ SmemS sh;
     __shared__ int s_tile;
     __shared__ int s_usepi;
     __shared__ double s_rem;
+    const int n_tiles = a.ws.n_tiles;
+    const int b = blockIdx.x;
+    const int G1 = a.G + 1;
+    const int n = accepted_prefix(a, b);
+    RowInfo ri;
+    const int j = residual_position(a, b, ri);
+    int32_t* out = a.out_tokens + (size_t)b * G1;
+    if (threadIdx.x == 0) {
+        for (int k = 0; k < n; ++k) out[k] = a.draft_tokens[(size_t)b * a.G + k];
+        for (int k = n + 1; k < G1; ++k) out[k] = -1;
+        a.out_num_accepted[b] = n;
+        if (j < 0) out[n] = n == a.G ? ri.token : ri.argmax;
+    }
+    if (j < 0) return;
+    const RowCtx c = spec_ctx<DT>(a, b, j);
+    const float* q = a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride;
     if (threadIdx.x == 0) {
         double R = 0.0, P = 0.0;
         for (int t = 0; t < n_tiles; ++t) {
@@ -1060,7 +1428,8 @@ __global__ __launch_bounds__(NT) void k_spec_residual(SpecArgs a) {
     const int st = s_tile;
     int token = -1;
     if (st >= 0) {
-        residual_values<DT>(c, ri, q, st * TILE, s_usepi != 0, su, r);
+        double r[EPT];
+        residual_values<DT>(c, ri, q, st * TILE, s_usepi != 0, tt, r);
         using L = Lay<DT>;
         double carry = 0.0;
         int found = INT_MAX, lastpos = -1;
@@ -1089,29 +1458,36 @@ __global__ __launch_bounds__(NT) void k_spec_residual(SpecArgs a) {
         lastpos = -block_min_i(-lastpos, sh.red);
         token = found != INT_MAX ? found : lastpos;
     }
-    if (threadIdx.x == 0) a.out_tokens[(size_t)b * G1 + j] = token;
+    if (threadIdx.x == 0) out[j] = token;
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 
+template <int DT>
+static void sample_chain(const SampleArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(k_sample_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(k_sample_rows<DT>, dim3(a.B), dim3(NT), 0, st, a);
+}
+
+template <int DT>
+static void spec_chain(const SpecArgs& a, hipStream_t st) {
+    const int rows = a.B * (a.G + 1);
+    hipLaunchKernelGGL(k_spec_tiles<DT>, dim3(rows * a.ws.n_tiles), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(k_spec_rows<DT>, dim3(rows), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(k_spec_resid_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(k_spec_finish<DT>, dim3(a.B), dim3(NT), 0, st, a);
+}
+
 hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st) {
-    const dim3 grid(a.B * a.ws.n_tiles);
-    if (dt == SS_F32) hipLaunchKernelGGL(k_sample<SS_F32>, grid, dim3(NT), 0, st, a);
-    else hipLaunchKernelGGL(k_sample<SS_BF16>, grid, dim3(NT), 0, st, a);
+    if (dt == SS_F32) sample_chain<SS_F32>(a, st);
+    else sample_chain<SS_BF16>(a, st);
     return hipGetLastError();
 }
 
 hipError_t launch_spec(const SpecArgs& a, ss_dtype dt, hipStream_t st) {
-    const dim3 grid1(a.B * (a.G + 1) * a.ws.n_tiles);
-    const dim3 grid2(a.B * a.ws.n_tiles);
-    if (dt == SS_F32) {
-        hipLaunchKernelGGL(k_spec_rows<SS_F32>, grid1, dim3(NT), 0, st, a);
-        hipLaunchKernelGGL(k_spec_residual<SS_F32>, grid2, dim3(NT), 0, st, a);
-    } else {
-        hipLaunchKernelGGL(k_spec_rows<SS_BF16>, grid1, dim3(NT), 0, st, a);
-        hipLaunchKernelGGL(k_spec_residual<SS_BF16>, grid2, dim3(NT), 0, st, a);
-    }
+    if (dt == SS_F32) spec_chain<SS_F32>(a, st);
+    else spec_chain<SS_BF16>(a, st);
     return hipGetLastError();
 }
 

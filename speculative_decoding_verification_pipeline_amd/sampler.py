@@ -62,11 +62,12 @@ class SamplerError(RuntimeError):
 _lib = None
 
 
-def load_library(path=LIB_PATH):
+def load_library(path=None):
     """Load libss_sampler.so and declare its signatures (raises if absent)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = LIB_PATH if path is None else path
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it first (__graft_entry__.build())")
     lib = ctypes.CDLL(path)

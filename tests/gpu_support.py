@@ -93,8 +93,13 @@ def oracle_filtered(w):
 
 
 class Tally:
-    def __init__(self, name):
+    """budget=False is for deliberately flat rows: with n CDF breakpoints about
+    2e-6 * n of the draws lie within 1e-6 of one, so the share rule cannot apply
+    there; unflagged draws must still match exactly."""
+
+    def __init__(self, name, budget=True):
         self.name = name
+        self.budget = budget
         self.draws = 0
         self.flagged = 0
         self.mismatch = []
@@ -110,6 +115,8 @@ class Tally:
         log(f"[{self.name}] draws={self.draws} flagged={self.flagged} "
             f"mismatches={len(self.mismatch)}")
         assert not self.mismatch, f"{self.name}: unflagged mismatches {self.mismatch[:10]}"
+        if not self.budget:
+            return
         # the share rule needs >= 10^4 draws to mean anything; smaller ad-hoc
         # cases may hold at most two flagged draws (all are reported above)
         limit = FLAG_BUDGET * self.draws if self.draws >= 10_000 else 2

@@ -132,7 +132,7 @@ def test_high_entropy_rows_take_the_exact_fallback():
                          positions=np.zeros(B, np.int32), seed=3)
     xs, filts = oracle_filtered(w)
     s = make_sampler(B, V)
-    tally = Tally("high-entropy")
+    tally = Tally("high-entropy", budget=False)
     toks, dbg = run_debug(s, w)
     compare_debug(w, xs, filts, toks, dbg, w.seed, tally)
     paths = dbg.path.cpu().numpy()
