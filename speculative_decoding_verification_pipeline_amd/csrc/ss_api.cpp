@@ -18,6 +18,11 @@ struct ss_sampler {
     int64_t ws_bytes;
     ss::Workspace ws;
     float2* lm_partials;
+    // defaults substituted for absent per-request parameters, [max_batch] each
+    int32_t* def_zero_i;
+    float* def_zero_f;
+    float* def_one_f;
+    int32_t* def_iota;
 };
 
 namespace {
@@ -28,26 +33,30 @@ int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-ss::ParamPtrs to_ptrs(const ss_params* p) {
+// Device pointers for every per-request parameter: an absent one points at the
+// handle's default array (so the kernels read every parameter unconditionally).
+ss::ParamPtrs to_ptrs(const ss_sampler* s, const ss_params* p) {
     ss::ParamPtrs q;
     q.temperature = p->temperature;
-    q.top_k = p->top_k;
-    q.top_p = p->top_p;
-    q.min_p = p->min_p;
-    q.rep = p->repetition_penalty;
-    q.freq = p->frequency_penalty;
-    q.pres = p->presence_penalty;
-    q.hist_ids = p->history_ids;
-    q.hist_len = p->history_len;
-    q.hist_stride = p->history_stride;
-    q.bias_ids = p->bias_ids;
-    q.bias_vals = p->bias_values;
-    q.bias_len = p->bias_len;
-    q.bias_stride = p->bias_stride;
+    q.top_k = p->top_k ? p->top_k : s->def_zero_i;
+    q.top_p = p->top_p ? p->top_p : s->def_one_f;
+    q.min_p = p->min_p ? p->min_p : s->def_zero_f;
+    q.rep = p->repetition_penalty ? p->repetition_penalty : s->def_one_f;
+    q.freq = p->frequency_penalty ? p->frequency_penalty : s->def_zero_f;
+    q.pres = p->presence_penalty ? p->presence_penalty : s->def_zero_f;
+    const bool hist = p->history_len && p->history_ids;
+    q.hist_ids = hist ? p->history_ids : s->def_zero_i;
+    q.hist_len = hist ? p->history_len : s->def_zero_i;
+    q.hist_stride = hist ? p->history_stride : 0;
+    const bool bias = p->bias_len && p->bias_ids && p->bias_values;
+    q.bias_ids = bias ? p->bias_ids : s->def_zero_i;
+    q.bias_vals = bias ? p->bias_values : s->def_zero_f;
+    q.bias_len = bias ? p->bias_len : s->def_zero_i;
+    q.bias_stride = bias ? p->bias_stride : 0;
     q.mask = p->grammar_mask;
     q.mask_stride = p->mask_stride;
-    q.request_ids = p->request_ids;
-    q.positions = p->positions;
+    q.request_ids = p->request_ids ? p->request_ids : s->def_iota;
+    q.positions = p->positions ? p->positions : s->def_zero_i;
     q.seed = p->seed;
     return q;
 }
@@ -122,12 +131,13 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
         return o;
     };
     const int64_t o_stats = take(R * nt * (int64_t)sizeof(ss::TileStat));
-    const int64_t o_cand = take(R * nt * ss::CW * (int64_t)sizeof(float2));
+    const int64_t o_cand = take(R * nt * ss::CW * (int64_t)sizeof(unsigned long long));
     const int64_t o_info = take(R * (int64_t)sizeof(ss::RowInfo));
     const int64_t o_acc = take(R * 4);
     const int64_t o_restile = take((int64_t)B * nt * (int64_t)sizeof(double2));
     const int64_t o_scratch = take(R * (int64_t)V * 4);
     const int64_t o_lmpart = cfg->hidden_size > 0 ? take(64 * (int64_t)s->n_vtiles * sizeof(float2)) : 0;
+    const int64_t o_defaults = take(4 * (int64_t)B * 4);
     s->ws_bytes = off;
     if (hipMalloc(&s->ws_base, (size_t)off) != hipSuccess) {
         (void)hipGetLastError();
@@ -137,7 +147,7 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     char* b = static_cast<char*>(s->ws_base);
     ss::Workspace& w = s->ws;
     w.stats = reinterpret_cast<ss::TileStat*>(b + o_stats);
-    w.cand = reinterpret_cast<float2*>(b + o_cand);
+    w.cand = reinterpret_cast<unsigned long long*>(b + o_cand);
     w.rowinfo = reinterpret_cast<ss::RowInfo*>(b + o_info);
     w.row_accept = reinterpret_cast<int32_t*>(b + o_acc);
     w.resid_tile = reinterpret_cast<double2*>(b + o_restile);
@@ -145,6 +155,33 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     w.n_tiles = s->n_tiles;
     w.V = V;
     s->lm_partials = cfg->hidden_size > 0 ? reinterpret_cast<float2*>(b + o_lmpart) : nullptr;
+    {
+        int32_t* d = reinterpret_cast<int32_t*>(b + o_defaults);
+        s->def_zero_i = d;
+        s->def_zero_f = reinterpret_cast<float*>(d + B);
+        s->def_one_f = reinterpret_cast<float*>(d + 2 * B);
+        s->def_iota = d + 3 * B;
+        int32_t* h = new (std::nothrow) int32_t[4 * (size_t)B];
+        if (!h) {
+            (void)hipFree(s->ws_base);
+            delete s;
+            return SS_ERR_OUT_OF_MEMORY;
+        }
+        for (int i = 0; i < B; ++i) {
+            const float one = 1.0f;
+            h[i] = 0;
+            h[B + i] = 0;  // +0.0f
+            std::memcpy(&h[2 * B + i], &one, 4);
+            h[3 * B + i] = i;
+        }
+        const bool ok = hipMemcpy(d, h, 4 * (size_t)B * 4, hipMemcpyHostToDevice) == hipSuccess;
+        delete[] h;
+        if (!ok) {
+            (void)hipFree(s->ws_base);
+            delete s;
+            return SS_ERR_HIP;
+        }
+    }
     *out = s;
     return SS_OK;
 }
@@ -175,7 +212,7 @@ ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t r
     a.row_stride = row_stride;
     a.B = B;
     a.V = s->cfg.vocab_size;
-    a.p = to_ptrs(params);
+    a.p = to_ptrs(s, params);
     a.out_tokens = out_tokens;
     if (debug) {
         a.dbg_processed = debug->processed_logits;
@@ -215,7 +252,7 @@ ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
     a.B = B;
     a.G = G;
     a.V = s->cfg.vocab_size;
-    a.p = to_ptrs(params);
+    a.p = to_ptrs(s, params);
     a.out_tokens = out_tokens;
     a.out_num_accepted = out_num_accepted;
     a.ws = s->ws;

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ss {
 
 constexpr int WAVE = 64;
@@ -94,117 +96,276 @@ __device__ __forceinline__ bool key_before(float za, int ia, float zb, int ib) {
 }
 
 // ---------------------------------------------------------------------------
-// wave64 / workgroup reductions (xor shuffles lower to DPP / ds_swizzle)
+// wave64 lane exchange through DPP and the gfx950 permlane swaps (VALU, no LDS
+// round trip). Reductions pair lanes by mirrors (quad swap, half-row and row
+// mirror, then the 16- and 32-lane swaps); scans shift within rows of 16 and
+// broadcast row ends across rows.
+
+template <int CTRL, int ROWMASK = 0xF, bool BOUND_ZERO = false>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xF, BOUND_ZERO);
+}
+
+enum : int {
+    DPP_QUAD_X1 = 0xB1,      // quad_perm [1,0,3,2]: lane ^ 1
+    DPP_QUAD_X2 = 0x4E,      // quad_perm [2,3,0,1]: lane ^ 2
+    DPP_ROW_SHL4 = 0x104,
+    DPP_ROW_SHR1 = 0x111,
+    DPP_ROW_SHR2 = 0x112,
+    DPP_ROW_SHR4 = 0x114,
+    DPP_ROW_SHR8 = 0x118,
+    DPP_ROW_ROR8 = 0x128,    // lane ^ 8 within a row of 16
+    DPP_ROW_MIRROR = 0x140,  // lane -> 15 - lane within a row
+    DPP_HALF_MIRROR = 0x141, // lane -> 7 - lane within 8
+    DPP_BCAST15 = 0x142,     // lane 15 of each row -> the next row
+    DPP_BCAST31 = 0x143,     // lane 31 -> rows 2 and 3
+};
+
+// The value held by lane ^ J (J a power of two below 64).
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    if constexpr (J == 1) {
+        return dpp_u32<DPP_QUAD_X1>(0u, v);
+    } else if constexpr (J == 2) {
+        return dpp_u32<DPP_QUAD_X2>(0u, v);
+    } else if constexpr (J == 4) {
+        const uint32_t up = dpp_u32<DPP_ROW_SHL4>(0u, v);
+        const uint32_t dn = dpp_u32<DPP_ROW_SHR4>(0u, v);
+        return (lane & 4) ? dn : up;
+    } else if constexpr (J == 8) {
+        return dpp_u32<DPP_ROW_ROR8>(0u, v);
+    } else if constexpr (J == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? p[0] : p[1];
+    } else {
+        static_assert(J == 32, "lane exchange distance");
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? p[0] : p[1];
+    }
+}
+
+template <int J>
+__device__ __forceinline__ float xor_lane_f(float v) {
+    return __uint_as_float(xor_lane<J>(__float_as_uint(v)));
+}
+
+template <int J>
+__device__ __forceinline__ int xor_lane_i(int v) {
+    return (int)xor_lane<J>((uint32_t)v);
+}
+
+template <int J>
+__device__ __forceinline__ unsigned long long xor_lane_u64(unsigned long long v) {
+    const uint32_t lo = xor_lane<J>((uint32_t)v);
+    const uint32_t hi = xor_lane<J>((uint32_t)(v >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Butterfly all-reduce: after the step with mirror M every lane holds the
+// reduction over its aligned group of 2M lanes.
+template <class T, class Op>
+__device__ __forceinline__ T wave_allreduce32(T v, Op op) {
+    auto sw = [](T x, auto tag) -> T {
+        constexpr int C = decltype(tag)::value;
+        uint32_t u;
+        __builtin_memcpy(&u, &x, 4);
+        u = dpp_u32<C>(0u, u);
+        T r;
+        __builtin_memcpy(&r, &u, 4);
+        return r;
+    };
+    v = op(v, sw(v, std::integral_constant<int, DPP_QUAD_X1>()));
+    v = op(v, sw(v, std::integral_constant<int, DPP_QUAD_X2>()));
+    v = op(v, sw(v, std::integral_constant<int, DPP_HALF_MIRROR>()));
+    v = op(v, sw(v, std::integral_constant<int, DPP_ROW_MIRROR>()));
+    {
+        uint32_t u;
+        __builtin_memcpy(&u, &v, 4);
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        T a, b;
+        const uint32_t pa = p[0], pb = p[1];
+        __builtin_memcpy(&a, &pa, 4);
+        __builtin_memcpy(&b, &pb, 4);
+        v = op(a, b);
+    }
+    {
+        uint32_t u;
+        __builtin_memcpy(&u, &v, 4);
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        T a, b;
+        const uint32_t pa = p[0], pb = p[1];
+        __builtin_memcpy(&a, &pa, 4);
+        __builtin_memcpy(&b, &pb, 4);
+        v = op(a, b);
+    }
+    return v;
+}
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return wave_allreduce32(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-    return v;
+    return wave_allreduce32(v, [](int a, int b) { return min(a, b); });
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+    return wave_allreduce32(v, [](int a, int b) { return max(a, b); });
 }
 
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return wave_allreduce32(v, [](int a, int b) { return a + b; });
 }
 
+template <int C>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const unsigned long long u = __double_as_longlong(v);
+    const uint32_t lo = dpp_u32<C>(0u, (uint32_t)u);
+    const uint32_t hi = dpp_u32<C>(0u, (uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Binary64 sum over the wave in a fixed pairing order (the same in every lane).
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan_i(int v) {
-    const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const int y = __shfl_up(v, o);
-        if (lane >= o) v += y;
+    // a + b and b + a round identically, so the mirrored partners agree exactly
+    v = v + dpp_f64<DPP_QUAD_X1>(v);
+    v = v + dpp_f64<DPP_QUAD_X2>(v);
+    v = v + dpp_f64<DPP_HALF_MIRROR>(v);
+    v = v + dpp_f64<DPP_ROW_MIRROR>(v);
+    {
+        const unsigned long long u = __double_as_longlong(v);
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+        const double a = __longlong_as_double((long long)(((unsigned long long)hi[0] << 32) | lo[0]));
+        const double b = __longlong_as_double((long long)(((unsigned long long)hi[1] << 32) | lo[1]));
+        v = a + b;
+    }
+    {
+        const unsigned long long u = __double_as_longlong(v);
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+        const double a = __longlong_as_double((long long)(((unsigned long long)hi[0] << 32) | lo[0]));
+        const double b = __longlong_as_double((long long)(((unsigned long long)hi[1] << 32) | lo[1]));
+        v = a + b;
     }
     return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+    unsigned long long o;
+    o = xor_lane_u64<1>(v); v = o > v ? o : v;
+    o = xor_lane_u64<2>(v); v = o > v ? o : v;
+    o = xor_lane_u64<4>(v); v = o > v ? o : v;
+    o = xor_lane_u64<8>(v); v = o > v ? o : v;
+    o = xor_lane_u64<16>(v); v = o > v ? o : v;
+    o = xor_lane_u64<32>(v); v = o > v ? o : v;
+    return v;
+}
+
+// Inclusive prefix sums across the wave (Hillis-Steele within rows of 16, then
+// the row ends carried across rows).
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+    uint32_t u = (uint32_t)v;
+    u += dpp_u32<DPP_ROW_SHR1, 0xF, true>(0u, u);
+    u += dpp_u32<DPP_ROW_SHR2, 0xF, true>(0u, u);
+    u += dpp_u32<DPP_ROW_SHR4, 0xF, true>(0u, u);
+    u += dpp_u32<DPP_ROW_SHR8, 0xF, true>(0u, u);
+    u += dpp_u32<DPP_BCAST15, 0xA, false>(0u, u);
+    u += dpp_u32<DPP_BCAST31, 0xC, false>(0u, u);
+    return (int)u;
+}
+
+template <int C, int ROWMASK, bool BZ>
+__device__ __forceinline__ double dpp_f64_masked(double v) {
+    const unsigned long long u = __double_as_longlong(v);
+    const uint32_t lo = dpp_u32<C, ROWMASK, BZ>(0u, (uint32_t)u);
+    const uint32_t hi = dpp_u32<C, ROWMASK, BZ>(0u, (uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
 __device__ __forceinline__ double wave_incl_scan_d(double v) {
-    const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const double y = __shfl_up(v, o);
-        if (lane >= o) v += y;
-    }
+    v = v + dpp_f64_masked<DPP_ROW_SHR1, 0xF, true>(v);
+    v = v + dpp_f64_masked<DPP_ROW_SHR2, 0xF, true>(v);
+    v = v + dpp_f64_masked<DPP_ROW_SHR4, 0xF, true>(v);
+    v = v + dpp_f64_masked<DPP_ROW_SHR8, 0xF, true>(v);
+    v = v + dpp_f64_masked<DPP_BCAST15, 0xA, false>(v);
+    v = v + dpp_f64_masked<DPP_BCAST31, 0xC, false>(v);
     return v;
 }
 
-// Scratch for workgroup-level reductions (NT / WAVE = 4 waves).
-struct RedScratch {
-    float f[NT / WAVE];
-    int i[NT / WAVE];
-    double d[NT / WAVE];
+// Scratch for workgroup-level reductions over NB threads (NB / WAVE waves).
+template <int NB>
+struct RedT {
+    float f[NB / WAVE];
+    int i[NB / WAVE];
+    double d[NB / WAVE];
 };
+using RedScratch = RedT<NT>;
 
-__device__ __forceinline__ float block_max(float v, RedScratch& r) {
+template <int NB>
+__device__ __forceinline__ float block_max(float v, RedT<NB>& r) {
     v = wave_max(v);
     const int w = threadIdx.x / WAVE;
     if ((threadIdx.x & (WAVE - 1)) == 0) r.f[w] = v;
     __syncthreads();
     float m = r.f[0];
 #pragma unroll
-    for (int k = 1; k < NT / WAVE; ++k) m = fmaxf(m, r.f[k]);
+    for (int k = 1; k < NB / WAVE; ++k) m = fmaxf(m, r.f[k]);
     __syncthreads();
     return m;
 }
 
-__device__ __forceinline__ int block_min_i(int v, RedScratch& r) {
+template <int NB>
+__device__ __forceinline__ int block_min_i(int v, RedT<NB>& r) {
     v = wave_min_i(v);
     const int w = threadIdx.x / WAVE;
     if ((threadIdx.x & (WAVE - 1)) == 0) r.i[w] = v;
     __syncthreads();
     int m = r.i[0];
 #pragma unroll
-    for (int k = 1; k < NT / WAVE; ++k) m = min(m, r.i[k]);
+    for (int k = 1; k < NB / WAVE; ++k) m = min(m, r.i[k]);
     __syncthreads();
     return m;
 }
 
-__device__ __forceinline__ int block_sum_i(int v, RedScratch& r) {
+template <int NB>
+__device__ __forceinline__ int block_sum_i(int v, RedT<NB>& r) {
     v = wave_sum_i(v);
     const int w = threadIdx.x / WAVE;
     if ((threadIdx.x & (WAVE - 1)) == 0) r.i[w] = v;
     __syncthreads();
     int m = 0;
 #pragma unroll
-    for (int k = 0; k < NT / WAVE; ++k) m += r.i[k];
+    for (int k = 0; k < NB / WAVE; ++k) m += r.i[k];
     __syncthreads();
     return m;
 }
 
-// Deterministic: fixed shuffle tree, then the four wave sums in wave order.
-__device__ __forceinline__ double block_sum_d(double v, RedScratch& r) {
+// Deterministic: fixed pairing within each wave, then the wave sums in wave order.
+template <int NB>
+__device__ __forceinline__ double block_sum_d(double v, RedT<NB>& r) {
     v = wave_sum_d(v);
     const int w = threadIdx.x / WAVE;
     if ((threadIdx.x & (WAVE - 1)) == 0) r.d[w] = v;
     __syncthreads();
     double m = 0.0;
 #pragma unroll
-    for (int k = 0; k < NT / WAVE; ++k) m += r.d[k];
+    for (int k = 0; k < NB / WAVE; ++k) m += r.d[k];
     __syncthreads();
     return m;
 }
 
 // Exclusive scan of one int per thread in thread order; returns the total too.
-__device__ __forceinline__ int block_excl_scan_i(int v, RedScratch& r, int& total) {
+template <int NB>
+__device__ __forceinline__ int block_excl_scan_i(int v, RedT<NB>& r, int& total) {
     const int inc = wave_incl_scan_i(v);
     const int w = threadIdx.x / WAVE;
     if ((threadIdx.x & (WAVE - 1)) == WAVE - 1) r.i[w] = inc;
     __syncthreads();
     int base = 0, tot = 0;
 #pragma unroll
-    for (int k = 0; k < NT / WAVE; ++k) {
+    for (int k = 0; k < NB / WAVE; ++k) {
         if (k < w) base += r.i[k];
         tot += r.i[k];
     }
@@ -213,14 +374,15 @@ __device__ __forceinline__ int block_excl_scan_i(int v, RedScratch& r, int& tota
     return base + inc - v;
 }
 
-__device__ __forceinline__ double block_excl_scan_d(double v, RedScratch& r, double& total) {
+template <int NB>
+__device__ __forceinline__ double block_excl_scan_d(double v, RedT<NB>& r, double& total) {
     const double inc = wave_incl_scan_d(v);
     const int w = threadIdx.x / WAVE;
     if ((threadIdx.x & (WAVE - 1)) == WAVE - 1) r.d[w] = inc;
     __syncthreads();
     double base = 0.0, tot = 0.0;
 #pragma unroll
-    for (int k = 0; k < NT / WAVE; ++k) {
+    for (int k = 0; k < NB / WAVE; ++k) {
         if (k < w) base += r.d[k];
         tot += r.d[k];
     }
@@ -229,8 +391,20 @@ __device__ __forceinline__ double block_excl_scan_d(double v, RedScratch& r, dou
     return base + inc - v;
 }
 
+__device__ __forceinline__ float xor_lane_dyn(float v, int j) {
+    switch (j) {
+    case 1: return xor_lane_f<1>(v);
+    case 2: return xor_lane_f<2>(v);
+    case 4: return xor_lane_f<4>(v);
+    case 8: return xor_lane_f<8>(v);
+    case 16: return xor_lane_f<16>(v);
+    default: return xor_lane_f<32>(v);
+    }
+}
+
 // Sorts one float per thread across the workgroup, descending (bitonic network;
-// strides below the wave width exchange through shuffles, the rest through LDS).
+// strides below the wave width exchange through DPP / permlane, the rest
+// through LDS).
 __device__ __forceinline__ float block_sort_desc(float v, float* tmp) {
     const int tid = threadIdx.x;
 #pragma unroll
@@ -244,7 +418,7 @@ __device__ __forceinline__ float block_sort_desc(float v, float* tmp) {
                 o = tmp[tid ^ j];
                 __syncthreads();
             } else {
-                o = __shfl_xor(v, j);
+                o = xor_lane_dyn(v, j);
             }
             const bool desc = (tid & k) == 0;
             const bool lower = (tid & j) == 0;

@@ -36,7 +36,8 @@ struct RowInfo {
 };
 static_assert(sizeof(RowInfo) == 48, "RowInfo layout");
 
-// Per-row view of the caller's parameters, as device pointers (host-built).
+// Per-row view of the caller's parameters, as device pointers (host-built;
+// every pointer but mask is valid: absent parameters point at defaults).
 struct ParamPtrs {
     const float* temperature;
     const int32_t* top_k;
@@ -61,7 +62,7 @@ struct ParamPtrs {
 
 struct Workspace {
     TileStat* stats;         // [max_rows * n_tiles]
-    float2* cand;            // [max_rows * n_tiles * CW]  (x', id bits)
+    unsigned long long* cand;  // [max_rows * n_tiles * CW]  candidate keys, sorted per tile
     RowInfo* rowinfo;        // [max_rows]
     int32_t* row_accept;     // [max_rows]: spec decision per draft row
     double2* resid_tile;     // [max_batch * n_tiles]: residual / target mass per tile

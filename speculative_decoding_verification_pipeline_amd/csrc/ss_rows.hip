@@ -85,31 +85,31 @@ struct RowCtx {
     uint64_t seed;
 };
 
-__device__ RowCtx make_ctx(const ParamPtrs& p, int b, const void* logits, int V,
-                           const int32_t* extra, int extra_len, const uint32_t* mask_row,
-                           uint32_t pos_offset) {
+// Every parameter pointer is valid (the host substitutes defaults for absent
+// ones), so all reads are unconditional and issue together.
+__device__ __forceinline__ RowCtx make_ctx(const ParamPtrs& p, int b, const void* logits, int V,
+                                           const int32_t* extra, int extra_len,
+                                           const uint32_t* mask_row, uint32_t pos_offset) {
     RowCtx c;
     c.logits = logits;
     c.V = V;
     c.T = p.temperature[b];
-    c.top_k = p.top_k ? p.top_k[b] : 0;
-    c.top_p = p.top_p ? p.top_p[b] : 1.0f;
-    c.min_p = p.min_p ? p.min_p[b] : 0.0f;
-    c.rep = p.rep ? p.rep[b] : 1.0f;
-    c.freq = p.freq ? p.freq[b] : 0.0f;
-    c.pres = p.pres ? p.pres[b] : 0.0f;
-    c.hist_len = p.hist_len ? p.hist_len[b] : 0;
-    c.hist = p.hist_ids ? p.hist_ids + (int64_t)b * p.hist_stride : nullptr;
-    if (!c.hist) c.hist_len = 0;
+    c.top_k = p.top_k[b];
+    c.top_p = p.top_p[b];
+    c.min_p = p.min_p[b];
+    c.rep = p.rep[b];
+    c.freq = p.freq[b];
+    c.pres = p.pres[b];
+    c.hist_len = p.hist_len[b];
+    c.hist = p.hist_ids + (int64_t)b * p.hist_stride;
     c.extra = extra;
     c.extra_len = extra ? extra_len : 0;
-    c.bias_len = p.bias_len ? p.bias_len[b] : 0;
-    c.bias_ids = p.bias_ids ? p.bias_ids + (int64_t)b * p.bias_stride : nullptr;
-    c.bias_vals = p.bias_vals ? p.bias_vals + (int64_t)b * p.bias_stride : nullptr;
-    if (!c.bias_ids || !c.bias_vals) c.bias_len = 0;
+    c.bias_len = p.bias_len[b];
+    c.bias_ids = p.bias_ids + (int64_t)b * p.bias_stride;
+    c.bias_vals = p.bias_vals + (int64_t)b * p.bias_stride;
     c.mask = mask_row;
-    c.req = p.request_ids ? (uint32_t)p.request_ids[b] : (uint32_t)b;
-    c.pos = (p.positions ? (uint32_t)p.positions[b] : 0u) + pos_offset;
+    c.req = (uint32_t)p.request_ids[b];
+    c.pos = (uint32_t)p.positions[b] + pos_offset;
     c.seed = p.seed;
     return c;
 }
@@ -120,16 +120,24 @@ __device__ RowCtx make_ctx(const ParamPtrs& p, int b, const void* logits, int V,
 struct SmemTile {
     uint32_t cnt[TILE / 2];   // u16 history multiplicities of the tile's entries
     uint32_t bias[TILE / 32]; // bit set: some bias entry targets this vocabulary entry
-    float sorted[NT];         // sorted per-thread maxima
+    int32_t bid[NT];          // the row's first NT bias entries, in array order
+    float bval[NT];
+    float lmax[NT];           // per-thread maxima
+    float sorted[NT];         // the same, in descending order
+    unsigned long long list[CW];  // the tile's candidate keys, unordered
+    int nlist;
 };
 
+// The row merge runs one 1024-thread workgroup per row (four waves per SIMD).
+constexpr int NTR = 1024;
+constexpr int PERR = POOL / NTR;  // candidate slots per merge thread
+constexpr int OCT = NTR / CW;     // tiles covered by one slot round
+
 struct SmemPool {
-    float z[POOL];            // trusted candidates (unsorted; sorted by the deep path)
-    int id[POOL];
-    float hz[NT];             // head gather / sort exchange
-    int hid[NT];
-    uint32_t hc[256];         // radix histogram over the pool
-    TileStat st[MAX_TILES];
+    unsigned long long buf[2][POOL];  // merge-tree ping-pong buffers (keys, zero = empty slot)
+    double cbase[NTR];                // exclusive prefix mass of each thread's chunk
+    int wcnt[PERR][NTR / WAVE];       // kept candidates per (slot round, wave)
+    int len[2][MAX_TILES];            // segment lengths per merge level
 };
 
 struct SmemRadix {
@@ -143,18 +151,16 @@ union SmemU {
     SmemRadix r;
 };
 
-struct SmemS {
-    RedScratch red;
-    int npool;
-    int nhead;
+template <int NB>
+struct SmemST {
+    RedT<NB> red;
+    RedT<NB> red2;
     int sel;
     int take_last;
-    int cnt;
     unsigned long long rem;
-    unsigned long long key;
-    float fz;
-    int fid;
 };
+using SmemS = SmemST<NT>;   // tile workgroups
+using SmemR = SmemST<NTR>;  // row-merge workgroups
 
 // ---------------------------------------------------------------------------
 // tile geometry: thread tid owns NG groups of VEC consecutive entries
@@ -226,15 +232,21 @@ __device__ __forceinline__ void load_tile(const RowCtx& c, int tb, float v[EPT])
 }
 
 // Penalties -> bias -> mask for one entry. Shared by every path that forms x'
-// so all of them produce the same binary32 value.
-__device__ __forceinline__ float process_entry(const RowCtx& c, int id, float x, uint32_t count,
-                                               bool bias_hit, bool allowed) {
+// so all of them produce the same binary32 value. Bias entries are applied in
+// array order; with tables, the first NT of them come from LDS.
+__device__ __forceinline__ float penalize(const RowCtx& c, float x, uint32_t count) {
     if (count) {
         x = (x > 0.0f) ? x / c.rep : x * c.rep;
         const float fc = c.freq * (float)count;
         x = x - fc;
         x = x - c.pres;
     }
+    return x;
+}
+
+__device__ __forceinline__ float process_entry(const RowCtx& c, int id, float x, uint32_t count,
+                                               bool bias_hit, bool allowed) {
+    x = penalize(c, x, count);
     if (bias_hit) {
         for (int k = 0; k < c.bias_len; ++k)
             if (gld(c.bias_ids + k) == id) x = x + gld(c.bias_vals + k);
@@ -242,39 +254,77 @@ __device__ __forceinline__ float process_entry(const RowCtx& c, int id, float x,
     return allowed ? x : NEG_INF;
 }
 
-// Builds the tile's multiplicity counts and bias bitmap in LDS (two barriers).
-// pre, if given, holds this thread's first two history ids, already loaded.
+__device__ __forceinline__ float process_entry_t(const RowCtx& c, int id, float x, uint32_t count,
+                                                 bool bias_hit, bool allowed, const SmemTile& t) {
+    x = penalize(c, x, count);
+    if (bias_hit) {
+        const int nl = min(c.bias_len, NT);
+        for (int k = 0; k < nl; ++k)
+            if (t.bid[k] == id) x = x + t.bval[k];
+        for (int k = NT; k < c.bias_len; ++k)
+            if (gld(c.bias_ids + k) == id) x = x + gld(c.bias_vals + k);
+    }
+    return allowed ? x : NEG_INF;
+}
+
+// The row's history and bias lists are small and shared by all its tiles:
+// each thread fetches its first two history ids and one bias entry before the
+// tile's logits, so their latency overlaps the tile stream.
+struct TablePrefetch {
+    int hist[2];
+    int bias_id;
+    float bias_val;
+};
+
+__device__ __forceinline__ TablePrefetch prefetch_tables(const RowCtx& c) {
+    TablePrefetch f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int i = (int)threadIdx.x + k * NT;
+        f.hist[k] = i < c.hist_len ? gld(c.hist + i)
+                    : (i < c.hist_len + c.extra_len ? gld(c.extra + (i - c.hist_len)) : -1);
+    }
+    const int i = threadIdx.x;
+    f.bias_id = i < c.bias_len ? gld(c.bias_ids + i) : -1;
+    f.bias_val = i < c.bias_len ? gld(c.bias_vals + i) : 0.0f;
+    return f;
+}
+
+// Builds the tile's multiplicity counts, bias bitmap and bias list in LDS (two
+// barriers).
 __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& t,
-                                             const int* pre = nullptr) {
+                                             const TablePrefetch& f, bool active = true) {
     const int tid = threadIdx.x;
-    const bool has_cnt = (c.hist_len + c.extra_len) > 0;
+    const bool has_cnt = active && (c.hist_len + c.extra_len) > 0;
+    const bool has_bias = active && c.bias_len > 0;
     if (has_cnt) {
         uint4* c4 = (uint4*)t.cnt;
 #pragma unroll
         for (int k = 0; k < TILE / 8 / NT; ++k) c4[tid + k * NT] = make_uint4(0, 0, 0, 0);
     }
-    if (c.bias_len > 0) t.bias[tid] = 0;
+    if (has_bias) {
+        t.bias[tid] = 0;
+        t.bid[tid] = f.bias_id;
+        t.bval[tid] = f.bias_val;
+    }
     __syncthreads();
     if (has_cnt) {
-        const int i0 = pre ? tid + 2 * NT : tid;
-        if (pre) {
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int id = pre[k];
-                const int l = id - tb;
-                if (id >= 0 && id < c.V && l >= 0 && l < TILE)
-                    atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
-            }
+        for (int k = 0; k < 2; ++k) {
+            const int id = f.hist[k];
+            const int l = id - tb;
+            if (id >= 0 && id < c.V && l >= 0 && l < TILE)
+                atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
         }
-        for (int i = i0; i < c.hist_len + c.extra_len; i += NT) {
+        for (int i = tid + 2 * NT; i < c.hist_len + c.extra_len; i += NT) {
             const int id = i < c.hist_len ? gld(c.hist + i) : gld(c.extra + (i - c.hist_len));
             const int l = id - tb;
             if (id >= 0 && id < c.V && l >= 0 && l < TILE)
                 atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
         }
     }
-    for (int i = tid; i < c.bias_len; i += NT) {
-        const int id = gld(c.bias_ids + i);
+    for (int i = tid; has_bias && i < c.bias_len; i += NT) {
+        const int id = i < NT ? f.bias_id : gld(c.bias_ids + i);
         const int l = id - tb;
         if (id >= 0 && id < c.V && l >= 0 && l < TILE) atomicOr(&t.bias[l >> 5], 1u << (l & 31));
     }
@@ -318,17 +368,17 @@ __device__ __forceinline__ void process_tile(const RowCtx& c, int tb, float v[EP
             const bool hit = (bb >> j) & 1u;
             const bool allowed = (mw >> j) & 1u;
             float x = v[g * L::VEC + j];
-            if (cnt | hit | !allowed) x = process_entry(c, id, x, cnt, hit, allowed);
+            if (cnt | hit | !allowed) x = process_entry_t(c, id, x, cnt, hit, allowed, t);
             v[g * L::VEC + j] = x;
         }
     }
 }
 
 // x' for a single entry (used by acceptance tests). Whole workgroup participates.
-template <int DT>
-__device__ float single_entry(const RowCtx& c, int id, SmemS& sh) {
+template <int DT, int NB>
+__device__ float single_entry(const RowCtx& c, int id, SmemST<NB>& sh) {
     int cnt = 0;
-    for (int i = threadIdx.x; i < c.hist_len + c.extra_len; i += NT) {
+    for (int i = threadIdx.x; i < c.hist_len + c.extra_len; i += NB) {
         const int h = i < c.hist_len ? gld(c.hist + i) : gld(c.extra + (i - c.hist_len));
         cnt += (h == id);
     }
@@ -352,23 +402,17 @@ __device__ __forceinline__ int row_cap(const RowCtx& c) {
 // stage 1: one tile of one row
 
 template <int DT>
-__device__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace& ws, SmemTile& tt,
+__device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace& ws, SmemTile& tt,
                             SmemS& sh, float* dbg_proc_row, float* dbg_probs_row) {
     const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    const int wv = tid / WAVE;
     const int tb = tile * TILE;
     float v[EPT];
     if (c.hist_len + c.extra_len + c.bias_len > 0) {
-        // the row's history and bias lists are small and shared by all its
-        // tiles: fetch them first so the LDS tables build while the tile streams
-        int pre[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int i = (int)threadIdx.x + k * NT;
-            pre[k] = i < c.hist_len ? gld(c.hist + i)
-                     : (i < c.hist_len + c.extra_len ? gld(c.extra + (i - c.hist_len)) : -1);
-        }
+        const TablePrefetch f = prefetch_tables(c);
         load_tile<DT>(c, tb, v);
-        build_tables(c, tb, tt, pre);
+        build_tables(c, tb, tt, f);
     } else {
         load_tile<DT>(c, tb, v);
     }
@@ -403,8 +447,21 @@ __device__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace&
             for (int s = EPT - 1; s >= 0; --s)
                 if (v[s] == m) am = slot_id<DT>(tb, s);
         }
-        am = block_min_i(am, sh.red);
-        nf = block_sum_i(nf, sh.red);
+        // argmin and finite count share one exchange
+        am = wave_min_i(am);
+        nf = wave_sum_i(nf);
+        if (lane == 0) {
+            sh.red.i[wv] = am;
+            sh.red2.i[wv] = nf;
+        }
+        __syncthreads();
+        am = sh.red.i[0];
+        nf = sh.red2.i[0];
+#pragma unroll
+        for (int k = 1; k < NT / WAVE; ++k) {
+            am = min(am, sh.red.i[k]);
+            nf += sh.red2.i[k];
+        }
         st.m = m;
         st.argmax = m > NEG_INF ? am : -1;
         st.s = 0.0;
@@ -412,29 +469,23 @@ __device__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace&
         st.ncand = 0;
         st.nfinite = nf;
     } else {
-        const float srt = block_sort_desc(lm, tt.sorted);
+        // the lane maxima, sorted descending, seed the candidate threshold
+        nf = wave_sum_i(nf);
+        if (lane == 0) sh.red.i[wv] = nf;
+        if (tid == 0) tt.nlist = 0;
+        const float srt = block_sort_desc(lm, tt.lmax);
+        nf = sh.red.i[0] + sh.red.i[1] + sh.red.i[2] + sh.red.i[3];
         tt.sorted[tid] = srt;
         __syncthreads();
         const float m = tt.sorted[0];
-        nf = block_sum_i(nf, sh.red);
-        float theta = NEG_INF;
-        int ncand = nf;
-        if (nf > cap) {
-            const int step = max(1, cap / 8);
-            int L = cap - step;
-            for (;;) {
-                theta = tt.sorted[L];
-                int cnt = 0;
+        // first threshold try and the softmax partial sum in one exchange
+        const int step = max(1, cap / 8);
+        int L = cap - step;
+        const bool cut = nf > cap;
+        float theta = cut ? tt.sorted[L] : NEG_INF;
+        int cnt = 0;
 #pragma unroll
-                for (int s = 0; s < EPT; ++s) cnt += v[s] > theta;
-                cnt = block_sum_i(cnt, sh.red);
-                if (cnt <= cap) {
-                    ncand = cnt;
-                    break;
-                }
-                L = L > step ? L - step : 0;  // L = 0 puts theta at the tile max: no candidates
-            }
-        }
+        for (int s = 0; s < EPT; ++s) cnt += v[s] > theta;
         double ssum = 0.0;
         if (m > NEG_INF) {
             const float c2 = 1.4426950408889634f / c.T;
@@ -443,25 +494,61 @@ __device__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace&
             for (int s = 0; s < EPT; ++s) acc += exp2f((v[s] - m) * c2);
             ssum = acc;
         }
-        ssum = block_sum_d(ssum, sh.red);
+        cnt = wave_sum_i(cnt);
+        ssum = wave_sum_d(ssum);
+        if (lane == 0) {
+            sh.red2.i[wv] = cnt;
+            sh.red2.d[wv] = ssum;
+        }
+        __syncthreads();
+        cnt = sh.red2.i[0] + sh.red2.i[1] + sh.red2.i[2] + sh.red2.i[3];
+        ssum = ((sh.red2.d[0] + sh.red2.d[1]) + sh.red2.d[2]) + sh.red2.d[3];
+        // lower the threshold until the candidates fit (L = 0 puts it at the
+        // tile maximum: no candidates)
+        while (cnt > cap) {
+            L = L > step ? L - step : 0;
+            theta = tt.sorted[L];
+            int k = 0;
+#pragma unroll
+            for (int s = 0; s < EPT; ++s) k += v[s] > theta;
+            cnt = block_sum_i(k, sh.red);
+        }
+        // candidate keys (z = x'/T, id) into LDS, one atomic per wave
         int mine = 0;
 #pragma unroll
         for (int s = 0; s < EPT; ++s) mine += v[s] > theta;
-        int tot;
-        int off = block_excl_scan_i(mine, sh.red, tot);
-        float2* cand = ws.cand + ((size_t)row * ws.n_tiles + tile) * CW;
+        const int inc = wave_incl_scan_i(mine);
+        const int wtot = __builtin_amdgcn_readlane(inc, WAVE - 1);
+        int base = 0;
+        if (lane == 0 && wtot > 0) base = atomicAdd(&tt.nlist, wtot);
+        base = __builtin_amdgcn_readfirstlane(base);
+        int off = base + inc - mine;
 #pragma unroll
         for (int s = 0; s < EPT; ++s) {
             if (v[s] > theta) {
-                cand[off] = make_float2(v[s], __int_as_float(slot_id<DT>(tb, s)));
+                tt.list[off] = key64(canon_zero(v[s] / c.T), slot_id<DT>(tb, s));
                 ++off;
             }
+        }
+        __syncthreads();
+        // sorted list: each key's rank among the tile's candidates
+        unsigned long long* cand = ws.cand + ((size_t)row * ws.n_tiles + tile) * CW;
+        if (tid < cnt) {
+            const unsigned long long my = tt.list[tid];
+            int r = 0;
+            int j = 0;
+            for (; j + 2 <= cnt; j += 2) {
+                const ulonglong2 q = *(const ulonglong2*)&tt.list[j];
+                r += (q.x > my) + (q.y > my);
+            }
+            if (j < cnt) r += tt.list[j] > my;
+            cand[r] = my;
         }
         st.m = m;
         st.argmax = -1;
         st.s = ssum;
         st.beta = theta;
-        st.ncand = ncand;
+        st.ncand = cnt;
         st.nfinite = nf;
     }
     if (tid == 0) ws.stats[(size_t)row * ws.n_tiles + tile] = st;
@@ -486,11 +573,13 @@ struct RowSummary {
     double W;
 };
 
-__device__ RowSummary summarize_tiles(const TileStat* st, int n_tiles, float T) {
+// Lane t of every wave holds tile t's summary (the others an empty one); each
+// wave reduces them identically, so no exchange between waves is needed.
+__device__ __forceinline__ TileStat load_tile_stat(const Workspace& ws, int row) {
     const int lane = threadIdx.x & (WAVE - 1);
     TileStat t;
-    if (lane < n_tiles) {
-        t = st[lane];
+    if (lane < ws.n_tiles) {
+        t = ws.stats[(size_t)row * ws.n_tiles + lane];
     } else {
         t.m = NEG_INF;
         t.argmax = INT_MAX;
@@ -498,7 +587,12 @@ __device__ RowSummary summarize_tiles(const TileStat* st, int n_tiles, float T) 
         t.beta = NEG_INF;
         t.ncand = 0;
         t.nfinite = 0;
+        t.pad = 0;
     }
+    return t;
+}
+
+__device__ RowSummary summarize_tiles(const TileStat& t, float T) {
     RowSummary r;
     r.m = wave_max(t.m);
     r.argmax = wave_min_i((t.m == r.m && t.argmax >= 0) ? t.argmax : INT_MAX);
@@ -523,18 +617,18 @@ __device__ __forceinline__ uint64_t wq(float w) { return (uint64_t)((double)w * 
 template <class Pred>
 __device__ unsigned long long radix_select(const float* zr, int V, float zmax, Pred pred,
                                            bool by_mass, unsigned long long target, SmemRadix& h,
-                                           SmemS& sh) {
+                                           SmemR& sh) {
     const int tid = threadIdx.x;
     unsigned long long prefix = 0, pmask = 0, rem = target;
     int take_last = 0;
     for (int d = 7; d >= 0; --d) {
-        for (int b = tid; b < 256; b += NT) {
+        for (int b = tid; b < 256; b += NTR) {
             h.hc[b] = 0;
             h.hm[b] = 0;
         }
         __syncthreads();
         const int sft = d * 8;
-        for (int v = tid; v < V; v += NT) {
+        for (int v = tid; v < V; v += NTR) {
             const float z = zr[v];
             if (!(z > NEG_INF)) continue;
             const unsigned long long k = key64(z, v);
@@ -582,10 +676,10 @@ __device__ unsigned long long radix_select(const float* zr, int V, float zmax, P
 
 template <class Pred>
 __device__ void count_and_mass(const float* zr, int V, float zmax, Pred pred, int& count,
-                               unsigned long long& mass, SmemS& sh) {
+                               unsigned long long& mass, SmemR& sh) {
     int cnt = 0;
     unsigned long long ms = 0;
-    for (int v = threadIdx.x; v < V; v += NT) {
+    for (int v = threadIdx.x; v < V; v += NTR) {
         const float z = zr[v];
         if (!(z > NEG_INF)) continue;
         const float w = expf(z - zmax);
@@ -598,35 +692,42 @@ __device__ void count_and_mass(const float* zr, int V, float zmax, Pred pred, in
     // u64 sum: exact in any order
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ms += __shfl_xor(ms, o);
-    __shared__ unsigned long long part[NT / WAVE];
+    __shared__ unsigned long long part[NTR / WAVE];
     if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x / WAVE] = ms;
     __syncthreads();
     unsigned long long t = 0;
 #pragma unroll
-    for (int k = 0; k < NT / WAVE; ++k) t += part[k];
+    for (int k = 0; k < NTR / WAVE; ++k) t += part[k];
     __syncthreads();
     mass = t;
 }
 
-// Exact whole-row resolution: recompute z for the whole row into scratch, then
-// select by count (top-k) and by mass (top-p, the draw) with radix passes.
+// Exact whole-row resolution: recompute z for the whole row into scratch (the
+// first NT threads, one tile at a time), then select by count (top-k) and by
+// mass (top-p, the draw) with radix passes over the whole workgroup.
 template <int DT>
 __device__ __noinline__ void finalize_slow(const RowCtx& c, int row, const Workspace& ws,
                                            int n_tiles, const RowSummary& rs, float u, SmemU& su,
-                                           SmemS& sh, RowInfo& info, const RowDbg& dbg) {
+                                           SmemR& sh, RowInfo& info, const RowDbg& dbg) {
     const int tid = threadIdx.x;
     const int V = c.V;
+    const bool tl = tid < NT;
     float* zr = ws.scratch_z + (size_t)row * V;
+    const bool tables = c.hist_len + c.extra_len + c.bias_len > 0;
+    TablePrefetch f = {{-1, -1}, -1, 0.0f};
+    if (tables && tl) f = prefetch_tables(c);
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
         float v[EPT];
-        load_tile<DT>(c, t * TILE, v);
-        if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, t * TILE, su.t);
-        process_tile<DT>(c, t * TILE, v, su.t);
+        if (tl) load_tile<DT>(c, t * TILE, v);
+        if (tables) build_tables(c, t * TILE, su.t, f, tl);
+        if (tl) {
+            process_tile<DT>(c, t * TILE, v, su.t);
 #pragma unroll
-        for (int s = 0; s < EPT; ++s) {
-            const int id = slot_id<DT>(t * TILE, s);
-            if (id < V) zr[id] = v[s] > NEG_INF ? canon_zero(v[s] / c.T) : NEG_INF;
+            for (int s = 0; s < EPT; ++s) {
+                const int id = slot_id<DT>(t * TILE, s);
+                if (id < V) zr[id] = v[s] > NEG_INF ? canon_zero(v[s] / c.T) : NEG_INF;
+            }
         }
         __syncthreads();
     }
@@ -666,7 +767,7 @@ __device__ __noinline__ void finalize_slow(const RowCtx& c, int row, const Works
     }
     if (dbg.probs) {
         const double Wd = (double)Wk / MASS_SCALE;
-        for (int v = tid; v < V; v += NT) {
+        for (int v = tid; v < V; v += NTR) {
             const float z = zr[v];
             float p = 0.0f;
             if (z > NEG_INF) {
@@ -678,19 +779,19 @@ __device__ __noinline__ void finalize_slow(const RowCtx& c, int row, const Works
     }
     if (dbg.topk) {
         int base = 0;
-        for (int v0 = 0; v0 < V; v0 += NT) {
+        for (int v0 = 0; v0 < V; v0 += NTR) {
             const int v = v0 + tid;
-            bool f = false;
+            bool fl = false;
             if (topk_on && v < V) {
                 const float z = zr[v];
-                f = z > NEG_INF && key64(z, v) >= kK;
+                fl = z > NEG_INF && key64(z, v) >= kK;
             }
             int tot;
-            const int off = block_excl_scan_i(f ? 1 : 0, sh.red, tot);
-            if (f && base + off < dbg.topk_stride) dbg.topk[base + off] = v;
+            const int off = block_excl_scan_i(fl ? 1 : 0, sh.red, tot);
+            if (fl && base + off < dbg.topk_stride) dbg.topk[base + off] = v;
             base += tot;
         }
-        for (int i = (topk_on ? min(base, dbg.topk_stride) : 0) + tid; i < dbg.topk_stride; i += NT)
+        for (int i = (topk_on ? min(base, dbg.topk_stride) : 0) + tid; i < dbg.topk_stride; i += NTR)
             dbg.topk[i] = -1;
     }
     if (tid == 0) {
@@ -701,384 +802,264 @@ __device__ __noinline__ void finalize_slow(const RowCtx& c, int row, const Works
 }
 
 // ---------------------------------------------------------------------------
-// pool helpers
+// the sorted pool
 
-// Appends the lanes whose pred is true to an LDS list: one atomic per wave.
-__device__ __forceinline__ int wave_append(bool pred, int* counter) {
-    const unsigned long long m = __ballot(pred);
-    const int lane = threadIdx.x & (WAVE - 1);
-    int base = 0;
-    if (m) {
-        const int leader = __ffsll((long long)m) - 1;
-        if (lane == leader) base = atomicAdd(counter, __popcll(m));
-        base = __shfl(base, leader);
-    }
-    return base + __popcll(m & __lanemask_lt());
+__device__ __forceinline__ float key_z(unsigned long long k) {
+    const uint32_t m = (uint32_t)(k >> 32);
+    return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
 }
 
-// Key of the rank-th (1-based) pool entry in key order: radix passes over the
-// 64-bit key (z then id), stopping as soon as the target's bucket is a single
-// entry.
-__device__ unsigned long long pool_select(const float* pz, const int* pid, int n, int rank,
-                                          uint32_t* hc, SmemS& sh) {
-    const int tid = threadIdx.x;
-    const int lane = tid & (WAVE - 1);
-    unsigned long long prefix = 0, pmask = 0;
-    int rem = rank;
-    for (int d = 7; d >= 0; --d) {
-        const int sft = d * 8;
-        if (tid < 256) hc[tid] = 0;
-        __syncthreads();
-        for (int i = tid; i < n; i += NT) {
-            const unsigned long long k = key64(pz[i], pid[i]);
-            if ((k & pmask) == prefix) atomicAdd(&hc[(k >> sft) & 255ull], 1u);
-        }
-        __syncthreads();
-        if (tid < WAVE) {
-            // lane l holds buckets 255-4l .. 252-4l, i.e. descending key order
-            uint32_t cb[4];
-            int s = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                cb[j] = hc[255 - 4 * lane - j];
-                s += (int)cb[j];
-            }
-            const int inc = wave_incl_scan_i(s);
-            const int exc = inc - s;
-            const bool hit = exc < rem && rem <= inc;
-            if (hit) {
-                int r = rem - exc;
-                for (int j = 0; j < 4; ++j) {
-                    if (r <= (int)cb[j]) {
-                        sh.sel = 255 - 4 * lane - j;
-                        sh.cnt = (int)cb[j];
-                        sh.rem = (unsigned long long)r;
-                        break;
-                    }
-                    r -= (int)cb[j];
-                }
-            }
-        }
-        __syncthreads();
-        prefix |= (unsigned long long)sh.sel << sft;
-        pmask |= 255ull << sft;
-        rem = (int)sh.rem;
-        const int cnt = sh.cnt;
-        __syncthreads();
-        if (cnt == 1 || d == 0) {
-            if (d > 0) {
-                for (int i = tid; i < n; i += NT) {
-                    const unsigned long long k = key64(pz[i], pid[i]);
-                    if ((k & pmask) == prefix) sh.key = k;
-                }
-                __syncthreads();
-                prefix = sh.key;
-                __syncthreads();
-            }
-            return prefix;
-        }
-    }
-    return prefix;
-}
-
-// Sorts one (z, id) pair per thread into key order across the workgroup.
-__device__ __forceinline__ void block_sort_pairs(float& z, int& id, float* tz, int* ti) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int k = 2; k <= NT; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            float oz;
-            int oi;
-            if (j >= WAVE) {
-                tz[tid] = z;
-                ti[tid] = id;
-                __syncthreads();
-                oz = tz[tid ^ j];
-                oi = ti[tid ^ j];
-                __syncthreads();
-            } else {
-                oz = __shfl_xor(z, j);
-                oi = __shfl_xor(id, j);
-            }
-            const bool desc = (tid & k) == 0;
-            const bool lower = (tid & j) == 0;
-            const bool mine_first = key_before(z, id, oz, oi);
-            const bool keep = (lower == desc) ? mine_first : !mine_first;
-            if (!keep) {
-                z = oz;
-                id = oi;
-            }
-        }
-    }
-}
-
-// Finds the first index i in [0, lim) of the sorted pool satisfying pred(i, excl,
-// incl, w), scanning each thread's contiguous chunk with binary64 prefix sums.
-template <class Pred>
-__device__ int pool_first(int lim, int cs, const SmemPool& p, float zmax, double base, Pred pred,
-                          SmemS& sh) {
-    int found = INT_MAX;
-    double run = base;
-    const int i0 = (int)threadIdx.x * cs;
-    for (int k = 0; k < cs; ++k) {
-        const int i = i0 + k;
-        if (i >= lim) break;
-        const float wf = expf(p.z[i] - zmax);
-        const double w = (double)wf;
-        if (pred(i, run, run + w, wf)) {
-            found = i;
-            break;
-        }
-        run += w;
-    }
-    return block_min_i(found, sh.red);
-}
-
-__device__ __forceinline__ double pool_prefix_sum(int lim, int cs, const SmemPool& p, float zmax) {
-    double s = 0.0;
-    const int i0 = (int)threadIdx.x * cs;
-    for (int k = 0; k < cs; ++k) {
-        const int i = i0 + k;
-        if (i >= lim) break;
-        s += (double)expf(p.z[i] - zmax);
-    }
+// Prefix mass S(x) = sum of w over the first x pool entries, from the chunk
+// bases: every thread computes it in the same order, so all agree exactly.
+__device__ __forceinline__ double prefix_mass(const SmemPool& p, const unsigned long long* f, int x,
+                                              int cs, float zmax) {
+    int ch = x / cs;
+    if (ch >= NTR) ch = NTR - 1;
+    double s = p.cbase[ch];
+    for (int i = ch * cs; i < x; ++i) s += (double)expf(key_z(f[i]) - zmax);
     return s;
 }
 
-// The deep path: sort the whole pool (bitonic in LDS) and resolve on it.
-// Returns false if the request reaches past the pool (then the caller runs the
-// whole-row fallback).
-__device__ __noinline__ bool finalize_deep(const RowCtx& c, int n, const RowSummary& rs, float zmax,
-                                           float u, SmemPool& p, SmemS& sh, RowInfo& info,
-                                           const RowDbg& dbg) {
+// Minimum over the workgroup of one int per thread (two values at once).
+__device__ __forceinline__ int2 rows_min2(int a, int b, SmemR& sh) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = threadIdx.x / WAVE;
+    a = wave_min_i(a);
+    b = wave_min_i(b);
+    __syncthreads();
+    if (lane == 0) {
+        sh.red.i[wv] = a;
+        sh.red2.i[wv] = b;
+    }
+    __syncthreads();
+    int ra = INT_MAX, rb = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < NTR / WAVE; ++k) {
+        ra = min(ra, sh.red.i[k]);
+        rb = min(rb, sh.red2.i[k]);
+    }
+    return make_int2(ra, rb);
+}
+
+// What the merge reads from stage 1: the row's candidate slots and the tile
+// summaries (lane t holds tile t). Issued before anything else so the row's
+// loads share one round trip.
+struct RowLoad {
+    unsigned long long cv[PERR];
+    TileStat ts;
+};
+
+__device__ __forceinline__ RowLoad row_load(const Workspace& ws, int row) {
+    RowLoad l;
+    const int n_tiles = ws.n_tiles;
+    const unsigned long long* cand = ws.cand + (size_t)row * n_tiles * CW;
+#pragma unroll
+    for (int k = 0; k < PERR; ++k) {
+        const int g = (int)threadIdx.x + k * NTR;
+        l.cv[k] = g < n_tiles * CW ? gld(cand + g) : 0ull;
+    }
+    l.ts = load_tile_stat(ws, row);
+    return l;
+}
+
+// One merge level over slots tid + r NTR, r < R (slot layout, segments of C
+// slots padded with zero keys): each kept entry moves to its index plus the
+// number of partner entries before it, each empty slot to the tail of its
+// merged segment. The R searches advance together so their LDS reads overlap.
+template <int R>
+__device__ __forceinline__ void merge_level(const unsigned long long* in, unsigned long long* out,
+                                            const int* len, int C, int lg, int nslots) {
     const int tid = threadIdx.x;
-    const int V = c.V;
-    int n_pad = 1;
-    while (n_pad < n) n_pad <<= 1;
-    for (int i = n + tid; i < n_pad; i += NT) {
-        p.z[i] = NEG_INF;
-        p.id[i] = INT_MAX;
+    unsigned long long key[R];
+    int pos[R], pb[R], ob[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int g = tid + r * NTR;
+        const int gg = g < nslots ? g : 0;
+        key[r] = in[gg];
+        const int sg = gg / C;
+        const int i = gg - sg * C;
+        const int lo = len[sg];
+        const int le = len[sg & ~1], lr = len[sg | 1];
+        pb[r] = (sg ^ 1) * C;
+        pos[r] = 0;
+        if (g >= nslots) ob[r] = -1;
+        else if (i < lo) ob[r] = (sg & ~1) * C + i;  // plus the partner count
+        else ob[r] = -2 - ((sg & ~1) * C + le + lr + ((sg & 1) ? (C - le) : 0) + (i - lo));
     }
-    __syncthreads();
-    for (int k = 2; k <= n_pad; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < n_pad; i += NT) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const float za = p.z[i], zb = p.z[ixj];
-                    const int ia = p.id[i], ib = p.id[ixj];
-                    const bool a_first = key_before(za, ia, zb, ib);
-                    const bool desc = (i & k) == 0;
-                    if (desc ? !a_first : a_first) {
-                        p.z[i] = zb;
-                        p.z[ixj] = za;
-                        p.id[i] = ib;
-                        p.id[ixj] = ia;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+    for (int bit = lg - 1; bit >= 0; --bit) {
+        unsigned long long x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = in[pb[r] + pos[r] + (1 << bit) - 1];
+#pragma unroll
+        for (int r = 0; r < R; ++r) pos[r] += x[r] > key[r] ? (1 << bit) : 0;
     }
-    const int cs = n_pad > NT ? n_pad / NT : 1;
-    double totw;
-    const double base = block_excl_scan_d(pool_prefix_sum(n, cs, p, zmax), sh.red, totw);
-    const int total = rs.nfinite;
-    const bool topk_on = c.top_k > 0 && c.top_k < V;
-    const int K_eff = topk_on ? min(c.top_k, total) : total;
-    const bool cut_k = topk_on && K_eff < total;
-    if ((cut_k && K_eff > n) || (dbg.topk && topk_on && !cut_k && total > n)) return false;
-    double WK = rs.W;
-    if (cut_k) WK = block_sum_d(pool_prefix_sum(K_eff, cs, p, zmax), sh.red);
-    int n_topp = cut_k ? K_eff : total;
-    if (c.top_p < 1.0f) {
-        const double thr = (double)c.top_p * WK;
-        const int f = pool_first(min(n, n_topp), cs, p, zmax, base,
-                                 [thr](int, double ex, double, float) { return ex >= thr; }, sh);
-        if (f != INT_MAX) n_topp = f;
-        else if (n_topp > n) return false;
+    {
+        unsigned long long x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = in[pb[r] + pos[r]];
+#pragma unroll
+        for (int r = 0; r < R; ++r) pos[r] += x[r] > key[r] ? 1 : 0;
     }
-    int n_kept = n_topp;
-    if (c.min_p > 0.0f) {
-        const float mp = c.min_p;
-        const int f = pool_first(min(n, n_topp), cs, p, zmax, base,
-                                 [mp](int, double, double, float w) { return w < mp; }, sh);
-        if (f != INT_MAX) n_kept = f;
-        else if (n_topp > n) return false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (ob[r] >= 0) out[ob[r] + pos[r]] = key[r];
+        else if (ob[r] <= -2) out[-2 - ob[r]] = 0ull;
     }
-    if (dbg.probs && n_kept > n) return false;
-    double Wk = rs.W;
-    if (n_kept < total) Wk = block_sum_d(pool_prefix_sum(n_kept, cs, p, zmax), sh.red);
-    const double tgt = (double)u * Wk;
-    const int f = pool_first(min(n, n_kept), cs, p, zmax, base,
-                             [tgt](int, double, double in, float) { return in > tgt; }, sh);
-    int token;
-    if (f != INT_MAX) token = p.id[f];
-    else if (n_kept <= n) token = p.id[n_kept - 1];
-    else return false;
-    if (tid == 0) {
-        info.kappa = n_kept < total ? key64(p.z[n_kept - 1], p.id[n_kept - 1]) : 0ull;
-        info.W = Wk;
-        info.zmax = zmax;
-        info.min_p = 0.0f;
-        info.n_kept = n_kept;
-        info.token = token;
-        info.argmax = -1;
-        info.path = 0;
-        if (dbg.kept) *dbg.kept = n_kept;
-        if (dbg.path) *dbg.path = 0;
-    }
-    if (dbg.probs)
-        for (int i = tid; i < n_kept; i += NT)
-            dbg.probs[p.id[i]] = (float)((double)expf(p.z[i] - zmax) / Wk);
-    if (dbg.topk) {
-        const int lim = cut_k ? K_eff : (topk_on ? total : 0);
-        for (int i = tid; i < dbg.topk_stride; i += NT)
-            dbg.topk[i] = (i < lim && i < n) ? p.id[i] : -1;
-    }
-    __syncthreads();
-    return true;
 }
 
 template <int DT>
-__device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Workspace& ws, float u, SmemU& su,
-                             SmemS& sh, const RowDbg& dbg, RowInfo& info_out) {
+__device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Workspace& ws,
+                                             const RowLoad& rl, float u, SmemU& su, SmemR& sh,
+                                             const RowDbg& dbg, RowInfo& info_out) {
     const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    const int wv = tid / WAVE;
     const int n_tiles = ws.n_tiles;
     const int V = c.V;
-    // issue the stats and every candidate slot together: one round trip
-    constexpr int PER = POOL / NT;
-    const float2* cand = ws.cand + (size_t)row * n_tiles * CW;
-    float2 cv[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int g = tid + k * NT;
-        cv[k] = g < n_tiles * CW ? gld(cand + g) : make_float2(NEG_INF, 0.0f);
-    }
-    if (tid < n_tiles) su.p.st[tid] = ws.stats[(size_t)row * n_tiles + tid];
-    if (tid == 0) sh.nhead = 0;
-    __syncthreads();
-    const RowSummary rs = summarize_tiles(su.p.st, n_tiles, c.T);
+    SmemPool& P = su.p;
+    const TileStat& ts = rl.ts;
+    const RowSummary rs = summarize_tiles(ts, c.T);
 
     __shared__ RowInfo info;
-    if (tid == 0) {
-        info.kappa = 0;
-        info.W = 1.0;
-        info.zmax = rs.m;
-        info.min_p = 0.0f;
-        info.n_kept = rs.m > NEG_INF ? 1 : 0;
-        info.token = rs.m > NEG_INF ? rs.argmax : -1;
-        info.argmax = rs.m > NEG_INF ? rs.argmax : -1;
-        info.path = 0;
-    }
     if (c.T == 0.0f || !(rs.m > NEG_INF)) {
-        __syncthreads();
+        RowInfo r;
+        r.kappa = 0;
+        r.W = 1.0;
+        r.zmax = rs.m;
+        r.min_p = 0.0f;
+        r.n_kept = rs.m > NEG_INF ? 1 : 0;
+        r.token = rs.m > NEG_INF ? rs.argmax : -1;
+        r.argmax = r.token;
+        r.path = 0;
         if (dbg.topk)
-            for (int i = tid; i < dbg.topk_stride; i += NT) dbg.topk[i] = -1;
+            for (int i = tid; i < dbg.topk_stride; i += NTR) dbg.topk[i] = -1;
         if (tid == 0) {
-            if (dbg.probs && info.token >= 0) dbg.probs[info.token] = 1.0f;
-            if (dbg.kept) *dbg.kept = info.n_kept;
+            if (dbg.probs && r.token >= 0) dbg.probs[r.token] = 1.0f;
+            if (dbg.kept) *dbg.kept = r.n_kept;
             if (dbg.path) *dbg.path = 0;
         }
-        __syncthreads();
-        info_out = info;
+        info_out = r;
         return;
     }
-    // the union of candidates above the highest tile threshold is exact: gather
-    // it into LDS in slot order with one scan
+    // The pool: every entry with z above the highest tile threshold. It is a
+    // prefix of each tile's sorted list and, as a whole, an exact prefix of the
+    // row in key order. Slot layout: tile t owns slots [t CW, (t + 1) CW), its
+    // kept entries first and zero keys after them, up to a power-of-two number
+    // of tiles, so every merge segment is padded with keys that precede none.
     const float zmax = canon_zero(rs.m / c.T);
     const float zb = rs.beta > NEG_INF ? canon_zero(rs.beta / c.T) : NEG_INF;
-    uint32_t keepm = 0;
+    const uint32_t mzb = mono32(zb);
+    int npad = 1;
+    while (npad < n_tiles) npad *= 2;
+    // slots per tile: the row's candidate cap rounded up to a power of two
+    int sw = 8;
+    while (sw < row_cap(c)) sw *= 2;
+    int lsw = 3;
+    while ((1 << lsw) < sw) ++lsw;
+    const int nslots = npad * sw;
+    const int oct = __builtin_amdgcn_readfirstlane(tid / CW);
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int g = tid + k * NT;
-        if (g < n_tiles * CW && (g % CW) < su.p.st[g / CW].ncand) {
-            const float z = canon_zero(cv[k].x / c.T);
-            if (z > zb) {
-                keepm |= 1u << k;
-                cv[k].x = z;
-            }
+    for (int k = 0; k < PERR; ++k) {
+        const int g = tid + k * NTR;
+        const int t = OCT * k + oct;  // tile of candidate slot g
+        const int i = g % CW;
+        bool keep = false;
+        if (t < n_tiles) {
+            const int nc = __builtin_amdgcn_readlane(ts.ncand, t);
+            keep = i < nc && (uint32_t)(rl.cv[k] >> 32) > mzb;
         }
-    }
-    int n;
-    {
-        int off = block_excl_scan_i(__popc(keepm), sh.red, n);
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            if (keepm & (1u << k)) {
-                su.p.z[off] = cv[k].x;
-                su.p.id[off] = __float_as_int(cv[k].y);
-                ++off;
-            }
-        }
+        if (t < npad && i < sw) P.buf[0][t * sw + i] = keep ? rl.cv[k] : 0ull;
+        const int wc = __popcll(__ballot(keep));
+        if (lane == 0) P.wcnt[k][wv] = wc;
     }
     __syncthreads();
+    if (tid < MAX_TILES) {
+        const int t = tid;
+        const int k = t / OCT, o = t % OCT;
+        P.len[0][t] = t < n_tiles ? P.wcnt[k][2 * o] + P.wcnt[k][2 * o + 1] : 0;
+    }
+    __syncthreads();
+    // Merge tree: level l merges segments of 2^l tiles. An entry's output
+    // position is its index in its segment plus the number of partner entries
+    // that precede it (binary search over the padded partner segment); empty
+    // slots fill the tail of each merged segment with zero keys.
+    int src = 0;
+    for (int seg_tiles = 1, lg = lsw; seg_tiles < n_tiles; seg_tiles *= 2, ++lg) {
+        const int C = seg_tiles * sw;
+        const unsigned long long* in = P.buf[src];
+        unsigned long long* out = P.buf[src ^ 1];
+        const int* len = P.len[src];
+        if (nslots <= NTR)
+            merge_level<1>(in, out, len, C, lg, nslots);
+        else if (nslots <= 2 * NTR)
+            merge_level<2>(in, out, len, C, lg, nslots);
+        else
+            merge_level<PERR>(in, out, len, C, lg, nslots);
+        if (tid < MAX_TILES) {
+            const int j = tid;
+            P.len[src ^ 1][j] = 2 * j + 1 < MAX_TILES ? len[2 * j] + len[2 * j + 1] : 0;
+        }
+        __syncthreads();
+        src ^= 1;
+    }
+    const int n = P.len[src][0];
+    const unsigned long long* F = P.buf[src];
+
     const int total = rs.nfinite;
     const bool topk_on = c.top_k > 0 && c.top_k < V;
     const int K_eff = topk_on ? min(c.top_k, total) : total;
     const bool cut_k = topk_on && K_eff < total;
     bool slow = n == 0 || (cut_k && K_eff > n);
-    bool deep = false;
-    int n_kept = 0, token = -1;
-    double Wk = rs.W;
-    unsigned long long kappa = 0, kK = 0;
-    int nh = 0;
     if (!slow) {
-        // head: the first min(n, 256) pool entries in key order, one per thread
-        unsigned long long khead = 0;
-        if (n > NT) khead = pool_select(su.p.z, su.p.id, n, NT, su.p.hc, sh);
-        for (int i0 = 0; i0 < n; i0 += NT) {
-            const int i = i0 + tid;
-            const bool in = i < n && key64(su.p.z[i], su.p.id[i]) >= khead;
-            const int pos = wave_append(in, &sh.nhead);
-            if (in) {
-                su.p.hz[pos] = su.p.z[i];
-                su.p.hid[pos] = su.p.id[i];
-            }
-        }
+        // binary64 prefix masses over contiguous chunks of the sorted pool
+        const int cs = (n + NTR - 1) / NTR;
+        const int i0 = min(tid * cs, n);
+        const int i1 = min(i0 + cs, n);
+        double part = 0.0;
+        for (int i = i0; i < i1; ++i) part += (double)expf(key_z(F[i]) - zmax);
+        const double winc = wave_incl_scan_d(part);
+        if (lane == WAVE - 1) sh.red.d[wv] = winc;
         __syncthreads();
-        nh = sh.nhead;
-        float hz = tid < nh ? su.p.hz[tid] : NEG_INF;
-        int hid = tid < nh ? su.p.hid[tid] : INT_MAX;
+        double base = winc - part;
+        for (int k = 0; k < wv; ++k) base += sh.red.d[k];
+        P.cbase[tid] = base;
         __syncthreads();
-        block_sort_pairs(hz, hid, su.p.hz, su.p.hid);
-        const float w = tid < nh ? expf(hz - zmax) : 0.0f;
-        double toth;
-        const double excl = block_excl_scan_d((double)w, sh.red, toth);
-        const double incl = excl + (double)w;
-        // top-k boundary and its mass
         double WK = rs.W;
+        unsigned long long kK = 0;
         if (cut_k) {
-            if (K_eff <= nh) {
-                WK = block_sum_d(tid < K_eff ? (double)w : 0.0, sh.red);
-                if (tid == K_eff - 1) sh.key = key64(hz, hid);
-                __syncthreads();
-                kK = sh.key;
-            } else {
-                kK = pool_select(su.p.z, su.p.id, n, K_eff, su.p.hc, sh);
-                double part = 0.0;
-                for (int i = tid; i < n; i += NT)
-                    if (key64(su.p.z[i], su.p.id[i]) >= kK) part += (double)expf(su.p.z[i] - zmax);
-                WK = block_sum_d(part, sh.red);
+            WK = prefix_mass(P, F, K_eff, cs, zmax);
+            kK = F[K_eff - 1];
+        }
+        // top-p cut and min-p cut in one pass over the chunks
+        const int lim_p = cut_k ? K_eff : total;
+        const double thr = (double)c.top_p * WK;
+        int fp = INT_MAX, fm = INT_MAX;
+        {
+            double run = base;
+            for (int i = i0; i < i1; ++i) {
+                const float w = expf(key_z(F[i]) - zmax);
+                if (fp == INT_MAX && c.top_p < 1.0f && i < lim_p && run >= thr) fp = i;
+                if (fm == INT_MAX && c.min_p > 0.0f && w < c.min_p) fm = i;
+                run += (double)w;
             }
         }
-        int n_topp = cut_k ? K_eff : total;
+        const int2 fpm = rows_min2(fp, fm, sh);
+        fp = fpm.x;
+        fm = fpm.y;
+        int n_topp = lim_p;
         if (c.top_p < 1.0f) {
-            const double thr = (double)c.top_p * WK;
-            const int lim = min(nh, n_topp);
-            const int f = block_min_i(tid < lim && excl >= thr ? tid : INT_MAX, sh.red);
-            if (f != INT_MAX) n_topp = f;
-            else if (n_topp > nh) deep = true;
+            if (fp != INT_MAX) n_topp = fp;
+            else if (lim_p > n) slow = true;
         }
-        n_kept = n_topp;
-        if (!deep && c.min_p > 0.0f) {
-            const int lim = min(nh, n_topp);
-            const int cnt = block_sum_i(tid < lim && w >= c.min_p ? 1 : 0, sh.red);
-            if (cnt < lim) n_kept = cnt;
-            else if (n_topp > nh) deep = true;
+        int n_kept = n_topp;
+        if (!slow && c.min_p > 0.0f) {
+            if (fm < n_topp) n_kept = fm;
+            else if (fm == INT_MAX && n_topp > n) slow = true;
         }
-        if (!deep) {
+        if (!slow) {
+            double Wk;
+            unsigned long long kappa;
             if (n_kept == total) {
                 Wk = rs.W;
                 kappa = 0;
@@ -1086,78 +1067,52 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
                 Wk = WK;
                 kappa = kK;
             } else {
-                Wk = block_sum_d(tid < n_kept ? (double)w : 0.0, sh.red);
-                if (tid == n_kept - 1) sh.key = key64(hz, hid);
-                __syncthreads();
-                kappa = sh.key;
+                Wk = prefix_mass(P, F, n_kept, cs, zmax);
+                kappa = F[n_kept - 1];
             }
+            // the draw: first kept entry whose inclusive mass exceeds u W
             const double tgt = (double)u * Wk;
-            const int lim = min(nh, n_kept);
-            const int f = block_min_i(tid < lim && incl > tgt ? tid : INT_MAX, sh.red);
-            const int pick = f != INT_MAX ? f : (n_kept <= nh ? n_kept - 1 : -1);
-            if (pick < 0) deep = true;
-            else {
-                if (tid == pick) sh.fid = hid;
-                __syncthreads();
-                token = sh.fid;
+            int fd = INT_MAX;
+            {
+                double run = base;
+                const int lim = min(n, n_kept);
+                for (int i = i0; i < min(i1, lim); ++i) {
+                    run += (double)expf(key_z(F[i]) - zmax);
+                    if (run > tgt) {
+                        fd = i;
+                        break;
+                    }
+                }
             }
-        }
-        if (!deep) {
+            fd = rows_min2(fd, INT_MAX, sh).x;
+            const int pick = fd != INT_MAX ? fd : (n_kept <= n ? n_kept - 1 : -1);
             // debug outputs need the kept / top-k sets listed in full
-            const bool kept_listed = n_kept <= nh || (cut_k && n_kept == K_eff) || total <= n;
-            const bool topk_listed = !topk_on || (cut_k ? true : total <= n);
-            if ((dbg.probs && !kept_listed) || (dbg.topk && !topk_listed)) slow = true;
-            else {
+            const int lim_list = cut_k ? K_eff : (topk_on ? total : 0);
+            if (pick < 0 || (dbg.probs && n_kept > n) || (dbg.topk && lim_list > n)) {
+                slow = true;
+            } else {
+                RowInfo r;
+                r.kappa = kappa;
+                r.W = Wk;
+                r.zmax = zmax;
+                r.min_p = 0.0f;
+                r.n_kept = n_kept;
+                r.token = key64_id(F[pick]);
+                r.argmax = -1;
+                r.path = 0;
                 if (tid == 0) {
-                    info.kappa = kappa;
-                    info.W = Wk;
-                    info.zmax = zmax;
-                    info.min_p = 0.0f;
-                    info.n_kept = n_kept;
-                    info.token = token;
-                    info.argmax = -1;
-                    info.path = 0;
                     if (dbg.kept) *dbg.kept = n_kept;
                     if (dbg.path) *dbg.path = 0;
                 }
-                if (dbg.probs) {
-                    if (n_kept <= nh) {
-                        if (tid < n_kept) dbg.probs[hid] = (float)((double)w / Wk);
-                    } else {
-                        for (int i = tid; i < n; i += NT) {
-                            if (key64(su.p.z[i], su.p.id[i]) >= kappa)
-                                dbg.probs[su.p.id[i]] = (float)((double)expf(su.p.z[i] - zmax) / Wk);
-                        }
-                    }
-                }
-                if (dbg.topk) {
-                    const int lim = cut_k ? K_eff : (topk_on ? total : 0);
-                    __syncthreads();
-                    if (tid == 0) sh.cnt = 0;
-                    __syncthreads();
-                    for (int i0 = 0; i0 < n; i0 += NT) {
-                        const int i = i0 + tid;
-                        const bool in = lim > 0 && i < n &&
-                                        (cut_k ? key64(su.p.z[i], su.p.id[i]) >= kK : true);
-                        const int pos = wave_append(in, &sh.cnt);
-                        if (in && pos < dbg.topk_stride) dbg.topk[pos] = su.p.id[i];
-                    }
-                    __syncthreads();
-                    for (int i = min(lim, dbg.topk_stride) + tid; i < dbg.topk_stride; i += NT)
-                        dbg.topk[i] = -1;
-                }
-                __syncthreads();
-                info_out = info;
+                if (dbg.probs)
+                    for (int i = tid; i < n_kept; i += NTR)
+                        dbg.probs[key64_id(F[i])] = (float)((double)expf(key_z(F[i]) - zmax) / Wk);
+                if (dbg.topk)
+                    for (int i = tid; i < dbg.topk_stride; i += NTR)
+                        dbg.topk[i] = i < lim_list ? key64_id(F[i]) : -1;
+                info_out = r;
                 return;
             }
-        }
-    }
-    __syncthreads();
-    if (!slow && deep) {
-        if (finalize_deep(c, n, rs, zmax, u, su.p, sh, info, dbg)) {
-            __syncthreads();
-            info_out = info;
-            return;
         }
     }
     finalize_slow<DT>(c, row, ws, n_tiles, rs, u, su, sh, info, dbg);
@@ -1213,10 +1168,11 @@ __global__ __launch_bounds__(NT) void k_sample_tiles(SampleArgs a) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(NT) void k_sample_rows(SampleArgs a) {
+__global__ __launch_bounds__(NTR) void k_sample_rows(SampleArgs a) {
     __shared__ SmemU su;
-    __shared__ SmemS sh;
+    __shared__ SmemR sh;
     const int row = xcd_linear(a.B);
+    const RowLoad rl = row_load(a.ws, row);
     const RowCtx c = sample_ctx<DT>(a, row);
     const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
     RowDbg dbg;
@@ -1226,7 +1182,7 @@ __global__ __launch_bounds__(NT) void k_sample_rows(SampleArgs a) {
     dbg.probs = a.dbg_probs ? a.dbg_probs + (size_t)row * a.V : nullptr;
     dbg.path = a.dbg_path ? a.dbg_path + row : nullptr;
     RowInfo info;
-    finalize_row<DT>(c, row, a.ws, u, su, sh, dbg, info);
+    finalize_row<DT>(c, row, a.ws, rl, u, su, sh, dbg, info);
     if (threadIdx.x == 0) a.out_tokens[row] = info.token;
 }
 
@@ -1248,18 +1204,19 @@ __global__ __launch_bounds__(NT) void k_spec_tiles(SpecArgs a) {
 // test of the draft token at that position (draft rows) or the bonus token
 // (last row).
 template <int DT>
-__global__ __launch_bounds__(NT) void k_spec_rows(SpecArgs a) {
+__global__ __launch_bounds__(NTR) void k_spec_rows(SpecArgs a) {
     __shared__ SmemU su;
-    __shared__ SmemS sh;
+    __shared__ SmemR sh;
     const int G1 = a.G + 1;
     const int row = xcd_linear(a.B * G1);
     const int b = row / G1;
     const int j = row % G1;
+    const RowLoad rl = row_load(a.ws, row);
     const RowCtx c = spec_ctx<DT>(a, b, j);
     RowDbg dbg = {nullptr, 0, nullptr, nullptr, nullptr};
     const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
     RowInfo info;
-    finalize_row<DT>(c, row, a.ws, u, su, sh, dbg, info);
+    finalize_row<DT>(c, row, a.ws, rl, u, su, sh, dbg, info);
     if (j < a.G) {
         const int d = a.draft_tokens[(size_t)b * a.G + j];
         int acc;
@@ -1318,7 +1275,7 @@ __device__ void residual_values(const RowCtx& c, const RowInfo& ri, const float*
                                 bool use_pi, SmemTile& tt, double r[EPT]) {
     float v[EPT];
     load_tile<DT>(c, tb, v);
-    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt);
+    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, prefetch_tables(c));
     process_tile<DT>(c, tb, v, tt);
 #pragma unroll
     for (int s = 0; s < EPT; ++s) {
@@ -1349,7 +1306,7 @@ __global__ __launch_bounds__(NT) void k_spec_resid_tiles(SpecArgs a) {
     const int tb = tile * TILE;
     float v[EPT];
     load_tile<DT>(c, tb, v);
-    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt);
+    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, prefetch_tables(c));
     process_tile<DT>(c, tb, v, tt);
     double sr = 0.0, sp = 0.0;
 #pragma unroll
@@ -1467,14 +1424,14 @@ __global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
 template <int DT>
 static void sample_chain(const SampleArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_sample_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), 0, st, a);
-    hipLaunchKernelGGL(k_sample_rows<DT>, dim3(a.B), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(k_sample_rows<DT>, dim3(a.B), dim3(NTR), 0, st, a);
 }
 
 template <int DT>
 static void spec_chain(const SpecArgs& a, hipStream_t st) {
     const int rows = a.B * (a.G + 1);
     hipLaunchKernelGGL(k_spec_tiles<DT>, dim3(rows * a.ws.n_tiles), dim3(NT), 0, st, a);
-    hipLaunchKernelGGL(k_spec_rows<DT>, dim3(rows), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(k_spec_rows<DT>, dim3(rows), dim3(NTR), 0, st, a);
     hipLaunchKernelGGL(k_spec_resid_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), 0, st, a);
     hipLaunchKernelGGL(k_spec_finish<DT>, dim3(a.B), dim3(NT), 0, st, a);
 }
