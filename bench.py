@@ -119,7 +119,7 @@ def time_graph(step_fns, steps, warmup):
 
 
 def time_launches(step_fns, n):
-    """Average duration (ms) of single launches, HIP events around each one."""
+    """Average duration (ms) of single calls, HIP events around each one."""
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
@@ -131,6 +131,36 @@ def time_launches(step_fns, n):
     torch.cuda.synchronize()
     d = np.array([a.elapsed_time(b) for a, b in ev])
     return float(d.mean()), float(np.median(d)), float(np.percentile(d, 10)), float(np.percentile(d, 90))
+
+
+def time_stages(sampler, step_fns, n, n_launches):
+    """Per-kernel durations (ms) of n calls: the library records HIP events on
+    the launch stream before each of its launches and after the last one."""
+    import torch
+    evs = []
+    for _ in range(n):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(n_launches + 1)]
+        for x in e:
+            x.record()  # creates the HIP event
+        evs.append(e)
+    torch.cuda.synchronize()
+    for i in range(n):
+        sampler.set_launch_events(evs[i])
+        step_fns[i % len(step_fns)]()
+    sampler.set_launch_events(None)
+    torch.cuda.synchronize()
+    d = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(n_launches)]
+                  for i in range(n)])
+    return d  # [n, n_launches] ms
+
+
+def stage_summary(d, names):
+    out = {}
+    for k, nm in enumerate(names):
+        col = d[:, k] * 1e3
+        out[nm] = {"us_mean": float(col.mean()), "us_median": float(np.median(col)),
+                   "us_p10": float(np.percentile(col, 10)), "us_p90": float(np.percentile(col, 90))}
+    return out
 
 
 def cpu_baseline(w, budget_s):
@@ -168,10 +198,13 @@ def headline(args, dev):
     out = torch.empty(B, dtype=torch.int32, device=dev)
     fns = [(lambda x=bufs[r], p=prms[r]: s.sample(x, p, out=out)) for r in range(R)]
     ms, g = time_graph(fns, args.steps, args.warmup)
-    k_mean, k_med, k_p10, k_p90 = time_launches(fns, max(args.steps, 50))
+    c_mean, c_med, c_p10, c_p90 = time_launches(fns, max(args.steps, 50))
+    st = time_stages(s, fns, max(args.steps, 50), 2)
+    stages = stage_summary(st, ["k_sample_tiles<f32>", "k_sample_rows<f32>"])
+    t_mean = stages["k_sample_tiles<f32>"]["us_mean"]
     alg = {"logits": logits_bytes, "history": B * 512 * 4, "bias": B * 16 * 8,
            "params": B * 7 * 4, "tokens": B * 4}
-    achieved = logits_bytes / (k_mean * 1e-3) / 1e9
+    achieved = logits_bytes / (t_mean * 1e-6) / 1e9
     traffic = committed_traffic()
     res = {
         "metric": "sampled tokens/s and HBM GB/s (% of peak) at B=64, V=128256 fp32",
@@ -192,9 +225,11 @@ def headline(args, dev):
                    "rotated_buffers": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
-        "kernel": {"name": "k_sample<f32>", "us_mean": k_mean * 1e3, "us_median": k_med * 1e3,
-                   "us_p10": k_p10 * 1e3, "us_p90": k_p90 * 1e3,
-                   "algorithmic_bytes": alg, "logits_pass_gbs": achieved},
+        "kernel": {"name": "k_sample_tiles<f32>", "stages": stages,
+                   "call_us_mean": c_mean * 1e3, "call_us_median": c_med * 1e3,
+                   "call_us_p10": c_p10 * 1e3, "call_us_p90": c_p90 * 1e3,
+                   "algorithmic_bytes": alg, "tile_kernel_logits_gbs": achieved,
+                   "whole_call_logits_gbs": logits_bytes / (c_mean * 1e-3) / 1e9},
     }
     return res, w
 
@@ -213,7 +248,9 @@ def secondary(args, dev):
     o = torch.empty(w.B, dtype=torch.int32, device=dev)
     ms, _ = time_graph([lambda: s.sample(x, p, out=o)], steps, 5)
     km = time_launches([lambda: s.sample(x, p, out=o)], steps)[0]
-    out["low_entropy"] = {"us_per_call": ms / steps * 1e3, "kernel_us": km * 1e3,
+    st = stage_summary(time_stages(s, [lambda: s.sample(x, p, out=o)], steps, 2),
+                       ["k_sample_tiles<f32>", "k_sample_rows<f32>"])
+    out["low_entropy"] = {"us_per_call": ms / steps * 1e3, "call_us": km * 1e3, "stages": st,
                           "tokens_per_s": w.B * steps / (ms * 1e-3)}
     s.close()
     # grammar, B=256, V=152064 bf16 + mask
@@ -230,9 +267,12 @@ def secondary(args, dev):
     fns = [(lambda x=bufs[r], pr=prms[r]: s.sample(x, pr, out=o)) for r in range(R)]
     ms, _ = time_graph(fns, steps, 5)
     km = time_launches(fns, steps)[0]
-    out["grammar"] = {"us_per_call": ms / steps * 1e3, "kernel_us": km * 1e3,
+    st = stage_summary(time_stages(s, fns, steps, 2), ["k_sample_tiles<bf16>", "k_sample_rows<bf16>"])
+    t_us = st["k_sample_tiles<bf16>"]["us_mean"]
+    out["grammar"] = {"us_per_call": ms / steps * 1e3, "call_us": km * 1e3, "stages": st,
                       "tokens_per_s": w.B * steps / (ms * 1e-3),
-                      "gbs": nbytes / (km * 1e-3) / 1e9, "bytes": nbytes}
+                      "tile_kernel_gbs": nbytes / (t_us * 1e-6) / 1e9,
+                      "whole_call_gbs": nbytes / (km * 1e-3) / 1e9, "bytes": nbytes}
     s.close()
     del bufs
     # speculative verification, 32 x (4 + 1) x 128256
@@ -259,10 +299,15 @@ def secondary(args, dev):
     emitted = int((on + 1).sum().item())
     ms, _ = time_graph(fns, steps, 5)
     km = time_launches(fns, steps)[0]
-    out["speculative"] = {"us_per_call": ms / steps * 1e3, "launch_pair_us": km * 1e3,
+    st = stage_summary(time_stages(s, fns, steps, 4),
+                       ["k_spec_tiles<f32>", "k_spec_rows<f32>", "k_spec_resid_tiles<f32>",
+                        "k_spec_finish<f32>"])
+    t_us = st["k_spec_tiles<f32>"]["us_mean"]
+    out["speculative"] = {"us_per_call": ms / steps * 1e3, "call_us": km * 1e3, "stages": st,
                           "emitted_tokens_per_call": emitted,
                           "emitted_tokens_per_s": emitted * steps / (ms * 1e-3),
-                          "target_gbs": nbytes / (km * 1e-3) / 1e9, "bytes": nbytes}
+                          "tile_kernel_gbs": nbytes / (t_us * 1e-6) / 1e9,
+                          "whole_call_gbs": nbytes / (km * 1e-3) / 1e9, "bytes": nbytes}
     s.close()
     del tgs
     # fused LM-head + Gumbel-max, hidden [64, 8192] x weight [128256, 8192] bf16
@@ -277,13 +322,47 @@ def secondary(args, dev):
     lsteps = max(10, steps // 4)
     ms, _ = time_graph(fn, lsteps, 3)
     km = time_launches(fn, lsteps)[0]
+    st = stage_summary(time_stages(s, fn, lsteps, 2), ["k_lmhead", "k_lmhead_reduce"])
+    g_us = st["k_lmhead"]["us_mean"]
     nbytes = V * K * 2 + B * K * 2
-    out["lmhead"] = {"us_per_call": ms / lsteps * 1e3, "kernel_us": km * 1e3,
+    out["lmhead"] = {"us_per_call": ms / lsteps * 1e3, "call_us": km * 1e3, "stages": st,
                      "tokens_per_s": B * lsteps / (ms * 1e-3),
-                     "gbs": nbytes / (km * 1e-3) / 1e9, "hbm_frac": nbytes / (km * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "tflops": 2.0 * B * K * V / (km * 1e-3) / 1e12}
+                     "gemm_kernel_gbs": nbytes / (g_us * 1e-6) / 1e9,
+                     "gemm_kernel_hbm_frac": nbytes / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "gemm_kernel_tflops": 2.0 * B * K * V / (g_us * 1e-6) / 1e12,
+                     "whole_call_gbs": nbytes / (km * 1e-3) / 1e9}
     s.close()
     return out
+
+
+COPY_BYTES = 256 << 20
+
+
+def counters_run(dev):
+    """A plain device-to-device copy of COPY_BYTES (reads and writes that many
+    bytes), then 5 headline calls on rotated buffers; the counter summary
+    scales the sampler's FETCH_SIZE / WRITE_SIZE by what the copy reads."""
+    import torch
+    from speculative_decoding_verification_pipeline_amd import workloads as W
+    from speculative_decoding_verification_pipeline_amd.sampler import Sampler
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"bench: copied {COPY_BYTES} bytes")
+    del a, b
+    w = W.heterogeneous()
+    R = max(2, -(-ROTATE_MIN // (w.B * w.V * 4)))
+    base = torch.from_numpy(w.logits).to(dev)
+    bufs = [base] + [base.clone() for _ in range(R - 1)]
+    prms = [sampling_params(w, dev, positions=np.full(w.B, r, np.int32)) for r in range(R)]
+    s = Sampler(w.B, w.V, device=0)
+    out = torch.empty(w.B, dtype=torch.int32, device=dev)
+    for r in range(5):
+        s.sample(bufs[r + 1], prms[r + 1], out=out)
+    torch.cuda.synchronize()
+    log("bench: 5 headline calls done")
 
 
 def main():
@@ -294,6 +373,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--counters", action="store_true",
+                    help="for rocprofv3 --pmc runs: a device copy of known size (counter "
+                         "scale), then a few headline calls; prints no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding is a "
@@ -302,10 +384,14 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
+    if args.counters:
+        counters_run(dev)
+        return
     log("bench: headline (heterogeneous B=64 V=128256)")
     res, w = headline(args, dev)
-    log(f"bench: headline done, kernel {res['kernel']['us_mean']:.2f} us, "
-        f"{res['roofline']['achieved']:.0f} GB/s")
+    log(f"bench: headline done, call {res['kernel']['call_us_mean']:.2f} us, tile kernel "
+        f"{res['kernel']['stages']['k_sample_tiles<f32>']['us_mean']:.2f} us "
+        f"({res['roofline']['achieved']:.0f} GB/s)")
     if not args.no_secondary:
         log("bench: secondary configurations")
         res["secondary"] = secondary(args, dev)

@@ -124,6 +124,20 @@ const char* ss_status_string(ss_status st);
 /* Bytes of device workspace the handle holds. */
 int64_t ss_sampler_workspace_bytes(const ss_sampler* s);
 
+/* ss_sampler_set_launch_events -- measurement hook (timing of the stages).
+ *   events    array of n_events hipEvent_t handles created by the caller, or
+ *             NULL to clear the hook. The library copies the handles.
+ *   n_events  0 .. 8.
+ * While set, every ss_sample / ss_spec_verify / ss_lmhead_sample call records
+ * events[k] on its stream just before its k-th kernel launch (k = 0, 1, ...)
+ * and events[n_launches] right after the last launch, for the k that are below
+ * n_events. ss_sample launches 2 kernels (tile scan, row merge),
+ * ss_spec_verify 4 (tile scan, row merge, residual tile sums, per-request
+ * finish) and ss_lmhead_sample 2 (fused GEMM tiles, cross-tile reduction).
+ * Returns SS_ERR_INVALID_ARG for a null handle or n_events outside 0 .. 8.
+ * Not meant for graph capture. */
+ss_status ss_sampler_set_launch_events(ss_sampler* s, void* const* events, int32_t n_events);
+
 /* ss_sample -- sample one token per row of a [B, V] logits matrix.
  *   logits      [B, row_stride] of dtype (SS_F32 or SS_BF16), element-aligned,
  *               row_stride >= V. Rows whose start is 16-byte aligned are read

@@ -18,6 +18,7 @@ struct ss_sampler {
     int64_t ws_bytes;
     ss::Workspace ws;
     float2* lm_partials;
+    ss::LaunchEvents events;
     // defaults substituted for absent per-request parameters, [max_batch] each
     int32_t* def_zero_i;
     float* def_zero_f;
@@ -195,6 +196,14 @@ void ss_sampler_destroy(ss_sampler* s) {
 
 int64_t ss_sampler_workspace_bytes(const ss_sampler* s) { return s ? s->ws_bytes : 0; }
 
+ss_status ss_sampler_set_launch_events(ss_sampler* s, void* const* events, int32_t n_events) {
+    if (!s || n_events < 0 || n_events > 8) return SS_ERR_INVALID_ARG;
+    s->events.n = events ? n_events : 0;
+    for (int k = 0; k < 8; ++k)
+        s->events.ev[k] = (events && k < n_events) ? static_cast<hipEvent_t>(events[k]) : nullptr;
+    return SS_OK;
+}
+
 ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t row_stride,
                     int32_t B, const ss_params* params, int32_t* out_tokens, const ss_debug* debug,
                     void* stream) {
@@ -224,7 +233,7 @@ ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t r
     }
     a.ws = s->ws;
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
-    return ss::launch_sample(a, dtype, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK
+    return ss::launch_sample(a, dtype, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
                                                                                        : SS_ERR_HIP;
 }
 
@@ -257,7 +266,7 @@ ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
     a.out_num_accepted = out_num_accepted;
     a.ws = s->ws;
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
-    return ss::launch_spec(a, dtype, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK
+    return ss::launch_spec(a, dtype, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
                                                                                      : SS_ERR_HIP;
 }
 
@@ -285,7 +294,7 @@ ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t
     a.partials = s->lm_partials;
     a.n_vtiles = s->n_vtiles;
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
-    return ss::launch_lmhead(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK
+    return ss::launch_lmhead(a, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
                                                                                 : SS_ERR_HIP;
 }
 

@@ -118,8 +118,18 @@ struct LmheadArgs {
     int n_vtiles;
 };
 
-hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st);
-hipError_t launch_spec(const SpecArgs& a, ss_dtype dt, hipStream_t st);
-hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st);
+// Optional timing events recorded around each launch of a call (see
+// ss_sampler_set_launch_events): ev[k] before launch k, ev[n] after the last.
+struct LaunchEvents {
+    hipEvent_t ev[8];
+    int n;
+    void mark(int k, hipStream_t st) const {
+        if (k < n && ev[k]) (void)hipEventRecord(ev[k], st);
+    }
+};
+
+hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le);
+hipError_t launch_spec(const SpecArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le);
+hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le);
 
 }  // namespace ss

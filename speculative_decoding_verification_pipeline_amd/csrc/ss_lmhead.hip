@@ -106,14 +106,22 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
 
+    // each workgroup walks K from its own starting step, so concurrent
+    // workgroups spread their weight reads over the whole row span
     const int nsteps = K / LM_KSTEP;
+    const int rot = (int)(((unsigned)tile * 2654435761u) % (unsigned)nsteps);
+    auto koff = [&](int it) {
+        int s = it + rot;
+        s = s >= nsteps ? s - nsteps : s;
+        return s * LM_KSTEP;
+    };
     Ops o0, o1;
-    load_ops(o0, w0, w1, h0, h1, 0);
+    load_ops(o0, w0, w1, h0, h1, koff(0));
     int it = 0;
     for (; it + 2 <= nsteps; it += 2) {
-        load_ops(o1, w0, w1, h0, h1, (it + 1) * LM_KSTEP);
+        load_ops(o1, w0, w1, h0, h1, koff(it + 1));
         mfma_ops(o0, acc);
-        if (it + 2 < nsteps) load_ops(o0, w0, w1, h0, h1, (it + 2) * LM_KSTEP);
+        if (it + 2 < nsteps) load_ops(o0, w0, w1, h0, h1, koff(it + 2));
         mfma_ops(o1, acc);
     }
     if (it < nsteps) mfma_ops(o0, acc);
@@ -185,46 +193,63 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
     }
 }
 
-// Cross-tile reduction: 4 threads per batch row, each over a strided quarter of
-// the tiles, then the lowest index among equal maxima.
-__global__ __launch_bounds__(LM_NT) void k_lmhead_reduce(LmheadArgs a) {
-    __shared__ float s_score[LM_NT / LM_MAXB][LM_MAXB];
-    __shared__ int s_idx[LM_NT / LM_MAXB][LM_MAXB];
-    const int tid = threadIdx.x;
-    const int j = tid & (LM_MAXB - 1);
-    const int part = tid / LM_MAXB;
-    float bs = -FLT_MAX;
-    int bi = INT_MAX;
-    if (j < a.B) {
-        const float2* pr = a.partials + (size_t)j * a.n_vtiles;
-        for (int t = part; t < a.n_vtiles; t += LM_NT / LM_MAXB) {
-            const float2 x = pr[t];
-            const int xi = __float_as_int(x.y);
-            if (better(x.x, xi, bs, bi)) {
-                bs = x.x;
-                bi = xi;
-            }
-        }
-    }
-    s_score[part][j] = bs;
-    s_idx[part][j] = bi;
-    __syncthreads();
-    if (tid < a.B) {
-        float fs = s_score[0][tid];
-        int fi = s_idx[0][tid];
-#pragma unroll
-        for (int w = 1; w < LM_NT / LM_MAXB; ++w)
-            if (better(s_score[w][tid], s_idx[w][tid], fs, fi)) {
-                fs = s_score[w][tid];
-                fi = s_idx[w][tid];
-            }
-        a.out_tokens[tid] = fi == INT_MAX ? -1 : fi;
+// Cross-tile reduction: one workgroup per batch row; each thread takes a
+// strided share of the tiles, then (max, lowest index) across the wave through
+// DPP / permlane exchanges and across the four waves through LDS.
+template <int J>
+__device__ __forceinline__ void better_xor(float& s, int& i) {
+    const float os = xor_lane_f<J>(s);
+    const int oi = xor_lane_i<J>(i);
+    if (better(os, oi, s, i)) {
+        s = os;
+        i = oi;
     }
 }
 
-hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
+__global__ __launch_bounds__(LM_NT) void k_lmhead_reduce(LmheadArgs a) {
+    __shared__ float s_score[LM_NT / WAVE];
+    __shared__ int s_idx[LM_NT / WAVE];
+    const int tid = threadIdx.x;
+    const int j = blockIdx.x;
+    float bs = -FLT_MAX;
+    int bi = INT_MAX;
+    const float2* pr = a.partials + (size_t)j * a.n_vtiles;
+    for (int t = tid; t < a.n_vtiles; t += LM_NT) {
+        const float2 x = pr[t];
+        const int xi = __float_as_int(x.y);
+        if (better(x.x, xi, bs, bi)) {
+            bs = x.x;
+            bi = xi;
+        }
+    }
+    better_xor<1>(bs, bi);
+    better_xor<2>(bs, bi);
+    better_xor<4>(bs, bi);
+    better_xor<8>(bs, bi);
+    better_xor<16>(bs, bi);
+    better_xor<32>(bs, bi);
+    if ((tid & (WAVE - 1)) == 0) {
+        s_score[tid / WAVE] = bs;
+        s_idx[tid / WAVE] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int w = 1; w < LM_NT / WAVE; ++w)
+            if (better(s_score[w], s_idx[w], bs, bi)) {
+                bs = s_score[w];
+                bi = s_idx[w];
+            }
+        a.out_tokens[j] = bi == INT_MAX ? -1 : bi;
+    }
+}
+
+hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le) {
+    le.mark(0, st);
     hipLaunchKernelGGL(k_lmhead, dim3(a.n_vtiles), dim3(LM_NT), 0, st, a);
-    hipLaunchKernelGGL(k_lmhead_reduce, dim3(1), dim3(LM_NT), 0, st, a);
+    le.mark(1, st);
+    hipLaunchKernelGGL(k_lmhead_reduce, dim3(a.B), dim3(LM_NT), 0, st, a);
+    le.mark(2, st);
     return hipGetLastError();
 }
 

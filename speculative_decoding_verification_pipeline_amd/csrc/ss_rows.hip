@@ -376,7 +376,7 @@ __device__ __forceinline__ void process_tile(const RowCtx& c, int tb, float v[EP
 
 // x' for a single entry (used by acceptance tests). Whole workgroup participates.
 template <int DT, int NB>
-__device__ float single_entry(const RowCtx& c, int id, SmemST<NB>& sh) {
+__device__ __forceinline__ float single_entry(const RowCtx& c, int id, SmemST<NB>& sh) {
     int cnt = 0;
     for (int i = threadIdx.x; i < c.hist_len + c.extra_len; i += NB) {
         const int h = i < c.hist_len ? gld(c.hist + i) : gld(c.extra + (i - c.hist_len));
@@ -592,7 +592,7 @@ __device__ __forceinline__ TileStat load_tile_stat(const Workspace& ws, int row)
     return t;
 }
 
-__device__ RowSummary summarize_tiles(const TileStat& t, float T) {
+__device__ __forceinline__ RowSummary summarize_tiles(const TileStat t, float T) {
     RowSummary r;
     r.m = wave_max(t.m);
     r.argmax = wave_min_i((t.m == r.m && t.argmax >= 0) ? t.argmax : INT_MAX);
@@ -706,7 +706,7 @@ __device__ void count_and_mass(const float* zr, int V, float zmax, Pred pred, in
 // first NT threads, one tile at a time), then select by count (top-k) and by
 // mass (top-p, the draw) with radix passes over the whole workgroup.
 template <int DT>
-__device__ __noinline__ void finalize_slow(const RowCtx& c, int row, const Workspace& ws,
+__device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Workspace& ws,
                                            int n_tiles, const RowSummary& rs, float u, SmemU& su,
                                            SmemR& sh, RowInfo& info, const RowDbg& dbg) {
     const int tid = threadIdx.x;
@@ -918,7 +918,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
     const int n_tiles = ws.n_tiles;
     const int V = c.V;
     SmemPool& P = su.p;
-    const TileStat& ts = rl.ts;
+    const TileStat ts = rl.ts;
     const RowSummary rs = summarize_tiles(ts, c.T);
 
     __shared__ RowInfo info;
@@ -1422,29 +1422,37 @@ __global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
 // launchers
 
 template <int DT>
-static void sample_chain(const SampleArgs& a, hipStream_t st) {
+static void sample_chain(const SampleArgs& a, hipStream_t st, const LaunchEvents& le) {
+    le.mark(0, st);
     hipLaunchKernelGGL(k_sample_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), 0, st, a);
+    le.mark(1, st);
     hipLaunchKernelGGL(k_sample_rows<DT>, dim3(a.B), dim3(NTR), 0, st, a);
+    le.mark(2, st);
 }
 
 template <int DT>
-static void spec_chain(const SpecArgs& a, hipStream_t st) {
+static void spec_chain(const SpecArgs& a, hipStream_t st, const LaunchEvents& le) {
     const int rows = a.B * (a.G + 1);
+    le.mark(0, st);
     hipLaunchKernelGGL(k_spec_tiles<DT>, dim3(rows * a.ws.n_tiles), dim3(NT), 0, st, a);
+    le.mark(1, st);
     hipLaunchKernelGGL(k_spec_rows<DT>, dim3(rows), dim3(NTR), 0, st, a);
+    le.mark(2, st);
     hipLaunchKernelGGL(k_spec_resid_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), 0, st, a);
+    le.mark(3, st);
     hipLaunchKernelGGL(k_spec_finish<DT>, dim3(a.B), dim3(NT), 0, st, a);
+    le.mark(4, st);
 }
 
-hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st) {
-    if (dt == SS_F32) sample_chain<SS_F32>(a, st);
-    else sample_chain<SS_BF16>(a, st);
+hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le) {
+    if (dt == SS_F32) sample_chain<SS_F32>(a, st, le);
+    else sample_chain<SS_BF16>(a, st, le);
     return hipGetLastError();
 }
 
-hipError_t launch_spec(const SpecArgs& a, ss_dtype dt, hipStream_t st) {
-    if (dt == SS_F32) spec_chain<SS_F32>(a, st);
-    else spec_chain<SS_BF16>(a, st);
+hipError_t launch_spec(const SpecArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le) {
+    if (dt == SS_F32) spec_chain<SS_F32>(a, st, le);
+    else spec_chain<SS_BF16>(a, st, le);
     return hipGetLastError();
 }
 

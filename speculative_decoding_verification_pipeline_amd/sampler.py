@@ -25,7 +25,8 @@ SS_F32 = 0
 SS_BF16 = 1
 
 EXPORTED = ("ss_sampler_create", "ss_sampler_destroy", "ss_status_string",
-            "ss_sampler_workspace_bytes", "ss_sample", "ss_spec_verify", "ss_lmhead_sample")
+            "ss_sampler_workspace_bytes", "ss_sampler_set_launch_events", "ss_sample",
+            "ss_spec_verify", "ss_lmhead_sample")
 
 
 class Config(ctypes.Structure):
@@ -80,6 +81,8 @@ def load_library(path=None):
     lib.ss_status_string.restype = ctypes.c_char_p
     lib.ss_sampler_workspace_bytes.argtypes = [vp]
     lib.ss_sampler_workspace_bytes.restype = i64
+    lib.ss_sampler_set_launch_events.argtypes = [vp, ctypes.POINTER(vp), i32]
+    lib.ss_sampler_set_launch_events.restype = i32
     lib.ss_sample.argtypes = [vp, vp, i32, i64, i32, ctypes.POINTER(CParams), vp,
                               ctypes.POINTER(CDebug), vp]
     lib.ss_sample.restype = i32
@@ -200,6 +203,18 @@ class Sampler:
 
     def workspace_bytes(self):
         return int(self.lib.ss_sampler_workspace_bytes(self.handle))
+
+    def set_launch_events(self, events):
+        """Record these torch.cuda.Event objects around each kernel launch of the
+        following calls (None clears). Each event must have been recorded once
+        so that its HIP event exists."""
+        if not events:
+            _check("ss_sampler_set_launch_events",
+                   self.lib.ss_sampler_set_launch_events(self.handle, None, 0))
+            return
+        arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        _check("ss_sampler_set_launch_events",
+               self.lib.ss_sampler_set_launch_events(self.handle, arr, len(events)))
 
     @staticmethod
     def _dtype(t):

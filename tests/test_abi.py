@@ -70,4 +70,5 @@ def test_calls_reject_null_handle(lib):
     assert lib.ss_lmhead_sample(None, None, None, 1, None, None, None, 0, None, None,
                                 None) == sampler.SS_ERR_INVALID_ARG
     assert lib.ss_sampler_workspace_bytes(None) == 0
+    assert lib.ss_sampler_set_launch_events(None, None, 0) == sampler.SS_ERR_INVALID_ARG
     lib.ss_sampler_destroy(None)
