@@ -134,12 +134,12 @@ def time_launches(step_fns, n):
 
 
 def time_stages(sampler, step_fns, n, n_launches):
-    """Per-kernel durations (ms) of n calls: the library records HIP events on
-    the launch stream before each of its launches and after the last one."""
+    """Per-kernel durations (ms) of n calls: the library launches each kernel
+    with a start and a stop HIP event that the dispatch itself records."""
     import torch
     evs = []
     for _ in range(n):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(n_launches + 1)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_launches)]
         for x in e:
             x.record()  # creates the HIP event
         evs.append(e)
@@ -149,7 +149,7 @@ def time_stages(sampler, step_fns, n, n_launches):
         step_fns[i % len(step_fns)]()
     sampler.set_launch_events(None)
     torch.cuda.synchronize()
-    d = np.array([[evs[i][k].elapsed_time(evs[i][k + 1]) for k in range(n_launches)]
+    d = np.array([[evs[i][2 * k].elapsed_time(evs[i][2 * k + 1]) for k in range(n_launches)]
                   for i in range(n)])
     return d  # [n, n_launches] ms
 

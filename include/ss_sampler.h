@@ -124,16 +124,17 @@ const char* ss_status_string(ss_status st);
 /* Bytes of device workspace the handle holds. */
 int64_t ss_sampler_workspace_bytes(const ss_sampler* s);
 
-/* ss_sampler_set_launch_events -- measurement hook (timing of the stages).
+/* ss_sampler_set_launch_events -- measurement hook (timing of the kernels).
  *   events    array of n_events hipEvent_t handles created by the caller, or
  *             NULL to clear the hook. The library copies the handles.
  *   n_events  0 .. 8.
- * While set, every ss_sample / ss_spec_verify / ss_lmhead_sample call records
- * events[k] on its stream just before its k-th kernel launch (k = 0, 1, ...)
- * and events[n_launches] right after the last launch, for the k that are below
- * n_events. ss_sample launches 2 kernels (tile scan, row merge),
- * ss_spec_verify 4 (tile scan, row merge, residual tile sums, per-request
- * finish) and ss_lmhead_sample 2 (fused GEMM tiles, cross-tile reduction).
+ * While set, every ss_sample / ss_spec_verify / ss_lmhead_sample call launches
+ * its k-th kernel (k = 0, 1, ...) with events[2k] as its start and
+ * events[2k + 1] as its stop event (hipExtLaunchKernel: the dispatch records
+ * them when the kernel begins and ends), for every k with 2k + 1 < n_events.
+ * ss_sample launches 2 kernels (tile scan, row merge), ss_spec_verify 4 (tile
+ * scan, row merge, residual tile sums, per-request finish) and
+ * ss_lmhead_sample 2 (fused GEMM tiles, cross-tile reduction).
  * Returns SS_ERR_INVALID_ARG for a null handle or n_events outside 0 .. 8.
  * Not meant for graph capture. */
 ss_status ss_sampler_set_launch_events(ss_sampler* s, void* const* events, int32_t n_events);

@@ -1,6 +1,7 @@
 // Internal structures shared by the host side of the library and its kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -118,15 +119,25 @@ struct LmheadArgs {
     int n_vtiles;
 };
 
-// Optional timing events recorded around each launch of a call (see
-// ss_sampler_set_launch_events): ev[k] before launch k, ev[n] after the last.
+// Optional timing events of a call (see ss_sampler_set_launch_events): launch
+// k is bracketed by ev[2k] (its start) and ev[2k + 1] (its end), recorded by
+// the dispatch itself.
 struct LaunchEvents {
     hipEvent_t ev[8];
     int n;
-    void mark(int k, hipStream_t st) const {
-        if (k < n && ev[k]) (void)hipEventRecord(ev[k], st);
-    }
+    hipEvent_t start(int k) const { return 2 * k + 1 < n ? ev[2 * k] : nullptr; }
+    hipEvent_t stop(int k) const { return 2 * k + 1 < n ? ev[2 * k + 1] : nullptr; }
 };
+
+// Launches kernel k of a call, with its timing events when they are set.
+template <class F, class... A>
+inline void launch_k(const LaunchEvents& le, int k, F kernel, dim3 grid, dim3 block,
+                     hipStream_t st, A... args) {
+    if (le.start(k))
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, le.start(k), le.stop(k), 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 
 hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le);
 hipError_t launch_spec(const SpecArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le);

@@ -245,11 +245,8 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_reduce(LmheadArgs a) {
 }
 
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le) {
-    le.mark(0, st);
-    hipLaunchKernelGGL(k_lmhead, dim3(a.n_vtiles), dim3(LM_NT), 0, st, a);
-    le.mark(1, st);
-    hipLaunchKernelGGL(k_lmhead_reduce, dim3(a.B), dim3(LM_NT), 0, st, a);
-    le.mark(2, st);
+    launch_k(le, 0, k_lmhead, dim3(a.n_vtiles), dim3(LM_NT), st, a);
+    launch_k(le, 1, k_lmhead_reduce, dim3(a.B), dim3(LM_NT), st, a);
     return hipGetLastError();
 }
 

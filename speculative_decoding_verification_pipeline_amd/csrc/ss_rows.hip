@@ -1423,25 +1423,17 @@ __global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
 
 template <int DT>
 static void sample_chain(const SampleArgs& a, hipStream_t st, const LaunchEvents& le) {
-    le.mark(0, st);
-    hipLaunchKernelGGL(k_sample_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), 0, st, a);
-    le.mark(1, st);
-    hipLaunchKernelGGL(k_sample_rows<DT>, dim3(a.B), dim3(NTR), 0, st, a);
-    le.mark(2, st);
+    launch_k(le, 0, k_sample_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
+    launch_k(le, 1, k_sample_rows<DT>, dim3(a.B), dim3(NTR), st, a);
 }
 
 template <int DT>
 static void spec_chain(const SpecArgs& a, hipStream_t st, const LaunchEvents& le) {
     const int rows = a.B * (a.G + 1);
-    le.mark(0, st);
-    hipLaunchKernelGGL(k_spec_tiles<DT>, dim3(rows * a.ws.n_tiles), dim3(NT), 0, st, a);
-    le.mark(1, st);
-    hipLaunchKernelGGL(k_spec_rows<DT>, dim3(rows), dim3(NTR), 0, st, a);
-    le.mark(2, st);
-    hipLaunchKernelGGL(k_spec_resid_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), 0, st, a);
-    le.mark(3, st);
-    hipLaunchKernelGGL(k_spec_finish<DT>, dim3(a.B), dim3(NT), 0, st, a);
-    le.mark(4, st);
+    launch_k(le, 0, k_spec_tiles<DT>, dim3(rows * a.ws.n_tiles), dim3(NT), st, a);
+    launch_k(le, 1, k_spec_rows<DT>, dim3(rows), dim3(NTR), st, a);
+    launch_k(le, 2, k_spec_resid_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
+    launch_k(le, 3, k_spec_finish<DT>, dim3(a.B), dim3(NT), st, a);
 }
 
 hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le) {

@@ -205,9 +205,9 @@ class Sampler:
         return int(self.lib.ss_sampler_workspace_bytes(self.handle))
 
     def set_launch_events(self, events):
-        """Record these torch.cuda.Event objects around each kernel launch of the
-        following calls (None clears). Each event must have been recorded once
-        so that its HIP event exists."""
+        """Bracket kernel k of the following calls with events[2k] / events[2k+1]
+        (torch.cuda.Event objects; None clears). Each event must have been
+        recorded once so that its HIP event exists."""
         if not events:
             _check("ss_sampler_set_launch_events",
                    self.lib.ss_sampler_set_launch_events(self.handle, None, 0))
