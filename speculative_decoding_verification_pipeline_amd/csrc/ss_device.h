@@ -402,6 +402,23 @@ __device__ __forceinline__ float xor_lane_dyn(float v, int j) {
     }
 }
 
+// Sorts one float per lane across the wave, descending (bitonic network over
+// DPP / permlane exchanges; lane i ends with the i-th largest).
+__device__ __forceinline__ float wave_sort_desc(float v) {
+    const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+    for (int k = 2; k <= WAVE; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const float o = xor_lane_dyn(v, j);
+            const bool desc = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
+        }
+    }
+    return v;
+}
+
 // Sorts one float per thread across the workgroup, descending (bitonic network;
 // strides below the wave width exchange through DPP / permlane, the rest
 // through LDS).

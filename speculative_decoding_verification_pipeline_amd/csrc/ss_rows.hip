@@ -74,12 +74,14 @@ struct RowCtx {
     float min_p;
     float rep, freq, pres;
     const int32_t* hist;
-    int hist_len;
+    int hist_len;          // clamped to hist_cap
+    int hist_cap;          // row stride of the history ids (entries readable for this row)
     const int32_t* extra;  // draft tokens that precede this row (verification)
     int extra_len;
     const int32_t* bias_ids;
     const float* bias_vals;
-    int bias_len;
+    int bias_len;          // clamped to bias_cap
+    int bias_cap;
     const uint32_t* mask;  // this row's mask words or null
     uint32_t req, pos;
     uint64_t seed;
@@ -100,11 +102,13 @@ __device__ __forceinline__ RowCtx make_ctx(const ParamPtrs& p, int b, const void
     c.rep = p.rep[b];
     c.freq = p.freq[b];
     c.pres = p.pres[b];
-    c.hist_len = p.hist_len[b];
+    c.hist_cap = p.hist_stride;
+    c.hist_len = min(p.hist_len[b], p.hist_stride);
     c.hist = p.hist_ids + (int64_t)b * p.hist_stride;
     c.extra = extra;
     c.extra_len = extra ? extra_len : 0;
-    c.bias_len = p.bias_len[b];
+    c.bias_cap = p.bias_stride;
+    c.bias_len = min(p.bias_len[b], p.bias_stride);
     c.bias_ids = p.bias_ids + (int64_t)b * p.bias_stride;
     c.bias_vals = p.bias_vals + (int64_t)b * p.bias_stride;
     c.mask = mask_row;
@@ -122,9 +126,14 @@ struct SmemTile {
     uint32_t bias[TILE / 32]; // bit set: some bias entry targets this vocabulary entry
     int32_t bid[NT];          // the row's first NT bias entries, in array order
     float bval[NT];
-    float lmax[NT];           // per-thread maxima
-    float sorted[NT];         // the same, in descending order
-    unsigned long long list[CW];  // the tile's candidate keys, unordered
+    union {
+        struct {
+            float lmax[NT];    // per-wave sorted thread maxima
+            float sorted[NT];  // all thread maxima in descending order
+        };
+        unsigned long long keys[CW];  // the candidates' keys (z, id), once the threshold is set
+    };
+    unsigned long long list[CW];  // the tile's candidates (x' bits, id), unordered
     int nlist;
 };
 
@@ -267,31 +276,34 @@ __device__ __forceinline__ float process_entry_t(const RowCtx& c, int id, float 
     return allowed ? x : NEG_INF;
 }
 
-// The row's history and bias lists are small and shared by all its tiles:
-// each thread fetches its first two history ids and one bias entry before the
-// tile's logits, so their latency overlaps the tile stream.
+// The row's history and bias lists are small and shared by all its tiles. Each
+// thread fetches its first two history ids, its draft token and one bias
+// entry with addresses that depend on kernel arguments only (the row strides
+// bound what is readable), so the loads issue ahead of the tile's logits
+// without waiting for the per-request lengths.
 struct TablePrefetch {
     int hist[2];
+    int extra;
     int bias_id;
     float bias_val;
 };
 
 __device__ __forceinline__ TablePrefetch prefetch_tables(const RowCtx& c) {
     TablePrefetch f;
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const int i = (int)threadIdx.x + k * NT;
-        f.hist[k] = i < c.hist_len ? gld(c.hist + i)
-                    : (i < c.hist_len + c.extra_len ? gld(c.extra + (i - c.hist_len)) : -1);
+        const int i = tid + k * NT;
+        f.hist[k] = i < c.hist_cap ? gld(c.hist + i) : -1;
     }
-    const int i = threadIdx.x;
-    f.bias_id = i < c.bias_len ? gld(c.bias_ids + i) : -1;
-    f.bias_val = i < c.bias_len ? gld(c.bias_vals + i) : 0.0f;
+    f.extra = tid < c.extra_len ? gld(c.extra + tid) : -1;
+    f.bias_id = tid < c.bias_cap ? gld(c.bias_ids + tid) : -1;
+    f.bias_val = tid < c.bias_cap ? gld(c.bias_vals + tid) : 0.0f;
     return f;
 }
 
 // Builds the tile's multiplicity counts, bias bitmap and bias list in LDS (two
-// barriers).
+// barriers). Threads with active = false only take part in the barriers.
 __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& t,
                                              const TablePrefetch& f, bool active = true) {
     const int tid = threadIdx.x;
@@ -308,20 +320,16 @@ __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& 
         t.bval[tid] = f.bias_val;
     }
     __syncthreads();
+    auto count = [&](int id) {
+        const int l = id - tb;
+        if (id >= 0 && id < c.V && l >= 0 && l < TILE) atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
+    };
     if (has_cnt) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int id = f.hist[k];
-            const int l = id - tb;
-            if (id >= 0 && id < c.V && l >= 0 && l < TILE)
-                atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
-        }
-        for (int i = tid + 2 * NT; i < c.hist_len + c.extra_len; i += NT) {
-            const int id = i < c.hist_len ? gld(c.hist + i) : gld(c.extra + (i - c.hist_len));
-            const int l = id - tb;
-            if (id >= 0 && id < c.V && l >= 0 && l < TILE)
-                atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
-        }
+        for (int k = 0; k < 2; ++k)
+            if (tid + k * NT < c.hist_len) count(f.hist[k]);
+        for (int i = tid + 2 * NT; i < c.hist_len; i += NT) count(gld(c.hist + i));
+        if (tid < c.extra_len) count(f.extra);
     }
     for (int i = tid; has_bias && i < c.bias_len; i += NT) {
         const int id = i < NT ? f.bias_id : gld(c.bias_ids + i);
@@ -331,8 +339,21 @@ __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& 
     __syncthreads();
 }
 
+// This thread's grammar-mask words (one per group of VEC entries), fetched with
+// the tile's logits; all-ones without a mask.
 template <int DT>
-__device__ __forceinline__ void process_tile(const RowCtx& c, int tb, float v[EPT], const SmemTile& t) {
+__device__ __forceinline__ void load_mask(const RowCtx& c, int tb, uint32_t mw[Lay<DT>::NG]) {
+    using L = Lay<DT>;
+#pragma unroll
+    for (int g = 0; g < L::NG; ++g) {
+        const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
+        mw[g] = (c.mask && e0 < c.V) ? gld(c.mask + (e0 >> 5)) : 0xFFFFFFFFu;
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void process_tile(const RowCtx& c, int tb, float v[EPT], const SmemTile& t,
+                                             const uint32_t mwords[Lay<DT>::NG]) {
     using L = Lay<DT>;
     const bool has_cnt = (c.hist_len + c.extra_len) > 0;
     const bool has_bias = c.bias_len > 0;
@@ -359,7 +380,13 @@ __device__ __forceinline__ void process_tile(const RowCtx& c, int tb, float v[EP
             for (int k = 0; k < L::VEC / 2; ++k) cw[k] = 0;
         }
         const uint32_t bb = has_bias ? (t.bias[l0 >> 5] >> (l0 & 31)) : 0u;
-        const uint32_t mw = (c.mask && e0 < c.V) ? (gld(c.mask + (e0 >> 5)) >> (e0 & 31)) : 0xFFFFFFFFu;
+        const uint32_t mw = mwords[g] >> (e0 & 31);
+        // most groups hold no history hit, bias or masked entry: skip them whole
+        constexpr uint32_t vm = (1u << L::VEC) - 1u;
+        uint32_t anyc = 0;
+#pragma unroll
+        for (int k = 0; k < L::VEC / 2; ++k) anyc |= cw[k];
+        if ((anyc | (bb & vm) | (~mw & vm)) == 0u) continue;
 #pragma unroll
         for (int j = 0; j < L::VEC; ++j) {
             const int id = e0 + j;
@@ -409,14 +436,13 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
     const int wv = tid / WAVE;
     const int tb = tile * TILE;
     float v[EPT];
-    if (c.hist_len + c.extra_len + c.bias_len > 0) {
-        const TablePrefetch f = prefetch_tables(c);
-        load_tile<DT>(c, tb, v);
-        build_tables(c, tb, tt, f);
-    } else {
-        load_tile<DT>(c, tb, v);
-    }
-    process_tile<DT>(c, tb, v, tt);
+    uint32_t mw[Lay<DT>::NG];
+    // issue order: history / bias (needed first), the tile, its mask words
+    const TablePrefetch f = prefetch_tables(c);
+    load_tile<DT>(c, tb, v);
+    load_mask<DT>(c, tb, mw);
+    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, f);
+    process_tile<DT>(c, tb, v, tt, mw);
 
     if (dbg_proc_row || dbg_probs_row) {
 #pragma unroll
@@ -469,13 +495,44 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
         st.ncand = 0;
         st.nfinite = nf;
     } else {
-        // the lane maxima, sorted descending, seed the candidate threshold
+        // the lane maxima, sorted descending, seed the candidate threshold: each
+        // wave sorts its 64 through DPP, then every maximum finds its place
+        // among the other waves' sorted lists (ties: lower wave first)
         nf = wave_sum_i(nf);
         if (lane == 0) sh.red.i[wv] = nf;
         if (tid == 0) tt.nlist = 0;
-        const float srt = block_sort_desc(lm, tt.lmax);
+        const float srt = wave_sort_desc(lm);
+        tt.lmax[tid] = srt;
+        __syncthreads();
         nf = sh.red.i[0] + sh.red.i[1] + sh.red.i[2] + sh.red.i[3];
-        tt.sorted[tid] = srt;
+        {
+            int pos[NT / WAVE - 1];
+            const float* lst[NT / WAVE - 1];
+            bool ge[NT / WAVE - 1];
+#pragma unroll
+            for (int q = 0; q < NT / WAVE - 1; ++q) {
+                const int w2 = q < wv ? q : q + 1;
+                lst[q] = tt.lmax + w2 * WAVE;
+                ge[q] = w2 < wv;
+                pos[q] = 0;
+            }
+#pragma unroll
+            for (int b = 5; b >= 0; --b) {
+                float x[NT / WAVE - 1];
+#pragma unroll
+                for (int q = 0; q < NT / WAVE - 1; ++q) x[q] = lst[q][pos[q] + (1 << b) - 1];
+#pragma unroll
+                for (int q = 0; q < NT / WAVE - 1; ++q)
+                    pos[q] += (x[q] > srt || (ge[q] && x[q] == srt)) ? (1 << b) : 0;
+            }
+            int rank = lane;
+#pragma unroll
+            for (int q = 0; q < NT / WAVE - 1; ++q) {
+                const float x = lst[q][pos[q]];
+                rank += pos[q] + ((x > srt || (ge[q] && x == srt)) ? 1 : 0);
+            }
+            tt.sorted[rank] = srt;
+        }
         __syncthreads();
         const float m = tt.sorted[0];
         // first threshold try and the softmax partial sum in one exchange
@@ -483,15 +540,18 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
         int L = cap - step;
         const bool cut = nf > cap;
         float theta = cut ? tt.sorted[L] : NEG_INF;
-        int cnt = 0;
+        int mine = 0;
 #pragma unroll
-        for (int s = 0; s < EPT; ++s) cnt += v[s] > theta;
+        for (int s = 0; s < EPT; ++s) mine += v[s] > theta;
+        int cnt = mine;
         double ssum = 0.0;
         if (m > NEG_INF) {
+            // raw v_exp_f32: terms below 2^-126 flush to zero, which cannot move
+            // a sum whose largest term is 1
             const float c2 = 1.4426950408889634f / c.T;
             float acc = 0.0f;
 #pragma unroll
-            for (int s = 0; s < EPT; ++s) acc += exp2f((v[s] - m) * c2);
+            for (int s = 0; s < EPT; ++s) acc += __builtin_amdgcn_exp2f((v[s] - m) * c2);
             ssum = acc;
         }
         cnt = wave_sum_i(cnt);
@@ -508,40 +568,47 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
         while (cnt > cap) {
             L = L > step ? L - step : 0;
             theta = tt.sorted[L];
-            int k = 0;
+            mine = 0;
 #pragma unroll
-            for (int s = 0; s < EPT; ++s) k += v[s] > theta;
-            cnt = block_sum_i(k, sh.red);
+            for (int s = 0; s < EPT; ++s) mine += v[s] > theta;
+            cnt = block_sum_i(mine, sh.red);
         }
-        // candidate keys (z = x'/T, id) into LDS, one atomic per wave
-        int mine = 0;
-#pragma unroll
-        for (int s = 0; s < EPT; ++s) mine += v[s] > theta;
+        // candidates (x', id) into LDS, one atomic per wave
         const int inc = wave_incl_scan_i(mine);
         const int wtot = __builtin_amdgcn_readlane(inc, WAVE - 1);
         int base = 0;
         if (lane == 0 && wtot > 0) base = atomicAdd(&tt.nlist, wtot);
         base = __builtin_amdgcn_readfirstlane(base);
         int off = base + inc - mine;
+        if (mine) {
 #pragma unroll
-        for (int s = 0; s < EPT; ++s) {
-            if (v[s] > theta) {
-                tt.list[off] = key64(canon_zero(v[s] / c.T), slot_id<DT>(tb, s));
-                ++off;
+            for (int s = 0; s < EPT; ++s) {
+                if (v[s] > theta) {
+                    tt.list[off] = ((unsigned long long)__float_as_uint(v[s]) << 32) |
+                                   (uint32_t)slot_id<DT>(tb, s);
+                    ++off;
+                }
             }
         }
         __syncthreads();
-        // sorted list: each key's rank among the tile's candidates
+        // one key (z = x'/T, id) per thread, then each key's rank among the
+        // tile's candidates: the list goes out sorted
+        unsigned long long my = 0;
+        if (tid < cnt) {
+            const unsigned long long e = tt.list[tid];
+            my = key64(canon_zero(__uint_as_float((uint32_t)(e >> 32)) / c.T), (int)(uint32_t)e);
+            tt.keys[tid] = my;
+        }
+        __syncthreads();
         unsigned long long* cand = ws.cand + ((size_t)row * ws.n_tiles + tile) * CW;
         if (tid < cnt) {
-            const unsigned long long my = tt.list[tid];
             int r = 0;
             int j = 0;
             for (; j + 2 <= cnt; j += 2) {
-                const ulonglong2 q = *(const ulonglong2*)&tt.list[j];
+                const ulonglong2 q = *(const ulonglong2*)&tt.keys[j];
                 r += (q.x > my) + (q.y > my);
             }
-            if (j < cnt) r += tt.list[j] > my;
+            if (j < cnt) r += tt.keys[j] > my;
             cand[r] = my;
         }
         st.m = m;
@@ -714,15 +781,19 @@ __device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Wo
     const bool tl = tid < NT;
     float* zr = ws.scratch_z + (size_t)row * V;
     const bool tables = c.hist_len + c.extra_len + c.bias_len > 0;
-    TablePrefetch f = {{-1, -1}, -1, 0.0f};
+    TablePrefetch f = {{-1, -1}, -1, -1, 0.0f};
     if (tables && tl) f = prefetch_tables(c);
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
         float v[EPT];
-        if (tl) load_tile<DT>(c, t * TILE, v);
+        uint32_t mw[Lay<DT>::NG];
+        if (tl) {
+            load_tile<DT>(c, t * TILE, v);
+            load_mask<DT>(c, t * TILE, mw);
+        }
         if (tables) build_tables(c, t * TILE, su.t, f, tl);
         if (tl) {
-            process_tile<DT>(c, t * TILE, v, su.t);
+            process_tile<DT>(c, t * TILE, v, su.t, mw);
 #pragma unroll
             for (int s = 0; s < EPT; ++s) {
                 const int id = slot_id<DT>(t * TILE, s);
@@ -1274,9 +1345,12 @@ template <int DT>
 __device__ void residual_values(const RowCtx& c, const RowInfo& ri, const float* q, int tb,
                                 bool use_pi, SmemTile& tt, double r[EPT]) {
     float v[EPT];
+    uint32_t mw[Lay<DT>::NG];
+    const TablePrefetch f = prefetch_tables(c);
     load_tile<DT>(c, tb, v);
-    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, prefetch_tables(c));
-    process_tile<DT>(c, tb, v, tt);
+    load_mask<DT>(c, tb, mw);
+    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, f);
+    process_tile<DT>(c, tb, v, tt, mw);
 #pragma unroll
     for (int s = 0; s < EPT; ++s) {
         const int id = slot_id<DT>(tb, s);
@@ -1305,9 +1379,12 @@ __global__ __launch_bounds__(NT) void k_spec_resid_tiles(SpecArgs a) {
     const float* q = a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride;
     const int tb = tile * TILE;
     float v[EPT];
+    uint32_t mw[Lay<DT>::NG];
+    const TablePrefetch f = prefetch_tables(c);
     load_tile<DT>(c, tb, v);
-    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, prefetch_tables(c));
-    process_tile<DT>(c, tb, v, tt);
+    load_mask<DT>(c, tb, mw);
+    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, f);
+    process_tile<DT>(c, tb, v, tt, mw);
     double sr = 0.0, sp = 0.0;
 #pragma unroll
     for (int s = 0; s < EPT; ++s) {
