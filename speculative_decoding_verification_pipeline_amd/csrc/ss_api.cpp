@@ -12,7 +12,7 @@
 struct ss_sampler {
     ss_sampler_config cfg;
     int n_tiles;       // 8192-entry tiles per row
-    int n_vtiles;      // 256-column LM-head tiles
+    int n_vtiles;      // 128-row LM-head vocabulary tiles
     int max_rows;      // rows of the row kernels (verification: B * (G + 1))
     void* ws_base;
     int64_t ws_bytes;
@@ -119,7 +119,7 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     const int V = cfg->vocab_size;
     const int B = cfg->max_batch;
     s->n_tiles = (V + ss::TILE - 1) / ss::TILE;
-    s->n_vtiles = (V + 255) / 256;
+    s->n_vtiles = (V + 127) / 128;
     s->max_rows = B * (cfg->max_draft + 1);
     const int64_t R = s->max_rows;
     const int64_t nt = s->n_tiles;

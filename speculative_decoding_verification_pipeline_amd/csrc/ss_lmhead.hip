@@ -7,22 +7,27 @@
 // (score, index) pair.
 //
 // Design for MI355X:
-//  * The product z = W H^T is computed with W as the MFMA A operand (vocabulary
-//    rows as M) and H^T as B (batch as N), v_mfma_f32_32x32x16_bf16 with fp32
-//    accumulators. With that orientation each lane's accumulators cover four
-//    consecutive vocabulary entries of one batch row, which is exactly one
-//    Philox block (4 words), so the noise costs one generator call per 4 logits.
-//  * One workgroup (4 wave64s) owns a 256-column vocabulary tile for all (up to
-//    64) batch rows: wave w streams vocabulary rows [64w, 64w + 64) of the tile.
-//    Each lane reads 64 contiguous bytes of a W row per step (the two lanes of a
-//    row cover a whole 128-byte line), and the K index of each MFMA is permuted
-//    consistently on both operands so the loads stay contiguous. The next
-//    step's operands are loaded before the current step's MFMAs (register
-//    double buffering) to keep the W stream in flight; W is read once from HBM
-//    and never written back, and the logits never leave registers.
+//  * One workgroup (4 wave64s) owns a 128-row vocabulary tile for all (up to
+//    64) batch rows and walks K in steps of 64. Each step's operands -- 128 x 64
+//    of W and 64 x 64 of H, bf16 -- are copied straight from global memory into
+//    LDS by global_load_lds_dwordx4 (every instruction moves 1 KB: 8 rows x 128
+//    contiguous bytes), three steps deep, so the W stream keeps many bytes in
+//    flight without holding them in registers. Each LDS stage is a separate
+//    object, waits are explicit (vmcnt for the copies, lgkmcnt for the LDS reads
+//    of the stage being overwritten) and the barrier is a bare s_barrier.
+//  * LDS rows are 128 bytes; the 16-byte chunk c of row r sits in slot
+//    c ^ (r & 7) so the MFMA operand reads spread over the banks.
+//  * z = W h^T with v_mfma_f32_32x32x16_bf16, W as the A operand (vocabulary
+//    rows as M), H as B (batch as N): wave w computes vocabulary rows
+//    [32w, 32w + 32) x 64 batch rows in two f32 accumulators. Each lane's
+//    accumulators then cover four consecutive vocabulary entries of one batch
+//    row, which is exactly one Philox block (4 words).
+//  * Each workgroup starts K at its own step so concurrent workgroups spread
+//    their weight reads over the row span. W is read once from HBM; the logits
+//    never leave registers.
 //  * Epilogue: s = z / T + g, per-row (max, lowest index) over the tile, written
-//    as one pair per row per tile; a second, single-workgroup launch reduces
-//    the pairs of every row.
+//    as one pair per row per tile; a second launch reduces the pairs of every
+//    row.
 #include <float.h>
 #include <limits.h>
 
@@ -37,40 +42,76 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int LM_NT = 256;
-constexpr int LM_COLS = 256;   // vocabulary entries per workgroup tile
-constexpr int LM_KSTEP = 64;   // K consumed per pipeline step (4 MFMAs of K = 16)
+constexpr int LM_ROWS = 128;   // vocabulary rows per workgroup tile
+constexpr int LM_KSTEP = 64;   // K per pipeline step (4 MFMAs of K = 16)
 constexpr int LM_MAXB = 64;
+constexpr int LM_W_BYTES = LM_ROWS * LM_KSTEP * 2;   // 16 KB per stage
+constexpr int LM_H_BYTES = LM_MAXB * LM_KSTEP * 2;   // 8 KB per stage
 
-struct Ops {
-    uint4 a[2][4];  // W rows: [vocab block][sub-step]
-    uint4 b[2][4];  // H rows: [batch block][sub-step]
-};
+#define LDS_PTR(x) ((__attribute__((address_space(3))) void*)(x))
 
-__device__ __forceinline__ void load_ops(Ops& o, const uint16_t* __restrict__ wrow0,
-                                         const uint16_t* __restrict__ wrow1,
-                                         const uint16_t* __restrict__ hrow0,
-                                         const uint16_t* __restrict__ hrow1, int koff) {
+// s_waitcnt immediates (gfx9 encoding): vmcnt N with lgkmcnt 0, expcnt free.
+constexpr int WAIT_VM6_LGK0 = 0x0076;
+constexpr int WAIT_VM0_LGK0 = 0x0070;
+
+// Copies step `ks` of the operands into one LDS stage: wave w moves W rows
+// [32w, 32w + 32) (4 instructions) and H rows [16w, 16w + 16) (2 instructions).
+__device__ __forceinline__ void lm_copy(uint8_t* wbuf, uint8_t* hbuf, const uint16_t* __restrict__ weight,
+                                        const uint16_t* __restrict__ hidden, int K, int V, int B,
+                                        int tile, int ks) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane >> 3;             // row within the 8 rows of an instruction
+    const int slot = lane & 7;             // destination 16-byte slot in the LDS row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        o.a[0][i] = wrow0 ? *(const uint4*)(wrow0 + koff + 8 * i) : make_uint4(0, 0, 0, 0);
-        o.a[1][i] = wrow1 ? *(const uint4*)(wrow1 + koff + 8 * i) : make_uint4(0, 0, 0, 0);
-        o.b[0][i] = hrow0 ? *(const uint4*)(hrow0 + koff + 8 * i) : make_uint4(0, 0, 0, 0);
-        o.b[1][i] = hrow1 ? *(const uint4*)(hrow1 + koff + 8 * i) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+        const int r = wave * 32 + q * 8 + sub;                // row in the tile
+        const int c = slot ^ (r & 7);                          // global chunk held by this slot
+        int v = tile * LM_ROWS + r;
+        v = v < V ? v : V - 1;
+        const uint16_t* src = weight + (size_t)v * K + ks * LM_KSTEP + c * 8;
+        __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(wbuf + (wave * 32 + q * 8) * 128),
+                                         16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = wave * 16 + q * 8 + sub;
+        const int c = slot ^ (r & 7);
+        const int j = r < B ? r : B - 1;
+        const uint16_t* src = hidden + (size_t)j * K + ks * LM_KSTEP + c * 8;
+        __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(hbuf + (wave * 16 + q * 8) * 128),
+                                         16, 0, 0);
     }
 }
 
-__device__ __forceinline__ void mfma_ops(const Ops& o, floatx16 acc[2][2]) {
+// One step's MFMA operands from an LDS stage (read before the next copy is
+// issued, so nothing of the stage being read is in flight behind them).
+struct LmOps {
+    bf16x8 a[4];
+    bf16x8 b0[4];
+    bf16x8 b1[4];
+};
+
+__device__ __forceinline__ void lm_read(const uint8_t* wbuf, const uint8_t* hbuf, LmOps& o) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int half = lane >> 5;
+    const int r = wave * 32 + (lane & 31);
+    const int j0 = lane & 31, j1 = j0 + 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int s = 0; s < 4; ++s) {
+        const int c = 2 * s + half;
+        o.a[s] = *(const bf16x8*)(wbuf + r * 128 + ((c ^ (r & 7)) << 4));
+        o.b0[s] = *(const bf16x8*)(hbuf + j0 * 128 + ((c ^ (j0 & 7)) << 4));
+        o.b1[s] = *(const bf16x8*)(hbuf + j1 * 128 + ((c ^ (j1 & 7)) << 4));
+    }
+}
+
+__device__ __forceinline__ void lm_mfma(const LmOps& o, floatx16 acc[2]) {
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
-            const bf16x8 a = __builtin_bit_cast(bf16x8, o.a[vb][i]);
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const bf16x8 b = __builtin_bit_cast(bf16x8, o.b[bb][i]);
-                acc[vb][bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[vb][bb], 0, 0, 0);
-            }
-        }
+    for (int s = 0; s < 4; ++s) {
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[s], o.b0[s], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[s], o.b1[s], acc[1], 0, 0, 0);
     }
 }
 
@@ -79,55 +120,61 @@ __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
 }
 
 __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t w0[LM_W_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t w1[LM_W_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t w2[LM_W_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t h0[LM_H_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t h1[LM_H_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t h2[LM_H_BYTES];
     __shared__ float s_score[LM_NT / WAVE][LM_MAXB];
     __shared__ int s_idx[LM_NT / WAVE][LM_MAXB];
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
     const int wave = tid / WAVE;
     const int tile = blockIdx.x;
-    const int half = lane >> 5;      // which 32-wide K half this lane feeds
+    const int half = lane >> 5;
     const int r32 = lane & 31;
     const int K = a.K;
 
-    // vocabulary rows of this lane (A operand) and batch rows (B operand)
-    const int v0 = tile * LM_COLS + wave * 64 + r32;
-    const int v1 = v0 + 32;
-    const int koff_lane = 32 * half;
-    const uint16_t* w0 = v0 < a.V ? a.weight + (size_t)v0 * K + koff_lane : nullptr;
-    const uint16_t* w1 = v1 < a.V ? a.weight + (size_t)v1 * K + koff_lane : nullptr;
-    const uint16_t* h0 = r32 < a.B ? a.hidden + (size_t)r32 * K + koff_lane : nullptr;
-    const uint16_t* h1 = r32 + 32 < a.B ? a.hidden + (size_t)(r32 + 32) * K + koff_lane : nullptr;
+    floatx16 acc[2];
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[y][r] = 0.0f;
 
-    floatx16 acc[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
-
-    // each workgroup walks K from its own starting step, so concurrent
-    // workgroups spread their weight reads over the whole row span
+    // each workgroup walks K from its own starting step
     const int nsteps = K / LM_KSTEP;
     const int rot = (int)(((unsigned)tile * 2654435761u) % (unsigned)nsteps);
-    auto koff = [&](int it) {
+    auto ks_of = [&](int it) {
         int s = it + rot;
-        s = s >= nsteps ? s - nsteps : s;
-        return s * LM_KSTEP;
+        return s >= nsteps ? s - nsteps : s;
     };
-    Ops o0, o1;
-    load_ops(o0, w0, w1, h0, h1, koff(0));
-    int it = 0;
-    for (; it + 2 <= nsteps; it += 2) {
-        load_ops(o1, w0, w1, h0, h1, koff(it + 1));
-        mfma_ops(o0, acc);
-        if (it + 2 < nsteps) load_ops(o0, w0, w1, h0, h1, koff(it + 2));
-        mfma_ops(o1, acc);
+    lm_copy(w0, h0, a.weight, a.hidden, K, a.V, a.B, tile, ks_of(0));
+    if (nsteps > 1) lm_copy(w1, h1, a.weight, a.hidden, K, a.V, a.B, tile, ks_of(1));
+    // step i: wait for its copies (the next stage's may stay in flight) and for
+    // this wave's reads of the stage about to be overwritten, barrier, read the
+    // operands, start the copy two steps ahead, multiply.
+#define LM_STEP(WB, HB, WN, HN, I)                                                        \
+    {                                                                                     \
+        const int i_ = (I);                                                               \
+        if (i_ >= nsteps) break;                                                          \
+        if (i_ + 1 < nsteps) __builtin_amdgcn_s_waitcnt(WAIT_VM6_LGK0);                   \
+        else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGK0);                                   \
+        __builtin_amdgcn_s_barrier();                                                     \
+        LmOps o_;                                                                         \
+        lm_read(WB, HB, o_);                                                              \
+        if (i_ + 2 < nsteps) lm_copy(WN, HN, a.weight, a.hidden, K, a.V, a.B, tile, ks_of(i_ + 2)); \
+        lm_mfma(o_, acc);                                                                 \
     }
-    if (it < nsteps) mfma_ops(o0, acc);
+    for (int it = 0; it < nsteps; it += 3) {
+        LM_STEP(w0, h0, w2, h2, it)
+        LM_STEP(w1, h1, w0, h0, it + 1)
+        LM_STEP(w2, h2, w1, h1, it + 2)
+    }
+#undef LM_STEP
 
     // epilogue: lane holds, for batch column j = bb*32 + r32, vocabulary entries
-    // tile*256 + wave*64 + vb*32 + 8*(r/4) + 4*half + (r%4)
+    // tile*128 + wave*32 + 8*(r/4) + 4*half + (r%4)
     float best_s[2];
     int best_i[2];
 #pragma unroll
@@ -140,27 +187,24 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
         const uint32_t req = a.request_ids ? (uint32_t)a.request_ids[j] : (uint32_t)j;
         const uint32_t pos = a.positions ? (uint32_t)a.positions[j] : 0u;
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
+        for (int g = 0; g < 4; ++g) {
+            const int vbase = tile * LM_ROWS + wave * 32 + 8 * g + 4 * half;
+            if (vbase >= a.V) continue;
+            uint4 wv = make_uint4(0, 0, 0, 0);
+            if (T != 0.0f)
+                wv = philox4x32_10(make_uint4(req, pos, (uint32_t)vbase >> 2, DOM_GUMBEL),
+                                   (uint32_t)a.seed, (uint32_t)(a.seed >> 32));
+            const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int vbase = tile * LM_COLS + wave * 64 + vb * 32 + 8 * g + 4 * half;
-                if (vbase >= a.V) continue;
-                uint4 wv = make_uint4(0, 0, 0, 0);
-                if (T != 0.0f)
-                    wv = philox4x32_10(make_uint4(req, pos, (uint32_t)vbase >> 2, DOM_GUMBEL),
-                                       (uint32_t)a.seed, (uint32_t)(a.seed >> 32));
-                const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int v = vbase + q;
-                    if (v >= a.V) continue;
-                    const float z = acc[vb][bb][4 * g + q];
-                    if (a.debug_logits) a.debug_logits[(size_t)j * a.V + v] = z;
-                    const float s = (T != 0.0f) ? z / T + gumbel32(ws[q]) : z;
-                    if (better(s, v, best_s[bb], best_i[bb])) {
-                        best_s[bb] = s;
-                        best_i[bb] = v;
-                    }
+            for (int q = 0; q < 4; ++q) {
+                const int v = vbase + q;
+                if (v >= a.V) continue;
+                const float z = acc[bb][4 * g + q];
+                if (a.debug_logits) a.debug_logits[(size_t)j * a.V + v] = z;
+                const float s = (T != 0.0f) ? z / T + gumbel32(ws[q]) : z;
+                if (better(s, v, best_s[bb], best_i[bb])) {
+                    best_s[bb] = s;
+                    best_i[bb] = v;
                 }
             }
         }

@@ -145,6 +145,7 @@ constexpr int OCT = NTR / CW;     // tiles covered by one slot round
 struct SmemPool {
     unsigned long long buf[2][POOL];  // merge-tree ping-pong buffers (keys, zero = empty slot)
     double cbase[NTR];                // exclusive prefix mass of each thread's chunk
+    float w[POOL];                    // exp(z - zmax) of the sorted pool
     int wcnt[PERR][NTR / WAVE];       // kept candidates per (slot round, wave)
     int len[2][MAX_TILES];            // segment lengths per merge level
 };
@@ -882,12 +883,11 @@ __device__ __forceinline__ float key_z(unsigned long long k) {
 
 // Prefix mass S(x) = sum of w over the first x pool entries, from the chunk
 // bases: every thread computes it in the same order, so all agree exactly.
-__device__ __forceinline__ double prefix_mass(const SmemPool& p, const unsigned long long* f, int x,
-                                              int cs, float zmax) {
+__device__ __forceinline__ double prefix_mass(const SmemPool& p, int x, int cs) {
     int ch = x / cs;
     if (ch >= NTR) ch = NTR - 1;
     double s = p.cbase[ch];
-    for (int i = ch * cs; i < x; ++i) s += (double)expf(key_z(f[i]) - zmax);
+    for (int i = ch * cs; i < x; ++i) s += (double)p.w[i];
     return s;
 }
 
@@ -1088,7 +1088,11 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
         const int i0 = min(tid * cs, n);
         const int i1 = min(i0 + cs, n);
         double part = 0.0;
-        for (int i = i0; i < i1; ++i) part += (double)expf(key_z(F[i]) - zmax);
+        for (int i = i0; i < i1; ++i) {
+            const float w = expf(key_z(F[i]) - zmax);
+            P.w[i] = w;
+            part += (double)w;
+        }
         const double winc = wave_incl_scan_d(part);
         if (lane == WAVE - 1) sh.red.d[wv] = winc;
         __syncthreads();
@@ -1099,7 +1103,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
         double WK = rs.W;
         unsigned long long kK = 0;
         if (cut_k) {
-            WK = prefix_mass(P, F, K_eff, cs, zmax);
+            WK = prefix_mass(P, K_eff, cs);
             kK = F[K_eff - 1];
         }
         // top-p cut and min-p cut in one pass over the chunks
@@ -1109,7 +1113,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
         {
             double run = base;
             for (int i = i0; i < i1; ++i) {
-                const float w = expf(key_z(F[i]) - zmax);
+                const float w = P.w[i];
                 if (fp == INT_MAX && c.top_p < 1.0f && i < lim_p && run >= thr) fp = i;
                 if (fm == INT_MAX && c.min_p > 0.0f && w < c.min_p) fm = i;
                 run += (double)w;
@@ -1138,7 +1142,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
                 Wk = WK;
                 kappa = kK;
             } else {
-                Wk = prefix_mass(P, F, n_kept, cs, zmax);
+                Wk = prefix_mass(P, n_kept, cs);
                 kappa = F[n_kept - 1];
             }
             // the draw: first kept entry whose inclusive mass exceeds u W
@@ -1148,7 +1152,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
                 double run = base;
                 const int lim = min(n, n_kept);
                 for (int i = i0; i < min(i1, lim); ++i) {
-                    run += (double)expf(key_z(F[i]) - zmax);
+                    run += (double)P.w[i];
                     if (run > tgt) {
                         fd = i;
                         break;
@@ -1177,7 +1181,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
                 }
                 if (dbg.probs)
                     for (int i = tid; i < n_kept; i += NTR)
-                        dbg.probs[key64_id(F[i])] = (float)((double)expf(key_z(F[i]) - zmax) / Wk);
+                        dbg.probs[key64_id(F[i])] = (float)((double)P.w[i] / Wk);
                 if (dbg.topk)
                     for (int i = tid; i < dbg.topk_stride; i += NTR)
                         dbg.topk[i] = i < lim_list ? key64_id(F[i]) : -1;
