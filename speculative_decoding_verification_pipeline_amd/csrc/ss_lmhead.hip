@@ -92,19 +92,35 @@ struct LmOps {
     bf16x8 b1[4];
 };
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The reads are issued as ds_read_b128 in inline assembly, and one explicit
+// lgkmcnt(0) that takes every result as an operand orders them before their
+// uses: the compiler then sees no LDS read it would have to order against the
+// copies still in flight into the other stages.
 __device__ __forceinline__ void lm_read(const uint8_t* wbuf, const uint8_t* hbuf, LmOps& o) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int half = lane >> 5;
     const int r = wave * 32 + (lane & 31);
     const int j0 = lane & 31, j1 = j0 + 32;
+    const uint32_t wb = lds_addr(wbuf), hb = lds_addr(hbuf);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int c = 2 * s + half;
-        o.a[s] = *(const bf16x8*)(wbuf + r * 128 + ((c ^ (r & 7)) << 4));
-        o.b0[s] = *(const bf16x8*)(hbuf + j0 * 128 + ((c ^ (j0 & 7)) << 4));
-        o.b1[s] = *(const bf16x8*)(hbuf + j1 * 128 + ((c ^ (j1 & 7)) << 4));
+        const uint32_t aa = wb + r * 128 + ((c ^ (r & 7)) << 4);
+        const uint32_t ab0 = hb + j0 * 128 + ((c ^ (j0 & 7)) << 4);
+        const uint32_t ab1 = hb + j1 * 128 + ((c ^ (j1 & 7)) << 4);
+        asm volatile("ds_read_b128 %0, %1" : "=v"(o.a[s]) : "v"(aa));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(o.b0[s]) : "v"(ab0));
+        asm volatile("ds_read_b128 %0, %1" : "=v"(o.b1[s]) : "v"(ab1));
     }
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(o.a[0]), "+v"(o.a[1]), "+v"(o.a[2]), "+v"(o.a[3]), "+v"(o.b0[0]),
+                   "+v"(o.b0[1]), "+v"(o.b0[2]), "+v"(o.b0[3]), "+v"(o.b1[0]), "+v"(o.b1[1]),
+                   "+v"(o.b1[2]), "+v"(o.b1[3]));
 }
 
 __device__ __forceinline__ void lm_mfma(const LmOps& o, floatx16 acc[2]) {
