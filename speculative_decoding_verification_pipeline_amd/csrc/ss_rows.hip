@@ -144,8 +144,6 @@ constexpr int OCT = NTR / CW;     // tiles covered by one slot round
 
 struct SmemPool {
     unsigned long long buf[2][POOL];  // merge-tree ping-pong buffers (keys, zero = empty slot)
-    double cbase[NTR];                // exclusive prefix mass of each thread's chunk
-    float w[POOL];                    // exp(z - zmax) of the sorted pool
     int wcnt[PERR][NTR / WAVE];       // kept candidates per (slot round, wave)
     int len[2][MAX_TILES];            // segment lengths per merge level
 };
@@ -881,37 +879,6 @@ __device__ __forceinline__ float key_z(unsigned long long k) {
     return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
 }
 
-// Prefix mass S(x) = sum of w over the first x pool entries, from the chunk
-// bases: every thread computes it in the same order, so all agree exactly.
-__device__ __forceinline__ double prefix_mass(const SmemPool& p, int x, int cs) {
-    int ch = x / cs;
-    if (ch >= NTR) ch = NTR - 1;
-    double s = p.cbase[ch];
-    for (int i = ch * cs; i < x; ++i) s += (double)p.w[i];
-    return s;
-}
-
-// Minimum over the workgroup of one int per thread (two values at once).
-__device__ __forceinline__ int2 rows_min2(int a, int b, SmemR& sh) {
-    const int lane = threadIdx.x & (WAVE - 1);
-    const int wv = threadIdx.x / WAVE;
-    a = wave_min_i(a);
-    b = wave_min_i(b);
-    __syncthreads();
-    if (lane == 0) {
-        sh.red.i[wv] = a;
-        sh.red2.i[wv] = b;
-    }
-    __syncthreads();
-    int ra = INT_MAX, rb = INT_MAX;
-#pragma unroll
-    for (int k = 0; k < NTR / WAVE; ++k) {
-        ra = min(ra, sh.red.i[k]);
-        rb = min(rb, sh.red2.i[k]);
-    }
-    return make_int2(ra, rb);
-}
-
 // What the merge reads from stage 1: the row's candidate slots and the tile
 // summaries (lane t holds tile t). Issued before anything else so the row's
 // loads share one round trip.
@@ -977,6 +944,127 @@ __device__ __forceinline__ void merge_level(const unsigned long long* in, unsign
         if (ob[r] >= 0) out[ob[r] + pos[r]] = key[r];
         else if (ob[r] <= -2) out[-2 - ob[r]] = 0ull;
     }
+}
+
+// Outcome of resolving a row on its sorted pool.
+struct RowOut {
+    unsigned long long kappa;
+    double Wk;
+    int n_kept;
+    int token;
+    int lim_list;
+    int slow;
+};
+
+// One wave answers top-k mass, top-p, min-p and the draw on the sorted pool
+// F[0, n), 64 entries per step: entry i's weight w_i = exp(z_i - zmax) (binary32,
+// as everywhere on this path), masses in binary64 with a running carry.
+// slow = 1 when a request reaches past the pool.
+__device__ __forceinline__ RowOut resolve_wave(const unsigned long long* F, int n, float zmax, const RowSummary& rs,
+                               const RowCtx& c, float u, int K_eff, bool cut_k, int total,
+                               bool topk_on, bool want_probs, bool want_topk, double WK_block) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    RowOut o;
+    o.slow = 0;
+    o.kappa = 0;
+    o.Wk = rs.W;
+    o.n_kept = 0;
+    o.token = -1;
+    o.lim_list = cut_k ? K_eff : (topk_on ? total : 0);
+    auto wat = [&](int i, int lim) -> float {
+        return i < lim ? expf(key_z(F[i]) - zmax) : 0.0f;
+    };
+    // mass of the top-k set (summed by the whole workgroup when it spans more
+    // than one chunk)
+    double WK = rs.W;
+    unsigned long long kK = 0;
+    if (cut_k) {
+        if (K_eff > WAVE) {
+            WK = WK_block;
+        } else {
+            WK = wave_sum_d((double)wat(lane, K_eff));
+        }
+        kK = F[K_eff - 1];
+    }
+    // top-p (first entry whose exclusive mass reaches top_p W_K) and min-p
+    // (first entry with w < min_p), scanned together
+    const int lim_p = cut_k ? K_eff : total;
+    const bool use_p = c.top_p < 1.0f, use_m = c.min_p > 0.0f;
+    const double thr = (double)c.top_p * WK;
+    const int end_p = min(n, lim_p);
+    int fp = INT_MAX, fm = INT_MAX;
+    {
+        double carry = 0.0;
+        for (int c0 = 0;; c0 += WAVE) {
+            const bool need_p = use_p && fp == INT_MAX && c0 < end_p;
+            const int n_topp_now = fp != INT_MAX ? fp : lim_p;
+            const bool need_m = use_m && fm == INT_MAX && c0 < min(n, n_topp_now);
+            if (!need_p && !need_m) break;
+            const int i = c0 + lane;
+            const float w = wat(i, n);
+            const double in = wave_incl_scan_d((double)w);
+            const double excl = carry + (in - (double)w);
+            if (need_p) {
+                const unsigned long long m = __ballot(i < end_p && excl >= thr);
+                if (m) fp = c0 + __ffsll((long long)m) - 1;
+            }
+            if (need_m) {
+                const unsigned long long m = __ballot(i < n && w < c.min_p);
+                if (m) fm = c0 + __ffsll((long long)m) - 1;
+            }
+            carry += __shfl(in, WAVE - 1);
+        }
+    }
+    int n_topp = lim_p;
+    if (use_p) {
+        if (fp != INT_MAX) n_topp = fp;
+        else if (lim_p > n) o.slow = 1;
+    }
+    int n_kept = n_topp;
+    if (!o.slow && use_m) {
+        if (fm < n_topp) n_kept = fm;
+        else if (fm == INT_MAX && n_topp > n) o.slow = 1;
+    }
+    if (o.slow) return o;
+    // kept mass and the cut key
+    double Wk;
+    unsigned long long kappa;
+    if (n_kept == total) {
+        Wk = rs.W;
+        kappa = 0;
+    } else if (cut_k && n_kept == K_eff) {
+        Wk = WK;
+        kappa = kK;
+    } else {
+        double carry = 0.0;
+        for (int c0 = 0; c0 < n_kept; c0 += WAVE) carry += wave_sum_d((double)wat(c0 + lane, n_kept));
+        Wk = carry;
+        kappa = F[n_kept - 1];
+    }
+    // the draw: first kept entry whose inclusive mass exceeds u Wk
+    const double tgt = (double)u * Wk;
+    const int lim = min(n, n_kept);
+    int fd = INT_MAX;
+    {
+        double carry = 0.0;
+        for (int c0 = 0; c0 < lim && fd == INT_MAX; c0 += WAVE) {
+            const int i = c0 + lane;
+            const double in = carry + wave_incl_scan_d((double)wat(i, lim));
+            const unsigned long long m = __ballot(i < lim && in > tgt);
+            if (m) fd = c0 + __ffsll((long long)m) - 1;
+            carry = __shfl(in, WAVE - 1);
+        }
+    }
+    const int pick = fd != INT_MAX ? fd : (n_kept <= n ? n_kept - 1 : -1);
+    if (pick < 0 || (want_probs && n_kept > n) || (want_topk && o.lim_list > n)) {
+        o.slow = 1;
+        return o;
+    }
+    o.kappa = kappa;
+    o.Wk = Wk;
+    o.n_kept = n_kept;
+    o.token = key64_id(F[pick]);
+    return o;
 }
 
 template <int DT>
@@ -1083,111 +1171,46 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
     const bool cut_k = topk_on && K_eff < total;
     bool slow = n == 0 || (cut_k && K_eff > n);
     if (!slow) {
-        // binary64 prefix masses over contiguous chunks of the sorted pool
-        const int cs = (n + NTR - 1) / NTR;
-        const int i0 = min(tid * cs, n);
-        const int i1 = min(i0 + cs, n);
-        double part = 0.0;
-        for (int i = i0; i < i1; ++i) {
-            const float w = expf(key_z(F[i]) - zmax);
-            P.w[i] = w;
-            part += (double)w;
+        // Wave 0 resolves the row on the sorted pool, 64 entries at a time with
+        // a running binary64 carry (every cut is a prefix question, and on
+        // low-entropy rows all of them fall in the first chunk or two); the
+        // rest of the workgroup waits at one barrier.
+        __shared__ RowOut s_out;
+        double WK_block = 0.0;
+        if (cut_k && K_eff > WAVE) {
+            double part = 0.0;
+            for (int i = tid; i < K_eff; i += NTR) part += (double)expf(key_z(F[i]) - zmax);
+            WK_block = block_sum_d(part, sh.red);
         }
-        const double winc = wave_incl_scan_d(part);
-        if (lane == WAVE - 1) sh.red.d[wv] = winc;
+        if (wv == 0) {
+            const RowOut o = resolve_wave(F, n, zmax, rs, c, u, K_eff, cut_k, total, topk_on,
+                                          dbg.probs != nullptr, dbg.topk != nullptr, WK_block);
+            if (lane == 0) s_out = o;
+        }
         __syncthreads();
-        double base = winc - part;
-        for (int k = 0; k < wv; ++k) base += sh.red.d[k];
-        P.cbase[tid] = base;
-        __syncthreads();
-        double WK = rs.W;
-        unsigned long long kK = 0;
-        if (cut_k) {
-            WK = prefix_mass(P, K_eff, cs);
-            kK = F[K_eff - 1];
-        }
-        // top-p cut and min-p cut in one pass over the chunks
-        const int lim_p = cut_k ? K_eff : total;
-        const double thr = (double)c.top_p * WK;
-        int fp = INT_MAX, fm = INT_MAX;
-        {
-            double run = base;
-            for (int i = i0; i < i1; ++i) {
-                const float w = P.w[i];
-                if (fp == INT_MAX && c.top_p < 1.0f && i < lim_p && run >= thr) fp = i;
-                if (fm == INT_MAX && c.min_p > 0.0f && w < c.min_p) fm = i;
-                run += (double)w;
+        const RowOut o = s_out;
+        if (!o.slow) {
+            RowInfo r;
+            r.kappa = o.kappa;
+            r.W = o.Wk;
+            r.zmax = zmax;
+            r.min_p = 0.0f;
+            r.n_kept = o.n_kept;
+            r.token = o.token;
+            r.argmax = -1;
+            r.path = 0;
+            if (tid == 0) {
+                if (dbg.kept) *dbg.kept = o.n_kept;
+                if (dbg.path) *dbg.path = 0;
             }
-        }
-        const int2 fpm = rows_min2(fp, fm, sh);
-        fp = fpm.x;
-        fm = fpm.y;
-        int n_topp = lim_p;
-        if (c.top_p < 1.0f) {
-            if (fp != INT_MAX) n_topp = fp;
-            else if (lim_p > n) slow = true;
-        }
-        int n_kept = n_topp;
-        if (!slow && c.min_p > 0.0f) {
-            if (fm < n_topp) n_kept = fm;
-            else if (fm == INT_MAX && n_topp > n) slow = true;
-        }
-        if (!slow) {
-            double Wk;
-            unsigned long long kappa;
-            if (n_kept == total) {
-                Wk = rs.W;
-                kappa = 0;
-            } else if (cut_k && n_kept == K_eff) {
-                Wk = WK;
-                kappa = kK;
-            } else {
-                Wk = prefix_mass(P, n_kept, cs);
-                kappa = F[n_kept - 1];
-            }
-            // the draw: first kept entry whose inclusive mass exceeds u W
-            const double tgt = (double)u * Wk;
-            int fd = INT_MAX;
-            {
-                double run = base;
-                const int lim = min(n, n_kept);
-                for (int i = i0; i < min(i1, lim); ++i) {
-                    run += (double)P.w[i];
-                    if (run > tgt) {
-                        fd = i;
-                        break;
-                    }
-                }
-            }
-            fd = rows_min2(fd, INT_MAX, sh).x;
-            const int pick = fd != INT_MAX ? fd : (n_kept <= n ? n_kept - 1 : -1);
-            // debug outputs need the kept / top-k sets listed in full
-            const int lim_list = cut_k ? K_eff : (topk_on ? total : 0);
-            if (pick < 0 || (dbg.probs && n_kept > n) || (dbg.topk && lim_list > n)) {
-                slow = true;
-            } else {
-                RowInfo r;
-                r.kappa = kappa;
-                r.W = Wk;
-                r.zmax = zmax;
-                r.min_p = 0.0f;
-                r.n_kept = n_kept;
-                r.token = key64_id(F[pick]);
-                r.argmax = -1;
-                r.path = 0;
-                if (tid == 0) {
-                    if (dbg.kept) *dbg.kept = n_kept;
-                    if (dbg.path) *dbg.path = 0;
-                }
-                if (dbg.probs)
-                    for (int i = tid; i < n_kept; i += NTR)
-                        dbg.probs[key64_id(F[i])] = (float)((double)P.w[i] / Wk);
-                if (dbg.topk)
-                    for (int i = tid; i < dbg.topk_stride; i += NTR)
-                        dbg.topk[i] = i < lim_list ? key64_id(F[i]) : -1;
-                info_out = r;
-                return;
-            }
+            if (dbg.probs)
+                for (int i = tid; i < o.n_kept; i += NTR)
+                    dbg.probs[key64_id(F[i])] = (float)((double)expf(key_z(F[i]) - zmax) / o.Wk);
+            if (dbg.topk)
+                for (int i = tid; i < dbg.topk_stride; i += NTR)
+                    dbg.topk[i] = i < o.lim_list ? key64_id(F[i]) : -1;
+            info_out = r;
+            return;
         }
     }
     finalize_slow<DT>(c, row, ws, n_tiles, rs, u, su, sh, info, dbg);
