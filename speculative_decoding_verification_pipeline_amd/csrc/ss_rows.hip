@@ -454,12 +454,19 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
         }
     }
 
-    float lm = NEG_INF;
-    int nf = 0;
+    // lane maximum and minimum; entries are counted one by one only in waves
+    // where some lane holds a -inf
+    float lm = v[0], lmin = v[0];
 #pragma unroll
-    for (int s = 0; s < EPT; ++s) {
+    for (int s = 1; s < EPT; ++s) {
         lm = fmaxf(lm, v[s]);
-        nf += v[s] > NEG_INF;
+        lmin = fminf(lmin, v[s]);
+    }
+    int nf = EPT;
+    if (__ballot(!(lmin > NEG_INF))) {
+        nf = 0;
+#pragma unroll
+        for (int s = 0; s < EPT; ++s) nf += v[s] > NEG_INF;
     }
     TileStat st;
     st.pad = 0;
@@ -467,7 +474,8 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
     if (cap == 0) {
         const float m = block_max(lm, sh.red);
         int am = INT_MAX;
-        if (m > NEG_INF) {
+        // only lanes holding the maximum look for its lowest index
+        if (m > NEG_INF && lm == m) {
 #pragma unroll
             for (int s = EPT - 1; s >= 0; --s)
                 if (v[s] == m) am = slot_id<DT>(tb, s);
@@ -544,7 +552,10 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
         for (int s = 0; s < EPT; ++s) mine += v[s] > theta;
         int cnt = mine;
         double ssum = 0.0;
-        if (m > NEG_INF) {
+        // The tile sum only feeds the row's normaliser, which a top-k cut makes
+        // unused: a tile with more than k finite entries proves the cut.
+        const bool need_s = !(c.top_k > 0 && c.top_k < c.V && nf > c.top_k);
+        if (need_s && m > NEG_INF) {
             // raw v_exp_f32: terms below 2^-126 flush to zero, which cannot move
             // a sum whose largest term is 1
             const float c2 = 1.4426950408889634f / c.T;
