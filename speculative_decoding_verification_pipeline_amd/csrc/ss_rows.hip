@@ -612,13 +612,16 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
         __syncthreads();
         unsigned long long* cand = ws.cand + ((size_t)row * ws.n_tiles + tile) * CW;
         if (tid < cnt) {
+            // four keys per batch, both reads issued before the compares
             int r = 0;
             int j = 0;
-            for (; j + 2 <= cnt; j += 2) {
-                const ulonglong2 q = *(const ulonglong2*)&tt.keys[j];
-                r += (q.x > my) + (q.y > my);
+            const ulonglong2* k2 = (const ulonglong2*)tt.keys;
+#pragma unroll 1
+            for (; j + 4 <= cnt; j += 4) {
+                const ulonglong2 q0 = k2[j >> 1], q1 = k2[(j >> 1) + 1];
+                r += (q0.x > my) + (q0.y > my) + (q1.x > my) + (q1.y > my);
             }
-            if (j < cnt) r += tt.keys[j] > my;
+            for (; j < cnt; ++j) r += tt.keys[j] > my;
             cand[r] = my;
         }
         st.m = m;
@@ -1263,7 +1266,11 @@ __device__ __forceinline__ RowCtx spec_ctx(const SpecArgs& a, int b, int j) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(NT) void k_sample_tiles(SampleArgs a) {
+// Tile kernels: seven 256-thread workgroups per CU fit the LDS (about 23 KB
+// each); the register budget is held to the same seven waves per SIMD.
+#define SS_TILE_OCC __attribute__((amdgpu_waves_per_eu(7)))
+
+__global__ __launch_bounds__(NT) SS_TILE_OCC void k_sample_tiles(SampleArgs a) {
     __shared__ SmemTile tt;
     __shared__ SmemS sh;
     const int n_tiles = a.ws.n_tiles;
@@ -1404,7 +1411,7 @@ __device__ void residual_values(const RowCtx& c, const RowInfo& ri, const float*
 // Verification, residual stage 1: per tile of each rejected row, the sums of the
 // residual max(0, pi - q) and of pi (the fallback when the residual is zero).
 template <int DT>
-__global__ __launch_bounds__(NT) void k_spec_resid_tiles(SpecArgs a) {
+__global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a) {
     __shared__ SmemTile tt;
     __shared__ SmemS sh;
     const int n_tiles = a.ws.n_tiles;
