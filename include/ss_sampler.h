@@ -143,6 +143,8 @@ ss_status ss_sampler_set_launch_events(ss_sampler* s, void* const* events, int32
  *   logits      [B, row_stride] of dtype (SS_F32 or SS_BF16), element-aligned,
  *               row_stride >= V. Rows whose start is 16-byte aligned are read
  *               with 16-byte vector loads, others element by element.
+ *               Entries are finite or -inf (-inf = never sampled); NaN and
+ *               +inf are outside the contract (the result is unspecified).
  *   B           0 .. max_batch (0 is a no-op).
  *   params      per-row parameters (host struct of device pointers).
  *   out_tokens  [B] int32: sampled token, or -1 when a row has no finite logit.
