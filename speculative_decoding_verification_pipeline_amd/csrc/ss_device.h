@@ -106,6 +106,13 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWMASK, 0xF, BOUND_ZERO);
 }
 
+// A DPP move whose lanes all read a lane of their own row (or whose edge lanes
+// are discarded by the caller): no old value is needed, so none is materialised.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+
 enum : int {
     DPP_QUAD_X1 = 0xB1,      // quad_perm [1,0,3,2]: lane ^ 1
     DPP_QUAD_X2 = 0x4E,      // quad_perm [2,3,0,1]: lane ^ 2
@@ -121,27 +128,39 @@ enum : int {
     DPP_BCAST31 = 0x143,     // lane 31 -> rows 2 and 3
 };
 
+// Lanes of a wave whose index has bit B set (B a power of two; 0 for B >= 64).
+__host__ __device__ constexpr unsigned long long lanes_with_bit(int b) {
+    return b == 1 ? 0xAAAAAAAAAAAAAAAAull : b == 2 ? 0xCCCCCCCCCCCCCCCCull
+         : b == 4 ? 0xF0F0F0F0F0F0F0F0ull : b == 8 ? 0xFF00FF00FF00FF00ull
+         : b == 16 ? 0xFFFF0000FFFF0000ull : b == 32 ? 0xFFFFFFFF00000000ull : 0ull;
+}
+
+// A lane-constant condition given as a wave mask: the mask stays in scalar
+// registers and feeds the select directly (no per-lane arithmetic).
+__device__ __forceinline__ bool lane_in(unsigned long long mask) {
+    return __builtin_amdgcn_inverse_ballot_w64(mask);
+}
+
 // The value held by lane ^ J (J a power of two below 64).
 template <int J>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-    const int lane = threadIdx.x & (WAVE - 1);
     if constexpr (J == 1) {
-        return dpp_u32<DPP_QUAD_X1>(0u, v);
+        return dpp_mov<DPP_QUAD_X1>(v);
     } else if constexpr (J == 2) {
-        return dpp_u32<DPP_QUAD_X2>(0u, v);
+        return dpp_mov<DPP_QUAD_X2>(v);
     } else if constexpr (J == 4) {
-        const uint32_t up = dpp_u32<DPP_ROW_SHL4>(0u, v);
-        const uint32_t dn = dpp_u32<DPP_ROW_SHR4>(0u, v);
-        return (lane & 4) ? dn : up;
+        const uint32_t up = dpp_mov<DPP_ROW_SHL4>(v);
+        const uint32_t dn = dpp_mov<DPP_ROW_SHR4>(v);
+        return lane_in(lanes_with_bit(4)) ? dn : up;
     } else if constexpr (J == 8) {
-        return dpp_u32<DPP_ROW_ROR8>(0u, v);
+        return dpp_mov<DPP_ROW_ROR8>(v);
     } else if constexpr (J == 16) {
         const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-        return (lane & 16) ? p[0] : p[1];
+        return lane_in(lanes_with_bit(16)) ? p[0] : p[1];
     } else {
         static_assert(J == 32, "lane exchange distance");
         const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-        return (lane & 32) ? p[0] : p[1];
+        return lane_in(lanes_with_bit(32)) ? p[0] : p[1];
     }
 }
 
@@ -170,7 +189,7 @@ __device__ __forceinline__ T wave_allreduce32(T v, Op op) {
         constexpr int C = decltype(tag)::value;
         uint32_t u;
         __builtin_memcpy(&u, &x, 4);
-        u = dpp_u32<C>(0u, u);
+        u = dpp_mov<C>(u);
         T r;
         __builtin_memcpy(&r, &u, 4);
         return r;
@@ -221,8 +240,8 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 template <int C>
 __device__ __forceinline__ double dpp_f64(double v) {
     const unsigned long long u = __double_as_longlong(v);
-    const uint32_t lo = dpp_u32<C>(0u, (uint32_t)u);
-    const uint32_t hi = dpp_u32<C>(0u, (uint32_t)(u >> 32));
+    const uint32_t lo = dpp_mov<C>((uint32_t)u);
+    const uint32_t hi = dpp_mov<C>((uint32_t)(u >> 32));
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
@@ -267,10 +286,10 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 // the row ends carried across rows).
 __device__ __forceinline__ int wave_incl_scan_i(int v) {
     uint32_t u = (uint32_t)v;
-    u += dpp_u32<DPP_ROW_SHR1, 0xF, true>(0u, u);
-    u += dpp_u32<DPP_ROW_SHR2, 0xF, true>(0u, u);
-    u += dpp_u32<DPP_ROW_SHR4, 0xF, true>(0u, u);
-    u += dpp_u32<DPP_ROW_SHR8, 0xF, true>(0u, u);
+    u += dpp_mov<DPP_ROW_SHR1>(u);
+    u += dpp_mov<DPP_ROW_SHR2>(u);
+    u += dpp_mov<DPP_ROW_SHR4>(u);
+    u += dpp_mov<DPP_ROW_SHR8>(u);
     u += dpp_u32<DPP_BCAST15, 0xA, false>(0u, u);
     u += dpp_u32<DPP_BCAST31, 0xC, false>(0u, u);
     return (int)u;
@@ -391,58 +410,37 @@ __device__ __forceinline__ double block_excl_scan_d(double v, RedT<NB>& r, doubl
     return base + inc - v;
 }
 
-__device__ __forceinline__ float xor_lane_dyn(float v, int j) {
+__device__ __forceinline__ uint32_t xor_lane_dyn_u(uint32_t v, int j) {
     switch (j) {
-    case 1: return xor_lane_f<1>(v);
-    case 2: return xor_lane_f<2>(v);
-    case 4: return xor_lane_f<4>(v);
-    case 8: return xor_lane_f<8>(v);
-    case 16: return xor_lane_f<16>(v);
-    default: return xor_lane_f<32>(v);
+    case 1: return xor_lane<1>(v);
+    case 2: return xor_lane<2>(v);
+    case 4: return xor_lane<4>(v);
+    case 8: return xor_lane<8>(v);
+    case 16: return xor_lane<16>(v);
+    default: return xor_lane<32>(v);
     }
 }
 
 // Sorts one float per lane across the wave, descending (bitonic network over
-// DPP / permlane exchanges; lane i ends with the i-th largest).
+// DPP / permlane exchanges; lane i ends with the i-th largest). The network runs
+// on order-preserving u32 images of the floats, and which lanes of a pair keep
+// the larger value is a constant lane mask per step, so a step costs one lane
+// exchange, one compare and one select.
 __device__ __forceinline__ float wave_sort_desc(float v) {
-    const int lane = threadIdx.x & (WAVE - 1);
+    uint32_t u = __float_as_uint(v);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 #pragma unroll
     for (int k = 2; k <= WAVE; k <<= 1) {
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            const float o = xor_lane_dyn(v, j);
-            const bool desc = (lane & k) == 0;
-            const bool lower = (lane & j) == 0;
-            v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
+            const uint32_t o = xor_lane_dyn_u(u, j);
+            // the lower lane of a pair keeps the larger value in descending blocks
+            const bool keep_max = lane_in(~(lanes_with_bit(k) ^ lanes_with_bit(j)));
+            u = ((u >= o) == keep_max) ? u : o;
         }
     }
-    return v;
-}
-
-// Sorts one float per thread across the workgroup, descending (bitonic network;
-// strides below the wave width exchange through DPP / permlane, the rest
-// through LDS).
-__device__ __forceinline__ float block_sort_desc(float v, float* tmp) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int k = 2; k <= NT; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            float o;
-            if (j >= WAVE) {
-                tmp[tid] = v;
-                __syncthreads();
-                o = tmp[tid ^ j];
-                __syncthreads();
-            } else {
-                o = xor_lane_dyn(v, j);
-            }
-            const bool desc = (tid & k) == 0;
-            const bool lower = (tid & j) == 0;
-            v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
-        }
-    }
-    return v;
+    u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+    return __uint_as_float(u);
 }
 
 }  // namespace ss
