@@ -141,6 +141,7 @@ struct SmemTile {
 constexpr int NTR = 1024;
 constexpr int PERR = POOL / NTR;  // candidate slots per merge thread
 constexpr int OCT = NTR / CW;     // tiles covered by one slot round
+constexpr int MERGE_LG_MAX = 12;  // log2 of the largest merge segment (POOL slots)
 
 struct SmemPool {
     unsigned long long buf[2][POOL];  // merge-tree ping-pong buffers (keys, zero = empty slot)
@@ -929,8 +930,8 @@ __device__ __forceinline__ void merge_level(const unsigned long long* in, unsign
         const int g = tid + r * NTR;
         const int gg = g < nslots ? g : 0;
         key[r] = in[gg];
-        const int sg = gg / C;
-        const int i = gg - sg * C;
+        const int sg = gg >> lg;
+        const int i = gg & (C - 1);
         const int lo = len[sg];
         const int le = len[sg & ~1], lr = len[sg | 1];
         pb[r] = (sg ^ 1) * C;
@@ -939,23 +940,104 @@ __device__ __forceinline__ void merge_level(const unsigned long long* in, unsign
         else if (i < lo) ob[r] = (sg & ~1) * C + i;  // plus the partner count
         else ob[r] = -2 - ((sg & ~1) * C + le + lr + ((sg & 1) ? (C - le) : 0) + (i - lo));
     }
-    for (int bit = lg - 1; bit >= 0; --bit) {
-        unsigned long long x[R];
+    const unsigned long long* sp[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) x[r] = in[pb[r] + pos[r] + (1 << bit) - 1];
+    for (int r = 0; r < R; ++r) sp[r] = in + pb[r];
+    bool kept = false;
 #pragma unroll
-        for (int r = 0; r < R; ++r) pos[r] += x[r] > key[r] ? (1 << bit) : 0;
-    }
-    {
-        unsigned long long x[R];
+    for (int r = 0; r < R; ++r) kept |= ob[r] >= 0;
+    if (__ballot(kept)) {  // waves holding only empty slots skip the searches
 #pragma unroll
-        for (int r = 0; r < R; ++r) x[r] = in[pb[r] + pos[r]];
+        for (int bit = MERGE_LG_MAX - 1; bit >= 0; --bit) {
+            if (bit >= lg) continue;
+            unsigned long long x[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) pos[r] += x[r] > key[r] ? 1 : 0;
+            for (int r = 0; r < R; ++r) x[r] = sp[r][(1 << bit) - 1];
+#pragma unroll
+            for (int r = 0; r < R; ++r) sp[r] += x[r] > key[r] ? (1 << bit) : 0;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) pos[r] = (int)(sp[r] - (in + pb[r])) + (sp[r][0] > key[r] ? 1 : 0);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if (ob[r] >= 0) out[ob[r] + pos[r]] = key[r];
+        else if (ob[r] <= -2) out[-2 - ob[r]] = 0ull;
+    }
+}
+
+// A four-way merge level: each group of four segments of C = 2^lg slots becomes
+// one segment of 4C. A kept entry moves to its index plus, for each of its three
+// partner segments, the number of partner entries before it (binary searches
+// over the padded partners, all 3R in lockstep); empty slots fill the group's
+// tail in segment order. Half the levels of pairwise merging, so half the chain
+// of dependent LDS reads.
+template <int R>
+__device__ __forceinline__ void merge_level4(const unsigned long long* in, unsigned long long* out,
+                                             const int* len, int C, int lg, int nslots) {
+    const int tid = threadIdx.x;
+    unsigned long long key[R];
+    int pos[R][3], pb[R][3], ob[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int g = tid + r * NTR;
+        const int gg = g < nslots ? g : 0;
+        key[r] = in[gg];
+        const int sg = gg >> lg;
+        const int q = sg & 3, g0 = sg & ~3;
+        const int i = gg & (C - 1);
+        const int lo = len[sg];
+        int tot = 0, before = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int lp = len[g0 + p];
+            tot += lp;
+            before += p < q ? C - lp : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            pb[r][k] = (g0 + k + (k >= q ? 1 : 0)) << lg;
+            pos[r][k] = 0;
+        }
+        if (g >= nslots) ob[r] = -1;
+        else if (i < lo) ob[r] = (g0 << lg) + i;  // plus the partner counts
+        else ob[r] = -2 - ((g0 << lg) + tot + before + (i - lo));
+    }
+    // kept entries sit at the front of each segment, so whole waves of slots
+    // are often empty: their searches are skipped (a wave-uniform branch)
+    // each search walks a pointer into its partner; the probe distance of a
+    // step is a constant, so it rides in the LDS instruction's offset field
+    const unsigned long long* sp[R][3];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) sp[r][k] = in + pb[r][k];
+    bool kept = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) kept |= ob[r] >= 0;
+    if (__ballot(kept)) {  // waves holding only empty slots skip the searches
+#pragma unroll
+        for (int bit = MERGE_LG_MAX - 1; bit >= 0; --bit) {
+            if (bit >= lg) continue;
+            unsigned long long x[R][3];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) x[r][k] = sp[r][k][(1 << bit) - 1];
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) sp[r][k] += x[r][k] > key[r] ? (1 << bit) : 0;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                pos[r][k] = (int)(sp[r][k] - (in + pb[r][k])) + (sp[r][k][0] > key[r] ? 1 : 0);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (ob[r] >= 0) out[ob[r] + pos[r][0] + pos[r][1] + pos[r][2]] = key[r];
         else if (ob[r] <= -2) out[-2 - ob[r]] = 0ull;
     }
 }
@@ -1157,24 +1239,43 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
     // position is its index in its segment plus the number of partner entries
     // that precede it (binary search over the padded partner segment); empty
     // slots fill the tail of each merged segment with zero keys.
+    // Four-way levels while a group of four segments exists in the padded
+    // layout, then at most one pairwise level.
     int src = 0;
-    for (int seg_tiles = 1, lg = lsw; seg_tiles < n_tiles; seg_tiles *= 2, ++lg) {
+    for (int seg_tiles = 1, lg = lsw; seg_tiles < n_tiles;) {
         const int C = seg_tiles * sw;
         const unsigned long long* in = P.buf[src];
         unsigned long long* out = P.buf[src ^ 1];
         const int* len = P.len[src];
-        if (nslots <= NTR)
-            merge_level<1>(in, out, len, C, lg, nslots);
-        else if (nslots <= 2 * NTR)
-            merge_level<2>(in, out, len, C, lg, nslots);
-        else
-            merge_level<PERR>(in, out, len, C, lg, nslots);
+        const bool four = seg_tiles * 4 <= npad;
+        if (four) {
+            if (nslots <= NTR)
+                merge_level4<1>(in, out, len, C, lg, nslots);
+            else if (nslots <= 2 * NTR)
+                merge_level4<2>(in, out, len, C, lg, nslots);
+            else
+                merge_level4<PERR>(in, out, len, C, lg, nslots);
+        } else {
+            if (nslots <= NTR)
+                merge_level<1>(in, out, len, C, lg, nslots);
+            else if (nslots <= 2 * NTR)
+                merge_level<2>(in, out, len, C, lg, nslots);
+            else
+                merge_level<PERR>(in, out, len, C, lg, nslots);
+        }
         if (tid < MAX_TILES) {
             const int j = tid;
-            P.len[src ^ 1][j] = 2 * j + 1 < MAX_TILES ? len[2 * j] + len[2 * j + 1] : 0;
+            if (four)
+                P.len[src ^ 1][j] = 4 * j + 3 < MAX_TILES
+                                        ? (len[4 * j] + len[4 * j + 1]) + (len[4 * j + 2] + len[4 * j + 3])
+                                        : 0;
+            else
+                P.len[src ^ 1][j] = 2 * j + 1 < MAX_TILES ? len[2 * j] + len[2 * j + 1] : 0;
         }
         __syncthreads();
         src ^= 1;
+        seg_tiles *= four ? 4 : 2;
+        lg += four ? 2 : 1;
     }
     const int n = P.len[src][0];
     const unsigned long long* F = P.buf[src];
