@@ -673,20 +673,32 @@ __device__ __forceinline__ TileStat load_tile_stat(const Workspace& ws, int row)
     return t;
 }
 
-__device__ __forceinline__ RowSummary summarize_tiles(const TileStat t, float T) {
+// The row's maximum, finite count and highest incomplete-tile threshold. Every
+// wave of the merge needs these before the pool is laid out; the argmax (greedy
+// rows) and the row mass (rows not cut by top-k) are formed only where needed.
+__device__ __forceinline__ RowSummary summarize_tiles(const TileStat t) {
     RowSummary r;
     r.m = wave_max(t.m);
-    r.argmax = wave_min_i((t.m == r.m && t.argmax >= 0) ? t.argmax : INT_MAX);
     r.nfinite = wave_sum_i(t.nfinite);
     const bool incomplete = t.ncand < t.nfinite;
     r.beta = wave_max(incomplete ? t.beta : NEG_INF);
-    double s = 0.0;
-    if (T > 0.0f && t.m > NEG_INF && r.m > NEG_INF) {
-        const float c2 = 1.4426950408889634f / T;
-        s = t.s * (double)exp2f((t.m - r.m) * c2);
-    }
-    r.W = wave_sum_d(s);
+    r.argmax = -1;
+    r.W = 0.0;
     return r;
+}
+
+__device__ __forceinline__ int row_argmax(const TileStat t, float m) {
+    return wave_min_i((t.m == m && t.argmax >= 0) ? t.argmax : INT_MAX);
+}
+
+// Σ exp((x' - m) / T) over the row from the tiles' partial sums.
+__device__ __forceinline__ double row_mass(const TileStat t, float m, float T) {
+    double s = 0.0;
+    if (T > 0.0f && t.m > NEG_INF && m > NEG_INF) {
+        const float c2 = 1.4426950408889634f / T;
+        s = t.s * (double)exp2f((t.m - m) * c2);
+    }
+    return wave_sum_d(s);
 }
 
 __device__ __forceinline__ uint64_t wq(float w) { return (uint64_t)((double)w * MASS_SCALE); }
@@ -1165,7 +1177,7 @@ __device__ __forceinline__ RowOut resolve_wave(const unsigned long long* F, int 
 
 template <int DT>
 __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Workspace& ws,
-                                             const RowLoad& rl, float u, SmemU& su, SmemR& sh,
+                                             const RowLoad& rl, SmemU& su, SmemR& sh,
                                              const RowDbg& dbg, RowInfo& info_out) {
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
@@ -1174,10 +1186,11 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
     const int V = c.V;
     SmemPool& P = su.p;
     const TileStat ts = rl.ts;
-    const RowSummary rs = summarize_tiles(ts, c.T);
+    RowSummary rs = summarize_tiles(ts);
 
     __shared__ RowInfo info;
     if (c.T == 0.0f || !(rs.m > NEG_INF)) {
+        rs.argmax = row_argmax(ts, rs.m);
         RowInfo r;
         r.kappa = 0;
         r.W = 1.0;
@@ -1298,7 +1311,11 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
             WK_block = block_sum_d(part, sh.red);
         }
         if (wv == 0) {
-            const RowOut o = resolve_wave(F, n, zmax, rs, c, u, K_eff, cut_k, total, topk_on,
+            // the draw's uniform and the row mass, in the resolving wave only
+            const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
+            RowSummary rw = rs;
+            if (!cut_k) rw.W = row_mass(ts, rs.m, c.T);
+            const RowOut o = resolve_wave(F, n, zmax, rw, c, u, K_eff, cut_k, total, topk_on,
                                           dbg.probs != nullptr, dbg.topk != nullptr, WK_block);
             if (lane == 0) s_out = o;
         }
@@ -1328,6 +1345,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
             return;
         }
     }
+    const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
     finalize_slow<DT>(c, row, ws, n_tiles, rs, u, su, sh, info, dbg);
     __syncthreads();
     info_out = info;
@@ -1391,7 +1409,6 @@ __global__ __launch_bounds__(NTR) void k_sample_rows(SampleArgs a) {
     const int row = xcd_linear(a.B);
     const RowLoad rl = row_load(a.ws, row);
     const RowCtx c = sample_ctx<DT>(a, row);
-    const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
     RowDbg dbg;
     dbg.topk = a.dbg_topk ? a.dbg_topk + (size_t)row * a.dbg_topk_stride : nullptr;
     dbg.topk_stride = a.dbg_topk_stride;
@@ -1399,7 +1416,7 @@ __global__ __launch_bounds__(NTR) void k_sample_rows(SampleArgs a) {
     dbg.probs = a.dbg_probs ? a.dbg_probs + (size_t)row * a.V : nullptr;
     dbg.path = a.dbg_path ? a.dbg_path + row : nullptr;
     RowInfo info;
-    finalize_row<DT>(c, row, a.ws, rl, u, su, sh, dbg, info);
+    finalize_row<DT>(c, row, a.ws, rl, su, sh, dbg, info);
     if (threadIdx.x == 0) a.out_tokens[row] = info.token;
 }
 
@@ -1431,9 +1448,8 @@ __global__ __launch_bounds__(NTR) void k_spec_rows(SpecArgs a) {
     const RowLoad rl = row_load(a.ws, row);
     const RowCtx c = spec_ctx<DT>(a, b, j);
     RowDbg dbg = {nullptr, 0, nullptr, nullptr, nullptr};
-    const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
     RowInfo info;
-    finalize_row<DT>(c, row, a.ws, rl, u, su, sh, dbg, info);
+    finalize_row<DT>(c, row, a.ws, rl, su, sh, dbg, info);
     if (j < a.G) {
         const int d = a.draft_tokens[(size_t)b * a.G + j];
         int acc;
