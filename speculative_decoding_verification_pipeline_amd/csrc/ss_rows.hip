@@ -143,6 +143,10 @@ constexpr int PERR = POOL / NTR;  // candidate slots per merge thread
 constexpr int OCT = NTR / CW;     // tiles covered by one slot round
 constexpr int MERGE_LG_MAX = 12;  // log2 of the largest merge segment (POOL slots)
 
+// A pointer into LDS that the compiler keeps in the LDS address space (32-bit
+// addresses, ds_read), also through the merge's unrolled pointer walks.
+typedef const unsigned long long __attribute__((address_space(3)))* lds_key_ptr;
+
 struct SmemPool {
     unsigned long long buf[2][POOL];  // merge-tree ping-pong buffers (keys, zero = empty slot)
     int wcnt[PERR][NTR / WAVE];       // kept candidates per (slot round, wave)
@@ -952,9 +956,10 @@ __device__ __forceinline__ void merge_level(const unsigned long long* in, unsign
         else if (i < lo) ob[r] = (sg & ~1) * C + i;  // plus the partner count
         else ob[r] = -2 - ((sg & ~1) * C + le + lr + ((sg & 1) ? (C - le) : 0) + (i - lo));
     }
-    const unsigned long long* sp[R];
+    const lds_key_ptr lin = (lds_key_ptr)in;
+    lds_key_ptr sp[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) sp[r] = in + pb[r];
+    for (int r = 0; r < R; ++r) sp[r] = lin + pb[r];
     bool kept = false;
 #pragma unroll
     for (int r = 0; r < R; ++r) kept |= ob[r] >= 0;
@@ -969,7 +974,7 @@ __device__ __forceinline__ void merge_level(const unsigned long long* in, unsign
             for (int r = 0; r < R; ++r) sp[r] += x[r] > key[r] ? (1 << bit) : 0;
         }
 #pragma unroll
-        for (int r = 0; r < R; ++r) pos[r] = (int)(sp[r] - (in + pb[r])) + (sp[r][0] > key[r] ? 1 : 0);
+        for (int r = 0; r < R; ++r) pos[r] = (int)(sp[r] - (lin + pb[r])) + (sp[r][0] > key[r] ? 1 : 0);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -1019,11 +1024,12 @@ __device__ __forceinline__ void merge_level4(const unsigned long long* in, unsig
     // are often empty: their searches are skipped (a wave-uniform branch)
     // each search walks a pointer into its partner; the probe distance of a
     // step is a constant, so it rides in the LDS instruction's offset field
-    const unsigned long long* sp[R][3];
+    const lds_key_ptr lin = (lds_key_ptr)in;
+    lds_key_ptr sp[R][3];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int k = 0; k < 3; ++k) sp[r][k] = in + pb[r][k];
+        for (int k = 0; k < 3; ++k) sp[r][k] = lin + pb[r][k];
     bool kept = false;
 #pragma unroll
     for (int r = 0; r < R; ++r) kept |= ob[r] >= 0;
@@ -1045,7 +1051,7 @@ __device__ __forceinline__ void merge_level4(const unsigned long long* in, unsig
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int k = 0; k < 3; ++k)
-                pos[r][k] = (int)(sp[r][k] - (in + pb[r][k])) + (sp[r][k][0] > key[r] ? 1 : 0);
+                pos[r][k] = (int)(sp[r][k] - (lin + pb[r][k])) + (sp[r][k][0] > key[r] ? 1 : 0);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
