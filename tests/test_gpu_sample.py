@@ -188,3 +188,38 @@ def test_graph_replay_with_changed_parameters():
             r = P.draw(filts[b], u)
             tally.add(int(got[b]) == r.token, r.flagged, (rep, b))
     tally.check()
+
+
+def test_long_history_and_bias_lists():
+    """Histories longer than two entries per thread, bias lists longer than one
+    per thread, duplicate ids, and a tile with more distinct penalised entries
+    than its patch list holds (row 0: 3000 history ids inside the first 8192
+    vocabulary entries), each against the oracle's processed logits bit for bit."""
+    rng = np.random.default_rng(77)
+    B, V, H, NB = 4, 20000, 3000, 300
+    x = np.stack([W.zipf_rows(rng, 1, V)[0] for _ in range(B)])
+    hist = rng.integers(-5, V + 5, (B, H)).astype(np.int32)
+    hist[0] = rng.integers(0, 8192, H)                 # > 256 distinct ids in one tile
+    hist[1, :H // 2] = hist[1, H // 2:]                # every id twice
+    bias_ids = rng.integers(-2, V + 2, (B, NB)).astype(np.int32)
+    bias_ids[:, 260:270] = bias_ids[:, 0:10]           # duplicates across the NT boundary
+    bias_ids[2, :NB // 2] = hist[2, :NB // 2]          # bias on penalised entries
+    w = W.SampleWorkload("long-lists", x, "f32", np.array([1.0, 0.7, 0.0, 1.0], np.float32),
+                         np.array([0, 50, 0, 1000], np.int32),
+                         np.array([1.0, 0.9, 1.0, 0.95], np.float32),
+                         np.array([0.0, 0.05, 0.0, 0.0], np.float32),
+                         rep=rng.uniform(0.8, 1.5, B).astype(np.float32),
+                         freq=rng.uniform(0, 0.5, B).astype(np.float32),
+                         pres=rng.uniform(0, 0.5, B).astype(np.float32),
+                         hist=hist, bias_ids=bias_ids,
+                         bias_vals=rng.uniform(-5, 5, (B, NB)).astype(np.float32),
+                         request_ids=np.arange(B, dtype=np.int32),
+                         positions=np.zeros(B, np.int32), seed=11)
+    log(f"[long-lists] B={B} V={V} H={H} NB={NB}")
+    xs, filts = oracle_filtered(w)
+    s = make_sampler(B, V)
+    tally = Tally("long-lists", budget=False)
+    for sd in (11, 12, 13):
+        toks, dbg = run_debug(s, w, seed=sd)
+        compare_debug(w, xs, filts, toks, dbg, sd, tally)
+    tally.check()
