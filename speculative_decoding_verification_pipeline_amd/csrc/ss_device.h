@@ -443,4 +443,21 @@ __device__ __forceinline__ float wave_sort_desc(float v) {
     return __uint_as_float(u);
 }
 
+// The same network on one 64-bit key per lane (descending; both halves move
+// with each exchange): lane i ends with the i-th largest key.
+__device__ __forceinline__ unsigned long long wave_sort_desc_u64(unsigned long long k) {
+#pragma unroll
+    for (int kk = 2; kk <= WAVE; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            const uint32_t lo = xor_lane_dyn_u((uint32_t)k, j);
+            const uint32_t hi = xor_lane_dyn_u((uint32_t)(k >> 32), j);
+            const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+            const bool keep_max = lane_in(~(lanes_with_bit(kk) ^ lanes_with_bit(j)));
+            k = ((k >= o) == keep_max) ? k : o;
+        }
+    }
+    return k;
+}
+
 }  // namespace ss

@@ -606,28 +606,32 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
             }
         }
         __syncthreads();
-        // one key (z = x'/T, id) per thread, then each key's rank among the
-        // tile's candidates: the list goes out sorted
-        unsigned long long my = 0;
-        if (tid < cnt) {
-            const unsigned long long e = tt.list[tid];
-            my = key64(canon_zero(__uint_as_float((uint32_t)(e >> 32)) / c.T), (int)(uint32_t)e);
-            tt.keys[tid] = my;
-        }
-        __syncthreads();
+        // one key (z = x'/T, id) per thread of the waves holding candidates
+        // (0, below every key, past cnt); each such wave sorts its keys in
+        // registers, and with more than 64 candidates every key also counts the
+        // larger keys of the other wave's sorted list: the list goes out sorted
         unsigned long long* cand = ws.cand + ((size_t)row * ws.n_tiles + tile) * CW;
-        if (tid < cnt) {
-            // four keys per batch, both reads issued before the compares
-            int r = 0;
-            int j = 0;
-            const ulonglong2* k2 = (const ulonglong2*)tt.keys;
-#pragma unroll 1
-            for (; j + 4 <= cnt; j += 4) {
-                const ulonglong2 q0 = k2[j >> 1], q1 = k2[(j >> 1) + 1];
-                r += (q0.x > my) + (q0.y > my) + (q1.x > my) + (q1.y > my);
+        const int nw = (cnt + WAVE - 1) / WAVE;  // at most CW / WAVE = 2
+        unsigned long long my = 0;
+        if (wv < nw) {
+            if (tid < cnt) {
+                const unsigned long long e = tt.list[tid];
+                my = key64(canon_zero(__uint_as_float((uint32_t)(e >> 32)) / c.T), (int)(uint32_t)e);
             }
-            for (; j < cnt; ++j) r += tt.keys[j] > my;
-            cand[r] = my;
+            my = wave_sort_desc_u64(my);
+            if (nw > 1) tt.keys[tid] = my;
+        }
+        if (nw > 1) __syncthreads();
+        if (wv < nw) {
+            int r = lane;
+            if (nw > 1) {
+                const unsigned long long* other = tt.keys + (wv ^ 1) * WAVE;
+                int pos = 0;
+#pragma unroll
+                for (int b = 5; b >= 0; --b) pos += other[pos + (1 << b) - 1] > my ? (1 << b) : 0;
+                r += pos + (other[pos] > my ? 1 : 0);
+            }
+            if (my != 0) cand[r] = my;
         }
         st.m = m;
         st.argmax = -1;
