@@ -134,7 +134,6 @@ struct SmemTile {
         unsigned long long keys[CW];  // the candidates' keys (z, id), once the threshold is set
     };
     unsigned long long list[CW];  // the tile's candidates (x' bits, id), unordered
-    int nlist;
 };
 
 // The row merge runs one 1024-thread workgroup per row (four waves per SIMD).
@@ -512,7 +511,6 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
         // among the other waves' sorted lists (ties: lower wave first)
         nf = wave_sum_i(nf);
         if (lane == 0) sh.red.i[wv] = nf;
-        if (tid == 0) tt.nlist = 0;
         const float srt = wave_sort_desc(lm);
         tt.lmax[tid] = srt;
         __syncthreads();
@@ -577,6 +575,7 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
         }
         __syncthreads();
         cnt = sh.red2.i[0] + sh.red2.i[1] + sh.red2.i[2] + sh.red2.i[3];
+        const int* wcnt = sh.red2.i;  // per-wave candidate counts of the final threshold
         ssum = ((sh.red2.d[0] + sh.red2.d[1]) + sh.red2.d[2]) + sh.red2.d[3];
         // lower the threshold until the candidates fit (L = 0 puts it at the
         // tile maximum: no candidates)
@@ -587,21 +586,26 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
 #pragma unroll
             for (int s = 0; s < EPT; ++s) mine += v[s] > theta;
             cnt = block_sum_i(mine, sh.red);
+            wcnt = sh.red.i;
         }
-        // candidates (x', id) into LDS, one atomic per wave
-        const int inc = wave_incl_scan_i(mine);
-        const int wtot = __builtin_amdgcn_readlane(inc, WAVE - 1);
+        // candidates (x', id) into LDS: each wave's slice starts after the
+        // earlier waves' counts; within it, slot by slot, lanes in order (a
+        // ballot per slot, skipped when no lane of the wave has a candidate)
         int base = 0;
-        if (lane == 0 && wtot > 0) base = atomicAdd(&tt.nlist, wtot);
+#pragma unroll
+        for (int w = 0; w < NT / WAVE - 1; ++w) base += w < wv ? wcnt[w] : 0;
         base = __builtin_amdgcn_readfirstlane(base);
-        int off = base + inc - mine;
-        if (mine) {
+        if (__builtin_amdgcn_readfirstlane(wcnt[wv]) > 0) {
 #pragma unroll
             for (int s = 0; s < EPT; ++s) {
-                if (v[s] > theta) {
-                    tt.list[off] = ((unsigned long long)__float_as_uint(v[s]) << 32) |
-                                   (uint32_t)slot_id<DT>(tb, s);
-                    ++off;
+                const bool hit = v[s] > theta;
+                const unsigned long long bm = __ballot(hit);
+                if (bm) {
+                    if (hit)
+                        tt.list[base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] =
+                            ((unsigned long long)__float_as_uint(v[s]) << 32) | (uint32_t)slot_id<DT>(tb, s);
+                    base += __popcll(bm);
                 }
             }
         }
