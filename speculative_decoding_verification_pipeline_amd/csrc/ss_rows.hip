@@ -214,11 +214,31 @@ __device__ __forceinline__ void unpack_group(const uint4 q, float* out) {
     }
 }
 
-template <int DT>
+template <int DT, bool ALIGNED = false>
 __device__ __forceinline__ void load_tile(const RowCtx& c, int tb, float v[EPT]) {
     using L = Lay<DT>;
     constexpr int ES = DT == SS_F32 ? 4 : 2;
     const char* row = (const char*)c.logits;
+    if constexpr (ALIGNED) {
+        // Rows 16-byte aligned and V a multiple of VEC (checked by the host):
+        // a group lies wholly inside or wholly past V, and a group past V reads
+        // the row's last group instead and is set to -inf. Branch-free, so the
+        // compiler can count these loads exactly behind earlier ones.
+        uint4 q[L::NG];
+#pragma unroll
+        for (int g = 0; g < L::NG; ++g) {
+            const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
+            q[g] = gld((const uint4*)(row + (size_t)min(e0, c.V - L::VEC) * ES));
+        }
+#pragma unroll
+        for (int g = 0; g < L::NG; ++g) {
+            const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
+            unpack_group<DT>(q[g], v + g * L::VEC);
+#pragma unroll
+            for (int j = 0; j < L::VEC; ++j) v[g * L::VEC + j] = e0 < c.V ? v[g * L::VEC + j] : NEG_INF;
+        }
+        return;
+    }
     // 16-byte loads need a 16-byte aligned row; a full tile needs no bounds checks
     const bool vec = ((uintptr_t)row & 15u) == 0;
     if (vec && tb + TILE <= c.V) {
@@ -284,6 +304,12 @@ __device__ __forceinline__ float process_entry_t(const RowCtx& c, int id, float 
 // entry with addresses that depend on kernel arguments only (the row strides
 // bound what is readable), so the loads issue ahead of the tile's logits
 // without waiting for the per-request lengths.
+// A 4-byte global load the optimiser keeps in program order (a relaxed
+// workgroup-scope atomic load: the same instruction as a plain load).
+__device__ __forceinline__ int pinned_load(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 struct TablePrefetch {
     int hist[2];
     int extra;
@@ -294,14 +320,26 @@ struct TablePrefetch {
 __device__ __forceinline__ TablePrefetch prefetch_tables(const RowCtx& c) {
     TablePrefetch f;
     const int tid = threadIdx.x;
+    // Unconditional loads at clamped indices (entry 0 of every list is
+    // readable: absent lists point at default arrays), so every path issues the
+    // same loads in the same order and the loads issued after these (the
+    // tile's) need not complete before the tables are built.
+    // They are relaxed atomic loads only so that the compiler keeps them here,
+    // ahead of the tile's, instead of sinking them into the table build.
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int i = tid + k * NT;
-        f.hist[k] = i < c.hist_cap ? gld(c.hist + i) : -1;
+        const int h = pinned_load(c.hist + min(i, max(c.hist_cap - 1, 0)));
+        f.hist[k] = i < c.hist_cap ? h : -1;
     }
-    f.extra = tid < c.extra_len ? gld(c.extra + tid) : -1;
-    f.bias_id = tid < c.bias_cap ? gld(c.bias_ids + tid) : -1;
-    f.bias_val = tid < c.bias_cap ? gld(c.bias_vals + tid) : 0.0f;
+    int e = -1;  // no draft list (sampling): no load at all
+    if (c.extra) e = pinned_load(c.extra + min(tid, max(c.extra_len - 1, 0)));
+    f.extra = tid < c.extra_len ? e : -1;
+    const int bi = min(tid, max(c.bias_cap - 1, 0));
+    const int bid = pinned_load(c.bias_ids + bi);
+    const float bv = __int_as_float(pinned_load((const int32_t*)c.bias_vals + bi));
+    f.bias_id = tid < c.bias_cap ? bid : -1;
+    f.bias_val = tid < c.bias_cap ? bv : 0.0f;
     return f;
 }
 
@@ -334,11 +372,12 @@ __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& 
         for (int i = tid + 2 * NT; i < c.hist_len; i += NT) count(gld(c.hist + i));
         if (tid < c.extra_len) count(f.extra);
     }
-    for (int i = tid; has_bias && i < c.bias_len; i += NT) {
-        const int id = i < NT ? f.bias_id : gld(c.bias_ids + i);
+    auto mark = [&](int id) {
         const int l = id - tb;
         if (id >= 0 && id < c.V && l >= 0 && l < TILE) atomicOr(&t.bias[l >> 5], 1u << (l & 31));
-    }
+    };
+    if (has_bias && tid < c.bias_len) mark(f.bias_id);
+    for (int i = tid + NT; has_bias && i < c.bias_len; i += NT) mark(gld(c.bias_ids + i));
     __syncthreads();
 }
 
@@ -431,7 +470,7 @@ __device__ __forceinline__ int row_cap(const RowCtx& c) {
 // ---------------------------------------------------------------------------
 // stage 1: one tile of one row
 
-template <int DT>
+template <int DT, bool ALIGNED>
 __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace& ws, SmemTile& tt,
                             SmemS& sh, float* dbg_proc_row, float* dbg_probs_row) {
     const int tid = threadIdx.x;
@@ -440,10 +479,12 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
     const int tb = tile * TILE;
     float v[EPT];
     uint32_t mw[Lay<DT>::NG];
-    // issue order: history / bias (needed first), the tile, its mask words
-    const TablePrefetch f = prefetch_tables(c);
-    load_tile<DT>(c, tb, v);
+    // issue order: mask words and history / bias (needed first), then the
+    // tile, which the tables' build does not wait for
     load_mask<DT>(c, tb, mw);
+    const TablePrefetch f = prefetch_tables(c);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile<DT, ALIGNED>(c, tb, v);
     if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, f);
     process_tile<DT>(c, tb, v, tt, mw);
 
@@ -1398,11 +1439,11 @@ __device__ __forceinline__ RowCtx spec_ctx(const SpecArgs& a, int b, int j) {
     return make_ctx(a.p, b, logits, a.V, a.draft_tokens + (size_t)b * a.G, j, mrow, (uint32_t)j);
 }
 
-template <int DT>
 // Tile kernels: seven 256-thread workgroups per CU fit the LDS (about 23 KB
 // each); the register budget is held to the same seven waves per SIMD.
 #define SS_TILE_OCC __attribute__((amdgpu_waves_per_eu(7)))
 
+template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(NT) SS_TILE_OCC void k_sample_tiles(SampleArgs a) {
     __shared__ SmemTile tt;
     __shared__ SmemS sh;
@@ -1411,7 +1452,7 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_sample_tiles(SampleArgs a) {
     const int row = lin / n_tiles;
     const int tile = lin % n_tiles;
     const RowCtx c = sample_ctx<DT>(a, row);
-    tile_stage1<DT>(c, row, tile, a.ws, tt, sh,
+    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt, sh,
                     a.dbg_processed ? a.dbg_processed + (size_t)row * a.V : nullptr,
                     a.dbg_probs ? a.dbg_probs + (size_t)row * a.V : nullptr);
 }
@@ -1435,7 +1476,7 @@ __global__ __launch_bounds__(NTR) void k_sample_rows(SampleArgs a) {
 }
 
 // Verification, stage 1 over every target row of every request.
-template <int DT>
+template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(NT) void k_spec_tiles(SpecArgs a) {
     __shared__ SmemTile tt;
     __shared__ SmemS sh;
@@ -1445,7 +1486,7 @@ __global__ __launch_bounds__(NT) void k_spec_tiles(SpecArgs a) {
     const int row = lin / n_tiles;
     const int tile = lin % n_tiles;
     const RowCtx c = spec_ctx<DT>(a, row / G1, row % G1);
-    tile_stage1<DT>(c, row, tile, a.ws, tt, sh, nullptr, nullptr);
+    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt, sh, nullptr, nullptr);
 }
 
 // Verification, per target row: the filtered distribution, then the accept
@@ -1674,16 +1715,30 @@ __global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
 // ---------------------------------------------------------------------------
 // launchers
 
+// Every row starts 16-byte aligned and V is a whole number of 16-byte groups:
+// the tile kernels then take the branch-free load.
+template <int DT>
+static bool rows_aligned(const void* base, int64_t row_stride, int V) {
+    constexpr int VEC = DT == SS_F32 ? 4 : 8;
+    return ((uintptr_t)base & 15u) == 0 && row_stride % VEC == 0 && V % VEC == 0 && V >= VEC;
+}
+
 template <int DT>
 static void sample_chain(const SampleArgs& a, hipStream_t st, const LaunchEvents& le) {
-    launch_k(le, 0, k_sample_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
+    if (rows_aligned<DT>(a.logits, a.row_stride, a.V))
+        launch_k(le, 0, k_sample_tiles<DT, true>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
+    else
+        launch_k(le, 0, k_sample_tiles<DT, false>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
     launch_k(le, 1, k_sample_rows<DT>, dim3(a.B), dim3(NTR), st, a);
 }
 
 template <int DT>
 static void spec_chain(const SpecArgs& a, hipStream_t st, const LaunchEvents& le) {
     const int rows = a.B * (a.G + 1);
-    launch_k(le, 0, k_spec_tiles<DT>, dim3(rows * a.ws.n_tiles), dim3(NT), st, a);
+    if (rows_aligned<DT>(a.target, a.row_stride, a.V))
+        launch_k(le, 0, k_spec_tiles<DT, true>, dim3(rows * a.ws.n_tiles), dim3(NT), st, a);
+    else
+        launch_k(le, 0, k_spec_tiles<DT, false>, dim3(rows * a.ws.n_tiles), dim3(NT), st, a);
     launch_k(le, 1, k_spec_rows<DT>, dim3(rows), dim3(NTR), st, a);
     launch_k(le, 2, k_spec_resid_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
     launch_k(le, 3, k_spec_finish<DT>, dim3(a.B), dim3(NT), st, a);
