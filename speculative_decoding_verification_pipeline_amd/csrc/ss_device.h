@@ -20,7 +20,6 @@ constexpr int NT = 256;            // threads per workgroup of the row kernels
 constexpr int EPT = 32;            // logits per thread
 constexpr int TILE = NT * EPT;     // 8192 vocabulary entries per workgroup tile
 constexpr int CW = 128;            // candidate slots per tile
-constexpr int LTARGET = 112;       // lane maxima that seed a tile's candidate threshold
 constexpr int MAX_TILES = 32;      // V <= 262144
 constexpr int POOL = MAX_TILES * CW;
 constexpr int MAX_VOCAB = MAX_TILES * TILE;
@@ -89,10 +88,6 @@ __device__ __forceinline__ unsigned long long key64(float z, int id) {
 
 __device__ __forceinline__ int key64_id(unsigned long long k) {
     return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
-}
-
-__device__ __forceinline__ bool key_before(float za, int ia, float zb, int ib) {
-    return za > zb || (za == zb && ia < ib);
 }
 
 // ---------------------------------------------------------------------------
@@ -174,13 +169,6 @@ __device__ __forceinline__ int xor_lane_i(int v) {
     return (int)xor_lane<J>((uint32_t)v);
 }
 
-template <int J>
-__device__ __forceinline__ unsigned long long xor_lane_u64(unsigned long long v) {
-    const uint32_t lo = xor_lane<J>((uint32_t)v);
-    const uint32_t hi = xor_lane<J>((uint32_t)(v >> 32));
-    return ((unsigned long long)hi << 32) | lo;
-}
-
 // Butterfly all-reduce: after the step with mirror M every lane holds the
 // reduction over its aligned group of 2M lanes.
 template <class T, class Op>
@@ -229,10 +217,6 @@ __device__ __forceinline__ int wave_min_i(int v) {
     return wave_allreduce32(v, [](int a, int b) { return min(a, b); });
 }
 
-__device__ __forceinline__ int wave_max_i(int v) {
-    return wave_allreduce32(v, [](int a, int b) { return max(a, b); });
-}
-
 __device__ __forceinline__ int wave_sum_i(int v) {
     return wave_allreduce32(v, [](int a, int b) { return a + b; });
 }
@@ -268,17 +252,6 @@ __device__ __forceinline__ double wave_sum_d(double v) {
         const double b = __longlong_as_double((long long)(((unsigned long long)hi[1] << 32) | lo[1]));
         v = a + b;
     }
-    return v;
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-    unsigned long long o;
-    o = xor_lane_u64<1>(v); v = o > v ? o : v;
-    o = xor_lane_u64<2>(v); v = o > v ? o : v;
-    o = xor_lane_u64<4>(v); v = o > v ? o : v;
-    o = xor_lane_u64<8>(v); v = o > v ? o : v;
-    o = xor_lane_u64<16>(v); v = o > v ? o : v;
-    o = xor_lane_u64<32>(v); v = o > v ? o : v;
     return v;
 }
 
@@ -320,7 +293,6 @@ struct RedT {
     int i[NB / WAVE];
     double d[NB / WAVE];
 };
-using RedScratch = RedT<NT>;
 
 template <int NB>
 __device__ __forceinline__ float block_max(float v, RedT<NB>& r) {
