@@ -378,8 +378,8 @@ def main():
                          "scale), then a few headline calls; prints no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding is a "
-                                   "design note, not code (run with --gpus 1)"}))
+        print(json.dumps({"error": "ss-sampler runs on one GPU; sharding across GPUs is not "
+                                   "implemented (run with --gpus 1)"}))
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"

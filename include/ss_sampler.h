@@ -54,7 +54,7 @@ typedef struct ss_sampler ss_sampler; /* opaque; owns its device workspace */
 typedef enum {
     SS_OK = 0,
     SS_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, size out of range */
-    SS_ERR_UNSUPPORTED = -2,   /* a valid request this build does not serve */
+    SS_ERR_UNSUPPORTED = -2,   /* a valid request the library does not serve */
     SS_ERR_OUT_OF_MEMORY = -3, /* workspace allocation failed (create only) */
     SS_ERR_HIP = -4            /* a HIP runtime call or launch failed */
 } ss_status;
