@@ -63,3 +63,45 @@ def test_full_configuration():
     log("[lmhead full] workload generated")
     run_case(64, 8192, 128256, [0, 1, 2], np.ones(64, np.float32), tally, wl=wl)
     tally.check()
+
+
+def test_graph_replay_with_changed_seed_inputs():
+    """ss_lmhead_sample captured once in a HIP graph: every replay (positions and
+    temperatures changed in place, eager work in between) equals an eager call,
+    and both match the oracle's Gumbel-max draws."""
+    from speculative_decoding_verification_pipeline_amd.sampler import Sampler
+    B, K, V = 16, 256, 3000
+    dev = device()
+    wl = W.lmhead(B=B, K=K, V=V, seed=41)
+    H = torch.from_numpy(wl.hidden.view(np.int16)).to(dev)
+    Wt = torch.from_numpy(wl.weight.view(np.int16)).to(dev)
+    s = Sampler(64, V, hidden_size=K, device=0)
+    z = L.logits_fp64(wl.hidden, wl.weight)
+    rng = np.random.default_rng(41)
+    req = np.arange(B, dtype=np.int32) + 7
+    reqd = torch.from_numpy(req).to(dev)
+    posd = torch.zeros(B, dtype=torch.int32, device=dev)
+    Td = torch.ones(B, dtype=torch.float32, device=dev)
+    out = torch.empty(B, dtype=torch.int32, device=dev)
+    s.lmhead_sample(H, Wt, Td, reqd, posd, seed=5, out=out)  # warm up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s.lmhead_sample(H, Wt, Td, reqd, posd, seed=5, out=out)
+    tally = Tally("lmhead graph", budget=False)
+    for rep in range(5):
+        pos = rng.integers(0, 1 << 16, B).astype(np.int32)
+        T = rng.choice(np.array([0.0, 0.5, 1.0], np.float32), B)
+        posd.copy_(torch.from_numpy(pos))
+        Td.copy_(torch.from_numpy(T))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().copy()
+        _ = (H[:1].float() * 2.0).sum()  # unrelated eager work between replays
+        eager = s.lmhead_sample(H, Wt, Td, reqd, posd, seed=5)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager.cpu().numpy()), rep
+        want, flags = L.sample(z, T, req, pos, 5)
+        for b in range(B):
+            tally.add(int(got[b]) == int(want[b]), bool(flags[b]), (rep, b, int(got[b]), int(want[b])))
+    tally.check()

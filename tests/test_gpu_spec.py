@@ -116,3 +116,45 @@ def test_small_vocab_many_positions(V, G, with_extras):
         toks, nacc = run(s, sw, pos, extra)
         compare(sw, pos, toks, nacc, tally, extra)
     tally.check()
+
+
+def test_graph_replay_with_changed_positions():
+    """ss_spec_verify captured once in a HIP graph: every replay (positions and
+    temperatures changed in place between replays, eager work in between)
+    equals an eager call, and both match the oracle."""
+    from speculative_decoding_verification_pipeline_amd.sampler import Sampler, SamplingParams
+    rng = np.random.default_rng(17)
+    B, G, V = 8, 3, 5000
+    sw = W.speculative(B=B, G=G, V=V, seed=17, draft_seed=18)
+    s = Sampler(B, V, max_draft=G, device=0)
+    tgt = to_dev(sw.target, torch.float32)
+    q = to_dev(sw.draft_probs, torch.float32)
+    d = to_dev(sw.draft_tokens, torch.int32)
+    prm = SamplingParams(temperature=to_dev(sw.temperature, torch.float32),
+                         top_k=to_dev(sw.top_k, torch.int32), top_p=to_dev(sw.top_p, torch.float32),
+                         min_p=to_dev(sw.min_p, torch.float32),
+                         request_ids=to_dev(sw.request_ids, torch.int32),
+                         positions=to_dev(np.zeros(B, np.int32), torch.int32), seed=sw.seed)
+    out_t = torch.empty(B, G + 1, dtype=torch.int32, device=device())
+    out_n = torch.empty(B, dtype=torch.int32, device=device())
+    s.spec_verify(tgt, q, d, prm, out_tokens=out_t, out_num_accepted=out_n)  # warm up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s.spec_verify(tgt, q, d, prm, out_tokens=out_t, out_num_accepted=out_n)
+    tally = Tally("spec graph", budget=False)
+    for rep in range(5):
+        pos = rng.integers(0, 1 << 16, B).astype(np.int32)
+        T = rng.choice(np.array([0.0, 0.7, 1.0], np.float32), B)
+        prm.positions.copy_(torch.from_numpy(pos))
+        prm.temperature.copy_(torch.from_numpy(T))
+        sw.temperature = T
+        g.replay()
+        torch.cuda.synchronize()
+        gt, gn = out_t.cpu().numpy().copy(), out_n.cpu().numpy().copy()
+        _ = (tgt[:1] * 2.0).sum()  # unrelated eager work between replays
+        et, en = s.spec_verify(tgt, q, d, prm)
+        torch.cuda.synchronize()
+        assert np.array_equal(gt, et.cpu().numpy()) and np.array_equal(gn, en.cpu().numpy()), rep
+        compare(sw, pos, gt, gn, tally)
+    tally.check()
