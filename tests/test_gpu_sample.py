@@ -262,3 +262,33 @@ def test_aligned_and_strided_rows_agree(dtype):
     tally = Tally(f"aligned/strided {dtype}", budget=False)
     compare_debug(w, xs_o, filts, ta, da, w.seed, tally)
     tally.check()
+
+
+def test_maximum_vocabulary():
+    """V = 262144, the largest vocabulary a handle accepts (32 tiles): rows with
+    top-k up to the 1024 limit fill the merge's whole candidate pool. Processed
+    logits, top-k sets, probabilities and tokens against the oracle; one entry
+    more is rejected when the handle is created."""
+    from speculative_decoding_verification_pipeline_amd.sampler import SamplerError
+    rng = np.random.default_rng(262144)
+    B, V = 6, 262144
+    x = W.zipf_rows(rng, B, V)
+    hist = rng.integers(0, V, (B, 64)).astype(np.int32)
+    w = W.SampleWorkload("max-vocab", x, "f32", np.array([1.0, 0.7, 1.0, 0.0, 1.0, 1.3], np.float32),
+                         np.array([1024, 1000, 0, 0, 50, 1024], np.int32),
+                         np.array([1.0, 0.95, 0.9, 1.0, 1.0, 0.5], np.float32),
+                         np.array([0.0, 0.0, 0.05, 0.0, 0.0, 0.0], np.float32),
+                         rep=np.full(B, 1.1, np.float32), freq=np.full(B, 0.2, np.float32),
+                         pres=np.full(B, 0.1, np.float32), hist=hist,
+                         request_ids=np.arange(B, dtype=np.int32) + 3,
+                         positions=np.arange(B, dtype=np.int32), seed=9)
+    log(f"[max-vocab] B={B} V={V}")
+    xs, filts = oracle_filtered(w)
+    s = make_sampler(B, V)
+    tally = Tally("max-vocab", budget=False)
+    for sd in (9, 10, 11):
+        toks, dbg = run_debug(s, w, seed=sd)
+        compare_debug(w, xs, filts, toks, dbg, sd, tally)
+    tally.check()
+    with pytest.raises(SamplerError):
+        make_sampler(B, V + 1)
