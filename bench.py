@@ -365,6 +365,33 @@ def counters_run(dev):
     log("bench: 5 headline calls done")
 
 
+def counters_lmhead_run(dev):
+    """The same known-size copy, then 3 fused LM-head calls at the full shape
+    (hidden [64, 8192] x weight [128256, 8192] bf16; the weight, 2.1 GB, is far
+    larger than the Infinity Cache, so every call streams it from HBM)."""
+    import torch
+    from speculative_decoding_verification_pipeline_amd.sampler import Sampler
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"bench: copied {COPY_BYTES} bytes")
+    del a, b
+    B, K, V = 64, 8192, 128256
+    gen = torch.Generator(device=dev).manual_seed(105)
+    Hd = torch.randn(B, K, device=dev, generator=gen).to(torch.bfloat16)
+    Wd = (torch.randn(V, K, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    T = torch.ones(B, device=dev)
+    s = Sampler(B, V, hidden_size=K, device=0)
+    o = torch.empty(B, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    for r in range(3):
+        s.lmhead_sample(Hd, Wd, T, seed=r, out=o)
+    torch.cuda.synchronize()
+    log("bench: 3 lmhead calls done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +403,9 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="for rocprofv3 --pmc runs: a device copy of known size (counter "
                          "scale), then a few headline calls; prints no JSON line")
+    ap.add_argument("--counters-lmhead", action="store_true",
+                    help="for rocprofv3 --pmc runs: the same copy, then a few full-size fused "
+                         "LM-head calls; prints no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "ss-sampler runs on one GPU; sharding across GPUs is not "
@@ -386,6 +416,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.counters:
         counters_run(dev)
+        return
+    if args.counters_lmhead:
+        counters_lmhead_run(dev)
         return
     log("bench: headline (heterogeneous B=64 V=128256)")
     res, w = headline(args, dev)
