@@ -53,6 +53,8 @@ constexpr int LM_H_BYTES = LM_MAXB * LM_KSTEP * 2;   // 8 KB per stage
 // s_waitcnt immediates (gfx9 encoding): vmcnt N with lgkmcnt 0, expcnt free.
 constexpr int WAIT_VM6_LGK0 = 0x0076;
 constexpr int WAIT_VM0_LGK0 = 0x0070;
+// Cache policy of the weight copies: the non-temporal (streaming) bit.
+constexpr int LM_W_CPOL = 2;
 
 // Copies step `ks` of the operands into one LDS stage: wave w moves W rows
 // [32w, 32w + 32) (4 instructions) and H rows [16w, 16w + 16) (2 instructions).
@@ -70,8 +72,10 @@ __device__ __forceinline__ void lm_copy(uint8_t* wbuf, uint8_t* hbuf, const uint
         int v = tile * LM_ROWS + r;
         v = v < V ? v : V - 1;
         const uint16_t* src = weight + (size_t)v * K + ks * LM_KSTEP + c * 8;
+        // the weight is read once: non-temporal, so it does not push the
+        // hidden states (re-read by every workgroup) out of L2
         __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(wbuf + (wave * 32 + q * 8) * 128),
-                                         16, 0, 0);
+                                         16, 0, LM_W_CPOL);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
