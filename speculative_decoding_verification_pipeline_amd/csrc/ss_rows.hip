@@ -228,7 +228,11 @@ __device__ __forceinline__ void load_tile(const RowCtx& c, int tb, float v[EPT])
 #pragma unroll
         for (int g = 0; g < L::NG; ++g) {
             const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
-            q[g] = gld((const uint4*)(row + (size_t)min(e0, c.V - L::VEC) * ES));
+            // the logits are read once: non-temporal, so they do not push the
+            // row's history ids and the tile summaries out of L2
+            const u32x4_t* src = (const u32x4_t*)(row + (size_t)min(e0, c.V - L::VEC) * ES);
+            const u32x4_t qv = __builtin_nontemporal_load(src);
+            q[g] = make_uint4(qv.x, qv.y, qv.z, qv.w);
         }
 #pragma unroll
         for (int g = 0; g < L::NG; ++g) {
