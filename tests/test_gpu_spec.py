@@ -20,7 +20,7 @@ def to_dev(a, dt):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device=device(), dtype=dt)
 
 
-def run(s, sw, positions, extra=None):
+def run(s, sw, positions, extra=None, target=None):
     from speculative_decoding_verification_pipeline_amd.sampler import SamplingParams
     extra = extra or {}
     B = sw.B
@@ -44,7 +44,9 @@ def run(s, sw, positions, extra=None):
                          min_p=to_dev(sw.min_p, torch.float32),
                          request_ids=to_dev(sw.request_ids, torch.int32),
                          positions=to_dev(positions, torch.int32), seed=sw.seed, **kw)
-    toks, nacc = s.spec_verify(to_dev(sw.target, torch.float32), to_dev(sw.draft_probs, torch.float32),
+    if target is None:
+        target = to_dev(sw.target, torch.float32)
+    toks, nacc = s.spec_verify(target, to_dev(sw.draft_probs, torch.float32),
                                to_dev(sw.draft_tokens, torch.int32), prm)
     torch.cuda.synchronize()
     return toks.cpu().numpy(), nacc.cpu().numpy()
@@ -157,4 +159,35 @@ def test_graph_replay_with_changed_positions():
         torch.cuda.synchronize()
         assert np.array_equal(gt, et.cpu().numpy()) and np.array_equal(gn, en.cpu().numpy()), rep
         compare(sw, pos, gt, gn, tally)
+    tally.check()
+
+
+@pytest.mark.parametrize("V", [1000, 1001])
+def test_bf16_target_many_positions(V):
+    """bf16 target logits (the aligned-row tile load at V = 1000, the general
+    load at V = 1001), with penalties, bias and per-position masks; the oracle
+    takes the same logits widened exactly to binary32."""
+    from speculative_decoding_verification_pipeline_amd.sampler import Sampler
+    rng = np.random.default_rng(V)
+    B, G = 16, 3
+    sw = W.speculative(B=B, G=G, V=V, seed=V + 5, draft_seed=V + 6)
+    bits = W.f32_to_bf16_bits(sw.target)
+    sw.target = P.bf16_bits_to_f32(bits).reshape(sw.target.shape)
+    tgt = torch.from_numpy(bits.view(np.int16)).to(device()).view(torch.bfloat16)
+    sw.top_k = rng.choice(np.array([0, 5, 50], np.int32), B)
+    sw.top_p = rng.choice(np.array([1.0, 0.9], np.float32), B)
+    sw.temperature = rng.choice(np.array([0.0, 0.8, 1.0], np.float32), B)
+    allowed = rng.random((B, G + 1, V)) < 0.7
+    allowed[..., :3] = True
+    extra = dict(hist=rng.integers(0, V, (B, 12)).astype(np.int32),
+                 bias_ids=rng.integers(0, V, (B, 3)).astype(np.int32),
+                 bias_vals=rng.uniform(-2, 2, (B, 3)).astype(np.float32),
+                 rep=np.full(B, 1.2, np.float32), freq=np.full(B, 0.3, np.float32),
+                 pres=np.full(B, 0.2, np.float32), mask=W.pack_mask(allowed))
+    s = Sampler(B, V, max_draft=G, device=0)
+    tally = Tally(f"spec bf16 V={V}", budget=False)
+    for p in range(20):
+        pos = rng.integers(0, 1 << 16, B).astype(np.int32)
+        toks, nacc = run(s, sw, pos, extra, target=tgt)
+        compare(sw, pos, toks, nacc, tally, extra)
     tally.check()
