@@ -190,8 +190,9 @@ ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
  *   debug_logits  NULL, or [B, V] float32 to receive the unscaled logits.
  * Token = lowest v attaining max_v (z[b,v] / T_b + g(Philox(seed; request,
  * position, v >> 2, domain 3)[v & 3])), g = -ln(-ln U), U = 1 - (w + 0.5) 2^-32.
- * Per 256-column vocabulary tile the kernel keeps only a (max, argmax) pair per
- * row; the last workgroup reduces the pairs. */
+ * Per 128-row vocabulary tile the GEMM kernel keeps only a (max, argmax) pair
+ * per batch row; a second launch reduces the pairs of each row (the result does
+ * not depend on the tiling: argmax decomposes over any partition). */
 ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t* weight,
                            int32_t B, const float* temperature, const int32_t* request_ids,
                            const int32_t* positions, uint64_t seed, int32_t* out_tokens,
