@@ -12,6 +12,7 @@
 struct ss_sampler {
     ss_sampler_config cfg;
     int n_tiles;       // 8192-entry tiles per row
+    int n_wt;          // wave tiles per row (WPT per 8192-entry tile)
     int n_vtiles;      // 128-row LM-head vocabulary tiles
     int max_rows;      // rows of the row kernels (verification: B * (G + 1))
     void* ws_base;
@@ -119,6 +120,7 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     const int V = cfg->vocab_size;
     const int B = cfg->max_batch;
     s->n_tiles = (V + ss::TILE - 1) / ss::TILE;
+    s->n_wt = s->n_tiles * ss::WPT;  // a wave's entries interleave across its whole tile
     s->n_vtiles = (V + 127) / 128;
     s->max_rows = B * (cfg->max_draft + 1);
     const int64_t R = s->max_rows;
@@ -131,8 +133,9 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
         off = align_up(off + bytes);
         return o;
     };
-    const int64_t o_stats = take(R * nt * (int64_t)sizeof(ss::TileStat));
-    const int64_t o_cand = take(R * nt * ss::CW * (int64_t)sizeof(unsigned long long));
+    const int64_t nw = s->n_wt;
+    const int64_t o_stats = take(R * nw * (int64_t)sizeof(ss::WaveStat));
+    const int64_t o_cand = take(R * nw * ss::WCAP * (int64_t)sizeof(unsigned long long));
     const int64_t o_info = take(R * (int64_t)sizeof(ss::RowInfo));
     const int64_t o_acc = take(R * 4);
     const int64_t o_restile = take((int64_t)B * nt * (int64_t)sizeof(double2));
@@ -147,13 +150,14 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     }
     char* b = static_cast<char*>(s->ws_base);
     ss::Workspace& w = s->ws;
-    w.stats = reinterpret_cast<ss::TileStat*>(b + o_stats);
+    w.wstats = reinterpret_cast<ss::WaveStat*>(b + o_stats);
     w.cand = reinterpret_cast<unsigned long long*>(b + o_cand);
     w.rowinfo = reinterpret_cast<ss::RowInfo*>(b + o_info);
     w.row_accept = reinterpret_cast<int32_t*>(b + o_acc);
     w.resid_tile = reinterpret_cast<double2*>(b + o_restile);
     w.scratch_z = reinterpret_cast<float*>(b + o_scratch);
     w.n_tiles = s->n_tiles;
+    w.n_wt = s->n_wt;
     w.V = V;
     s->lm_partials = cfg->hidden_size > 0 ? reinterpret_cast<float2*>(b + o_lmpart) : nullptr;
     {

@@ -19,9 +19,11 @@ constexpr int WAVE = 64;
 constexpr int NT = 256;            // threads per workgroup of the row kernels
 constexpr int EPT = 32;            // logits per thread
 constexpr int TILE = NT * EPT;     // 8192 vocabulary entries per workgroup tile
-constexpr int CW = 128;            // candidate slots per tile
+constexpr int WT = WAVE * EPT;     // 2048 entries per wave tile (one wave's share of a tile)
+constexpr int WPT = NT / WAVE;     // wave tiles per workgroup tile
+constexpr int WCAP = 64;           // candidate slots per wave tile
 constexpr int MAX_TILES = 32;      // V <= 262144
-constexpr int POOL = MAX_TILES * CW;
+constexpr int MAX_WT = MAX_TILES * WPT;
 constexpr int MAX_VOCAB = MAX_TILES * TILE;
 
 constexpr uint32_t PH_M0 = 0xD2511F53u;

@@ -9,17 +9,33 @@
 
 namespace ss {
 
-// Stage-1 summary of one 8192-entry vocabulary tile of one row.
-struct TileStat {
-    float m;        // max processed logit in the tile (-inf if none finite)
-    int argmax;     // lowest id attaining m (greedy rows), else -1
-    double s;       // sum of exp((x' - m) / T) over the tile (T > 0 rows)
-    float beta;     // largest processed logit NOT among the candidates (-inf: all are)
-    int ncand;      // candidates written for the tile
-    int nfinite;    // finite processed logits in the tile
-    int pad;
+// Stage-1 summary of one 2048-entry wave tile of one row (32 bytes).
+//  * Candidates are written as keys (z, id), unsorted, in cand[row][wave tile].
+//  * Every finite entry of the wave tile that is not a candidate has
+//    z <= zbeta; zbeta = -inf when every finite entry is a candidate.
+struct WaveStat {
+    float m;        // max processed logit x' (-inf if none is finite)
+    int argmax;     // greedy rows: lowest id attaining m; -1 otherwise
+    float zbeta;    // RN(beta / T) of the cut beta in x' (x' < beta, window; x' <= beta, count)
+    int ncand;      // candidates written (<= WCAP)
+    int nfinite;    // finite processed logits
+    int flags;      // WS_OVF, WS_SUM, WS_APX
+    float zmin;     // smallest z among the candidates (+inf: none)
+    float zm;       // RN(m / T), the z of the maximum (T > 0)
+    double s;       // WS_SUM / WS_APX: a mass relative to exp(zm)
+    double sc;      // the candidates' mass relative to exp(zm) (binary32 terms)
 };
-static_assert(sizeof(TileStat) == 32, "TileStat layout");
+static_assert(sizeof(WaveStat) == 48, "WaveStat layout");
+
+// The window held more than WCAP entries: the candidates are the head of the
+// wave tile by count instead.
+constexpr int WS_OVF = 1;
+// s holds the wave tile's whole mass, exact (count-cut tiles of rows top-k may
+// not cut).
+constexpr int WS_SUM = 2;
+// s holds the mass of the wave tile's non-candidates, relative to RN(m / T) and
+// approximate (window-cut tiles of rows top-k may not cut).
+constexpr int WS_APX = 4;
 
 // What the row finaliser knows about one row's filtered distribution.
 // kept(v) <=> key64(z_v, v) >= kappa and (min_p <= 0 or exp(z_v - zmax) >= min_p),
@@ -62,13 +78,14 @@ struct ParamPtrs {
 };
 
 struct Workspace {
-    TileStat* stats;         // [max_rows * n_tiles]
-    unsigned long long* cand;  // [max_rows * n_tiles * CW]  candidate keys, sorted per tile
+    WaveStat* wstats;        // [max_rows * n_wt]
+    unsigned long long* cand;  // [max_rows * n_wt * WCAP]  candidate keys per wave tile
     RowInfo* rowinfo;        // [max_rows]
     int32_t* row_accept;     // [max_rows]: spec decision per draft row
     double2* resid_tile;     // [max_batch * n_tiles]: residual / target mass per tile
     float* scratch_z;        // [max_rows * V] fallback rows
-    int n_tiles;
+    int n_tiles;             // 8192-entry workgroup tiles per row
+    int n_wt;                // wave tiles per row (WPT per workgroup tile)
     int V;
 };
 

@@ -3,34 +3,36 @@
 // The pipeline and its order follow the SonicSampler abstract (arxivdaily page,
 // English abstract): per request, grammar mask, repetition / frequency /
 // presence penalties, logit bias, temperature, then top-k, top-p and min-p, all
-// in one batched launch, with a hierarchical two-stage top-k. Verification
-// follows "Accelerating Sonar through speculation" (Perplexity blog, sections
-// on speculative decoding and target-draft decoding).
+// in one batched pass, with a hierarchical two-stage top-k that exploits the
+// low entropy of LLM outputs. Verification follows "Accelerating Sonar through
+// speculation" (Perplexity blog, sections on speculative decoding and
+// target-draft decoding).
 //
 // Design (MI355X-first, not a translation of the pages' Triton kernels):
-//  * One workgroup (256 threads, 4 wave64s) per 8192-entry vocabulary tile of a
-//    row; the grid is rows x tiles and depends only on (B, V), so one launch
-//    serves any mix of per-request parameters and can be graph-captured.
-//  * Stage 1 streams the tile once with 16-byte global loads (float4 / 8 x
-//    bf16), applies penalties (multiplicities counted in LDS), bias and the
-//    packed mask in registers, and reduces: tile max, softmax partial sum, and a
-//    candidate list -- every entry above a threshold taken from the sorted
-//    per-thread maxima, so the list is always an exact prefix of the tile in
-//    key order. Its length is capped per request: greedy rows need none, a
-//    top-k row never more than k from one tile, other rows a short head (the
-//    low-entropy structure of LLM logits puts nearly all mass there).
-//  * A second launch, one workgroup per row, merges (the kernel boundary is the
-//    only synchronisation, so stage 1 carries no fences and only its own
-//    registers): candidates above the highest tile threshold form an exact
-//    prefix of the whole row (the pool, in LDS). Its first 256 entries are
-//    sorted across the workgroup with a bitonic network in registers; the
-//    top-k boundary deeper than that comes from a radix selection over the
-//    pool; top-p, min-p and the inverse-CDF draw are ballots over binary64
-//    prefix sums of the sorted head. Requests that reach
-//    past the head sort the whole pool ("deep" path), and requests that reach
-//    past the pool run an exact whole-row fallback (radix selection by count
-//    and by mass over the row's recomputed z). Results never depend on which
-//    path resolved them.
+//  * Stage 1: one workgroup (256 threads, 4 wave64s) per 8192-entry vocabulary
+//    tile of a row; the grid is rows x tiles and depends only on (B, V), so one
+//    launch serves any mix of per-request parameters and can be graph-captured.
+//    The tile is streamed once with 16-byte non-temporal loads; penalties
+//    (multiplicities counted in LDS while the tile is in flight), bias and the
+//    packed mask are applied in registers, and only threads whose slots hold a
+//    penalised or biased entry do any per-entry work.
+//  * After the data lands every wave works alone on its 2048-entry share (a
+//    wave tile): no workgroup barrier, only DPP / permlane reductions and
+//    ballots. Its candidates are every entry whose z lies within DELTA of the
+//    wave maximum when those fit 64 slots, so on low-entropy rows the wave
+//    holding the row maximum keeps everything that can matter; a wave deep in
+//    a steep tail that overflows modestly takes a narrower window; a flat wave
+//    keeps its head by count (sorted lane maxima and a binary search of the
+//    cut). Rows that top-k may leave uncut also get the mass outside the
+//    candidates: exact for count-cut waves, a bounded approximation otherwise.
+//  * Stage 2, one workgroup per row: the pool -- every candidate above the
+//    highest wave-tile bound -- is an exact prefix of the row in key order. It
+//    is sorted by a counting sort over buckets of (zmax - z), which are
+//    monotone in key order, followed by a rank within each bucket; top-k,
+//    top-p, min-p and the inverse-CDF draw are then wave scans over binary64
+//    prefix sums. Requests that reach past the pool run an exact whole-row
+//    fallback (radix selection by count and by mass). Results never depend on
+//    which path resolved them.
 #include <float.h>
 #include <limits.h>
 
@@ -43,8 +45,15 @@ namespace ss {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr double MASS_SCALE = 17592186044416.0;  // 2^44 fixed-point weights in the fallback
-constexpr int CAP_FREE = 32;   // candidates per tile for rows without top-k
-constexpr int CAP_MIN = 8;     // smallest cap for a top-k row
+// Widest candidate window below a wave tile's maximum, in units of z = x' / T:
+// on the wave holding the row maximum it keeps every entry weighing more than
+// e^-24 = 3.8e-11 of it.
+constexpr float DELTA = 24.0f;
+// Largest share of the top-k mass a top-k set deeper than the pool may leave
+// out of its normaliser (each probability and CDF breakpoint moves by at most
+// this much; the parity rule allows 1e-6).
+constexpr double TAIL_EPS = 2e-7;
+
 
 // Loads through the global address space (16-byte vector loads, no flat path).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -124,33 +133,44 @@ __device__ __forceinline__ RowCtx make_ctx(const ParamPtrs& p, int b, const void
 struct SmemTile {
     uint32_t cnt[TILE / 2];   // u16 history multiplicities of the tile's entries
     uint32_t bias[TILE / 32]; // bit set: some bias entry targets this vocabulary entry
+    uint32_t xw[NT];          // per thread: bit s set when its slot s is penalised or biased
     int32_t bid[NT];          // the row's first NT bias entries, in array order
     float bval[NT];
+    unsigned long long wl[WPT][WCAP];  // per wave: its candidates (x' bits, id) in slot order
+};
+
+// The row merge runs one 256-thread workgroup per row: one wave per SIMD, so
+// the per-row bookkeeping every wave repeats costs one issue slot per SIMD.
+constexpr int NTR = 1024;
+constexpr int NWR = NTR / WAVE;                // waves of the merge workgroup
+constexpr int MSLOT = MAX_WT * WCAP / NTR;     // candidate slots per merge thread
+constexpr int POOL = 4096;                     // largest pool the merge sorts
+constexpr int NBK = 2048;                      // buckets of the pool's counting sort
+constexpr int BKPT = NBK / NTR;                // buckets per merge thread
+constexpr int BK_MAX = 1024;                   // largest bucket ranked by direct comparison
+
+// Arrays of the sorting phase and of the resolving phase share storage: a
+// barrier separates the last read of the first from the first write of the
+// second.
+struct SmemPool {
+    unsigned long long F[POOL];       // the pool in key order
+    union {
+        unsigned long long bk[POOL];  // sorting: the pool in bucket order (arrival order within a bucket)
+        struct {
+            double P2[POOL / 2];      // resolving: second half of the inclusive prefix masses
+            float w[POOL];            // resolving: weights exp(z - zmax) in key order
+        };
+    };
     union {
         struct {
-            float lmax[NT];    // per-wave sorted thread maxima
-            float sorted[NT];  // all thread maxima in descending order
+            uint32_t cnt[NBK];        // sorting: bucket sizes
+            uint32_t start[NBK];      // sorting: bucket offsets
         };
-        unsigned long long keys[CW];  // the candidates' keys (z, id), once the threshold is set
+        double P[POOL / 2];           // resolving: first half of the inclusive prefix masses
     };
-    unsigned long long list[CW];  // the tile's candidates (x' bits, id), unordered
 };
-
-// The row merge runs one 1024-thread workgroup per row (four waves per SIMD).
-constexpr int NTR = 1024;
-constexpr int PERR = POOL / NTR;  // candidate slots per merge thread
-constexpr int OCT = NTR / CW;     // tiles covered by one slot round
-constexpr int MERGE_LG_MAX = 12;  // log2 of the largest merge segment (POOL slots)
-
-// A pointer into LDS that the compiler keeps in the LDS address space (32-bit
-// addresses, ds_read), also through the merge's unrolled pointer walks.
-typedef const unsigned long long __attribute__((address_space(3)))* lds_key_ptr;
-
-struct SmemPool {
-    unsigned long long buf[2][POOL];  // merge-tree ping-pong buffers (keys, zero = empty slot)
-    int wcnt[PERR][NTR / WAVE];       // kept candidates per (slot round, wave)
-    int len[2][MAX_TILES];            // segment lengths per merge level
-};
+constexpr int EPTR = POOL / NTR;  // pool entries per merge thread in the prefix pass
+constexpr int AREG = POOL / NWR;  // per-wave region of the unsorted pool
 
 struct SmemRadix {
     uint32_t hc[256];
@@ -167,6 +187,8 @@ template <int NB>
 struct SmemST {
     RedT<NB> red;
     RedT<NB> red2;
+    float fmin[NB / WAVE];
+    int imax[NB / WAVE];
     int sel;
     int take_last;
     unsigned long long rem;
@@ -188,6 +210,16 @@ template <int DT>
 __device__ __forceinline__ int slot_id(int tb, int s) {
     using L = Lay<DT>;
     return tb + (s / L::VEC) * L::GSTRIDE + (int)threadIdx.x * L::VEC + (s % L::VEC);
+}
+
+// Slot s's id formed from one base register at the point of use: the empty asm
+// hides the base's value so the compiler does not keep one id register per
+// group alive across the kernel (it has no memory operands).
+template <int DT>
+__device__ __forceinline__ int slot_id_late(int base, int s) {
+    using L = Lay<DT>;
+    asm volatile("" : "+v"(base));
+    return base + (s / L::VEC) * L::GSTRIDE + (s % L::VEC);
 }
 
 template <int DT>
@@ -214,6 +246,50 @@ __device__ __forceinline__ void unpack_group(const uint4 q, float* out) {
     }
 }
 
+// The branch-free tile load of aligned rows, kept as raw 16-byte words so that
+// work issued after it (the tables' build) need not wait for the data: the
+// unpack comes later.
+template <int DT>
+struct RawTile {
+    uint4 q[Lay<DT>::NG];
+};
+
+template <int DT>
+__device__ __forceinline__ RawTile<DT> load_tile_raw(const RowCtx& c, int tb) {
+    using L = Lay<DT>;
+    constexpr int ES = DT == SS_F32 ? 4 : 2;
+    const char* row = (const char*)c.logits;
+    RawTile<DT> r;
+#pragma unroll
+    for (int g = 0; g < L::NG; ++g) {
+        const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
+        // the logits are read once: non-temporal, so they do not push the
+        // row's history ids out of L2; a 32-bit offset from the row's
+        // (uniform) base keeps one register per load; a group past V reads the
+        // row's last group instead (rows are 16-byte aligned, V a multiple of
+        // the group) and is set to -inf when unpacked
+        const uint32_t off = (uint32_t)min(e0, c.V - L::VEC) * (uint32_t)ES;
+        const u32x4_t qv = __builtin_nontemporal_load((const u32x4_t*)(row + off));
+        r.q[g] = make_uint4(qv.x, qv.y, qv.z, qv.w);
+    }
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_tile(const RowCtx& c, int tb, const RawTile<DT>& r, float v[EPT]) {
+    using L = Lay<DT>;
+#pragma unroll
+    for (int g = 0; g < L::NG; ++g) unpack_group<DT>(r.q[g], v + g * L::VEC);
+    if (tb + TILE > c.V) {  // only the row's last tile reaches past V
+#pragma unroll
+        for (int g = 0; g < L::NG; ++g) {
+            const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
+#pragma unroll
+            for (int j = 0; j < L::VEC; ++j) v[g * L::VEC + j] = e0 < c.V ? v[g * L::VEC + j] : NEG_INF;
+        }
+    }
+}
+
 template <int DT, bool ALIGNED = false>
 __device__ __forceinline__ void load_tile(const RowCtx& c, int tb, float v[EPT]) {
     using L = Lay<DT>;
@@ -229,17 +305,22 @@ __device__ __forceinline__ void load_tile(const RowCtx& c, int tb, float v[EPT])
         for (int g = 0; g < L::NG; ++g) {
             const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
             // the logits are read once: non-temporal, so they do not push the
-            // row's history ids and the tile summaries out of L2
-            const u32x4_t* src = (const u32x4_t*)(row + (size_t)min(e0, c.V - L::VEC) * ES);
+            // row's history ids and the tile summaries out of L2; a 32-bit
+            // offset from the row's (uniform) base keeps one register per load
+            const uint32_t off = (uint32_t)min(e0, c.V - L::VEC) * (uint32_t)ES;
+            const u32x4_t* src = (const u32x4_t*)(row + off);
             const u32x4_t qv = __builtin_nontemporal_load(src);
             q[g] = make_uint4(qv.x, qv.y, qv.z, qv.w);
         }
 #pragma unroll
-        for (int g = 0; g < L::NG; ++g) {
-            const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
-            unpack_group<DT>(q[g], v + g * L::VEC);
+        for (int g = 0; g < L::NG; ++g) unpack_group<DT>(q[g], v + g * L::VEC);
+        if (tb + TILE > c.V) {  // only the row's last tile reaches past V
 #pragma unroll
-            for (int j = 0; j < L::VEC; ++j) v[g * L::VEC + j] = e0 < c.V ? v[g * L::VEC + j] : NEG_INF;
+            for (int g = 0; g < L::NG; ++g) {
+                const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
+#pragma unroll
+                for (int j = 0; j < L::VEC; ++j) v[g * L::VEC + j] = e0 < c.V ? v[g * L::VEC + j] : NEG_INF;
+            }
         }
         return;
     }
@@ -347,10 +428,14 @@ __device__ __forceinline__ TablePrefetch prefetch_tables(const RowCtx& c) {
     return f;
 }
 
-// Builds the tile's multiplicity counts, bias bitmap and bias list in LDS (two
-// barriers). Threads with active = false only take part in the barriers.
+// Builds the tile's multiplicity counts, bias bitmap and bias list in LDS, and
+// for every thread a word with bit s set when its slot s holds a penalised or
+// biased entry (two barriers). Threads with active = false only take part in
+// the barriers.
+template <int DT>
 __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& t,
                                              const TablePrefetch& f, bool active = true) {
+    using L = Lay<DT>;
     const int tid = threadIdx.x;
     const bool has_cnt = active && (c.hist_len + c.extra_len) > 0;
     const bool has_bias = active && c.bias_len > 0;
@@ -364,10 +449,19 @@ __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& 
         t.bid[tid] = f.bias_id;
         t.bval[tid] = f.bias_val;
     }
+    if (active) t.xw[tid] = 0;
     __syncthreads();
+    // owner thread and slot of local entry l (the inverse of slot_id)
+    auto flag = [&](int l) {
+        const int g = l / L::GSTRIDE, r = l % L::GSTRIDE;
+        atomicOr(&t.xw[r / L::VEC], 1u << (g * L::VEC + r % L::VEC));
+    };
     auto count = [&](int id) {
         const int l = id - tb;
-        if (id >= 0 && id < c.V && l >= 0 && l < TILE) atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
+        if (id >= 0 && id < c.V && l >= 0 && l < TILE) {
+            atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
+            flag(l);
+        }
     };
     if (has_cnt) {
 #pragma unroll
@@ -378,12 +472,16 @@ __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& 
     }
     auto mark = [&](int id) {
         const int l = id - tb;
-        if (id >= 0 && id < c.V && l >= 0 && l < TILE) atomicOr(&t.bias[l >> 5], 1u << (l & 31));
+        if (id >= 0 && id < c.V && l >= 0 && l < TILE) {
+            atomicOr(&t.bias[l >> 5], 1u << (l & 31));
+            flag(l);
+        }
     };
     if (has_bias && tid < c.bias_len) mark(f.bias_id);
     for (int i = tid + NT; has_bias && i < c.bias_len; i += NT) mark(gld(c.bias_ids + i));
     __syncthreads();
 }
+
 
 // This thread's grammar-mask words (one per group of VEC entries), fetched with
 // the tile's logits; all-ones without a mask.
@@ -397,55 +495,45 @@ __device__ __forceinline__ void load_mask(const RowCtx& c, int tb, uint32_t mw[L
     }
 }
 
+// Penalties, bias and mask on this thread's entries. A thread whose slots hold
+// no penalised or biased entry (its exception word is zero) and that has no
+// mask does nothing; otherwise whole groups without an exception or a masked
+// entry are skipped.
 template <int DT>
 __device__ __forceinline__ void process_tile(const RowCtx& c, int tb, float v[EPT], const SmemTile& t,
-                                             const uint32_t mwords[Lay<DT>::NG]) {
+                                             const uint32_t mwords[Lay<DT>::NG], bool tables) {
     using L = Lay<DT>;
+    const uint32_t xw = tables ? t.xw[threadIdx.x] : 0u;
+    if (!c.mask && xw == 0u) return;
     const bool has_cnt = (c.hist_len + c.extra_len) > 0;
     const bool has_bias = c.bias_len > 0;
-    if (!has_cnt && !has_bias && !c.mask) return;
+    constexpr uint32_t vm = (1u << L::VEC) - 1u;
 #pragma unroll
     for (int g = 0; g < L::NG; ++g) {
         const int l0 = g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
         const int e0 = tb + l0;
-        uint32_t cw[L::VEC / 2];
-        if (has_cnt) {
-            if constexpr (L::VEC == 4) {
-                const uint2 q = *(const uint2*)&t.cnt[l0 >> 1];
-                cw[0] = q.x;
-                cw[1] = q.y;
-            } else {
-                const uint4 q = *(const uint4*)&t.cnt[l0 >> 1];
-                cw[0] = q.x;
-                cw[1] = q.y;
-                cw[2] = q.z;
-                cw[3] = q.w;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < L::VEC / 2; ++k) cw[k] = 0;
-        }
-        const uint32_t bb = has_bias ? (t.bias[l0 >> 5] >> (l0 & 31)) : 0u;
+        const uint32_t xb = (xw >> (g * L::VEC)) & vm;
         const uint32_t mw = mwords[g] >> (e0 & 31);
-        // most groups hold no history hit, bias or masked entry: skip them whole
-        constexpr uint32_t vm = (1u << L::VEC) - 1u;
-        uint32_t anyc = 0;
-#pragma unroll
-        for (int k = 0; k < L::VEC / 2; ++k) anyc |= cw[k];
-        if ((anyc | (bb & vm) | (~mw & vm)) == 0u) continue;
+        if ((xb | (~mw & vm)) == 0u) continue;
 #pragma unroll
         for (int j = 0; j < L::VEC; ++j) {
             const int id = e0 + j;
             if (id >= c.V) continue;
-            const uint32_t cnt = (cw[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-            const bool hit = (bb >> j) & 1u;
             const bool allowed = (mw >> j) & 1u;
             float x = v[g * L::VEC + j];
-            if (cnt | hit | !allowed) x = process_entry_t(c, id, x, cnt, hit, allowed, t);
+            if ((xb >> j) & 1u) {
+                const int l = l0 + j;
+                const uint32_t cnt = has_cnt ? (t.cnt[l >> 1] >> ((l & 1) * 16)) & 0xFFFFu : 0u;
+                const bool bh = has_bias && ((t.bias[l >> 5] >> (l & 31)) & 1u);
+                x = process_entry_t(c, id, x, cnt, bh, allowed, t);
+            } else if (!allowed) {
+                x = NEG_INF;
+            }
             v[g * L::VEC + j] = x;
         }
     }
 }
+
 
 // x' for a single entry (used by acceptance tests). Whole workgroup participates.
 template <int DT, int NB>
@@ -463,24 +551,35 @@ __device__ __forceinline__ float single_entry(const RowCtx& c, int id, SmemST<NB
     return process_entry(c, id, x, (uint32_t)cnt, hit, allowed);
 }
 
-// Candidate cap of one tile for this request: no tile can hold more than k of a
-// row's top-k; rows without top-k keep a short head.
-__device__ __forceinline__ int row_cap(const RowCtx& c) {
-    if (c.T == 0.0f) return 0;
-    if (c.top_k > 0 && c.top_k < c.V) return min(CW, max(c.top_k, CAP_MIN));
-    return CAP_FREE;
+// ---------------------------------------------------------------------------
+// stage 1: one tile of one row; each wave summarises its own wave tile
+
+__device__ __forceinline__ float wave_min_f(float v) {
+    return wave_allreduce32(v, [](float a, float b) { return fminf(a, b); });
 }
 
-// ---------------------------------------------------------------------------
-// stage 1: one tile of one row
+__device__ __forceinline__ int wave_max_i(int v) {
+    return wave_allreduce32(v, [](int a, int b) { return max(a, b); });
+}
+
+
+// Entries of this lane above theta (strict) or at or above it, counted over the
+// wave (the ballot counts stay in scalar registers).
+__device__ __forceinline__ int wave_count_above(const float v[EPT], float theta, bool strict) {
+    int n = 0;
+#pragma unroll
+    for (int s = 0; s < EPT; ++s) n += __popcll(__ballot(strict ? v[s] > theta : v[s] >= theta));
+    return n;
+}
 
 template <int DT, bool ALIGNED>
-__device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace& ws, SmemTile& tt,
-                            SmemS& sh, float* dbg_proc_row, float* dbg_probs_row) {
+__device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace& ws,
+                                            SmemTile& tt, float* dbg_proc_row, float* dbg_probs_row) {
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
     const int wv = tid / WAVE;
     const int tb = tile * TILE;
+    const int sid0 = tb + tid * Lay<DT>::VEC;  // id of this thread's slot 0
     float v[EPT];
     uint32_t mw[Lay<DT>::NG];
     // issue order: mask words and history / bias (needed first), then the
@@ -488,209 +587,203 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
     load_mask<DT>(c, tb, mw);
     const TablePrefetch f = prefetch_tables(c);
     __builtin_amdgcn_sched_barrier(0);
-    load_tile<DT, ALIGNED>(c, tb, v);
-    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, f);
-    process_tile<DT>(c, tb, v, tt, mw);
+    const bool tables = c.hist_len + c.extra_len + c.bias_len > 0;
+    if constexpr (ALIGNED) {
+        const RawTile<DT> raw = load_tile_raw<DT>(c, tb);
+        if (tables) build_tables<DT>(c, tb, tt, f);
+        unpack_tile<DT>(c, tb, raw, v);
+    } else {
+        load_tile<DT, false>(c, tb, v);
+        if (tables) build_tables<DT>(c, tb, tt, f);
+    }
+    process_tile<DT>(c, tb, v, tt, mw, tables);
 
     if (dbg_proc_row || dbg_probs_row) {
+        // 32-bit offsets from the row's (uniform) base: no per-lane 64-bit
+        // addresses are kept for this cold path
 #pragma unroll
         for (int s = 0; s < EPT; ++s) {
-            const int id = slot_id<DT>(tb, s);
+            const int id = slot_id_late<DT>(sid0, s);
             if (id < c.V) {
-                if (dbg_proc_row) dbg_proc_row[id] = v[s];
-                if (dbg_probs_row) dbg_probs_row[id] = 0.0f;
+                const uint32_t off = (uint32_t)id * 4u;
+                if (dbg_proc_row) *(float*)((char*)dbg_proc_row + off) = v[s];
+                if (dbg_probs_row) *(float*)((char*)dbg_probs_row + off) = 0.0f;
             }
         }
     }
 
-    // lane maximum and minimum; entries are counted one by one only in waves
-    // where some lane holds a -inf
+    // From here on each wave works alone on its wave tile (its entries
+    // interleave across the workgroup tile, so every wave tile of the last
+    // tile may hold entries below V).
+    const int wt = tile * WPT + __builtin_amdgcn_readfirstlane(wv);  // uniform per wave
+    unsigned long long* const cand = ws.cand + ((size_t)row * ws.n_wt + wt) * WCAP;
     float lm = v[0], lmin = v[0];
 #pragma unroll
     for (int s = 1; s < EPT; ++s) {
         lm = fmaxf(lm, v[s]);
         lmin = fminf(lmin, v[s]);
     }
+    // entries are counted one by one only in waves where some lane holds a -inf
     int nf = EPT;
     if (__ballot(!(lmin > NEG_INF))) {
         nf = 0;
 #pragma unroll
         for (int s = 0; s < EPT; ++s) nf += v[s] > NEG_INF;
     }
-    TileStat st;
-    st.pad = 0;
-    const int cap = row_cap(c);
-    if (cap == 0) {
-        const float m = block_max(lm, sh.red);
+    const float m = wave_max(lm);
+    WaveStat st;
+    st.m = m;
+    st.argmax = -1;
+    st.zbeta = NEG_INF;
+    st.ncand = 0;
+    st.nfinite = wave_sum_i(nf);
+    st.flags = 0;
+    st.zmin = __builtin_huge_valf();
+    st.zm = NEG_INF;
+    st.s = 0.0;
+    st.sc = 0.0;
+    if (c.T == 0.0f) {
+        // greedy: lowest id among the maxima; only lanes holding the maximum scan
         int am = INT_MAX;
-        // only lanes holding the maximum look for its lowest index
         if (m > NEG_INF && lm == m) {
 #pragma unroll
             for (int s = EPT - 1; s >= 0; --s)
-                if (v[s] == m) am = slot_id<DT>(tb, s);
+                if (v[s] == m) am = slot_id_late<DT>(sid0, s);
         }
-        // argmin and finite count share one exchange
         am = wave_min_i(am);
-        nf = wave_sum_i(nf);
-        if (lane == 0) {
-            sh.red.i[wv] = am;
-            sh.red2.i[wv] = nf;
-        }
-        __syncthreads();
-        am = sh.red.i[0];
-        nf = sh.red2.i[0];
-#pragma unroll
-        for (int k = 1; k < NT / WAVE; ++k) {
-            am = min(am, sh.red.i[k]);
-            nf += sh.red2.i[k];
-        }
-        st.m = m;
         st.argmax = m > NEG_INF ? am : -1;
-        st.s = 0.0;
-        st.beta = NEG_INF;
-        st.ncand = 0;
-        st.nfinite = nf;
-    } else {
-        // the lane maxima, sorted descending, seed the candidate threshold: each
-        // wave sorts its 64 through DPP, then every maximum finds its place
-        // among the other waves' sorted lists (ties: lower wave first)
-        nf = wave_sum_i(nf);
-        if (lane == 0) sh.red.i[wv] = nf;
-        const float srt = wave_sort_desc(lm);
-        tt.lmax[tid] = srt;
-        __syncthreads();
-        nf = sh.red.i[0] + sh.red.i[1] + sh.red.i[2] + sh.red.i[3];
-        {
-            int pos[NT / WAVE - 1];
-            const float* lst[NT / WAVE - 1];
-            bool ge[NT / WAVE - 1];
+    } else if (m > NEG_INF) {
+        // Windows x' >= m - d T for d = DELTA, DELTA / 2, DELTA / 4: the first
+        // whose entries fit the wave's WCAP slots gives the candidates (written
+        // to the wave's LDS list in slot order while they are counted). On a
+        // low-entropy row the wave holding the row maximum keeps everything
+        // within DELTA of it; a wave deep in the tail sees a locally dense
+        // region and settles for a narrower window.
+        unsigned long long* wl = tt.wl[wv];
+        bool strict = false;
+        auto window = [&](float th) -> int {
+            int n = 0;
 #pragma unroll
-            for (int q = 0; q < NT / WAVE - 1; ++q) {
-                const int w2 = q < wv ? q : q + 1;
-                lst[q] = tt.lmax + w2 * WAVE;
-                ge[q] = w2 < wv;
-                pos[q] = 0;
+            for (int s = 0; s < EPT; ++s) {
+                const bool hit = v[s] >= th;
+                const unsigned long long bm = __ballot(hit);
+                if (bm) {
+                    const int p = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+                    if (hit && p < WCAP)
+                        wl[p] = ((unsigned long long)__float_as_uint(v[s]) << 32) | (uint32_t)slot_id_late<DT>(sid0, s);
+                    n += __popcll(bm);
+                }
             }
-#pragma unroll
-            for (int b = 5; b >= 0; --b) {
-                float x[NT / WAVE - 1];
-#pragma unroll
-                for (int q = 0; q < NT / WAVE - 1; ++q) x[q] = lst[q][pos[q] + (1 << b) - 1];
-#pragma unroll
-                for (int q = 0; q < NT / WAVE - 1; ++q)
-                    pos[q] += (x[q] > srt || (ge[q] && x[q] == srt)) ? (1 << b) : 0;
+            return n;
+        };
+        float theta = fmaxf(m - DELTA * c.T, -FLT_MAX);
+        int base = window(theta);
+        // A narrower window only shortens the search: the head by count always
+        // cuts lower. It is worth taking where the wide window overflowed
+        // modestly (a locally dense stretch of a steep tail, whose narrower
+        // cut still lies far below the row maximum); a wave with three quarters
+        // of its entries inside the wide window is flat and goes to the count cut.
+        if (base > WCAP && base <= 3 * (WT / 4)) {
+            theta = fmaxf(m - (0.5f * DELTA) * c.T, -FLT_MAX);
+            base = window(theta);
+            if (base > WCAP) {
+                theta = fmaxf(m - (0.25f * DELTA) * c.T, -FLT_MAX);
+                base = window(theta);
             }
-            int rank = lane;
-#pragma unroll
-            for (int q = 0; q < NT / WAVE - 1; ++q) {
-                const float x = lst[q][pos[q]];
-                rank += pos[q] + ((x > srt || (ge[q] && x == srt)) ? 1 : 0);
+        }
+        if (base > WCAP) {
+            // Even the narrowest window overflows (a flat wave): keep the head by
+            // count. With the lane maxima sorted descending, count(x' > sorted[L])
+            // grows with L; take the largest L whose count fits (L = 0 always
+            // does: nothing exceeds the maximum).
+            const float srt = wave_sort_desc(lm);
+            int lo = 0, hi = WAVE - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                const float th = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(srt), mid));
+                if (wave_count_above(v, th, true) <= WCAP) lo = mid;
+                else hi = mid - 1;
             }
-            tt.sorted[rank] = srt;
-        }
-        __syncthreads();
-        const float m = tt.sorted[0];
-        // first threshold try and the softmax partial sum in one exchange
-        const int step = max(1, cap / 8);
-        int L = cap - step;
-        const bool cut = nf > cap;
-        float theta = cut ? tt.sorted[L] : NEG_INF;
-        int mine = 0;
-#pragma unroll
-        for (int s = 0; s < EPT; ++s) mine += v[s] > theta;
-        int cnt = mine;
-        double ssum = 0.0;
-        // The tile sum only feeds the row's normaliser, which a top-k cut makes
-        // unused: a tile with more than k finite entries proves the cut.
-        const bool need_s = !(c.top_k > 0 && c.top_k < c.V && nf > c.top_k);
-        if (need_s && m > NEG_INF) {
-            // raw v_exp_f32: terms below 2^-126 flush to zero, which cannot move
-            // a sum whose largest term is 1
-            const float c2 = 1.4426950408889634f / c.T;
-            float acc = 0.0f;
-#pragma unroll
-            for (int s = 0; s < EPT; ++s) acc += __builtin_amdgcn_exp2f((v[s] - m) * c2);
-            ssum = acc;
-        }
-        cnt = wave_sum_i(cnt);
-        ssum = wave_sum_d(ssum);
-        if (lane == 0) {
-            sh.red2.i[wv] = cnt;
-            sh.red2.d[wv] = ssum;
-        }
-        __syncthreads();
-        cnt = sh.red2.i[0] + sh.red2.i[1] + sh.red2.i[2] + sh.red2.i[3];
-        const int* wcnt = sh.red2.i;  // per-wave candidate counts of the final threshold
-        ssum = ((sh.red2.d[0] + sh.red2.d[1]) + sh.red2.d[2]) + sh.red2.d[3];
-        // lower the threshold until the candidates fit (L = 0 puts it at the
-        // tile maximum: no candidates)
-        while (cnt > cap) {
-            L = L > step ? L - step : 0;
-            theta = tt.sorted[L];
-            mine = 0;
-#pragma unroll
-            for (int s = 0; s < EPT; ++s) mine += v[s] > theta;
-            cnt = block_sum_i(mine, sh.red);
-            wcnt = sh.red.i;
-        }
-        // candidates (x', id) into LDS: each wave's slice starts after the
-        // earlier waves' counts; within it, slot by slot, lanes in order (a
-        // ballot per slot, skipped when no lane of the wave has a candidate)
-        int base = 0;
-#pragma unroll
-        for (int w = 0; w < NT / WAVE - 1; ++w) base += w < wv ? wcnt[w] : 0;
-        base = __builtin_amdgcn_readfirstlane(base);
-        if (__builtin_amdgcn_readfirstlane(wcnt[wv]) > 0) {
+            theta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(srt), lo));
+            strict = true;
+            st.flags |= WS_OVF;
+            base = 0;
 #pragma unroll
             for (int s = 0; s < EPT; ++s) {
                 const bool hit = v[s] > theta;
                 const unsigned long long bm = __ballot(hit);
                 if (bm) {
                     if (hit)
-                        tt.list[base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
-                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] =
-                            ((unsigned long long)__float_as_uint(v[s]) << 32) | (uint32_t)slot_id<DT>(tb, s);
+                        wl[base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] =
+                            ((unsigned long long)__float_as_uint(v[s]) << 32) | (uint32_t)slot_id_late<DT>(sid0, s);
                     base += __popcll(bm);
                 }
             }
         }
-        __syncthreads();
-        // one key (z = x'/T, id) per thread of the waves holding candidates
-        // (0, below every key, past cnt); each such wave sorts its keys in
-        // registers, and with more than 64 candidates every key also counts the
-        // larger keys of the other wave's sorted list: the list goes out sorted
-        unsigned long long* cand = ws.cand + ((size_t)row * ws.n_tiles + tile) * CW;
-        const int nw = (cnt + WAVE - 1) / WAVE;  // at most CW / WAVE = 2
-        unsigned long long my = 0;
-        if (wv < nw) {
-            if (tid < cnt) {
-                const unsigned long long e = tt.list[tid];
-                my = key64(canon_zero(__uint_as_float((uint32_t)(e >> 32)) / c.T), (int)(uint32_t)e);
+        st.ncand = base;
+        st.zm = canon_zero(m / c.T);
+        // non-candidates have x' below (or at) theta, so z at most RN(theta / T)
+        st.zbeta = base < st.nfinite ? canon_zero(theta / c.T) : NEG_INF;
+        // the LDS list was written by other lanes of this wave: LDS operations
+        // of one wave complete in order, the fences keep the compiler's order
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // each lane below the count turns one candidate into its key (z, id)
+        // and weighs it against the wave maximum: the merge takes the tile's
+        // candidate mass whole instead of re-forming every weight
+        {
+            const float zm = st.zm;
+            float zc = __builtin_huge_valf();
+            float wcand = 0.0f;
+            if (lane < base) {
+                const unsigned long long e = wl[lane];
+                const float x = __uint_as_float((uint32_t)(e >> 32));
+                zc = canon_zero(x / c.T);
+                wcand = expf(zc - zm);
+                *(unsigned long long*)((char*)cand + (uint32_t)lane * 8u) = key64(zc, (int)(uint32_t)e);
             }
-            my = wave_sort_desc_u64(my);
-            if (nw > 1) tt.keys[tid] = my;
+            st.zmin = wave_min_f(zc);
+            st.sc = wave_sum_d((double)wcand);
         }
-        if (nw > 1) __syncthreads();
-        if (wv < nw) {
-            int r = lane;
-            if (nw > 1) {
-                const unsigned long long* other = tt.keys + (wv ^ 1) * WAVE;
-                int pos = 0;
+        // The mass outside the candidates. A count-cut (flat) wave tile of a row
+        // top-k may leave uncut sums its whole mass exactly, z = x' / T entry by
+        // entry (the row's normaliser then rests on it). Every other wave tile
+        // sums its non-candidates with exp2 on x' log2(e) / T - m log2(e) / T,
+        // an approximation whose error the merge bounds: it serves as the
+        // normaliser's far tail, or shows that a top-k set deeper than the pool
+        // adds nothing that matters. A wave tile with more than k finite
+        // entries proves the row is cut by top-k.
+        const bool certainly_cut = c.top_k > 0 && c.top_k < c.V && st.nfinite > c.top_k;
+        if (strict && !certainly_cut) {
+            const float zm = st.zm;
+            double acc = 0.0;
 #pragma unroll
-                for (int b = 5; b >= 0; --b) pos += other[pos + (1 << b) - 1] > my ? (1 << b) : 0;
-                r += pos + (other[pos] > my ? 1 : 0);
+            for (int s = 0; s < EPT; ++s)
+                if (v[s] > NEG_INF) acc += (double)expf(canon_zero(v[s] / c.T) - zm);
+            st.s = wave_sum_d(acc);
+            st.flags |= WS_SUM;
+        } else {
+            float acc = 0.0f;
+            if (base < st.nfinite) {
+                const float c2 = 1.4426950408889634f / c.T;
+                const float mc = m * c2;
+#pragma unroll
+                for (int s = 0; s < EPT; ++s) {
+                    // one fused rounding: x' c2 - m c2
+                    const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(v[s], c2, -mc));
+                    const bool cand = strict ? v[s] > theta : v[s] >= theta;
+                    acc += cand ? 0.0f : t;
+                }
             }
-            if (my != 0) cand[r] = my;
+            st.s = wave_sum_d((double)acc);
+            st.flags |= WS_APX;
         }
-        st.m = m;
-        st.argmax = -1;
-        st.s = ssum;
-        st.beta = theta;
-        st.ncand = cnt;
-        st.nfinite = nf;
     }
-    if (tid == 0) ws.stats[(size_t)row * ws.n_tiles + tile] = st;
+    if (lane == 0) ws.wstats[(size_t)row * ws.n_wt + wt] = st;
 }
+
 
 // ---------------------------------------------------------------------------
 // stage 2: row finaliser
@@ -705,60 +798,123 @@ struct RowDbg {
 
 struct RowSummary {
     float m;
-    int argmax;
     int nfinite;
-    float beta;
-    double W;
 };
 
-// Lane t of every wave holds tile t's summary (the others an empty one); each
-// wave reduces them identically, so no exchange between waves is needed.
-__device__ __forceinline__ TileStat load_tile_stat(const Workspace& ws, int row) {
-    const int lane = threadIdx.x & (WAVE - 1);
-    TileStat t;
-    if (lane < ws.n_tiles) {
-        t = ws.stats[(size_t)row * ws.n_tiles + lane];
-    } else {
-        t.m = NEG_INF;
-        t.argmax = INT_MAX;
-        t.s = 0.0;
-        t.beta = NEG_INF;
-        t.ncand = 0;
-        t.nfinite = 0;
-        t.pad = 0;
-    }
-    return t;
+__device__ __forceinline__ WaveStat empty_stat() {
+    WaveStat s;
+    s.m = NEG_INF;
+    s.argmax = -1;
+    s.zbeta = NEG_INF;
+    s.ncand = 0;
+    s.nfinite = 0;
+    s.flags = 0;
+    s.zmin = __builtin_huge_valf();
+    s.zm = NEG_INF;
+    s.s = 0.0;
+    s.sc = 0.0;
+    return s;
 }
 
-// The row's maximum, finite count and highest incomplete-tile threshold. Every
-// wave of the merge needs these before the pool is laid out; the argmax (greedy
-// rows) and the row mass (rows not cut by top-k) are formed only where needed.
-__device__ __forceinline__ RowSummary summarize_tiles(const TileStat t) {
-    RowSummary r;
-    r.m = wave_max(t.m);
-    r.nfinite = wave_sum_i(t.nfinite);
-    const bool incomplete = t.ncand < t.nfinite;
-    r.beta = wave_max(incomplete ? t.beta : NEG_INF);
-    r.argmax = -1;
-    r.W = 0.0;
+// What the merge reads from stage 1, issued before anything else so the row's
+// loads share one round trip: lane t of every wave holds the summaries of wave
+// tiles t and t + 64, and thread (wave w, lane l) candidate slot l of wave
+// tiles w, w + 16, ... (read whether or not the slot is filled).
+struct RowLoad {
+    unsigned long long cv[MSLOT];
+    WaveStat s0, s1;
+};
+
+__device__ __forceinline__ RowLoad row_load(const Workspace& ws, int row) {
+    RowLoad l;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wv = threadIdx.x / WAVE;
+    const unsigned long long* cand = ws.cand + (size_t)row * ws.n_wt * WCAP;
+#pragma unroll
+    for (int k = 0; k < MSLOT; ++k) {
+        const int wt = wv + NWR * k;
+        l.cv[k] = wt < ws.n_wt ? gld(cand + (size_t)wt * WCAP + lane) : 0ull;
+    }
+    const WaveStat* st = ws.wstats + (size_t)row * ws.n_wt;
+    l.s0 = lane < ws.n_wt ? st[lane] : empty_stat();
+    l.s1 = lane + WAVE < ws.n_wt ? st[lane + WAVE] : empty_stat();
+    return l;
+}
+
+// A field of wave tile wt's summary (wt uniform across the wave).
+__device__ __forceinline__ int stat_ncand(const RowLoad& l, int wt) {
+    return wt < WAVE ? __builtin_amdgcn_readlane(l.s0.ncand, wt) : __builtin_amdgcn_readlane(l.s1.ncand, wt - WAVE);
+}
+__device__ __forceinline__ int stat_flags(const RowLoad& l, int wt) {
+    return wt < WAVE ? __builtin_amdgcn_readlane(l.s0.flags, wt) : __builtin_amdgcn_readlane(l.s1.flags, wt - WAVE);
+}
+
+// The row as the wave-tile summaries describe it (formed by every wave alike).
+struct RowView {
+    float zmax;    // z of the row maximum
+    float zb;      // the pool is every candidate with z > zb (-inf: every finite entry)
+    float zlo;     // a lower bound of the pool's z
+    double W;      // the row mass: candidates, WS_SUM tiles whole, WS_APX non-candidates
+    double err;    // bound on the error of the approximate part of W
+    int missing;   // some tile leaves mass outside its candidates that no sum covers
+};
+
+// Relative error bound of a window-cut tile's approximate non-candidate mass:
+// each term exp2(fma(x', c2, -m c2)) differs from exp(RN(x'/T) - RN(m/T)) by
+// the roundings of m c2, the fused product-difference and the reciprocal (each
+// 2^-24 of terms up to |z| + d, d <= 104 for any term that is not zero in
+// binary32), exp2's own error and the binary32 sum of 32 terms.
+__device__ __forceinline__ double apx_eps(float zm) {
+    return 0x1p-21 * ((double)fabsf(zm) + 104.0) + 0x1p-19;
+}
+
+__device__ __forceinline__ RowView row_view(const RowLoad& l, float m, float T) {
+    RowView r;
+    r.zmax = canon_zero(m / T);
+    float zb[2];
+    double sum = 0.0, err = 0.0;
+    float zmin = __builtin_huge_valf();
+    int missing = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const WaveStat& s = h ? l.s1 : l.s0;
+        const bool incomplete = s.ncand < s.nfinite;
+        zb[h] = incomplete ? s.zbeta : NEG_INF;
+        zmin = fminf(zmin, s.zmin);
+        if (s.nfinite > 0) {
+            const float zm = s.zm;
+            // binary32 exp of a binary32 difference: relative error ~1e-7 on
+            // each tile's share of the mass
+            const double scale = (double)expf(zm - r.zmax);
+            if (s.flags & WS_SUM) {
+                sum += s.s * scale;  // the whole tile, candidates included
+            } else {
+                sum += s.sc * scale;
+                if (s.flags & WS_APX) {
+                    sum += s.s * scale;
+                    err += s.s * scale * apx_eps(zm);
+                } else if (incomplete) {
+                    missing = 1;
+                }
+            }
+        }
+    }
+    r.zb = wave_max(fmaxf(zb[0], zb[1]));
+    r.zlo = r.zb > NEG_INF ? r.zb : wave_min_f(zmin);
+    r.W = wave_sum_d(sum);
+    r.err = wave_sum_d(err);
+    r.missing = wave_max_i(missing);
     return r;
 }
 
-__device__ __forceinline__ int row_argmax(const TileStat t, float m) {
-    return wave_min_i((t.m == m && t.argmax >= 0) ? t.argmax : INT_MAX);
-}
-
-// Σ exp((x' - m) / T) over the row from the tiles' partial sums.
-__device__ __forceinline__ double row_mass(const TileStat t, float m, float T) {
-    double s = 0.0;
-    if (T > 0.0f && t.m > NEG_INF && m > NEG_INF) {
-        const float c2 = 1.4426950408889634f / T;
-        s = t.s * (double)exp2f((t.m - m) * c2);
-    }
-    return wave_sum_d(s);
+__device__ __forceinline__ int row_argmax(const RowLoad& l, float m) {
+    const int a = (l.s0.m == m && l.s0.argmax >= 0) ? l.s0.argmax : INT_MAX;
+    const int b = (l.s1.m == m && l.s1.argmax >= 0) ? l.s1.argmax : INT_MAX;
+    return wave_min_i(min(a, b));
 }
 
 __device__ __forceinline__ uint64_t wq(float w) { return (uint64_t)((double)w * MASS_SCALE); }
+
 
 // Radix selection over the row's z (scratch), 8 passes of 8-bit digits on key64.
 // by_mass = false: the key of the rank-`target` element (1-based) in key order.
@@ -874,9 +1030,9 @@ __device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Wo
             load_tile<DT>(c, t * TILE, v);
             load_mask<DT>(c, t * TILE, mw);
         }
-        if (tables) build_tables(c, t * TILE, su.t, f, tl);
+        if (tables) build_tables<DT>(c, t * TILE, su.t, f, tl);
         if (tl) {
-            process_tile<DT>(c, t * TILE, v, su.t, mw);
+            process_tile<DT>(c, t * TILE, v, su.t, mw, tables);
 #pragma unroll
             for (int s = 0; s < EPT; ++s) {
                 const int id = slot_id<DT>(t * TILE, s);
@@ -955,162 +1111,13 @@ __device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Wo
     __syncthreads();
 }
 
+
 // ---------------------------------------------------------------------------
 // the sorted pool
 
 __device__ __forceinline__ float key_z(unsigned long long k) {
     const uint32_t m = (uint32_t)(k >> 32);
     return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
-}
-
-// What the merge reads from stage 1: the row's candidate slots and the tile
-// summaries (lane t holds tile t). Issued before anything else so the row's
-// loads share one round trip.
-struct RowLoad {
-    unsigned long long cv[PERR];
-    TileStat ts;
-};
-
-__device__ __forceinline__ RowLoad row_load(const Workspace& ws, int row) {
-    RowLoad l;
-    const int n_tiles = ws.n_tiles;
-    const unsigned long long* cand = ws.cand + (size_t)row * n_tiles * CW;
-#pragma unroll
-    for (int k = 0; k < PERR; ++k) {
-        const int g = (int)threadIdx.x + k * NTR;
-        l.cv[k] = g < n_tiles * CW ? gld(cand + g) : 0ull;
-    }
-    l.ts = load_tile_stat(ws, row);
-    return l;
-}
-
-// One merge level over slots tid + r NTR, r < R (slot layout, segments of C
-// slots padded with zero keys): each kept entry moves to its index plus the
-// number of partner entries before it, each empty slot to the tail of its
-// merged segment. The R searches advance together so their LDS reads overlap.
-template <int R>
-__device__ __forceinline__ void merge_level(const unsigned long long* in, unsigned long long* out,
-                                            const int* len, int C, int lg, int nslots) {
-    const int tid = threadIdx.x;
-    unsigned long long key[R];
-    int pos[R], pb[R], ob[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int g = tid + r * NTR;
-        const int gg = g < nslots ? g : 0;
-        key[r] = in[gg];
-        const int sg = gg >> lg;
-        const int i = gg & (C - 1);
-        const int lo = len[sg];
-        const int le = len[sg & ~1], lr = len[sg | 1];
-        pb[r] = (sg ^ 1) * C;
-        pos[r] = 0;
-        if (g >= nslots) ob[r] = -1;
-        else if (i < lo) ob[r] = (sg & ~1) * C + i;  // plus the partner count
-        else ob[r] = -2 - ((sg & ~1) * C + le + lr + ((sg & 1) ? (C - le) : 0) + (i - lo));
-    }
-    const lds_key_ptr lin = (lds_key_ptr)in;
-    lds_key_ptr sp[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) sp[r] = lin + pb[r];
-    bool kept = false;
-#pragma unroll
-    for (int r = 0; r < R; ++r) kept |= ob[r] >= 0;
-    if (__ballot(kept)) {  // waves holding only empty slots skip the searches
-#pragma unroll
-        for (int bit = MERGE_LG_MAX - 1; bit >= 0; --bit) {
-            if (bit >= lg) continue;
-            unsigned long long x[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) x[r] = sp[r][(1 << bit) - 1];
-#pragma unroll
-            for (int r = 0; r < R; ++r) sp[r] += x[r] > key[r] ? (1 << bit) : 0;
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) pos[r] = (int)(sp[r] - (lin + pb[r])) + (sp[r][0] > key[r] ? 1 : 0);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (ob[r] >= 0) out[ob[r] + pos[r]] = key[r];
-        else if (ob[r] <= -2) out[-2 - ob[r]] = 0ull;
-    }
-}
-
-// A four-way merge level: each group of four segments of C = 2^lg slots becomes
-// one segment of 4C. A kept entry moves to its index plus, for each of its three
-// partner segments, the number of partner entries before it (binary searches
-// over the padded partners, all 3R in lockstep); empty slots fill the group's
-// tail in segment order. Half the levels of pairwise merging, so half the chain
-// of dependent LDS reads.
-template <int R>
-__device__ __forceinline__ void merge_level4(const unsigned long long* in, unsigned long long* out,
-                                             const int* len, int C, int lg, int nslots) {
-    const int tid = threadIdx.x;
-    unsigned long long key[R];
-    int pos[R][3], pb[R][3], ob[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int g = tid + r * NTR;
-        const int gg = g < nslots ? g : 0;
-        key[r] = in[gg];
-        const int sg = gg >> lg;
-        const int q = sg & 3, g0 = sg & ~3;
-        const int i = gg & (C - 1);
-        const int lo = len[sg];
-        int tot = 0, before = 0;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int lp = len[g0 + p];
-            tot += lp;
-            before += p < q ? C - lp : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            pb[r][k] = (g0 + k + (k >= q ? 1 : 0)) << lg;
-            pos[r][k] = 0;
-        }
-        if (g >= nslots) ob[r] = -1;
-        else if (i < lo) ob[r] = (g0 << lg) + i;  // plus the partner counts
-        else ob[r] = -2 - ((g0 << lg) + tot + before + (i - lo));
-    }
-    // kept entries sit at the front of each segment, so whole waves of slots
-    // are often empty: their searches are skipped (a wave-uniform branch)
-    // each search walks a pointer into its partner; the probe distance of a
-    // step is a constant, so it rides in the LDS instruction's offset field
-    const lds_key_ptr lin = (lds_key_ptr)in;
-    lds_key_ptr sp[R][3];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int k = 0; k < 3; ++k) sp[r][k] = lin + pb[r][k];
-    bool kept = false;
-#pragma unroll
-    for (int r = 0; r < R; ++r) kept |= ob[r] >= 0;
-    if (__ballot(kept)) {  // waves holding only empty slots skip the searches
-#pragma unroll
-        for (int bit = MERGE_LG_MAX - 1; bit >= 0; --bit) {
-            if (bit >= lg) continue;
-            unsigned long long x[R][3];
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int k = 0; k < 3; ++k) x[r][k] = sp[r][k][(1 << bit) - 1];
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int k = 0; k < 3; ++k) sp[r][k] += x[r][k] > key[r] ? (1 << bit) : 0;
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int k = 0; k < 3; ++k)
-                pos[r][k] = (int)(sp[r][k] - (lin + pb[r][k])) + (sp[r][k][0] > key[r] ? 1 : 0);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (ob[r] >= 0) out[ob[r] + pos[r][0] + pos[r][1] + pos[r][2]] = key[r];
-        else if (ob[r] <= -2) out[-2 - ob[r]] = 0ull;
-    }
 }
 
 // Outcome of resolving a row on its sorted pool.
@@ -1123,105 +1130,97 @@ struct RowOut {
     int slow;
 };
 
-// One wave answers top-k mass, top-p, min-p and the draw on the sorted pool
-// F[0, n), 64 entries per step: entry i's weight w_i = exp(z_i - zmax) (binary32,
-// as everywhere on this path), masses in binary64 with a running carry.
-// slow = 1 when a request reaches past the pool.
-__device__ __forceinline__ RowOut resolve_wave(const unsigned long long* F, int n, float zmax, const RowSummary& rs,
-                               const RowCtx& c, float u, int K_eff, bool cut_k, int total,
-                               bool topk_on, bool want_probs, bool want_topk, double WK_block) {
+// Inclusive prefix mass of sorted-pool entry i (binary64).
+__device__ __forceinline__ double pool_prefix(const SmemPool& P, int i) {
+    return i < POOL / 2 ? P.P[i] : P.P2[i - POOL / 2];
+}
+
+// First index i in [0, lim) whose predicate holds (INT_MAX if none), 64
+// entries per step; pred(i) reads only LDS.
+template <class Pred>
+__device__ __forceinline__ int wave_first(int lim, Pred pred) {
     const int lane = threadIdx.x & (WAVE - 1);
+    for (int c0 = 0; c0 < lim; c0 += WAVE) {
+        const int i = c0 + lane;
+        const unsigned long long m = __ballot(i < lim && pred(i));
+        if (m) return c0 + __ffsll((long long)m) - 1;
+    }
+    return INT_MAX;
+}
+
+// One wave answers top-k mass, top-p, min-p and the draw on the sorted pool
+// F[0, n) from the weights w_i = exp(z_i - zmax) (binary32, as everywhere on
+// this path) and their binary64 inclusive prefix sums, both already in LDS.
+// W is the row mass (used when top-k does not cut) and err a bound on its
+// error; every entry past the pool weighs at most exp(zb - zmax). slow = 1 when
+// a request needs entries past the pool.
+__device__ __forceinline__ RowOut resolve_wave(const SmemPool& P, int n, float zmax, float zb, double W,
+                                               double err, const RowCtx& c, float u, int K_eff, bool cut_k,
+                                               int total, bool topk_on, bool want_probs, bool want_topk) {
     RowOut o;
     o.slow = 0;
     o.kappa = 0;
-    o.Wk = rs.W;
+    o.Wk = W;
     o.n_kept = 0;
     o.token = -1;
     o.lim_list = cut_k ? K_eff : (topk_on ? total : 0);
-    auto wat = [&](int i, int lim) -> float {
-        return i < lim ? expf(key_z(F[i]) - zmax) : 0.0f;
-    };
-    // mass of the top-k set (summed by the whole workgroup when it spans more
-    // than one chunk)
-    double WK = rs.W;
+    // mass of the top-k set; a top-k set deeper than the pool adds only
+    // entries the caller has shown to be negligible
+    double WK = W;
     unsigned long long kK = 0;
     if (cut_k) {
-        if (K_eff > WAVE) {
-            WK = WK_block;
-        } else {
-            WK = wave_sum_d((double)wat(lane, K_eff));
+        WK = pool_prefix(P, min(K_eff, n) - 1);
+        kK = K_eff <= n ? P.F[K_eff - 1] : 0ull;
+        // A top-k set deeper than the pool takes the pool's mass as its own:
+        // the entries past the pool (all of them, approximately, and the bound
+        // of that approximation) must weigh at most TAIL_EPS of it.
+        if (K_eff > n && (W - WK) + err > TAIL_EPS * WK) {
+            o.slow = 1;
+            return o;
         }
-        kK = F[K_eff - 1];
     }
-    // top-p (first entry whose exclusive mass reaches top_p W_K) and min-p
-    // (first entry with w < min_p), scanned together
+    // top-p: the first entry whose exclusive mass reaches top_p W_K
     const int lim_p = cut_k ? K_eff : total;
-    const bool use_p = c.top_p < 1.0f, use_m = c.min_p > 0.0f;
-    const double thr = (double)c.top_p * WK;
-    const int end_p = min(n, lim_p);
-    int fp = INT_MAX, fm = INT_MAX;
-    {
-        double carry = 0.0;
-        for (int c0 = 0;; c0 += WAVE) {
-            const bool need_p = use_p && fp == INT_MAX && c0 < end_p;
-            const int n_topp_now = fp != INT_MAX ? fp : lim_p;
-            const bool need_m = use_m && fm == INT_MAX && c0 < min(n, n_topp_now);
-            if (!need_p && !need_m) break;
-            const int i = c0 + lane;
-            const float w = wat(i, n);
-            const double in = wave_incl_scan_d((double)w);
-            const double excl = carry + (in - (double)w);
-            if (need_p) {
-                const unsigned long long m = __ballot(i < end_p && excl >= thr);
-                if (m) fp = c0 + __ffsll((long long)m) - 1;
-            }
-            if (need_m) {
-                const unsigned long long m = __ballot(i < n && w < c.min_p);
-                if (m) fm = c0 + __ffsll((long long)m) - 1;
-            }
-            carry += __shfl(in, WAVE - 1);
-        }
-    }
     int n_topp = lim_p;
-    if (use_p) {
+    if (c.top_p < 1.0f) {
+        const double thr = (double)c.top_p * WK;
+        const int fp = wave_first(min(n, lim_p), [&](int i) { return i > 0 && pool_prefix(P, i - 1) >= thr; });
         if (fp != INT_MAX) n_topp = fp;
         else if (lim_p > n) o.slow = 1;
     }
+    // min-p: the first entry with w < min_p (w is non-increasing along the
+    // pool up to rounding; entries near the cut are boundary cases)
     int n_kept = n_topp;
-    if (!o.slow && use_m) {
-        if (fm < n_topp) n_kept = fm;
-        else if (fm == INT_MAX && n_topp > n) o.slow = 1;
+    if (!o.slow && c.min_p > 0.0f) {
+        const int fm = wave_first(min(n, n_topp), [&](int i) { return P.w[i] < c.min_p; });
+        if (fm != INT_MAX) {
+            n_kept = fm;
+        } else if (n_topp > n) {
+            // every pool entry passes min-p; one past the pool passes only if
+            // its weight, at most exp(zb - zmax), could reach min_p
+            if ((double)c.min_p > exp((double)zb - (double)zmax)) n_kept = n;
+            else o.slow = 1;
+        }
     }
     if (o.slow) return o;
-    // kept mass and the cut key
+    // kept mass and the cut key (0: every finite entry, or a top-k set deeper
+    // than the pool)
     double Wk;
     unsigned long long kappa;
     if (n_kept == total) {
-        Wk = rs.W;
+        Wk = W;
         kappa = 0;
     } else if (cut_k && n_kept == K_eff) {
         Wk = WK;
         kappa = kK;
     } else {
-        double carry = 0.0;
-        for (int c0 = 0; c0 < n_kept; c0 += WAVE) carry += wave_sum_d((double)wat(c0 + lane, n_kept));
-        Wk = carry;
-        kappa = F[n_kept - 1];
+        Wk = pool_prefix(P, n_kept - 1);
+        kappa = P.F[n_kept - 1];
     }
     // the draw: first kept entry whose inclusive mass exceeds u Wk
     const double tgt = (double)u * Wk;
     const int lim = min(n, n_kept);
-    int fd = INT_MAX;
-    {
-        double carry = 0.0;
-        for (int c0 = 0; c0 < lim && fd == INT_MAX; c0 += WAVE) {
-            const int i = c0 + lane;
-            const double in = carry + wave_incl_scan_d((double)wat(i, lim));
-            const unsigned long long m = __ballot(i < lim && in > tgt);
-            if (m) fd = c0 + __ffsll((long long)m) - 1;
-            carry = __shfl(in, WAVE - 1);
-        }
-    }
+    const int fd = wave_first(lim, [&](int i) { return pool_prefix(P, i) > tgt; });
     const int pick = fd != INT_MAX ? fd : (n_kept <= n ? n_kept - 1 : -1);
     if (pick < 0 || (want_probs && n_kept > n) || (want_topk && o.lim_list > n)) {
         o.slow = 1;
@@ -1230,7 +1229,7 @@ __device__ __forceinline__ RowOut resolve_wave(const unsigned long long* F, int 
     o.kappa = kappa;
     o.Wk = Wk;
     o.n_kept = n_kept;
-    o.token = key64_id(F[pick]);
+    o.token = key64_id(P.F[pick]);
     return o;
 }
 
@@ -1241,141 +1240,216 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
     const int tid = threadIdx.x;
     const int lane = tid & (WAVE - 1);
     const int wv = tid / WAVE;
-    const int n_tiles = ws.n_tiles;
     const int V = c.V;
     SmemPool& P = su.p;
-    const TileStat ts = rl.ts;
-    RowSummary rs = summarize_tiles(ts);
+    RowSummary rs;
+    rs.m = wave_max(fmaxf(rl.s0.m, rl.s1.m));
+    rs.nfinite = wave_sum_i(rl.s0.nfinite + rl.s1.nfinite);
 
     __shared__ RowInfo info;
     if (c.T == 0.0f || !(rs.m > NEG_INF)) {
-        rs.argmax = row_argmax(ts, rs.m);
+        const int am = rs.m > NEG_INF ? row_argmax(rl, rs.m) : -1;
         RowInfo r;
         r.kappa = 0;
         r.W = 1.0;
         r.zmax = rs.m;
         r.min_p = 0.0f;
-        r.n_kept = rs.m > NEG_INF ? 1 : 0;
-        r.token = rs.m > NEG_INF ? rs.argmax : -1;
-        r.argmax = r.token;
+        r.n_kept = am >= 0 ? 1 : 0;
+        r.token = am;
+        r.argmax = am;
         r.path = 0;
         if (dbg.topk)
             for (int i = tid; i < dbg.topk_stride; i += NTR) dbg.topk[i] = -1;
         if (tid == 0) {
-            if (dbg.probs && r.token >= 0) dbg.probs[r.token] = 1.0f;
+            if (dbg.probs && am >= 0) dbg.probs[am] = 1.0f;
             if (dbg.kept) *dbg.kept = r.n_kept;
             if (dbg.path) *dbg.path = 0;
         }
         info_out = r;
         return;
     }
-    // The pool: every entry with z above the highest tile threshold. It is a
-    // prefix of each tile's sorted list and, as a whole, an exact prefix of the
-    // row in key order. Slot layout: tile t owns slots [t CW, (t + 1) CW), its
-    // kept entries first and zero keys after them, up to a power-of-two number
-    // of tiles, so every merge segment is padded with keys that precede none.
-    const float zmax = canon_zero(rs.m / c.T);
-    const float zb = rs.beta > NEG_INF ? canon_zero(rs.beta / c.T) : NEG_INF;
-    const uint32_t mzb = mono32(zb);
-    int npad = 1;
-    while (npad < n_tiles) npad *= 2;
-    // slots per tile: the row's candidate cap rounded up to a power of two
-    int sw = 8;
-    while (sw < row_cap(c)) sw *= 2;
-    int lsw = 3;
-    while ((1 << lsw) < sw) ++lsw;
-    const int nslots = npad * sw;
-    const int oct = __builtin_amdgcn_readfirstlane(tid / CW);
-#pragma unroll
-    for (int k = 0; k < PERR; ++k) {
-        const int g = tid + k * NTR;
-        const int t = OCT * k + oct;  // tile of candidate slot g
-        const int i = g % CW;
-        bool keep = false;
-        if (t < n_tiles) {
-            const int nc = __builtin_amdgcn_readlane(ts.ncand, t);
-            keep = i < nc && (uint32_t)(rl.cv[k] >> 32) > mzb;
-        }
-        if (t < npad && i < sw) P.buf[0][t * sw + i] = keep ? rl.cv[k] : 0ull;
-        const int wc = __popcll(__ballot(keep));
-        if (lane == 0) P.wcnt[k][wv] = wc;
-    }
-    __syncthreads();
-    if (tid < MAX_TILES) {
-        const int t = tid;
-        const int k = t / OCT, o = t % OCT;
-        P.len[0][t] = t < n_tiles ? P.wcnt[k][2 * o] + P.wcnt[k][2 * o + 1] : 0;
-    }
-    __syncthreads();
-    // Merge tree: level l merges segments of 2^l tiles. An entry's output
-    // position is its index in its segment plus the number of partner entries
-    // that precede it (binary search over the padded partner segment); empty
-    // slots fill the tail of each merged segment with zero keys.
-    // Four-way levels while a group of four segments exists in the padded
-    // layout, then at most one pairwise level.
-    int src = 0;
-    for (int seg_tiles = 1, lg = lsw; seg_tiles < n_tiles;) {
-        const int C = seg_tiles * sw;
-        const unsigned long long* in = P.buf[src];
-        unsigned long long* out = P.buf[src ^ 1];
-        const int* len = P.len[src];
-        const bool four = seg_tiles * 4 <= npad;
-        if (four) {
-            if (nslots <= NTR)
-                merge_level4<1>(in, out, len, C, lg, nslots);
-            else if (nslots <= 2 * NTR)
-                merge_level4<2>(in, out, len, C, lg, nslots);
-            else
-                merge_level4<PERR>(in, out, len, C, lg, nslots);
-        } else {
-            if (nslots <= NTR)
-                merge_level<1>(in, out, len, C, lg, nslots);
-            else if (nslots <= 2 * NTR)
-                merge_level<2>(in, out, len, C, lg, nslots);
-            else
-                merge_level<PERR>(in, out, len, C, lg, nslots);
-        }
-        if (tid < MAX_TILES) {
-            const int j = tid;
-            if (four)
-                P.len[src ^ 1][j] = 4 * j + 3 < MAX_TILES
-                                        ? (len[4 * j] + len[4 * j + 1]) + (len[4 * j + 2] + len[4 * j + 3])
-                                        : 0;
-            else
-                P.len[src ^ 1][j] = 2 * j + 1 < MAX_TILES ? len[2 * j] + len[2 * j + 1] : 0;
-        }
-        __syncthreads();
-        src ^= 1;
-        seg_tiles *= four ? 4 : 2;
-        lg += four ? 2 : 1;
-    }
-    const int n = P.len[src][0];
-    const unsigned long long* F = P.buf[src];
+    // the draw's uniform, formed while the row's loads are in flight
+    const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
+    const RowView rv = row_view(rl, rs.m, c.T);
+    const float zmax = rv.zmax;
+    const uint32_t mzb = mono32(rv.zb);
 
+    // The pool: every candidate with z above zb. It is an exact prefix of the
+    // row in key order (no entry outside the candidates lies above zb). Each
+    // wave appends its pool entries, one ballot per slot round, to its own
+    // region of A (A shares storage with F, which is written only after every
+    // read of A).
+    unsigned long long* A = P.F;
+    unsigned long long* Aw = A + wv * AREG;
+    int cw = 0;
+#pragma unroll
+    for (int k = 0; k < MSLOT; ++k) {
+        const int wt = wv + NWR * k;
+        if (wt < ws.n_wt) {
+            const int nc = stat_ncand(rl, wt);
+            const bool inp = lane < nc && (uint32_t)(rl.cv[k] >> 32) > mzb;
+            const unsigned long long bm = __ballot(inp);
+            if (bm) {
+                const int p = cw + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+                if (inp && p < AREG) Aw[p] = rl.cv[k];
+                cw += __popcll(bm);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < BKPT; ++j) P.cnt[tid * BKPT + j] = 0u;
+    if (lane == 0) sh.red.i[wv] = cw;
+    __syncthreads();
+    // wave w's entries occupy A[w AREG, w AREG + cnt_w); entry j of the pool in
+    // wave order sits in region r at j - (entries of the regions before r)
+    int n = 0, regmax = 0;
+    int rcnt[NWR];
+#pragma unroll
+    for (int w = 0; w < NWR; ++w) {
+        rcnt[w] = sh.red.i[w];
+        n += rcnt[w];
+        regmax = max(regmax, rcnt[w]);
+    }
+    auto pool_entry = [&](int j) -> unsigned long long {
+        int r = 0;
+#pragma unroll
+        for (int w = 0; w < NWR - 1; ++w) {
+            const bool past = j >= rcnt[r];
+            j -= past ? rcnt[r] : 0;
+            r += past ? 1 : 0;
+        }
+        return A[r * AREG + j];
+    };
+    const float zlo = rv.zlo;
+    const double W = rv.W;
     const int total = rs.nfinite;
     const bool topk_on = c.top_k > 0 && c.top_k < V;
     const int K_eff = topk_on ? min(c.top_k, total) : total;
     const bool cut_k = topk_on && K_eff < total;
-    bool slow = n == 0 || (cut_k && K_eff > n);
+    bool slow = n == 0 || regmax > AREG || rv.missing != 0;
+    // An uncut row's normaliser must be accurate: a relative error e of W moves
+    // every probability and every CDF breakpoint by at most e, and the parity
+    // rule allows 1e-6. (A top-k set deeper than the pool is checked once the
+    // pool's mass is known.)
+    if (!slow && !cut_k) slow = rv.err > 5e-7 * W;
+
     if (!slow) {
-        // Wave 0 resolves the row on the sorted pool, 64 entries at a time with
-        // a running binary64 carry (every cut is a prefix question, and on
-        // low-entropy rows all of them fall in the first chunk or two); the
-        // rest of the workgroup waits at one barrier.
-        __shared__ RowOut s_out;
-        double WK_block = 0.0;
-        if (cut_k && K_eff > WAVE) {
-            double part = 0.0;
-            for (int i = tid; i < K_eff; i += NTR) part += (double)expf(key_z(F[i]) - zmax);
-            WK_block = block_sum_d(part, sh.red);
+        if (n <= WAVE) {
+            // A pool of one wave's size: wave 0 sorts it in registers (a bitonic
+            // network over lane exchanges) and forms its weights and binary64
+            // prefix masses; it alone reads them, so no barrier follows.
+            if (wv == 0) {
+                unsigned long long key = lane < n ? pool_entry(lane) : 0ull;
+                key = wave_sort_desc_u64(key);  // zero keys (empty lanes) sort last
+                const float w = lane < n ? expf(key_z(key) - zmax) : 0.0f;
+                const double pre = wave_incl_scan_d((double)w);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                if (lane < n) {
+                    P.F[lane] = key;
+                    P.w[lane] = w;
+                    P.P[lane] = pre;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        } else {
+            // Counting sort by bucket b = (zmax - z) S, non-decreasing along key
+            // order, then each entry's rank among its bucket's entries.
+            const float R = zmax - zlo;
+            const float S = R > 0.0f ? fminf((float)NBK / R, 3.0e38f) : 0.0f;
+            unsigned long long key[EPTR];
+            int bkt[EPTR], arr[EPTR];
+#pragma unroll
+            for (int j = 0; j < EPTR; ++j) {
+                const int e = tid + j * NTR;
+                key[j] = 0ull;
+                bkt[j] = 0;
+                arr[j] = 0;
+                if (e < n) {
+                    key[j] = pool_entry(e);
+                    bkt[j] = (int)fminf((zmax - key_z(key[j])) * S, (float)(NBK - 1));
+                    arr[j] = (int)atomicAdd(&P.cnt[bkt[j]], 1u);
+                }
+            }
+            __syncthreads();
+            {
+                uint32_t cb[BKPT];
+                int tot = 0, mx = 0;
+#pragma unroll
+                for (int j = 0; j < BKPT; ++j) {
+                    cb[j] = P.cnt[tid * BKPT + j];
+                    tot += (int)cb[j];
+                    mx = max(mx, (int)cb[j]);
+                }
+                const int inc = wave_incl_scan_i(tot);
+                const int wmx = wave_max_i(mx);
+                if (lane == WAVE - 1) sh.red2.i[wv] = inc;
+                if (lane == 0) sh.imax[wv] = wmx;
+                __syncthreads();
+                int base = inc - tot, bmax = 0;
+#pragma unroll
+                for (int w = 0; w < NWR; ++w) {
+                    base += w < wv ? sh.red2.i[w] : 0;
+                    bmax = max(bmax, sh.imax[w]);
+                }
+#pragma unroll
+                for (int j = 0; j < BKPT; ++j) {
+                    P.start[tid * BKPT + j] = (uint32_t)base;
+                    base += (int)cb[j];
+                }
+                slow = bmax > BK_MAX;
+            }
+            __syncthreads();
+            if (!slow) {
+#pragma unroll
+                for (int j = 0; j < EPTR; ++j)
+                    if (tid + j * NTR < n) P.bk[P.start[bkt[j]] + arr[j]] = key[j];
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < EPTR; ++j) {
+                    if (tid + j * NTR < n) {
+                        const int s0 = (int)P.start[bkt[j]], cbk = (int)P.cnt[bkt[j]];
+                        int r = 0;
+                        for (int q = 0; q < cbk; ++q) r += P.bk[s0 + q] > key[j] ? 1 : 0;
+                        P.F[s0 + r] = key[j];
+                    }
+                }
+                __syncthreads();
+                // Weights and binary64 inclusive prefix masses of the sorted pool
+                // (each thread sums EPTR consecutive entries, then the thread
+                // totals are scanned in thread order); the bucket arrays they
+                // overwrite are dead.
+                float wl[EPTR];
+                double pre[EPTR];
+                double run = 0.0;
+#pragma unroll
+                for (int j = 0; j < EPTR; ++j) {
+                    const int i = tid * EPTR + j;
+                    wl[j] = i < n ? expf(key_z(P.F[i]) - zmax) : 0.0f;
+                    run += (double)wl[j];
+                    pre[j] = run;
+                }
+                double tot;
+                const double base = block_excl_scan_d(run, sh.red, tot);
+#pragma unroll
+                for (int j = 0; j < EPTR; ++j) {
+                    const int i = tid * EPTR + j;
+                    if (i < n) {
+                        P.w[i] = wl[j];
+                        if (i < POOL / 2) P.P[i] = base + pre[j];
+                        else P.P2[i - POOL / 2] = base + pre[j];
+                    }
+                }
+                __syncthreads();
+            }
         }
+    }
+    if (!slow) {
+        const unsigned long long* F = P.F;
+        __shared__ RowOut s_out;
         if (wv == 0) {
-            // the draw's uniform and the row mass, in the resolving wave only
-            const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
-            RowSummary rw = rs;
-            if (!cut_k) rw.W = row_mass(ts, rs.m, c.T);
-            const RowOut o = resolve_wave(F, n, zmax, rw, c, u, K_eff, cut_k, total, topk_on,
-                                          dbg.probs != nullptr, dbg.topk != nullptr, WK_block);
+            const RowOut o = resolve_wave(P, n, zmax, rv.zb, W, rv.err, c, u, K_eff, cut_k, total, topk_on,
+                                          dbg.probs != nullptr, dbg.topk != nullptr);
             if (lane == 0) s_out = o;
         }
         __syncthreads();
@@ -1396,7 +1470,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
             }
             if (dbg.probs)
                 for (int i = tid; i < o.n_kept; i += NTR)
-                    dbg.probs[key64_id(F[i])] = (float)((double)expf(key_z(F[i]) - zmax) / o.Wk);
+                    dbg.probs[key64_id(F[i])] = (float)((double)P.w[i] / o.Wk);
             if (dbg.topk)
                 for (int i = tid; i < dbg.topk_stride; i += NTR)
                     dbg.topk[i] = i < o.lim_list ? key64_id(F[i]) : -1;
@@ -1404,11 +1478,11 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
             return;
         }
     }
-    const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
-    finalize_slow<DT>(c, row, ws, n_tiles, rs, u, su, sh, info, dbg);
+    finalize_slow<DT>(c, row, ws, ws.n_tiles, rs, u, su, sh, info, dbg);
     __syncthreads();
     info_out = info;
 }
+
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -1443,20 +1517,20 @@ __device__ __forceinline__ RowCtx spec_ctx(const SpecArgs& a, int b, int j) {
     return make_ctx(a.p, b, logits, a.V, a.draft_tokens + (size_t)b * a.G, j, mrow, (uint32_t)j);
 }
 
-// Tile kernels: seven 256-thread workgroups per CU fit the LDS (about 23 KB
-// each); the register budget is held to the same seven waves per SIMD.
-#define SS_TILE_OCC __attribute__((amdgpu_waves_per_eu(7)))
+// Tile kernels: six 256-thread workgroups per CU (about 23 KB of LDS each);
+// the register budget is held to six waves per SIMD, which keeps the tile's 32
+// values per lane and the window passes in registers without spilling.
+#define SS_TILE_OCC __attribute__((amdgpu_waves_per_eu(6)))
 
 template <int DT, bool ALIGNED>
 __global__ __launch_bounds__(NT) SS_TILE_OCC void k_sample_tiles(SampleArgs a) {
     __shared__ SmemTile tt;
-    __shared__ SmemS sh;
     const int n_tiles = a.ws.n_tiles;
     const int lin = xcd_linear(a.B * n_tiles);
     const int row = lin / n_tiles;
     const int tile = lin % n_tiles;
     const RowCtx c = sample_ctx<DT>(a, row);
-    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt, sh,
+    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt,
                     a.dbg_processed ? a.dbg_processed + (size_t)row * a.V : nullptr,
                     a.dbg_probs ? a.dbg_probs + (size_t)row * a.V : nullptr);
 }
@@ -1481,16 +1555,15 @@ __global__ __launch_bounds__(NTR) void k_sample_rows(SampleArgs a) {
 
 // Verification, stage 1 over every target row of every request.
 template <int DT, bool ALIGNED>
-__global__ __launch_bounds__(NT) void k_spec_tiles(SpecArgs a) {
+__global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_tiles(SpecArgs a) {
     __shared__ SmemTile tt;
-    __shared__ SmemS sh;
     const int n_tiles = a.ws.n_tiles;
     const int G1 = a.G + 1;
     const int lin = xcd_linear(a.B * G1 * n_tiles);
     const int row = lin / n_tiles;
     const int tile = lin % n_tiles;
     const RowCtx c = spec_ctx<DT>(a, row / G1, row % G1);
-    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt, sh, nullptr, nullptr);
+    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt, nullptr, nullptr);
 }
 
 // Verification, per target row: the filtered distribution, then the accept
@@ -1570,8 +1643,9 @@ __device__ void residual_values(const RowCtx& c, const RowInfo& ri, const float*
     const TablePrefetch f = prefetch_tables(c);
     load_tile<DT>(c, tb, v);
     load_mask<DT>(c, tb, mw);
-    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, f);
-    process_tile<DT>(c, tb, v, tt, mw);
+    const bool tables = c.hist_len + c.extra_len + c.bias_len > 0;
+    if (tables) build_tables<DT>(c, tb, tt, f);
+    process_tile<DT>(c, tb, v, tt, mw, tables);
 #pragma unroll
     for (int s = 0; s < EPT; ++s) {
         const int id = slot_id<DT>(tb, s);
@@ -1604,8 +1678,9 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a)
     const TablePrefetch f = prefetch_tables(c);
     load_tile<DT>(c, tb, v);
     load_mask<DT>(c, tb, mw);
-    if (c.hist_len + c.extra_len + c.bias_len > 0) build_tables(c, tb, tt, f);
-    process_tile<DT>(c, tb, v, tt, mw);
+    const bool tables = c.hist_len + c.extra_len + c.bias_len > 0;
+    if (tables) build_tables<DT>(c, tb, tt, f);
+    process_tile<DT>(c, tb, v, tt, mw, tables);
     double sr = 0.0, sp = 0.0;
 #pragma unroll
     for (int s = 0; s < EPT; ++s) {
