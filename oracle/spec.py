@@ -21,7 +21,8 @@ if those were accepted; a per-position grammar mask is used when given):
   * T > 0: with pi_j the filtered target distribution and q_j the draft
     probabilities, draw u = u24(Philox ACCEPT word at (seed, request, pos + j, 0))
     and accept iff u < pi_j(d_j) / q_j(d_j) (if q_j(d_j) == 0: accept iff
-    pi_j(d_j) > 0). On the first rejection draw u' = u24(Philox RESIDUAL word at
+    pi_j(d_j) > 0); the decision is flagged when |u - pi/q| < 1e-6, whichever
+    side of 1 the ratio lies. On the first rejection draw u' = u24(Philox RESIDUAL word at
     (seed, request, pos + j, 0)) and emit the token of the normalised residual
     r = max(0, pi_j - q_j) by inverse CDF in ascending token-id order (pi_j if
     the residual sums to zero); then stop.
@@ -113,7 +114,10 @@ def verify_request(target_rows, draft_probs, draft_tokens, *, temperature, top_k
         if q > 0.0:
             ratio = p / q
             accept = u < ratio
-            if ratio < 1.0 and abs(u - ratio) < BOUNDARY_EPS:
+            # the decision u < ratio is a boundary case whenever u lies within
+            # 1e-6 of the ratio, on either side of 1: a ratio just above 1 in
+            # binary64 can round below u on a binary32 device
+            if abs(u - ratio) < BOUNDARY_EPS:
                 flagged = True
         else:
             ratio = np.inf if p > 0.0 else 0.0

@@ -139,7 +139,10 @@ def compare_debug(w, xs, filts, tokens, dbg, seed, tally, positions=None):
         u = philox.uniform(seed, int(w.request_ids[b]), int(pos[b]), 0, philox.SAMPLE)
         r = P.draw(f, u)
         flagged = r.flagged
-        if not flagged:
+        # a draw near a CDF breakpoint says nothing about the distribution: the
+        # kept count and the probabilities are excused only when a top-p or
+        # min-p cut itself lies on a boundary
+        if not (f.flag_topp or f.flag_minp):
             assert int(kept[b]) == f.n_kept, (b, int(kept[b]), f.n_kept)
             err = np.abs(probs[b].astype(np.float64) - f.probs).max()
             assert err <= PROB_TOL, (b, err)
