@@ -76,7 +76,9 @@ typedef struct {
  * takes the stated default. */
 typedef struct {
     const float* temperature;        /* [B] required; >= 0 and finite; 0 = greedy */
-    const int32_t* top_k;            /* [B]; <= 0 or >= V: off */
+    const int32_t* top_k;            /* [B]; <= 0 or >= V: off; any k in between is served:
+                                        a top-k set reaching past the tile candidates with
+                                        non-negligible mass takes the exact whole-row path */
     const float* top_p;              /* [B]; in (0, 1]; 1 = off (NULL: 1) */
     const float* min_p;              /* [B]; in [0, 1]; 0 = off (NULL: 0) */
     const float* repetition_penalty; /* [B]; > 0 (NULL: 1) */
@@ -84,14 +86,17 @@ typedef struct {
     const float* presence_penalty;   /* [B] (NULL: 0) */
     const int32_t* history_ids;      /* [B, history_stride]; ids outside [0,V) ignored */
     const int32_t* history_len;      /* [B], each in [0, history_stride]; NULL: no history */
-    int32_t history_stride;          /* >= 0, <= 65535 */
+    int32_t history_stride;          /* >= 0, <= 65000 (multiplicities are counted in 16 bits,
+                                        with room for up to 16 draft tokens) */
     const int32_t* bias_ids;         /* [B, bias_stride]; ids outside [0,V) ignored */
     const float* bias_values;        /* [B, bias_stride]; applied in array order */
     const int32_t* bias_len;         /* [B], each in [0, bias_stride]; NULL: no bias */
-    int32_t bias_stride;             /* >= 0 */
+    int32_t bias_stride;             /* >= 0; bias_ids and bias_values share it */
     const uint32_t* grammar_mask;    /* [B, mask_stride] (verify: [B, G+1, mask_stride]);
                                         bit (v & 31) of word (v >> 5), 1 = allowed */
-    int32_t mask_stride;             /* >= ceil(V / 32) when grammar_mask is set */
+    int32_t mask_stride;             /* words between consecutive rows, >= ceil(V / 32) when
+                                        grammar_mask is set (verification: between positions,
+                                        row b * (G + 1) + j) */
     const int32_t* request_ids;      /* [B] Philox counter word 0 (NULL: row index) */
     const int32_t* positions;        /* [B] Philox counter word 1 (NULL: 0) */
     uint64_t seed;                   /* Philox key (host value) */
@@ -107,12 +112,15 @@ typedef struct {
     int32_t* kept_count;     /* [B]: size of the sampling support after all filters */
     float* probs;            /* [B, V]: filtered probabilities (0 outside the support) */
     int32_t* path;           /* [B]: 0 = resolved from the tile candidates,
-                                1 = resolved by the exact whole-row fallback */
+                                1 = resolved by the exact whole-row fallback (top-k ids and
+                                probabilities asked for here can send rows there that
+                                would otherwise resolve from the candidates) */
 } ss_debug;
 
 /* Creates a sampler on cfg->device and allocates its workspace (the only call
- * that allocates). Returns SS_ERR_INVALID_ARG for out-of-range limits,
- * SS_ERR_OUT_OF_MEMORY if the workspace does not fit, SS_ERR_HIP otherwise. */
+ * that allocates). Returns SS_ERR_INVALID_ARG for out-of-range limits (checked
+ * before any HIP call), SS_ERR_OUT_OF_MEMORY if the workspace does not fit,
+ * SS_ERR_HIP otherwise (for instance a device ordinal that does not exist). */
 ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out);
 
 /* Frees the workspace. The caller must ensure no enqueued call is pending. */
@@ -153,6 +161,13 @@ ss_status ss_sampler_set_launch_events(ss_sampler* s, void* const* events, int32
  * lowest id among the maxima) -> top-k -> top-p -> min-p -> inverse-CDF draw in
  * (z descending, id ascending) order with u = u24(Philox(seed; request,
  * position, 0, domain 0)). Ties always go to the lower token id. */
+/* Errors (returned before any launch): SS_ERR_INVALID_ARG for a null handle,
+ * B < 0 or B > max_batch, null logits / out_tokens / params / temperature, a
+ * dtype other than SS_F32 / SS_BF16, row_stride < V, logits not aligned to
+ * their element size, history_stride outside 0 .. 65000, bias or history
+ * pointers given without their companions, mask_stride < ceil(V / 32) with a
+ * mask, or topk_ids given with topk_stride < 1; SS_ERR_HIP if the launch fails.
+ * B = 0 returns SS_OK without touching any pointer but the handle. */
 ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t row_stride,
                     int32_t B, const ss_params* params, int32_t* out_tokens,
                     const ss_debug* debug, void* stream);
@@ -173,7 +188,12 @@ ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t r
  * probability min(1, p/q) (u from domain 1 at position + j), on rejection
  * resample from the normalised max(0, p - q) in token-id order (domain 2), and
  * after full acceptance draw the bonus token as ss_sample would at position + G.
- * Launches two kernels (the residual pass only does work for rejected rows). */
+ * Launches four kernels: the tile scan over every target row, the row merge and
+ * accept tests, the residual tile sums and the per-request finish (the last
+ * two only do work for rejected requests). */
+/* Errors: as ss_sample, plus SS_ERR_INVALID_ARG for G outside 1 .. max_draft,
+ * null draft_probs / draft_tokens / out_tokens / out_num_accepted, or
+ * draft_stride < V. */
 ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtype,
                          int64_t row_stride, const float* draft_probs, int64_t draft_stride,
                          const int32_t* draft_tokens, int32_t B, int32_t G,
@@ -192,7 +212,11 @@ ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
  * position, v >> 2, domain 3)[v & 3])), g = -ln(-ln U), U = 1 - (w + 0.5) 2^-32.
  * Per 128-row vocabulary tile the GEMM kernel keeps only a (max, argmax) pair
  * per batch row; a second launch reduces the pairs of each row (the result does
- * not depend on the tiling: argmax decomposes over any partition). */
+ * not depend on the tiling: argmax decomposes over any partition).
+ * Errors: SS_ERR_INVALID_ARG for a null handle, a handle created with
+ * hidden_size 0, B outside 1 .. min(max_batch, 64), or null hidden / weight /
+ * temperature / out_tokens; SS_ERR_UNSUPPORTED for hidden or weight not 16-byte
+ * aligned; SS_ERR_HIP if a launch fails. */
 ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t* weight,
                            int32_t B, const float* temperature, const int32_t* request_ids,
                            const int32_t* positions, uint64_t seed, int32_t* out_tokens,

@@ -109,6 +109,33 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_dev(t, name, dtypes, device):
+    _require(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _require(t.is_cuda and t.device.index == device, f"{name} must live on cuda:{device}")
+    _require(t.dtype in dtypes, f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _check_vec(t, name, n, dtype, device):
+    """A per-row array: at least n entries, unit stride (the ABI takes a bare pointer)."""
+    if t is None:
+        return
+    _check_dev(t, name, (dtype,), device)
+    _require(t.dim() == 1 and t.shape[0] >= n and (t.shape[0] <= 1 or t.stride(0) == 1),
+             f"{name} must be a 1-D array of >= {n} entries with unit stride")
+
+
+def _check_rows(t, name, n, dtypes, device):
+    """A [rows, cols] matrix with unit column stride: the ABI takes its row stride."""
+    _check_dev(t, name, dtypes, device)
+    _require(t.dim() == 2 and t.shape[0] >= n, f"{name} must be 2-D with >= {n} rows")
+    _require(t.shape[1] <= 1 or t.stride(1) == 1, f"{name} must have unit stride along its last dim")
+
+
 @dataclass
 class SamplingParams:
     """Per-request parameters as device tensors (None disables a feature)."""
@@ -129,7 +156,51 @@ class SamplingParams:
     positions: torch.Tensor | None = None
     seed: int = 0
 
-    def to_c(self):
+    def validate(self, B, V, device, mask_rows=None):
+        """Check every tensor against what the C ABI can express for B rows of a
+        V-entry vocabulary; mask_rows = G + 1 for a per-position [B, G+1, W]
+        mask (verification). Raises ValueError; returns the mask row stride."""
+        _require(self.temperature is not None, "temperature is required")
+        _check_vec(self.temperature, "temperature", B, torch.float32, device)
+        _check_vec(self.top_k, "top_k", B, torch.int32, device)
+        for name in ("top_p", "min_p", "repetition_penalty", "frequency_penalty",
+                     "presence_penalty"):
+            _check_vec(getattr(self, name), name, B, torch.float32, device)
+        _check_vec(self.request_ids, "request_ids", B, torch.int32, device)
+        _check_vec(self.positions, "positions", B, torch.int32, device)
+        if self.history_len is not None or self.history_ids is not None:
+            _require(self.history_len is not None and self.history_ids is not None,
+                     "history_ids and history_len go together")
+            _check_rows(self.history_ids, "history_ids", B, (torch.int32,), device)
+            _check_vec(self.history_len, "history_len", B, torch.int32, device)
+        if self.bias_len is not None or self.bias_ids is not None or self.bias_values is not None:
+            _require(self.bias_len is not None and self.bias_ids is not None and
+                     self.bias_values is not None, "bias_ids, bias_values and bias_len go together")
+            _check_rows(self.bias_ids, "bias_ids", B, (torch.int32,), device)
+            _check_rows(self.bias_values, "bias_values", B, (torch.float32,), device)
+            _require(self.bias_values.shape[1] >= self.bias_ids.shape[1] and
+                     self.bias_values.stride(0) == self.bias_ids.stride(0),
+                     "bias_values must share bias_ids' row stride (one stride in the ABI)")
+            _check_vec(self.bias_len, "bias_len", B, torch.int32, device)
+        mask_stride = 0
+        if self.grammar_mask is not None:
+            m = self.grammar_mask
+            _check_dev(m, "grammar_mask", (torch.int32,), device)
+            words = (V + 31) // 32
+            _require(m.shape[-1] >= words and (m.shape[-1] <= 1 or m.stride(-1) == 1),
+                     f"grammar_mask needs >= {words} unit-stride words per row")
+            if mask_rows is None:
+                _require(m.dim() == 2 and m.shape[0] >= B, "grammar_mask must be [B, words]")
+                mask_stride = m.stride(0)
+            else:
+                _require(m.dim() == 3 and m.shape[0] >= B and m.shape[1] == mask_rows and
+                         (B <= 1 or m.stride(0) == mask_rows * m.stride(1)),
+                         "a verification grammar_mask must be [B, G+1, words] with rows "
+                         "evenly spaced")
+                mask_stride = m.stride(1)
+        return mask_stride
+
+    def to_c(self, mask_stride=None):
         c = CParams()
         c.temperature = _ptr(self.temperature)
         c.top_k = _ptr(self.top_k)
@@ -146,7 +217,9 @@ class SamplingParams:
         c.bias_len = _ptr(self.bias_len)
         c.bias_stride = 0 if self.bias_ids is None else int(self.bias_ids.stride(0))
         c.grammar_mask = _ptr(self.grammar_mask)
-        c.mask_stride = 0 if self.grammar_mask is None else int(self.grammar_mask.shape[-1])
+        if mask_stride is None:
+            mask_stride = 0 if self.grammar_mask is None else int(self.grammar_mask.stride(-2))
+        c.mask_stride = int(mask_stride)
         c.request_ids = _ptr(self.request_ids)
         c.positions = _ptr(self.positions)
         c.seed = int(self.seed) & 0xFFFFFFFFFFFFFFFF
@@ -191,6 +264,8 @@ class Sampler:
         _check("ss_sampler_create", self.lib.ss_sampler_create(ctypes.byref(cfg), ctypes.byref(h)))
         self.handle = h
         self.vocab_size = vocab_size
+        self.hidden_size = hidden_size
+        self.max_draft = max_draft
         self.device = device
 
     def close(self):
@@ -226,10 +301,26 @@ class Sampler:
 
     def sample(self, logits, params: SamplingParams, out=None, debug: Debug | None = None,
                stream=None):
-        B = logits.shape[0]
+        _check_rows(logits, "logits", 0, (torch.float32, torch.bfloat16), self.device)
+        B, V = logits.shape
+        _require(V == self.vocab_size, f"logits have {V} columns, the sampler {self.vocab_size}")
         if out is None:
             out = torch.empty(B, dtype=torch.int32, device=logits.device)
-        cp = params.to_c()
+        _check_vec(out, "out", B, torch.int32, self.device)
+        if debug is not None:
+            for name, cols in (("processed_logits", V), ("probs", V)):
+                t = getattr(debug, name)
+                if t is not None:
+                    _check_rows(t, f"debug.{name}", B, (torch.float32,), self.device)
+                    _require(t.shape[1] == V and (B <= 1 or t.stride(0) == V),
+                             f"debug.{name} must be a contiguous [B, V] array")
+            if debug.topk_ids is not None:
+                _check_rows(debug.topk_ids, "debug.topk_ids", B, (torch.int32,), self.device)
+                _require(B <= 1 or debug.topk_ids.stride(0) == debug.topk_ids.shape[1],
+                         "debug.topk_ids must be contiguous")
+            _check_vec(debug.kept_count, "debug.kept_count", B, torch.int32, self.device)
+            _check_vec(debug.path, "debug.path", B, torch.int32, self.device)
+        cp = params.to_c(params.validate(B, V, self.device))
         cd = debug.to_c() if debug is not None else None
         st = self.lib.ss_sample(self.handle, _ptr(logits), self._dtype(logits),
                                 int(logits.stride(0)), B, ctypes.byref(cp), _ptr(out),
@@ -239,14 +330,33 @@ class Sampler:
 
     def spec_verify(self, target_logits, draft_probs, draft_tokens, params: SamplingParams,
                     out_tokens=None, out_num_accepted=None, stream=None):
+        _check_dev(target_logits, "target_logits", (torch.float32, torch.bfloat16), self.device)
+        _require(target_logits.dim() == 3, "target_logits must be [B, G+1, V]")
         B, G1, V = target_logits.shape
         G = G1 - 1
+        _require(V == self.vocab_size, f"target_logits have {V} columns, the sampler {self.vocab_size}")
+        # the ABI addresses row b * (G + 1) + j at one row stride
+        _require(target_logits.stride(2) == 1 and
+                 (B <= 1 or target_logits.stride(0) == G1 * target_logits.stride(1)),
+                 "target_logits rows must be evenly spaced with unit stride along V")
+        _check_dev(draft_probs, "draft_probs", (torch.float32,), self.device)
+        _require(draft_probs.dim() == 3 and tuple(draft_probs.shape) == (B, G, V) and
+                 draft_probs.stride(2) == 1 and
+                 (B <= 1 or draft_probs.stride(0) == G * draft_probs.stride(1)),
+                 "draft_probs must be [B, G, V] with evenly spaced rows and unit stride along V")
+        _check_dev(draft_tokens, "draft_tokens", (torch.int32,), self.device)
+        _require(tuple(draft_tokens.shape) == (B, G) and draft_tokens.is_contiguous(),
+                 "draft_tokens must be a contiguous [B, G] int32 array")
         dev = target_logits.device
         if out_tokens is None:
             out_tokens = torch.empty(B, G1, dtype=torch.int32, device=dev)
         if out_num_accepted is None:
             out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
-        cp = params.to_c()
+        _check_dev(out_tokens, "out_tokens", (torch.int32,), self.device)
+        _require(tuple(out_tokens.shape) == (B, G1) and out_tokens.is_contiguous(),
+                 "out_tokens must be a contiguous [B, G+1] int32 array")
+        _check_vec(out_num_accepted, "out_num_accepted", B, torch.int32, self.device)
+        cp = params.to_c(params.validate(B, V, self.device, mask_rows=G1))
         st = self.lib.ss_spec_verify(self.handle, _ptr(target_logits), self._dtype(target_logits),
                                      int(target_logits.stride(1)), _ptr(draft_probs),
                                      int(draft_probs.stride(1)), _ptr(draft_tokens), B, G,
@@ -257,9 +367,23 @@ class Sampler:
 
     def lmhead_sample(self, hidden, weight, temperature, request_ids=None, positions=None,
                       seed=0, out=None, debug_logits=None, stream=None):
-        B = hidden.shape[0]
+        _check_dev(hidden, "hidden", (torch.bfloat16, torch.int16), self.device)
+        _check_dev(weight, "weight", (torch.bfloat16, torch.int16), self.device)
+        _require(hidden.dim() == 2 and hidden.is_contiguous(), "hidden must be a contiguous [B, K] array")
+        B, K = hidden.shape
+        _require(K == self.hidden_size, f"hidden has K = {K}, the sampler {self.hidden_size}")
+        _require(tuple(weight.shape) == (self.vocab_size, K) and weight.is_contiguous(),
+                 f"weight must be a contiguous [{self.vocab_size}, {K}] array")
+        _check_vec(temperature, "temperature", B, torch.float32, self.device)
+        _check_vec(request_ids, "request_ids", B, torch.int32, self.device)
+        _check_vec(positions, "positions", B, torch.int32, self.device)
         if out is None:
             out = torch.empty(B, dtype=torch.int32, device=hidden.device)
+        _check_vec(out, "out", B, torch.int32, self.device)
+        if debug_logits is not None:
+            _check_dev(debug_logits, "debug_logits", (torch.float32,), self.device)
+            _require(tuple(debug_logits.shape) == (B, self.vocab_size) and debug_logits.is_contiguous(),
+                     "debug_logits must be a contiguous [B, V] float32 array")
         st = self.lib.ss_lmhead_sample(self.handle, _ptr(hidden), _ptr(weight), B,
                                        _ptr(temperature), _ptr(request_ids), _ptr(positions),
                                        int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out),

@@ -1,0 +1,233 @@
+"""Argument checks of a live handle (GPU): every call below is rejected on the
+host before any launch, and the handle still works afterwards.
+
+Two layers are covered: the C ABI itself (raw ctypes calls with a pointer or
+size that include/ss_sampler.h rules out) and the Python binding (tensor
+shapes, dtypes and strides that the ABI could not express, rejected with
+ValueError before the C call)."""
+import ctypes
+
+import pytest
+import torch
+
+from speculative_decoding_verification_pipeline_amd import sampler as SM
+from tests.gpu_support import device, log
+
+pytestmark = pytest.mark.gpu
+
+B, V, G, K = 4, 1000, 3, 128
+
+
+@pytest.fixture(scope="module")
+def live():
+    log(f"abi: creating a handle B={B} V={V} G={G} K={K}")
+    s = SM.Sampler(B, V, max_draft=G, hidden_size=K, device=0)
+    yield s
+    s.close()
+
+
+def _logits(rows=B, cols=V, dtype=torch.float32, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(rows, cols, generator=g).to(device=device(), dtype=dtype)
+
+
+def _temps(value=0.0, n=B):
+    return torch.full((n,), value, dtype=torch.float32, device=device())
+
+
+def _vp(t, byte_offset=0):
+    return ctypes.c_void_p(t.data_ptr() + byte_offset)
+
+
+def _raw_sample(s, logits, row_stride, rows, params, out, debug=None, dtype=SM.SS_F32, offset=0):
+    return s.lib.ss_sample(s.handle, None if logits is None else _vp(logits, offset), dtype,
+                           row_stride, rows, ctypes.byref(params) if params is not None else None,
+                           None if out is None else _vp(out),
+                           ctypes.byref(debug) if debug is not None else None, None)
+
+
+def test_create_reports_a_missing_device():
+    lib = SM.load_library()
+    h = ctypes.c_void_p()
+    cfg = SM.Config(4, 100, 0, 0, torch.cuda.device_count())
+    assert lib.ss_sampler_create(ctypes.byref(cfg), ctypes.byref(h)) == SM.SS_ERR_HIP
+    assert not h.value
+
+
+def test_sample_rejects_bad_arguments(live):
+    x = _logits()
+    out = torch.empty(B, dtype=torch.int32, device=device())
+    p = SM.SamplingParams(temperature=_temps()).to_c()
+    ok = _raw_sample(live, x, V, B, p, out)
+    assert ok == SM.SS_OK
+    bad = {
+        "batch above max_batch": dict(rows=B + 1),
+        "negative batch": dict(rows=-1),
+        "row stride below V": dict(row_stride=V - 1),
+        "null logits": dict(logits=None),
+        "null out_tokens": dict(out=None),
+        "null params": dict(params=None),
+        "dtype code": dict(dtype=7),
+        "misaligned f32 logits": dict(offset=2),
+    }
+    for name, kw in bad.items():
+        args = dict(logits=x, row_stride=V, rows=B, params=p, out=out)
+        args.update(kw)
+        log(f"abi: ss_sample with {name}")
+        assert _raw_sample(live, **args) == SM.SS_ERR_INVALID_ARG, name
+
+
+def test_sample_rejects_bad_parameter_layouts(live):
+    x = _logits()
+    out = torch.empty(B, dtype=torch.int32, device=device())
+    ids = torch.zeros(B, 8, dtype=torch.int32, device=device())
+    lens = torch.full((B,), 8, dtype=torch.int32, device=device())
+    vals = torch.zeros(B, 8, dtype=torch.float32, device=device())
+    mask = torch.full((B, (V + 31) // 32), -1, dtype=torch.int32, device=device())
+
+    def params(**kw):
+        return SM.SamplingParams(temperature=_temps(), **kw).to_c()
+
+    p = params()
+    p.temperature = None
+    cases = {"null temperature": p}
+    p = params(history_ids=ids, history_len=lens)
+    p.history_stride = 65001
+    cases["history stride above 65000"] = p
+    p = params(history_ids=ids, history_len=lens)
+    p.history_stride = -1
+    cases["negative history stride"] = p
+    p = params(history_len=lens)
+    cases["history lengths without ids"] = p
+    p = params(bias_ids=ids, bias_values=vals, bias_len=lens)
+    p.bias_values = None
+    cases["bias ids without values"] = p
+    p = params(grammar_mask=mask)
+    p.mask_stride = (V + 31) // 32 - 1
+    cases["mask stride below ceil(V / 32)"] = p
+    for name, cp in cases.items():
+        log(f"abi: ss_sample with {name}")
+        assert _raw_sample(live, x, V, B, cp, out) == SM.SS_ERR_INVALID_ARG, name
+    d = SM.Debug(topk_ids=torch.zeros(B, 4, dtype=torch.int32, device=device())).to_c()
+    d.topk_stride = 0
+    assert _raw_sample(live, x, V, B, params(), out, debug=d) == SM.SS_ERR_INVALID_ARG
+
+
+def test_empty_batch_touches_no_pointer(live):
+    assert live.lib.ss_sample(live.handle, None, 0, 0, 0, None, None, None, None) == SM.SS_OK
+    assert live.lib.ss_spec_verify(live.handle, None, 0, 0, None, 0, None, 0, 1, None, None,
+                                   None, None) == SM.SS_OK
+
+
+def test_spec_verify_rejects_bad_arguments(live):
+    tgt = _logits(B * (G + 1))
+    q = torch.full((B * G, V), 1.0 / V, dtype=torch.float32, device=device())
+    d = torch.zeros(B, G, dtype=torch.int32, device=device())
+    out = torch.empty(B, G + 1, dtype=torch.int32, device=device())
+    na = torch.empty(B, dtype=torch.int32, device=device())
+    p = SM.SamplingParams(temperature=_temps(1.0)).to_c()
+
+    def call(g=G, draft_stride=V, row_stride=V, rows=B, q_ptr=True, na_ptr=True):
+        return live.lib.ss_spec_verify(live.handle, _vp(tgt), SM.SS_F32, row_stride,
+                                       _vp(q) if q_ptr else None, draft_stride, _vp(d), rows, g,
+                                       ctypes.byref(p), _vp(out), _vp(na) if na_ptr else None,
+                                       None)
+
+    assert call() == SM.SS_OK
+    bad = {"G above max_draft": dict(g=G + 1), "G zero": dict(g=0),
+           "draft stride below V": dict(draft_stride=V - 1),
+           "target row stride below V": dict(row_stride=V - 1),
+           "batch above max_batch": dict(rows=B + 1), "null draft_probs": dict(q_ptr=False),
+           "null out_num_accepted": dict(na_ptr=False)}
+    for name, kw in bad.items():
+        log(f"abi: ss_spec_verify with {name}")
+        assert call(**kw) == SM.SS_ERR_INVALID_ARG, name
+
+
+def test_lmhead_rejects_bad_arguments(live):
+    g = torch.Generator().manual_seed(1)
+    h = (torch.randn(B, K, generator=g) * 0.1).to(device(), torch.bfloat16)
+    w = (torch.randn(V, K, generator=g) * 0.1).to(device(), torch.bfloat16)
+    t = _temps(1.0)
+    out = torch.empty(B, dtype=torch.int32, device=device())
+    lib = live.lib
+
+    def call(handle=None, hid=0, rows=B, temp=True):
+        return lib.ss_lmhead_sample(handle or live.handle, _vp(h, hid), _vp(w), rows,
+                                    _vp(t) if temp else None, None, None, 5, _vp(out), None, None)
+
+    assert call() == SM.SS_OK
+    assert call(hid=2) == SM.SS_ERR_UNSUPPORTED  # not 16-byte aligned
+    assert call(rows=0) == SM.SS_ERR_INVALID_ARG
+    assert call(rows=B + 1) == SM.SS_ERR_INVALID_ARG
+    assert call(temp=False) == SM.SS_ERR_INVALID_ARG
+    no_k = SM.Sampler(B, V, device=0)
+    try:
+        assert call(handle=no_k.handle) == SM.SS_ERR_INVALID_ARG  # created with hidden_size 0
+    finally:
+        no_k.close()
+
+
+def test_binding_rejects_layouts_the_abi_cannot_express(live):
+    x = _logits()
+    T = _temps()
+    cases = {
+        "column-strided logits": lambda: live.sample(_logits(B, 2 * V)[:, ::2], SM.SamplingParams(T)),
+        "wrong vocabulary": lambda: live.sample(_logits(B, V + 1), SM.SamplingParams(T)),
+        "host logits": lambda: live.sample(x.cpu(), SM.SamplingParams(T)),
+        "float16 logits": lambda: live.sample(x.half(), SM.SamplingParams(T)),
+        "short temperature": lambda: live.sample(x, SM.SamplingParams(_temps(n=B - 1))),
+        "strided temperature": lambda: live.sample(x, SM.SamplingParams(_temps(n=2 * B)[::2])),
+        "float64 top_p": lambda: live.sample(x, SM.SamplingParams(
+            T, top_p=torch.ones(B, dtype=torch.float64, device=device()))),
+        "narrow mask": lambda: live.sample(x, SM.SamplingParams(
+            T, grammar_mask=torch.zeros(B, (V + 31) // 32 - 1, dtype=torch.int32, device=device()))),
+        "bias without values": lambda: live.sample(x, SM.SamplingParams(
+            T, bias_ids=torch.zeros(B, 2, dtype=torch.int32, device=device()),
+            bias_len=torch.zeros(B, dtype=torch.int32, device=device()))),
+        "bias values with their own stride": lambda: live.sample(x, SM.SamplingParams(
+            T, bias_ids=torch.zeros(B, 2, dtype=torch.int32, device=device()),
+            bias_values=torch.zeros(B, 4, dtype=torch.float32, device=device())[:, :2],
+            bias_len=torch.zeros(B, dtype=torch.int32, device=device()))),
+        "non-contiguous debug probs": lambda: live.sample(x, SM.SamplingParams(T), debug=SM.Debug(
+            probs=torch.zeros(B, 2 * V, dtype=torch.float32, device=device())[:, :V])),
+    }
+    tgt = _logits(B * (G + 1)).view(B, G + 1, V)
+    q = torch.full((B, G, V), 1.0 / V, dtype=torch.float32, device=device())
+    d = torch.zeros(B, G, dtype=torch.int32, device=device())
+    T1 = _temps(1.0)
+    cases.update({
+        "unevenly spaced target rows": lambda: live.spec_verify(
+            _logits(B * (G + 2)).view(B, G + 2, V)[:, :G + 1], q, d, SM.SamplingParams(T1)),
+        "draft probs of the wrong shape": lambda: live.spec_verify(tgt, q[:, :G - 1], d,
+                                                                   SM.SamplingParams(T1)),
+        "transposed draft tokens": lambda: live.spec_verify(
+            tgt, q, torch.zeros(G, B, dtype=torch.int32, device=device()).t(), SM.SamplingParams(T1)),
+        "per-row mask for verification": lambda: live.spec_verify(tgt, q, d, SM.SamplingParams(
+            T1, grammar_mask=torch.zeros(B, (V + 31) // 32, dtype=torch.int32, device=device()))),
+    })
+    g = torch.Generator().manual_seed(2)
+    h = torch.randn(B, K, generator=g).to(device(), torch.bfloat16)
+    w = torch.randn(V, K, generator=g).to(device(), torch.bfloat16)
+    cases.update({
+        "hidden of the wrong width": lambda: live.lmhead_sample(h[:, :K // 2].contiguous(), w, T1),
+        "transposed weight": lambda: live.lmhead_sample(h, w.t().contiguous().t(), T1),
+    })
+    for name, fn in cases.items():
+        log(f"abi: binding with {name}")
+        with pytest.raises(ValueError):
+            fn()
+
+
+def test_handle_still_works_after_rejections(live):
+    # temperature 0 draws the argmax (ties to the lower id; none here)
+    x = _logits(seed=3)
+    tok = live.sample(x, SM.SamplingParams(_temps()))
+    torch.cuda.synchronize()
+    assert tok.cpu().tolist() == torch.argmax(x, dim=1).int().cpu().tolist()
+    with pytest.raises(SM.SamplerError) as e:
+        live.sample(_logits(B + 1), SM.SamplingParams(_temps(n=B + 1)))
+    assert e.value.status == SM.SS_ERR_INVALID_ARG
+    tok = live.sample(x, SM.SamplingParams(_temps()))
+    torch.cuda.synchronize()
+    assert tok.cpu().tolist() == torch.argmax(x, dim=1).int().cpu().tolist()
