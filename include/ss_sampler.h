@@ -222,6 +222,36 @@ ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t
                            const int32_t* positions, uint64_t seed, int32_t* out_tokens,
                            float* debug_logits, void* stream);
 
+/* ss_sample_noalloc -- ss_sample without a handle, for callers that cannot
+ * allocate device memory: code recorded under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. It runs the same kernels as
+ * ss_sample and returns the same tokens for the same arguments.
+ *   Device:   the current HIP device; `stream` must belong to it.
+ *   Scratch:  a static device array of SS_NOALLOC_SCRATCH_BYTES per GPU,
+ *             reserved with the library's code object (held until the process
+ *             ends). The first call on a device looks up its address there
+ *             (make that first call outside graph capture); no call allocates
+ *             or frees memory.
+ *   Limits:   B <= SS_NOALLOC_MAX_BATCH and B * V <= SS_NOALLOC_MAX_ENTRIES
+ *             (every size up to B = 64 rows of a 131072-entry vocabulary);
+ *             larger requests return SS_ERR_UNSUPPORTED before any launch.
+ *   Arguments as for ss_sample, with V (1 .. 262144) passed per call; no
+ *   debug outputs. Nothing in the scratch needs clearing between calls.
+ *   Every call on one GPU shares that GPU's scratch: two calls whose work
+ *   overlaps in time on the same GPU (different streams, or different host
+ *   threads) race and may return wrong tokens. Calls ordered on one stream do
+ *   not race.
+ * Errors: SS_ERR_INVALID_ARG for B < 0, V outside 1 .. 262144, or any check
+ * ss_sample makes on logits, params and out_tokens; SS_ERR_UNSUPPORTED beyond
+ * the limits above or on a device ordinal >= 64; SS_ERR_HIP if the address
+ * lookup or a launch fails. B = 0 returns SS_OK at once. */
+#define SS_NOALLOC_MAX_BATCH 64
+#define SS_NOALLOC_MAX_ENTRIES 8388608
+#define SS_NOALLOC_SCRATCH_BYTES 37748736
+ss_status ss_sample_noalloc(const void* logits, ss_dtype dtype, int64_t row_stride, int32_t B,
+                            int32_t V, const ss_params* params, int32_t* out_tokens,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

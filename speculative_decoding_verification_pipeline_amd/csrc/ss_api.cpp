@@ -1,9 +1,13 @@
 // Host side of the C ABI: handle lifetime, workspace, argument validation and
-// kernel launches. Nothing here allocates or synchronises after create.
+// kernel launches. Nothing here allocates or synchronises after create; the
+// handle-free ss_sample_noalloc never allocates at all (its scratch is a static
+// device array of this file).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "ss_device.h"
@@ -29,43 +33,58 @@ struct ss_sampler {
 
 namespace {
 
+// Device arrays read in place of absent per-request parameters.
+struct Defaults {
+    const int32_t* zero_i;
+    const float* zero_f;
+    const float* one_f;
+    const int32_t* iota;
+};
+
+Defaults defaults_of(const ss_sampler* s) {
+    return {s->def_zero_i, s->def_zero_f, s->def_one_f, s->def_iota};
+}
+
+}  // namespace
+
+namespace {
+
 constexpr int64_t kAlign = 256;
 
-int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+constexpr int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Device pointers for every per-request parameter: an absent one points at the
 // handle's default array (so the kernels read every parameter unconditionally).
-ss::ParamPtrs to_ptrs(const ss_sampler* s, const ss_params* p) {
+ss::ParamPtrs to_ptrs(const Defaults& d, const ss_params* p) {
     ss::ParamPtrs q;
     q.temperature = p->temperature;
-    q.top_k = p->top_k ? p->top_k : s->def_zero_i;
-    q.top_p = p->top_p ? p->top_p : s->def_one_f;
-    q.min_p = p->min_p ? p->min_p : s->def_zero_f;
-    q.rep = p->repetition_penalty ? p->repetition_penalty : s->def_one_f;
-    q.freq = p->frequency_penalty ? p->frequency_penalty : s->def_zero_f;
-    q.pres = p->presence_penalty ? p->presence_penalty : s->def_zero_f;
+    q.top_k = p->top_k ? p->top_k : d.zero_i;
+    q.top_p = p->top_p ? p->top_p : d.one_f;
+    q.min_p = p->min_p ? p->min_p : d.zero_f;
+    q.rep = p->repetition_penalty ? p->repetition_penalty : d.one_f;
+    q.freq = p->frequency_penalty ? p->frequency_penalty : d.zero_f;
+    q.pres = p->presence_penalty ? p->presence_penalty : d.zero_f;
     const bool hist = p->history_len && p->history_ids;
-    q.hist_ids = hist ? p->history_ids : s->def_zero_i;
-    q.hist_len = hist ? p->history_len : s->def_zero_i;
+    q.hist_ids = hist ? p->history_ids : d.zero_i;
+    q.hist_len = hist ? p->history_len : d.zero_i;
     q.hist_stride = hist ? p->history_stride : 0;
     const bool bias = p->bias_len && p->bias_ids && p->bias_values;
-    q.bias_ids = bias ? p->bias_ids : s->def_zero_i;
-    q.bias_vals = bias ? p->bias_values : s->def_zero_f;
-    q.bias_len = bias ? p->bias_len : s->def_zero_i;
+    q.bias_ids = bias ? p->bias_ids : d.zero_i;
+    q.bias_vals = bias ? p->bias_values : d.zero_f;
+    q.bias_len = bias ? p->bias_len : d.zero_i;
     q.bias_stride = bias ? p->bias_stride : 0;
     q.mask = p->grammar_mask;
     q.mask_stride = p->mask_stride;
-    q.request_ids = p->request_ids ? p->request_ids : s->def_iota;
-    q.positions = p->positions ? p->positions : s->def_zero_i;
+    q.request_ids = p->request_ids ? p->request_ids : d.iota;
+    q.positions = p->positions ? p->positions : d.zero_i;
     q.seed = p->seed;
     return q;
 }
 
-ss_status check_params(const ss_sampler* s, const ss_params* p) {
+ss_status check_params(int V, const ss_params* p) {
     if (!p || !p->temperature) return SS_ERR_INVALID_ARG;
-    const int V = s->cfg.vocab_size;
     if (p->history_len) {
         if (!p->history_ids || p->history_stride < 0 || p->history_stride > 65000)
             return SS_ERR_INVALID_ARG;
@@ -79,12 +98,124 @@ ss_status check_params(const ss_sampler* s, const ss_params* p) {
     return SS_OK;
 }
 
-ss_status check_logits(const ss_sampler* s, const void* logits, ss_dtype dtype, int64_t row_stride) {
+ss_status check_logits(int V, const void* logits, ss_dtype dtype, int64_t row_stride) {
     if (!logits) return SS_ERR_INVALID_ARG;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_INVALID_ARG;
-    if (row_stride < s->cfg.vocab_size) return SS_ERR_INVALID_ARG;
+    if (row_stride < V) return SS_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(logits) & (dtype == SS_F32 ? 3u : 1u)) != 0)
         return SS_ERR_INVALID_ARG;  // not even element-aligned
+    return SS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// ss_sample_noalloc: the same kernels as ss_sample, with the workspace carved
+// from a static device array instead of a handle's allocation.
+
+// Per-row workspace of a sampling call over B rows of V entries (the buffers a
+// handle gives ss_sample, sized for exactly B rows); with base set, points w at
+// them. Returns the bytes used.
+constexpr int64_t sample_scratch_layout(int64_t B, int64_t V, char* base, ss::Workspace* w) {
+    const int64_t n_tiles = (V + ss::TILE - 1) / ss::TILE;
+    const int64_t n_wt = n_tiles * ss::WPT;
+    int64_t off = 0;
+    const int64_t o_stats = off;
+    off = align_up(off + B * n_wt * (int64_t)sizeof(ss::WaveStat));
+    const int64_t o_cand = off;
+    off = align_up(off + B * n_wt * ss::WCAP * (int64_t)sizeof(unsigned long long));
+    const int64_t o_info = off;
+    off = align_up(off + B * (int64_t)sizeof(ss::RowInfo));
+    const int64_t o_z = off;
+    off = align_up(off + B * V * 4);
+    if (base && w) {
+        w->wstats = reinterpret_cast<ss::WaveStat*>(base + o_stats);
+        w->cand = reinterpret_cast<unsigned long long*>(base + o_cand);
+        w->rowinfo = reinterpret_cast<ss::RowInfo*>(base + o_info);
+        w->row_accept = nullptr;  // verification only
+        w->resid_tile = nullptr;
+        w->scratch_z = reinterpret_cast<float*>(base + o_z);
+        w->n_tiles = (int)n_tiles;
+        w->n_wt = (int)n_wt;
+        w->V = (int)V;
+    }
+    return off;
+}
+
+// The layout grows with V for a fixed B, so its largest size under the limits
+// is at the largest V each B allows.
+constexpr int64_t largest_sample_scratch() {
+    int64_t m = 0;
+    for (int64_t b = 1; b <= SS_NOALLOC_MAX_BATCH; ++b) {
+        int64_t v = SS_NOALLOC_MAX_ENTRIES / b;
+        if (v > ss::MAX_VOCAB) v = ss::MAX_VOCAB;
+        const int64_t n = sample_scratch_layout(b, v, nullptr, nullptr);
+        if (n > m) m = n;
+    }
+    return m;
+}
+static_assert(largest_sample_scratch() <= SS_NOALLOC_SCRATCH_BYTES,
+              "the static scratch must hold the largest call the limits admit");
+
+// Values read in place of absent per-request parameters (one row each).
+struct DefaultTable {
+    int32_t zero_i[SS_NOALLOC_MAX_BATCH];
+    float zero_f[SS_NOALLOC_MAX_BATCH];
+    float one_f[SS_NOALLOC_MAX_BATCH];
+    int32_t iota[SS_NOALLOC_MAX_BATCH];
+};
+
+constexpr DefaultTable make_default_table() {
+    DefaultTable t{};
+    for (int i = 0; i < SS_NOALLOC_MAX_BATCH; ++i) {
+        t.zero_i[i] = 0;
+        t.zero_f[i] = 0.0f;
+        t.one_f[i] = 1.0f;
+        t.iota[i] = i;
+    }
+    return t;
+}
+
+}  // namespace
+
+// One copy of each per GPU, reserved with the library's code object. Host code
+// never passes these names to a kernel: it uses the device addresses that
+// hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[SS_NOALLOC_SCRATCH_BYTES];
+static __device__ __align__(256) DefaultTable noalloc_defaults = make_default_table();
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct NoAllocDevice {
+    std::atomic<char*> scratch;
+    std::atomic<const DefaultTable*> defaults;
+};
+NoAllocDevice g_noalloc[kMaxDevices];  // static storage: starts null
+std::mutex g_noalloc_mutex;
+
+// This GPU's addresses of the two arrays, looked up once per device with that
+// device current (the first call on a device; later calls read the cache).
+ss_status noalloc_arrays(int dev, char** scr, const DefaultTable** defs) {
+    char* p = g_noalloc[dev].scratch.load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+        p = g_noalloc[dev].scratch.load(std::memory_order_relaxed);
+        if (!p) {
+            void* sp = nullptr;
+            void* dp = nullptr;
+            if (hipGetSymbolAddress(&sp, HIP_SYMBOL(scratch)) != hipSuccess || !sp ||
+                hipGetSymbolAddress(&dp, HIP_SYMBOL(noalloc_defaults)) != hipSuccess || !dp) {
+                (void)hipGetLastError();
+                return SS_ERR_HIP;
+            }
+            g_noalloc[dev].defaults.store(static_cast<const DefaultTable*>(dp),
+                                          std::memory_order_relaxed);
+            p = static_cast<char*>(sp);
+            g_noalloc[dev].scratch.store(p, std::memory_order_release);
+        }
+    }
+    *scr = p;
+    *defs = g_noalloc[dev].defaults.load(std::memory_order_relaxed);
     return SS_OK;
 }
 
@@ -214,9 +345,9 @@ ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t r
     if (!s || B < 0 || B > s->cfg.max_batch) return SS_ERR_INVALID_ARG;
     if (B == 0) return SS_OK;
     if (!out_tokens) return SS_ERR_INVALID_ARG;
-    ss_status st = check_logits(s, logits, dtype, row_stride);
+    ss_status st = check_logits(s->cfg.vocab_size, logits, dtype, row_stride);
     if (st != SS_OK) return st;
-    st = check_params(s, params);
+    st = check_params(s->cfg.vocab_size, params);
     if (st != SS_OK) return st;
     if (debug && debug->topk_ids && debug->topk_stride < 1) return SS_ERR_INVALID_ARG;
     ss::SampleArgs a;
@@ -225,7 +356,7 @@ ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t r
     a.row_stride = row_stride;
     a.B = B;
     a.V = s->cfg.vocab_size;
-    a.p = to_ptrs(s, params);
+    a.p = to_ptrs(defaults_of(s), params);
     a.out_tokens = out_tokens;
     if (debug) {
         a.dbg_processed = debug->processed_logits;
@@ -251,9 +382,9 @@ ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
     if (B == 0) return SS_OK;
     if (!draft_probs || !draft_tokens || !out_tokens || !out_num_accepted) return SS_ERR_INVALID_ARG;
     if (draft_stride < s->cfg.vocab_size) return SS_ERR_INVALID_ARG;
-    ss_status st = check_logits(s, target_logits, dtype, row_stride);
+    ss_status st = check_logits(s->cfg.vocab_size, target_logits, dtype, row_stride);
     if (st != SS_OK) return st;
-    st = check_params(s, params);
+    st = check_params(s->cfg.vocab_size, params);
     if (st != SS_OK) return st;
     ss::SpecArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -265,7 +396,7 @@ ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
     a.B = B;
     a.G = G;
     a.V = s->cfg.vocab_size;
-    a.p = to_ptrs(s, params);
+    a.p = to_ptrs(defaults_of(s), params);
     a.out_tokens = out_tokens;
     a.out_num_accepted = out_num_accepted;
     a.ws = s->ws;
@@ -300,6 +431,42 @@ ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
     return ss::launch_lmhead(a, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
                                                                                 : SS_ERR_HIP;
+}
+
+ss_status ss_sample_noalloc(const void* logits, ss_dtype dtype, int64_t row_stride, int32_t B,
+                            int32_t V, const ss_params* params, int32_t* out_tokens,
+                            void* stream) {
+    if (B < 0 || V < 1 || V > ss::MAX_VOCAB) return SS_ERR_INVALID_ARG;
+    if (B == 0) return SS_OK;
+    if (B > SS_NOALLOC_MAX_BATCH || (int64_t)B * V > SS_NOALLOC_MAX_ENTRIES) return SS_ERR_UNSUPPORTED;
+    if (!out_tokens) return SS_ERR_INVALID_ARG;
+    ss_status st = check_logits(V, logits, dtype, row_stride);
+    if (st != SS_OK) return st;
+    st = check_params(V, params);
+    if (st != SS_OK) return st;
+    if (sample_scratch_layout(B, V, nullptr, nullptr) > SS_NOALLOC_SCRATCH_BYTES)
+        return SS_ERR_UNSUPPORTED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SS_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SS_ERR_UNSUPPORTED;
+    char* scr = nullptr;
+    const DefaultTable* defs = nullptr;
+    st = noalloc_arrays(dev, &scr, &defs);
+    if (st != SS_OK) return st;
+    ss::SampleArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.logits = logits;
+    a.row_stride = row_stride;
+    a.B = B;
+    a.V = V;
+    a.p = to_ptrs(Defaults{defs->zero_i, defs->zero_f, defs->one_f, defs->iota}, params);
+    a.out_tokens = out_tokens;
+    sample_scratch_layout(B, V, scr, &a.ws);
+    ss::LaunchEvents none;
+    std::memset(&none, 0, sizeof(none));
+    return ss::launch_sample(a, dtype, static_cast<hipStream_t>(stream), none) == hipSuccess
+               ? SS_OK
+               : SS_ERR_HIP;
 }
 
 }  // extern "C"

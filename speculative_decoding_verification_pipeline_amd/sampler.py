@@ -26,7 +26,9 @@ SS_BF16 = 1
 
 EXPORTED = ("ss_sampler_create", "ss_sampler_destroy", "ss_status_string",
             "ss_sampler_workspace_bytes", "ss_sampler_set_launch_events", "ss_sample",
-            "ss_spec_verify", "ss_lmhead_sample")
+            "ss_spec_verify", "ss_lmhead_sample", "ss_sample_noalloc")
+NOALLOC_MAX_BATCH = 64
+NOALLOC_MAX_ENTRIES = 1 << 23
 
 
 class Config(ctypes.Structure):
@@ -91,6 +93,8 @@ def load_library(path=None):
     lib.ss_spec_verify.restype = i32
     lib.ss_lmhead_sample.argtypes = [vp, vp, vp, i32, vp, vp, vp, u64, vp, vp, vp]
     lib.ss_lmhead_sample.restype = i32
+    lib.ss_sample_noalloc.argtypes = [vp, i32, i64, i32, i32, ctypes.POINTER(CParams), vp, vp]
+    lib.ss_sample_noalloc.restype = i32
     _lib = lib
     return lib
 
@@ -390,3 +394,23 @@ class Sampler:
                                        _ptr(debug_logits), _stream(stream))
         _check("ss_lmhead_sample", st)
         return out
+
+
+def sample_noalloc(logits, params: SamplingParams, out=None, stream=None):
+    """ss_sample without a handle: the library's static per-GPU scratch serves
+    as workspace, so the call allocates nothing when `out` is given (B rows of
+    at most 64, B * V at most 2^23). Calls that overlap on one GPU race."""
+    _require(isinstance(logits, torch.Tensor) and logits.is_cuda, "logits must be a device tensor")
+    dev = logits.device.index
+    _check_rows(logits, "logits", 0, (torch.float32, torch.bfloat16), dev)
+    B, V = logits.shape
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _check_vec(out, "out", B, torch.int32, dev)
+    cp = params.to_c(params.validate(B, V, dev))
+    with torch.cuda.device(dev):
+        st = load_library().ss_sample_noalloc(_ptr(logits), Sampler._dtype(logits),
+                                              int(logits.stride(0)), B, V, ctypes.byref(cp),
+                                              _ptr(out), _stream(stream))
+    _check("ss_sample_noalloc", st)
+    return out
