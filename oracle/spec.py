@@ -70,15 +70,40 @@ def residual_draw(pi, q, u):
     return int(pos[i]), boundary_draw(cdf, u)
 
 
+def filtered_rows(target_rows, draft_tokens, *, temperature, top_k=0, top_p=1.0, min_p=0.0,
+                  rep=1.0, freq=0.0, pres=0.0, hist=(), bias_ids=(), bias_vals=(), masks=None):
+    """rows(j): target row j's filtered distribution, formed on first use.
+
+    Row j is processed with the request's history followed by the draft tokens
+    d_0 .. d_{j-1} (it is only reached if those were accepted) and, when given,
+    its own position's grammar mask. It depends on neither the seed nor the
+    position, so one rows() serves every draw over the same request.
+    """
+    hist = [int(h) for h in hist]
+    cache = {}
+
+    def rows(j):
+        if j not in cache:
+            hj = hist + [int(d) for d in draft_tokens[:j]]
+            mj = None if masks is None else masks[j]
+            xp = process_row(target_rows[j], hj, rep, freq, pres, bias_ids, bias_vals, mj)
+            cache[j] = filter_row(xp, temperature, top_k, top_p, min_p)
+        return cache[j]
+
+    return rows
+
+
 def verify_request(target_rows, draft_probs, draft_tokens, *, temperature, top_k=0,
                    top_p=1.0, min_p=0.0, rep=1.0, freq=0.0, pres=0.0, hist=(),
                    bias_ids=(), bias_vals=(), masks=None, seed=0, request=0, position=0,
-                   uniform=None):
+                   uniform=None, rows=None):
     """Verify one request's linear draft. target_rows: [G+1, V] float32.
 
     uniform(domain, pos) -> u overrides the Philox uniforms (used by tests that
     integrate over the uniforms); by default u = u24 of the Philox word at
     (seed, request, pos, draw 0, domain).
+    rows: the request's filtered_rows() (tests that sweep seeds and positions
+    over fixed rows form it once); by default it is formed here.
     """
     if uniform is None:
         def uniform(domain, pos):
@@ -87,12 +112,12 @@ def verify_request(target_rows, draft_probs, draft_tokens, *, temperature, top_k
     out = np.full(G + 1, -1, dtype=np.int32)
     flagged = False
     ratios = []
-    hist = [int(h) for h in hist]
+    if rows is None:
+        rows = filtered_rows(target_rows, draft_tokens, temperature=temperature, top_k=top_k,
+                             top_p=top_p, min_p=min_p, rep=rep, freq=freq, pres=pres, hist=hist,
+                             bias_ids=bias_ids, bias_vals=bias_vals, masks=masks)
     for j in range(G + 1):
-        hj = hist + [int(d) for d in draft_tokens[:j]]
-        mj = None if masks is None else masks[j]
-        xp = process_row(target_rows[j], hj, rep, freq, pres, bias_ids, bias_vals, mj)
-        filt = filter_row(xp, temperature, top_k, top_p, min_p)
+        filt = rows(j)
         flagged = flagged or filt.flag_topp or filt.flag_minp
         if j == G:
             u = uniform(philox.SAMPLE, position + G)
@@ -133,17 +158,29 @@ def verify_request(target_rows, draft_probs, draft_tokens, *, temperature, top_k
     raise AssertionError("unreachable")
 
 
-def verify_batch(target, draft_probs, draft_tokens, params):
-    """target [B, G+1, V] f32, draft_probs [B, G, V] f32, draft_tokens [B, G] int."""
+def _filter_args(params, b):
+    pr = params.row(b)
+    return dict(temperature=float(params.temperature[b]), top_k=int(params.top_k[b]),
+                top_p=float(params.top_p[b]), min_p=float(params.min_p[b]),
+                rep=pr["rep"], freq=pr["freq"], pres=pr["pres"], hist=pr["hist"],
+                bias_ids=pr["bias_ids"], bias_vals=pr["bias_vals"],
+                masks=None if params.mask is None else params.mask[b])
+
+
+def batch_rows(target, draft_tokens, params):
+    """filtered_rows() of every request of a batch (seed and position independent)."""
+    return [filtered_rows(target[b], draft_tokens[b], **_filter_args(params, b))
+            for b in range(target.shape[0])]
+
+
+def verify_batch(target, draft_probs, draft_tokens, params, rows=None):
+    """target [B, G+1, V] f32, draft_probs [B, G, V] f32, draft_tokens [B, G] int.
+    rows: batch_rows() of the same target, drafts and parameters, or None."""
     res = []
     for b in range(target.shape[0]):
         pr = params.row(b)
-        masks = None if params.mask is None else params.mask[b]
         res.append(verify_request(
-            target[b], draft_probs[b], draft_tokens[b],
-            temperature=float(params.temperature[b]), top_k=int(params.top_k[b]),
-            top_p=float(params.top_p[b]), min_p=float(params.min_p[b]),
-            rep=pr["rep"], freq=pr["freq"], pres=pr["pres"], hist=pr["hist"],
-            bias_ids=pr["bias_ids"], bias_vals=pr["bias_vals"], masks=masks,
-            seed=params.seed, request=pr["request"], position=pr["position"]))
+            target[b], draft_probs[b], draft_tokens[b], **_filter_args(params, b),
+            seed=params.seed, request=pr["request"], position=pr["position"],
+            rows=None if rows is None else rows[b]))
     return res

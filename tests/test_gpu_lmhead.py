@@ -4,7 +4,10 @@ Debug logits agree with the binary64 GEMM within 2e-3 relative (floor 1 near 0);
 tokens equal the oracle's Gumbel-max draws except rows whose top-two perturbed
 scores are within 1e-5 (flagged, counted). Small shapes (ragged vocabulary
 tile, partial batch) over many seeds, and the full configuration (B=64, K=8192,
-V=128256) over a few seeds."""
+V=128256) over 157 seeds (>= 10^4 draws)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -39,11 +42,16 @@ def run_case(B, K, V, seeds, temps, tally, check_logits=True, wl=None):
         err = np.abs(got - z) / np.maximum(1.0, np.abs(z))
         log(f"[lmhead {B}x{K}x{V}] max logit rel err {err.max():.3e}")
         assert err.max() <= 2e-3
+    outs = []
     for sd in seeds:
-        out = s.lmhead_sample(H, Wt, Td, reqd, posd, seed=sd)
-        torch.cuda.synchronize()
-        got = out.cpu().numpy()
-        want, flags = L.sample(z, T, req, pos, sd)
+        outs.append(s.lmhead_sample(H, Wt, Td, reqd, posd, seed=sd))
+    torch.cuda.synchronize()
+    got_all = [o.cpu().numpy() for o in outs]
+    # the oracle's Gumbel noise is numpy work that releases the GIL: seeds in
+    # threads (one fp64 z serves them all)
+    with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+        wants = list(ex.map(lambda sd: L.sample(z, T, req, pos, sd), seeds))
+    for sd, got, (want, flags) in zip(seeds, got_all, wants):
         for b in range(B):
             tally.add(int(got[b]) == int(want[b]), bool(flags[b]), (sd, b, int(got[b]), int(want[b])))
 
@@ -58,10 +66,12 @@ def test_small_shapes(B, K, V):
 
 
 def test_full_configuration():
+    """B = 64, K = 8192, V = 128256 over 157 seeds: >= 10^4 draws, so the flagged
+    share is held to 1e-4."""
     tally = Tally("lmhead full")
     wl = W.lmhead()
     log("[lmhead full] workload generated")
-    run_case(64, 8192, 128256, [0, 1, 2], np.ones(64, np.float32), tally, wl=wl)
+    run_case(64, 8192, 128256, list(range(157)), np.ones(64, np.float32), tally, wl=wl)
     tally.check()
 
 

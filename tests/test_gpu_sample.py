@@ -143,6 +143,37 @@ def test_high_entropy_rows_take_the_exact_fallback():
     tally.check()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_logits_at_low_temperature(dtype):
+    # logits near +50 at T = 0.7 put z near 71, where a binary32 step is 2^-17:
+    # the row normaliser must still be the sum of exp(z - zmax) over the row.
+    # Rows 0-3 are Zipf rows shifted by +50; rows 4-7 have a flat head (1000
+    # entries within 0.01 of the maximum) over an N(40, 1) body. No filter on
+    # rows 0-5, so the normaliser is the whole row's mass; top-p 0.9 / 0.5 on
+    # rows 6 and 7.
+    rng = np.random.default_rng(71)
+    B, V = 8, 128256
+    x = W.zipf_rows(rng, B, V) + np.float32(50.0)
+    for b in range(4, B):
+        x[b] = (40.0 + rng.standard_normal(V)).astype(np.float32)
+        head = rng.choice(V, 1000, replace=False)
+        x[b, head] = (50.0 + 0.01 * rng.standard_normal(1000)).astype(np.float32)
+    logits = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    w = W.SampleWorkload("shifted", logits, dtype, np.full(B, 0.7, np.float32),
+                         np.zeros(B, np.int32),
+                         np.array([1, 1, 1, 1, 1, 1, 0.9, 0.5], np.float32),
+                         np.zeros(B, np.float32), request_ids=np.arange(B, dtype=np.int32),
+                         positions=np.full(B, 9, np.int32), seed=17)
+    xs, filts = oracle_filtered(w)
+    s = make_sampler(B, V)
+    tally = Tally(f"shifted {dtype}", budget=False)
+    toks, dbg = run_debug(s, w)
+    compare_debug(w, xs, filts, toks, dbg, w.seed, tally)
+    log(f"[shifted {dtype}] paths {dbg.path.cpu().numpy().tolist()}")
+    seed_sweep(s, w, filts, range(100, 400), tally)
+    tally.check()
+
+
 def test_empty_batch_is_a_noop():
     s = make_sampler(4, 100)
     dev = device()
