@@ -70,6 +70,41 @@ def residual_draw(pi, q, u):
     return int(pos[i]), boundary_draw(cdf, u)
 
 
+def greedy_draft_probs(draft_tokens, V):
+    """The draft distributions of a draft model that takes its top token at every
+    step ("Accelerating Sonar through speculation", Perplexity blog, section on
+    target-draft decoding: the draft samples its top token): one-hot at each
+    draft token, [G, V] binary32. An id outside [0, V) gives an all-zero row.
+
+    With this q the general rule specialises to: accept d_j iff u < pi_j(d_j);
+    on rejection the residual max(0, pi_j - q_j) is pi_j with d_j removed."""
+    G = len(draft_tokens)
+    q = np.zeros((G, V), dtype=np.float32)
+    for j, d in enumerate(draft_tokens):
+        if 0 <= int(d) < V:
+            q[j, int(d)] = 1.0
+    return q
+
+
+def append_to_sequences(seq_tokens, seq_len, capacity, results):
+    """Device-side bookkeeping after verification (Perplexity blog, section on
+    single-token MTP scheduling: after acceptance a kernel places the next
+    target tokens into their slots, so no GPU-to-CPU synchronisation is needed).
+
+    Reading: each request's emitted tokens -- its accepted drafts, then its final
+    token -- are appended to its token sequence at its current length, and the
+    length advances by their number; slots at or beyond `capacity` are not
+    written and the length stops at `capacity`. seq_tokens [B, >= capacity] and
+    seq_len [B] are updated in place (numpy int32 arrays)."""
+    for b, r in enumerate(results):
+        n = r.n_acc + 1
+        L = int(seq_len[b])
+        for k in range(n):
+            if 0 <= L + k < capacity:
+                seq_tokens[b, L + k] = r.tokens[k]
+        seq_len[b] = min(L + n, capacity)
+
+
 def filtered_rows(target_rows, draft_tokens, *, temperature, top_k=0, top_p=1.0, min_p=0.0,
                   rep=1.0, freq=0.0, pres=0.0, hist=(), bias_ids=(), bias_vals=(), masks=None):
     """rows(j): target row j's filtered distribution, formed on first use.
@@ -97,7 +132,8 @@ def verify_request(target_rows, draft_probs, draft_tokens, *, temperature, top_k
                    top_p=1.0, min_p=0.0, rep=1.0, freq=0.0, pres=0.0, hist=(),
                    bias_ids=(), bias_vals=(), masks=None, seed=0, request=0, position=0,
                    uniform=None, rows=None):
-    """Verify one request's linear draft. target_rows: [G+1, V] float32.
+    """Verify one request's linear draft. target_rows: [G+1, V] float32;
+    draft_probs: [G, V] float32, or None for a greedy draft (greedy_draft_probs).
 
     uniform(domain, pos) -> u overrides the Philox uniforms (used by tests that
     integrate over the uniforms); by default u = u24 of the Philox word at
@@ -109,6 +145,8 @@ def verify_request(target_rows, draft_probs, draft_tokens, *, temperature, top_k
         def uniform(domain, pos):
             return philox.uniform(seed, request, pos, 0, domain)
     G = len(draft_tokens)
+    if draft_probs is None:
+        draft_probs = greedy_draft_probs(draft_tokens, target_rows.shape[1])
     out = np.full(G + 1, -1, dtype=np.int32)
     flagged = False
     ratios = []
@@ -174,13 +212,15 @@ def batch_rows(target, draft_tokens, params):
 
 
 def verify_batch(target, draft_probs, draft_tokens, params, rows=None):
-    """target [B, G+1, V] f32, draft_probs [B, G, V] f32, draft_tokens [B, G] int.
-    rows: batch_rows() of the same target, drafts and parameters, or None."""
+    """target [B, G+1, V] f32, draft_probs [B, G, V] f32 (None: greedy drafts),
+    draft_tokens [B, G] int. rows: batch_rows() of the same target, drafts and
+    parameters, or None."""
     res = []
     for b in range(target.shape[0]):
         pr = params.row(b)
         res.append(verify_request(
-            target[b], draft_probs[b], draft_tokens[b], **_filter_args(params, b),
+            target[b], None if draft_probs is None else draft_probs[b], draft_tokens[b],
+            **_filter_args(params, b),
             seed=params.seed, request=pr["request"], position=pr["position"],
             rows=None if rows is None else rows[b]))
     return res

@@ -145,3 +145,72 @@ def test_draft_prefix_enters_penalty_history():
     q = np.full((2, V), 0.1, np.float32)
     r = call(target, q, [4, 4], T=1.0, freq=100.0, uni=lambda dom, pos: 0.5)
     assert r.n_acc == 1 and r.tokens[0] == 4 and r.tokens[1] != 4
+
+
+# --- greedy drafts (q one-hot at the draft token) -----------------------------
+
+def test_greedy_draft_closed_form():
+    # equal 4-token row: pi = 1/4 each. Draft d = 1 with one-hot q: accept iff
+    # u < pi(1) = 1/4; on rejection the residual is pi without token 1, i.e.
+    # 1/3 on each of tokens 0, 2, 3 in id order (breakpoints 1/3, 2/3)
+    target = np.zeros((2, 4), np.float32)
+
+    def run(ua, ur):
+        def uni(dom, pos):
+            return {philox.ACCEPT: ua, philox.RESIDUAL: ur}.get(dom, 0.1)
+        return call(target, None, [1], uni=uni)
+
+    r = run(0.24, 0.5)
+    assert r.n_acc == 1 and r.tokens[0] == 1
+    assert r.accept_ratios == [0.25]
+    for ur, tok in ((0.2, 0), (0.34, 2), (0.5, 2), (0.67, 3), (0.99, 3)):
+        r = run(0.26, ur)
+        assert r.n_acc == 0 and r.tokens[0] == tok, (ur, r.tokens)
+        assert r.tokens[1] == -1
+
+
+def test_greedy_draft_first_token_follows_target():
+    # the rejection rule's law holds for any q, one-hot included: integrate the
+    # first emitted token over the uniforms for each possible draft token
+    rng = np.random.default_rng(6)
+    V = 5
+    target = (rng.standard_normal((2, V)) * 1.5).astype(np.float32)
+    pi = pi_of(target[0])
+    for d in range(V):
+        # acceptance share over the accept uniform, then the law of the
+        # residual token over the residual uniform given a rejection
+        acc = sum(call(target, None, [d], uni=lambda dom, pos, ua=ua:
+                       ua if dom == philox.ACCEPT else 0.5).n_acc for ua in GRID) / N_GRID
+        rho = np.zeros(V)
+        for ur in GRID:
+            r = call(target, None, [d], uni=lambda dom, pos, ur=ur:
+                     1.0 - 2.0 ** -24 if dom == philox.ACCEPT else ur)
+            if r.n_acc == 0:
+                rho[r.tokens[0]] += 1
+        law = acc * np.eye(V)[d]
+        if rho.sum() > 0:
+            law += (1.0 - acc) * rho / rho.sum()
+        assert np.abs(law - pi).max() < 6.0 / N_GRID, (d, law, pi)
+
+
+def test_greedy_draft_probs_shape_and_out_of_range_ids():
+    q = S.greedy_draft_probs([2, -1, 7], 5)
+    assert q.dtype == np.float32 and q.shape == (3, 5)
+    assert q[0].tolist() == [0, 0, 1, 0, 0]
+    assert not q[1].any() and not q[2].any()
+
+
+def test_append_to_sequences():
+    seq = np.full((3, 6), -9, np.int32)
+    ln = np.array([1, 4, 6], np.int32)
+    res = [S.SpecResult(np.array([5, 6, 7], np.int32), 2, False, []),
+           S.SpecResult(np.array([8, 9, -1], np.int32), 1, False, []),
+           S.SpecResult(np.array([3, -1, -1], np.int32), 0, False, [])]
+    S.append_to_sequences(seq, ln, 6, res)
+    assert seq[0].tolist() == [-9, 5, 6, 7, -9, -9] and ln[0] == 4
+    assert seq[1].tolist() == [-9, -9, -9, -9, 8, 9] and ln[1] == 6
+    assert seq[2].tolist() == [-9] * 6 and ln[2] == 6  # full: nothing written
+    ln2 = np.array([5], np.int32)
+    seq2 = np.zeros((1, 6), np.int32)
+    S.append_to_sequences(seq2, ln2, 6, res[:1])  # only one slot left
+    assert seq2[0].tolist() == [0, 0, 0, 0, 0, 5] and ln2[0] == 6
