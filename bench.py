@@ -371,6 +371,30 @@ def secondary(args, dev):
                           "roofline": dict(fraction(nbytes_all, ms / steps * 1e-3),
                                            kernel=dict(name="k_spec_tiles<f32>",
                                                        **fraction(nbytes, t_us * 1e-6)))}
+    # the same verification with greedy drafts (q one-hot, no draft rows read),
+    # the emitted tokens appended to device-side sequences (positions = lengths)
+    swg = W.speculative(greedy_draft=True)
+    dg = torch.from_numpy(swg.draft_tokens).to(dev)
+    seq_t = torch.zeros(sw.B, 1 << 16, dtype=torch.int32, device=dev)
+    seq_l = torch.zeros(sw.B, dtype=torch.int32, device=dev)
+    spg = SamplingParams(temperature=sp.temperature, request_ids=sp.request_ids, positions=seq_l,
+                         seed=sw.seed)
+    gfns = [(lambda t=tgs[r]: s.spec_verify(t, None, dg, spg, ot, on, seq_tokens=seq_t,
+                                            seq_len=seq_l)) for r in range(R)]
+    gfns[0]()
+    torch.cuda.synchronize()
+    g_emitted = int((on + 1).sum().item())
+    seq_l.zero_()
+    ms, _ = time_graph(gfns, steps, 5)
+    st = stage_summary(time_stages(s, gfns, steps, 4),
+                       ["k_spec_tiles<f32>", "k_spec_rows<f32>", "k_spec_resid_tiles<f32>",
+                        "k_spec_finish<f32>"])
+    gbytes = nbytes + swg.B * swg.G * 4 + swg.B * (swg.G + 2) * 4
+    out["speculative_greedy_draft"] = {
+        "us_per_call": ms / steps * 1e3, "stages": st, "emitted_tokens_per_call": g_emitted,
+        "emitted_tokens_per_s": g_emitted * steps / (ms * 1e-3), "bytes": gbytes,
+        "roofline": fraction(gbytes, ms / steps * 1e-3),
+        "note": "no draft rows read; emitted tokens appended on the device"}
     s.close()
     del tgs
     # fused LM-head + Gumbel-max, hidden [64, 8192] x weight [128256, 8192] bf16

@@ -175,7 +175,12 @@ ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t r
 /* ss_spec_verify -- verify a linear draft of G tokens per request.
  *   target_logits [B, G+1, row_stride] of dtype: target logits at the G draft
  *                 positions and the bonus position (same layout rules as above).
- *   draft_probs   [B, G, draft_stride] float32 draft probabilities (draft_stride >= V).
+ *   draft_probs   [B, G, draft_stride] float32 draft probabilities (draft_stride >= V),
+ *                 or NULL for a greedy draft, one that takes its top token at every
+ *                 step ("Accelerating Sonar through speculation", target-draft
+ *                 section): q is then one-hot at each draft token, so draft j is
+ *                 accepted iff u < p(d_j) and a rejection resamples from p with d_j
+ *                 removed; no draft row is read (draft_stride is ignored).
  *   draft_tokens  [B, G] int32 draft tokens.
  *   B, G          0 .. max_batch, 1 .. max_draft.
  *   out_tokens    [B, G+1] int32: accepted drafts, then the final (corrected or
@@ -192,13 +197,44 @@ ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t r
  * accept tests, the residual tile sums and the per-request finish (the last
  * two only do work for rejected requests). */
 /* Errors: as ss_sample, plus SS_ERR_INVALID_ARG for G outside 1 .. max_draft,
- * null draft_probs / draft_tokens / out_tokens / out_num_accepted, or
+ * null draft_tokens / out_tokens / out_num_accepted, or draft_probs given with
  * draft_stride < V. */
 ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtype,
                          int64_t row_stride, const float* draft_probs, int64_t draft_stride,
                          const int32_t* draft_tokens, int32_t B, int32_t G,
                          const ss_params* params, int32_t* out_tokens,
                          int32_t* out_num_accepted, void* stream);
+
+/* Per-request token sequences kept on the device (all pointers device). */
+typedef struct {
+    int32_t* tokens;   /* [B, stride] int32: request b's tokens, slots 0 .. capacity-1 */
+    int64_t stride;    /* >= capacity */
+    int32_t capacity;  /* slots per request, >= 0 */
+    int32_t* len;      /* [B] int32: tokens already in each sequence, 0 .. capacity;
+                          read and advanced in place */
+} ss_sequences;
+
+/* ss_spec_verify_scatter -- ss_spec_verify, then the emitted tokens placed into
+ * the request sequences on the device ("Accelerating Sonar through
+ * speculation", section on single-token MTP scheduling: after acceptance a
+ * kernel puts the next target tokens into their slots, so no GPU-to-CPU
+ * synchronisation follows acceptance). Request b's accepted drafts and final
+ * token, out_tokens[b, 0 .. n_b], go to seq->tokens[b, len_b .. len_b + n_b]
+ * and len_b becomes len_b + n_b + 1; slots at or beyond capacity are not
+ * written and len_b stops at capacity (keep capacity >= len_b + G + 1 to lose
+ * nothing). params->positions may be seq->len itself: every read of a
+ * request's position precedes its length update, so consecutive calls on one
+ * stream advance the Philox positions with the sequences, and nothing needs
+ * to be read back between steps. Same kernels as ss_spec_verify (the append is
+ * part of the last launch); seq = NULL is ss_spec_verify.
+ * Errors: as ss_spec_verify, plus SS_ERR_INVALID_ARG for a seq with null
+ * tokens or len, capacity < 0 or stride < capacity. */
+ss_status ss_spec_verify_scatter(ss_sampler* s, const void* target_logits, ss_dtype dtype,
+                                 int64_t row_stride, const float* draft_probs,
+                                 int64_t draft_stride, const int32_t* draft_tokens, int32_t B,
+                                 int32_t G, const ss_params* params, int32_t* out_tokens,
+                                 int32_t* out_num_accepted, const ss_sequences* seq,
+                                 void* stream);
 
 /* ss_lmhead_sample -- fused LM-head GEMM + Gumbel-max sampling.
  *   hidden        [B, K] bfloat16 bits (row-major), 16-byte aligned.

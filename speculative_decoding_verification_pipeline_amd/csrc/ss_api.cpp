@@ -377,11 +377,24 @@ ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
                          const int32_t* draft_tokens, int32_t B, int32_t G,
                          const ss_params* params, int32_t* out_tokens,
                          int32_t* out_num_accepted, void* stream) {
+    return ss_spec_verify_scatter(s, target_logits, dtype, row_stride, draft_probs, draft_stride,
+                                  draft_tokens, B, G, params, out_tokens, out_num_accepted,
+                                  nullptr, stream);
+}
+
+ss_status ss_spec_verify_scatter(ss_sampler* s, const void* target_logits, ss_dtype dtype,
+                                 int64_t row_stride, const float* draft_probs,
+                                 int64_t draft_stride, const int32_t* draft_tokens, int32_t B,
+                                 int32_t G, const ss_params* params, int32_t* out_tokens,
+                                 int32_t* out_num_accepted, const ss_sequences* seq,
+                                 void* stream) {
     if (!s || B < 0 || B > s->cfg.max_batch) return SS_ERR_INVALID_ARG;
     if (G < 1 || G > s->cfg.max_draft) return SS_ERR_INVALID_ARG;
     if (B == 0) return SS_OK;
-    if (!draft_probs || !draft_tokens || !out_tokens || !out_num_accepted) return SS_ERR_INVALID_ARG;
-    if (draft_stride < s->cfg.vocab_size) return SS_ERR_INVALID_ARG;
+    if (!draft_tokens || !out_tokens || !out_num_accepted) return SS_ERR_INVALID_ARG;
+    if (draft_probs && draft_stride < s->cfg.vocab_size) return SS_ERR_INVALID_ARG;
+    if (seq && (!seq->tokens || !seq->len || seq->capacity < 0 || seq->stride < seq->capacity))
+        return SS_ERR_INVALID_ARG;
     ss_status st = check_logits(s->cfg.vocab_size, target_logits, dtype, row_stride);
     if (st != SS_OK) return st;
     st = check_params(s->cfg.vocab_size, params);
@@ -391,7 +404,7 @@ ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
     a.target = target_logits;
     a.row_stride = row_stride;
     a.draft_probs = draft_probs;
-    a.draft_stride = draft_stride;
+    a.draft_stride = draft_probs ? draft_stride : 0;
     a.draft_tokens = draft_tokens;
     a.B = B;
     a.G = G;
@@ -399,6 +412,12 @@ ss_status ss_spec_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
     a.p = to_ptrs(defaults_of(s), params);
     a.out_tokens = out_tokens;
     a.out_num_accepted = out_num_accepted;
+    if (seq) {
+        a.seq_tokens = seq->tokens;
+        a.seq_stride = seq->stride;
+        a.seq_capacity = seq->capacity;
+        a.seq_len = seq->len;
+    }
     a.ws = s->ws;
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
     return ss::launch_spec(a, dtype, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK

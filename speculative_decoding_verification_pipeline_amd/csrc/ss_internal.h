@@ -108,7 +108,7 @@ struct SampleArgs {
 struct SpecArgs {
     const void* target;
     int64_t row_stride;
-    const float* draft_probs;
+    const float* draft_probs;  // null: greedy draft, q one-hot at the draft token
     int64_t draft_stride;
     const int32_t* draft_tokens;
     int B;
@@ -117,6 +117,10 @@ struct SpecArgs {
     ParamPtrs p;
     int32_t* out_tokens;
     int32_t* out_num_accepted;
+    int32_t* seq_tokens;       // null: no append to the request sequences
+    int64_t seq_stride;
+    int32_t seq_capacity;
+    int32_t* seq_len;
     Workspace ws;
 };
 

@@ -1598,7 +1598,10 @@ __global__ __launch_bounds__(NTR) void k_spec_rows(SpecArgs a) {
                 const bool kept = key64(zd, d) >= info.kappa && (info.min_p <= 0.0f || w >= info.min_p);
                 if (kept) pi = (double)w / info.W;
             }
-            const double q = (double)a.draft_probs[((size_t)b * a.G + j) * a.draft_stride + d];
+            // a greedy draft puts all its mass on d
+            const double q = a.draft_probs
+                                 ? (double)a.draft_probs[((size_t)b * a.G + j) * a.draft_stride + d]
+                                 : 1.0;
             const float ua = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_ACCEPT));
             acc = q > 0.0 ? ((double)ua < pi / q ? 1 : 0) : (pi > 0.0 ? 1 : 0);
         }
@@ -1635,8 +1638,14 @@ __device__ __forceinline__ float filtered_prob(const RowCtx& c, const RowInfo& r
 
 // Residual mass of one tile of a rejected row: r = max(0, pi - q) per entry (or
 // pi itself when use_pi), in token-id order within each thread group.
+// q(id) of the draft distribution at a rejected position: the draft row, or
+// for a greedy draft (q null) one at the draft token d and zero elsewhere.
+__device__ __forceinline__ float draft_q(const float* q, int id, int d) {
+    return q ? gld(q + id) : (id == d ? 1.0f : 0.0f);
+}
+
 template <int DT>
-__device__ void residual_values(const RowCtx& c, const RowInfo& ri, const float* q, int tb,
+__device__ void residual_values(const RowCtx& c, const RowInfo& ri, const float* q, int d, int tb,
                                 bool use_pi, SmemTile& tt, double r[EPT]) {
     float v[EPT];
     uint32_t mw[Lay<DT>::NG];
@@ -1652,7 +1661,7 @@ __device__ void residual_values(const RowCtx& c, const RowInfo& ri, const float*
         double val = 0.0;
         if (id < c.V) {
             const float pi = filtered_prob(c, ri, id, v[s]);
-            val = use_pi ? (double)pi : (double)fmaxf(0.0f, pi - gld(q + id));
+            val = use_pi ? (double)pi : (double)fmaxf(0.0f, pi - draft_q(q, id, d));
         }
         r[s] = val;
     }
@@ -1671,7 +1680,8 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a)
     const int j = residual_position(a, b, ri);
     if (j < 0) return;
     const RowCtx c = spec_ctx<DT>(a, b, j);
-    const float* q = a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride;
+    const float* q = a.draft_probs ? a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride : nullptr;
+    const int d = a.draft_tokens[(size_t)b * a.G + j];
     const int tb = tile * TILE;
     float v[EPT];
     uint32_t mw[Lay<DT>::NG];
@@ -1687,7 +1697,7 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a)
         const int id = slot_id<DT>(tb, s);
         if (id < c.V) {
             const float pi = filtered_prob(c, ri, id, v[s]);
-            sr += (double)fmaxf(0.0f, pi - gld(q + id));
+            sr += (double)fmaxf(0.0f, pi - draft_q(q, id, d));
             sp += (double)pi;
         }
     }
@@ -1696,32 +1706,16 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a)
     if (threadIdx.x == 0) a.ws.resid_tile[(size_t)b * n_tiles + tile] = make_double2(sr, sp);
 }
 
-// Verification, per request: the output row. Accepted drafts, then the bonus
-// token, the greedy target token, or a draw from the residual distribution in
-// token-id order (tile by the per-tile sums, then the entry within the tile).
+// The token of rejected position j of request b: a draw from the residual
+// distribution in token-id order (tile by the per-tile sums, then the entry
+// within the tile). Called by the whole workgroup.
 template <int DT>
-__global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
-    __shared__ SmemTile tt;
-    __shared__ SmemS sh;
-    __shared__ int s_tile;
-    __shared__ int s_usepi;
-    __shared__ double s_rem;
+__device__ int residual_token(const SpecArgs& a, int b, int j, const RowInfo& ri, SmemTile& tt,
+                              SmemS& sh, int& s_tile, int& s_usepi, double& s_rem) {
     const int n_tiles = a.ws.n_tiles;
-    const int b = blockIdx.x;
-    const int G1 = a.G + 1;
-    const int n = accepted_prefix(a, b);
-    RowInfo ri;
-    const int j = residual_position(a, b, ri);
-    int32_t* out = a.out_tokens + (size_t)b * G1;
-    if (threadIdx.x == 0) {
-        for (int k = 0; k < n; ++k) out[k] = a.draft_tokens[(size_t)b * a.G + k];
-        for (int k = n + 1; k < G1; ++k) out[k] = -1;
-        a.out_num_accepted[b] = n;
-        if (j < 0) out[n] = n == a.G ? ri.token : ri.argmax;
-    }
-    if (j < 0) return;
     const RowCtx c = spec_ctx<DT>(a, b, j);
-    const float* q = a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride;
+    const float* q = a.draft_probs ? a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride : nullptr;
+    const int d = a.draft_tokens[(size_t)b * a.G + j];
     if (threadIdx.x == 0) {
         double R = 0.0, P = 0.0;
         for (int t = 0; t < n_tiles; ++t) {
@@ -1759,7 +1753,7 @@ __global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
     int token = -1;
     if (st >= 0) {
         double r[EPT];
-        residual_values<DT>(c, ri, q, st * TILE, s_usepi != 0, tt, r);
+        residual_values<DT>(c, ri, q, d, st * TILE, s_usepi != 0, tt, r);
         using L = Lay<DT>;
         double carry = 0.0;
         int found = INT_MAX, lastpos = -1;
@@ -1788,8 +1782,55 @@ __global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
         lastpos = -block_min_i(-lastpos, sh.red);
         token = found != INT_MAX ? found : lastpos;
     }
-    if (threadIdx.x == 0) out[j] = token;
+    return token;
 }
+
+// Verification, per request: the output row (accepted drafts, then the bonus
+// token, the greedy target token, or the residual draw) and, when the caller
+// keeps per-request token sequences on the device, their append: the emitted
+// tokens go into the slots after each sequence's length, which then advances,
+// so the host need not read the accepted counts before the next step.
+template <int DT>
+__global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
+    __shared__ SmemTile tt;
+    __shared__ SmemS sh;
+    __shared__ int s_tile;
+    __shared__ int s_usepi;
+    __shared__ double s_rem;
+    const int b = blockIdx.x;
+    const int G1 = a.G + 1;
+    const int n = accepted_prefix(a, b);
+    RowInfo ri;
+    const int j = residual_position(a, b, ri);
+    int32_t* out = a.out_tokens + (size_t)b * G1;
+    int final_token = n == a.G ? ri.token : ri.argmax;
+    if (threadIdx.x == 0) {
+        for (int k = 0; k < n; ++k) out[k] = a.draft_tokens[(size_t)b * a.G + k];
+        for (int k = n + 1; k < G1; ++k) out[k] = -1;
+        a.out_num_accepted[b] = n;
+        if (j < 0) out[n] = final_token;
+    }
+    if (j >= 0) {  // uniform over the workgroup
+        final_token = residual_token<DT>(a, b, j, ri, tt, sh, s_tile, s_usepi, s_rem);
+        if (threadIdx.x == 0) out[j] = final_token;
+    }
+    if (a.seq_tokens) {
+        // every read of this request's parameters (its position may be the
+        // length array itself) precedes the length update
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int32_t* seq = a.seq_tokens + (size_t)b * a.seq_stride;
+            const int L = a.seq_len[b];
+            for (int k = 0; k <= n; ++k) {
+                const int slot = L + k;
+                if (slot >= 0 && slot < a.seq_capacity)
+                    seq[slot] = k < n ? a.draft_tokens[(size_t)b * a.G + k] : final_token;
+            }
+            a.seq_len[b] = min(L + n + 1, a.seq_capacity);
+        }
+    }
+}
+
 
 // ---------------------------------------------------------------------------
 // launchers

@@ -26,7 +26,7 @@ SS_BF16 = 1
 
 EXPORTED = ("ss_sampler_create", "ss_sampler_destroy", "ss_status_string",
             "ss_sampler_workspace_bytes", "ss_sampler_set_launch_events", "ss_sample",
-            "ss_spec_verify", "ss_lmhead_sample", "ss_sample_noalloc")
+            "ss_spec_verify", "ss_spec_verify_scatter", "ss_lmhead_sample", "ss_sample_noalloc")
 NOALLOC_MAX_BATCH = 64
 NOALLOC_MAX_ENTRIES = 1 << 23
 
@@ -54,6 +54,11 @@ class CDebug(ctypes.Structure):
     _fields_ = [("processed_logits", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p),
                 ("topk_stride", ctypes.c_int32), ("kept_count", ctypes.c_void_p),
                 ("probs", ctypes.c_void_p), ("path", ctypes.c_void_p)]
+
+
+class CSequences(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_void_p), ("stride", ctypes.c_int64),
+                ("capacity", ctypes.c_int32), ("len", ctypes.c_void_p)]
 
 
 class SamplerError(RuntimeError):
@@ -91,6 +96,10 @@ def load_library(path=None):
     lib.ss_spec_verify.argtypes = [vp, vp, i32, i64, vp, i64, vp, i32, i32,
                                    ctypes.POINTER(CParams), vp, vp, vp]
     lib.ss_spec_verify.restype = i32
+    lib.ss_spec_verify_scatter.argtypes = [vp, vp, i32, i64, vp, i64, vp, i32, i32,
+                                           ctypes.POINTER(CParams), vp, vp,
+                                           ctypes.POINTER(CSequences), vp]
+    lib.ss_spec_verify_scatter.restype = i32
     lib.ss_lmhead_sample.argtypes = [vp, vp, vp, i32, vp, vp, vp, u64, vp, vp, vp]
     lib.ss_lmhead_sample.restype = i32
     lib.ss_sample_noalloc.argtypes = [vp, i32, i64, i32, i32, ctypes.POINTER(CParams), vp, vp]
@@ -333,7 +342,12 @@ class Sampler:
         return out
 
     def spec_verify(self, target_logits, draft_probs, draft_tokens, params: SamplingParams,
-                    out_tokens=None, out_num_accepted=None, stream=None):
+                    out_tokens=None, out_num_accepted=None, stream=None, seq_tokens=None,
+                    seq_len=None):
+        """draft_probs None: a greedy draft (q one-hot at each draft token).
+        seq_tokens [B, capacity] / seq_len [B] int32: append the emitted tokens
+        to these per-request sequences on the device and advance seq_len
+        (params.positions may be seq_len itself)."""
         _check_dev(target_logits, "target_logits", (torch.float32, torch.bfloat16), self.device)
         _require(target_logits.dim() == 3, "target_logits must be [B, G+1, V]")
         B, G1, V = target_logits.shape
@@ -343,11 +357,13 @@ class Sampler:
         _require(target_logits.stride(2) == 1 and
                  (B <= 1 or target_logits.stride(0) == G1 * target_logits.stride(1)),
                  "target_logits rows must be evenly spaced with unit stride along V")
-        _check_dev(draft_probs, "draft_probs", (torch.float32,), self.device)
-        _require(draft_probs.dim() == 3 and tuple(draft_probs.shape) == (B, G, V) and
-                 draft_probs.stride(2) == 1 and
-                 (B <= 1 or draft_probs.stride(0) == G * draft_probs.stride(1)),
-                 "draft_probs must be [B, G, V] with evenly spaced rows and unit stride along V")
+        if draft_probs is not None:
+            _check_dev(draft_probs, "draft_probs", (torch.float32,), self.device)
+            _require(draft_probs.dim() == 3 and tuple(draft_probs.shape) == (B, G, V) and
+                     draft_probs.stride(2) == 1 and
+                     (B <= 1 or draft_probs.stride(0) == G * draft_probs.stride(1)),
+                     "draft_probs must be [B, G, V] with evenly spaced rows and unit stride "
+                     "along V")
         _check_dev(draft_tokens, "draft_tokens", (torch.int32,), self.device)
         _require(tuple(draft_tokens.shape) == (B, G) and draft_tokens.is_contiguous(),
                  "draft_tokens must be a contiguous [B, G] int32 array")
@@ -361,12 +377,21 @@ class Sampler:
                  "out_tokens must be a contiguous [B, G+1] int32 array")
         _check_vec(out_num_accepted, "out_num_accepted", B, torch.int32, self.device)
         cp = params.to_c(params.validate(B, V, self.device, mask_rows=G1))
-        st = self.lib.ss_spec_verify(self.handle, _ptr(target_logits), self._dtype(target_logits),
-                                     int(target_logits.stride(1)), _ptr(draft_probs),
-                                     int(draft_probs.stride(1)), _ptr(draft_tokens), B, G,
-                                     ctypes.byref(cp), _ptr(out_tokens), _ptr(out_num_accepted),
-                                     _stream(stream))
-        _check("ss_spec_verify", st)
+        seq = None
+        if seq_tokens is not None or seq_len is not None:
+            _require(seq_tokens is not None and seq_len is not None,
+                     "seq_tokens and seq_len go together")
+            _check_rows(seq_tokens, "seq_tokens", B, (torch.int32,), self.device)
+            _check_vec(seq_len, "seq_len", B, torch.int32, self.device)
+            seq = CSequences(_ptr(seq_tokens), int(seq_tokens.stride(0)) if B > 1 else
+                             int(seq_tokens.shape[1]), int(seq_tokens.shape[1]), _ptr(seq_len))
+        dstride = 0 if draft_probs is None else int(draft_probs.stride(1))
+        st = self.lib.ss_spec_verify_scatter(
+            self.handle, _ptr(target_logits), self._dtype(target_logits),
+            int(target_logits.stride(1)), _ptr(draft_probs), dstride, _ptr(draft_tokens), B, G,
+            ctypes.byref(cp), _ptr(out_tokens), _ptr(out_num_accepted),
+            ctypes.byref(seq) if seq is not None else None, _stream(stream))
+        _check("ss_spec_verify_scatter", st)
         return out_tokens, out_num_accepted
 
     def lmhead_sample(self, hidden, weight, temperature, request_ids=None, positions=None,

@@ -21,8 +21,9 @@ Recipes (all numpy PCG64 generators; data seeds 101..105 are fixed here):
   speculative     B=32, G=4, V=128256. Target [32, 5, V] Zipf float32; draft
                   logits = target[:, :4] + N(0, 0.5); draft probabilities =
                   softmax of the draft logits (binary64, stored float32); draft
-                  tokens drawn from them with numpy's generator; 16 requests
-                  greedy (T=0), the others T=1 with no filters.
+                  tokens drawn from them with numpy's generator (or, for a
+                  greedy draft, each draft row's argmax); 16 requests greedy
+                  (T=0), the others T=1 with no filters.
   lmhead          hidden [64, 8192] bf16 from N(0,1); weight [128256, 8192] bf16
                   from N(0, 0.02^2); T=1.0.
 """
@@ -176,7 +177,8 @@ class SpecWorkload:
         return self.target.shape[2]
 
 
-def speculative(B=32, G=4, V=128256, seed=104, draft_seed=1, n_greedy=None):
+def speculative(B=32, G=4, V=128256, seed=104, draft_seed=1, n_greedy=None,
+                greedy_draft=False):
     rng = np.random.default_rng(seed)
     target = zipf_rows(rng, B * (G + 1), V).reshape(B, G + 1, V)
     draft = target[:, :G].astype(np.float64) + rng.normal(0.0, 0.5, (B, G, V))
@@ -188,6 +190,9 @@ def speculative(B=32, G=4, V=128256, seed=104, draft_seed=1, n_greedy=None):
     toks = np.empty((B, G), dtype=np.int32)
     for b in range(B):
         for j in range(G):
+            if greedy_draft:  # the draft takes its top token
+                toks[b, j] = int(np.argmax(draft[b, j]))
+                continue
             c = np.cumsum(q[b, j])
             toks[b, j] = min(int(np.searchsorted(c, drng.random() * c[-1], side="right")), V - 1)
     n_greedy = B // 2 if n_greedy is None else n_greedy

@@ -127,21 +127,38 @@ def test_spec_verify_rejects_bad_arguments(live):
     na = torch.empty(B, dtype=torch.int32, device=device())
     p = SM.SamplingParams(temperature=_temps(1.0)).to_c()
 
-    def call(g=G, draft_stride=V, row_stride=V, rows=B, q_ptr=True, na_ptr=True):
-        return live.lib.ss_spec_verify(live.handle, _vp(tgt), SM.SS_F32, row_stride,
-                                       _vp(q) if q_ptr else None, draft_stride, _vp(d), rows, g,
-                                       ctypes.byref(p), _vp(out), _vp(na) if na_ptr else None,
-                                       None)
+    seq_t = torch.zeros(B, 16, dtype=torch.int32, device=device())
+    seq_l = torch.zeros(B, dtype=torch.int32, device=device())
+
+    def seqs(stride=16, capacity=16, tokens=True, length=True):
+        return SM.CSequences(_vp(seq_t) if tokens else None, stride, capacity,
+                             _vp(seq_l) if length else None)
+
+    def call(g=G, draft_stride=V, row_stride=V, rows=B, q_ptr=True, na_ptr=True, d_ptr=True,
+             seq=None):
+        return live.lib.ss_spec_verify_scatter(
+            live.handle, _vp(tgt), SM.SS_F32, row_stride, _vp(q) if q_ptr else None, draft_stride,
+            _vp(d) if d_ptr else None, rows, g, ctypes.byref(p), _vp(out),
+            _vp(na) if na_ptr else None, ctypes.byref(seq) if seq is not None else None, None)
 
     assert call() == SM.SS_OK
+    assert call(q_ptr=False, draft_stride=0) == SM.SS_OK  # a greedy draft reads no draft rows
+    assert call(seq=seqs()) == SM.SS_OK
     bad = {"G above max_draft": dict(g=G + 1), "G zero": dict(g=0),
            "draft stride below V": dict(draft_stride=V - 1),
            "target row stride below V": dict(row_stride=V - 1),
-           "batch above max_batch": dict(rows=B + 1), "null draft_probs": dict(q_ptr=False),
-           "null out_num_accepted": dict(na_ptr=False)}
+           "batch above max_batch": dict(rows=B + 1), "null draft_tokens": dict(d_ptr=False),
+           "null out_num_accepted": dict(na_ptr=False),
+           "sequence stride below capacity": dict(seq=seqs(stride=8)),
+           "negative capacity": dict(seq=seqs(capacity=-1)),
+           "null sequence tokens": dict(seq=seqs(tokens=False)),
+           "null sequence lengths": dict(seq=seqs(length=False))}
     for name, kw in bad.items():
-        log(f"abi: ss_spec_verify with {name}")
+        log(f"abi: ss_spec_verify_scatter with {name}")
         assert call(**kw) == SM.SS_ERR_INVALID_ARG, name
+    assert live.lib.ss_spec_verify(live.handle, _vp(tgt), SM.SS_F32, V, _vp(q), V - 1, _vp(d), B,
+                                   G, ctypes.byref(p), _vp(out), _vp(na), None) == \
+        SM.SS_ERR_INVALID_ARG
 
 
 def test_lmhead_rejects_bad_arguments(live):
