@@ -44,6 +44,7 @@
 namespace ss {
 
 constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr int NTR_MAX = 1024;  // largest workgroup of the row kernels
 constexpr double MASS_SCALE = 17592186044416.0;  // 2^44 fixed-point weights in the fallback
 // Widest candidate window below a wave tile's maximum, in units of z = x' / T:
 // on the wave holding the row maximum it keeps every entry weighing more than
@@ -139,9 +140,9 @@ struct SmemTile {
     unsigned long long wl[WPT][WCAP];  // per wave: its candidates (x' bits, id) in slot order
 };
 
-// The row merge runs one 256-thread workgroup per row: one wave per SIMD, so
-// the per-row bookkeeping every wave repeats costs one issue slot per SIMD.
-constexpr int NTR = 1024;
+// The row merge runs one 1024-thread workgroup per row (16 waves): the
+// candidate loads, the pool compaction and the sort spread over all of them.
+constexpr int NTR = NTR_MAX;
 constexpr int NWR = NTR / WAVE;                // waves of the merge workgroup
 constexpr int MSLOT = MAX_WT * WCAP / NTR;     // candidate slots per merge thread
 constexpr int POOL = 4096;                     // largest pool the merge sorts
@@ -177,10 +178,49 @@ struct SmemRadix {
     unsigned long long hm[256];
 };
 
+// Whole-row selection by buckets of d = zmax - z (HB buckets of width 1/HSCALE
+// over d in [0, HB / HSCALE), one more for everything deeper): per-bucket
+// counts and fixed-point masses, then the one bucket that holds the answer.
+constexpr int HB = 4096;
+constexpr float HSCALE = 128.0f;
+constexpr int HCAP = 2048;  // largest bucket resolved in LDS (else the radix passes)
+
+struct SmemHist {
+    uint32_t hc[HB + 1];
+    unsigned long long hm[HB + 1];
+};
+
+struct SmemBucket {
+    unsigned long long key[HCAP];
+    unsigned long long wq[HCAP];
+};
+
+struct SmemHistState {
+    unsigned long long wsum[NTR_MAX / WAVE];
+    unsigned long long cum;     // count or mass of the buckets before the selected one
+    unsigned long long target;
+    unsigned long long key;
+    unsigned long long total_mass;
+    int total_count;
+    int sel;                    // selected bucket (INT_MAX: none crosses)
+    int lastnz;                 // deepest non-empty bucket
+    int n;                      // entries collected from the selected bucket
+};
+
+constexpr int SU = 8;            // entries per thread in flight in the fallback's passes
+constexpr int LIST_CAP = 8192;  // history + draft + bias ids staged in LDS by the fallback
+
+struct SmemList {
+    int32_t ids[LIST_CAP];
+};
+
 union SmemU {
     SmemTile t;
     SmemPool p;
     SmemRadix r;
+    SmemHist h;
+    SmemBucket k;
+    SmemList l;
 };
 
 template <int NB>
@@ -192,6 +232,7 @@ struct SmemST {
     int sel;
     int take_last;
     unsigned long long rem;
+    SmemHistState hs;
 };
 using SmemS = SmemST<NT>;   // tile workgroups
 using SmemR = SmemST<NTR>;  // row-merge workgroups
@@ -855,6 +896,7 @@ struct RowView {
     float zb;      // the pool is every candidate with z > zb (-inf: every finite entry)
     float zlo;     // a lower bound of the pool's z
     double W;      // the row mass: candidates, WS_SUM tiles whole, WS_APX non-candidates
+    double Wc;     // the candidates' mass: at least the pool's
     double err;    // bound on the error of the approximate part of W
     int missing;   // some tile leaves mass outside its candidates that no sum covers
 };
@@ -872,7 +914,7 @@ __device__ __forceinline__ RowView row_view(const RowLoad& l, float m, float T) 
     RowView r;
     r.zmax = canon_zero(m / T);
     float zb[2];
-    double sum = 0.0, err = 0.0;
+    double sum = 0.0, err = 0.0, csum = 0.0;
     float zmin = __builtin_huge_valf();
     int missing = 0;
 #pragma unroll
@@ -886,6 +928,7 @@ __device__ __forceinline__ RowView row_view(const RowLoad& l, float m, float T) 
             // binary32 exp of a binary32 difference: relative error ~1e-7 on
             // each tile's share of the mass
             const double scale = (double)expf(zm - r.zmax);
+            csum += s.sc * scale;
             if (s.flags & WS_SUM) {
                 sum += s.s * scale;  // the whole tile, candidates included
             } else {
@@ -902,6 +945,7 @@ __device__ __forceinline__ RowView row_view(const RowLoad& l, float m, float T) 
     r.zb = wave_max(fmaxf(zb[0], zb[1]));
     r.zlo = r.zb > NEG_INF ? r.zb : wave_min_f(zmin);
     r.W = wave_sum_d(sum);
+    r.Wc = wave_sum_d(csum);
     r.err = wave_sum_d(err);
     r.missing = wave_max_i(missing);
     return r;
@@ -980,91 +1024,306 @@ __device__ unsigned long long radix_select(const float* zr, int V, float zmax, P
     return prefix;
 }
 
-template <class Pred>
-__device__ void count_and_mass(const float* zr, int V, float zmax, Pred pred, int& count,
-                               unsigned long long& mass, SmemR& sh) {
-    int cnt = 0;
-    unsigned long long ms = 0;
-    for (int v = threadIdx.x; v < V; v += NTR) {
-        const float z = zr[v];
-        if (!(z > NEG_INF)) continue;
-        const float w = expf(z - zmax);
-        if (pred(key64(z, v), w)) {
-            ++cnt;
-            ms += wq(w);
-        }
-    }
-    count = block_sum_i(cnt, sh.red);
-    // u64 sum: exact in any order
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ms += __shfl_xor(ms, o);
-    __shared__ unsigned long long part[NTR / WAVE];
-    if ((threadIdx.x & (WAVE - 1)) == 0) part[threadIdx.x / WAVE] = ms;
-    __syncthreads();
-    unsigned long long t = 0;
-#pragma unroll
-    for (int k = 0; k < NTR / WAVE; ++k) t += part[k];
-    __syncthreads();
-    mass = t;
+__device__ __forceinline__ int hbucket(float z, float zmax) {
+    // zmax - z >= 0 rounded, then scaled exactly: monotone in z
+    const float d = (zmax - z) * HSCALE;
+    return d < (float)HB ? (int)d : HB;
 }
 
-// Exact whole-row resolution: recompute z for the whole row into scratch (the
-// first NT threads, one tile at a time), then select by count (top-k) and by
-// mass (top-p, the draw) with radix passes over the whole workgroup.
+__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int d) {
+    const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, d);
+    const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), d);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Exclusive prefix of one u64 per thread in thread order (exact); total too.
+__device__ unsigned long long block_excl_scan_u64(unsigned long long v, SmemHistState& hs,
+                                                  unsigned long long& total) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int w = threadIdx.x / WAVE;
+    unsigned long long inc = v;
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+        const unsigned long long o = shfl_up_u64(inc, d);
+        if (lane >= d) inc += o;
+    }
+    if (lane == WAVE - 1) hs.wsum[w] = inc;
+    __syncthreads();
+    unsigned long long base = 0, tot = 0;
+    for (int k = 0; k < NTR / WAVE; ++k) {
+        if (k < w) base += hs.wsum[k];
+        tot += hs.wsum[k];
+    }
+    __syncthreads();
+    total = tot;
+    return base + inc - v;
+}
+
+// Totals of the entries where pred holds (count, fixed-point mass) and, when
+// want_key, the key selected among them exactly as radix_select defines it:
+// by count, the key of rank `target` (1-based); by mass, the key of the first
+// entry whose inclusive mass exceeds target = frac x total mass (frac > 0) or
+// `target` (frac = 0); the smallest such key if none does. One pass builds the
+// bucket histogram; a second collects the selected bucket's entries, which are
+// resolved by pairwise comparison. A bucket too large for LDS, or the deepest
+// bucket, is left to radix_select.
+template <class Pred>
+__device__ void hist_select(const float* zr, int V, float zmax, Pred pred, bool by_mass,
+                            bool want_key, unsigned long long target, double frac, SmemU& su,
+                            SmemR& sh, int& count, unsigned long long& mass,
+                            unsigned long long& key) {
+    const int tid = threadIdx.x;
+    SmemHist& h = su.h;
+    SmemHistState& hs = sh.hs;
+    for (int b = tid; b <= HB; b += NTR) {
+        h.hc[b] = 0;
+        h.hm[b] = 0;
+    }
+    __syncthreads();
+    for (int v0 = tid; v0 < V; v0 += NTR * SU) {
+        float zs[SU];
+#pragma unroll
+        for (int k = 0; k < SU; ++k) zs[k] = v0 + k * NTR < V ? zr[v0 + k * NTR] : NEG_INF;
+#pragma unroll
+        for (int k = 0; k < SU; ++k) {
+            const float z = zs[k];
+            const int v = v0 + k * NTR;
+            if (!(z > NEG_INF)) continue;
+            const float w = expf(z - zmax);
+            if (!pred(key64(z, v), w)) continue;
+            const int b = hbucket(z, zmax);
+            atomicAdd(&h.hc[b], 1u);
+            atomicAdd(&h.hm[b], (unsigned long long)wq(w));
+        }
+    }
+    __syncthreads();
+    // thread t owns buckets 4t .. 4t + 3; the last thread also the deepest one
+    constexpr int PER = HB / NTR;
+    static_assert(PER * NTR == HB, "bucket ownership");
+    const int b0 = tid * PER;
+    const int nb = PER + (tid == NTR - 1 ? 1 : 0);
+    unsigned long long mine_c = 0, mine_m = 0;
+    int lastnz = -1;
+    for (int i = 0; i < nb; ++i) {
+        mine_c += h.hc[b0 + i];
+        mine_m += h.hm[b0 + i];
+        if (h.hc[b0 + i]) lastnz = b0 + i;
+    }
+    unsigned long long tot_c, tot_m;
+    const unsigned long long pre_c = block_excl_scan_u64(mine_c, hs, tot_c);
+    const unsigned long long pre_m = block_excl_scan_u64(mine_m, hs, tot_m);
+    count = (int)tot_c;
+    mass = tot_m;
+    if (!want_key) return;
+    const unsigned long long tgt =
+        by_mass && frac > 0.0 ? (unsigned long long)(frac * (double)tot_m) : target;
+    if (tid == 0) {
+        hs.sel = INT_MAX;
+        hs.lastnz = -1;
+        hs.n = 0;
+    }
+    __syncthreads();
+    {
+        unsigned long long cum = by_mass ? pre_m : pre_c;
+        for (int i = 0; i < nb; ++i) {
+            const int b = b0 + i;
+            if (h.hc[b] == 0) continue;
+            const unsigned long long amt = by_mass ? h.hm[b] : (unsigned long long)h.hc[b];
+            if (by_mass ? (cum + amt > tgt) : (cum + amt >= tgt)) {
+                atomicMin(&hs.sel, b);
+                break;
+            }
+            cum += amt;
+        }
+        if (lastnz >= 0) atomicMax(&hs.lastnz, lastnz);
+    }
+    __syncthreads();
+    int sel = hs.sel;
+    const bool take_last = sel == INT_MAX;
+    if (take_last) sel = hs.lastnz;
+    if (sel < 0) {  // nothing satisfies pred
+        key = 0;
+        return;
+    }
+    if (sel >= b0 && sel < b0 + nb) {  // the owner records what precedes the bucket
+        unsigned long long cum = by_mass ? pre_m : pre_c;
+        for (int b = b0; b < sel; ++b) cum += by_mass ? h.hm[b] : (unsigned long long)h.hc[b];
+        hs.cum = cum;
+        hs.target = tgt;
+        hs.total_count = (int)h.hc[sel];
+    }
+    __syncthreads();
+    const int csel = hs.total_count;
+    if (sel == HB || csel > HCAP) {
+        key = radix_select(zr, V, zmax, pred, by_mass, tgt, su.r, sh);
+        return;
+    }
+    const unsigned long long cum = hs.cum;
+    __syncthreads();  // the histogram is dead from here: its memory holds the bucket
+    SmemBucket& kb = su.k;
+    for (int v0 = tid; v0 < V; v0 += NTR * SU) {
+        float zs[SU];
+#pragma unroll
+        for (int k = 0; k < SU; ++k) zs[k] = v0 + k * NTR < V ? zr[v0 + k * NTR] : NEG_INF;
+#pragma unroll
+        for (int k = 0; k < SU; ++k) {
+            const float z = zs[k];
+            const int v = v0 + k * NTR;
+            if (!(z > NEG_INF) || hbucket(z, zmax) != sel) continue;
+            const float w = expf(z - zmax);
+            const unsigned long long kk = key64(z, v);
+            if (!pred(kk, w)) continue;
+            const int slot = atomicAdd(&hs.n, 1);
+            if (slot < HCAP) {  // the histogram counted exactly these entries
+                kb.key[slot] = kk;
+                kb.wq[slot] = wq(w);
+            }
+        }
+    }
+    __syncthreads();
+    const int n = min(hs.n, HCAP);
+    if (tid == 0) hs.key = ~0ull;
+    __syncthreads();
+    if (take_last) {
+        for (int i = tid; i < n; i += NTR) atomicMin(&hs.key, kb.key[i]);
+    } else {
+        // count and mass of the bucket's entries that precede entry i in key
+        // order: G lanes of one wave share entry i, each over every G-th entry
+        int G = 1;
+        while (G < WAVE && n * (2 * G) <= NTR) G *= 2;
+        const unsigned long long rem = tgt - cum;
+        for (int base = 0; base < n; base += NTR / G) {  // the same trip count in every lane
+            const int i = base + tid / G;
+            const bool live = i < n;
+            const unsigned long long ki = live ? kb.key[i] : 0ull;
+            unsigned long long before = 0;
+            if (live)
+                for (int j = tid % G; j < n; j += G) {
+                    const unsigned long long kj = kb.key[j];
+                    if (kj > ki) before += by_mass ? kb.wq[j] : 1ull;
+                }
+            for (int o = 1; o < G; o <<= 1) {
+                const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)before, o);
+                const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(before >> 32), o);
+                before += ((unsigned long long)hi << 32) | lo;
+            }
+            if (live && tid % G == 0) {
+                const bool hit = by_mass ? (before <= rem && rem < before + kb.wq[i]) : (before + 1 == rem);
+                if (hit) hs.key = ki;  // exactly one entry qualifies
+            }
+        }
+    }
+    __syncthreads();
+    key = hs.key;
+    __syncthreads();
+}
+
+// z of every entry of the row into scratch, by the whole workgroup: first from
+// the raw logits and the mask alone, then the entries a history, draft or bias
+// entry touches are formed again with their multiplicity and bias (each
+// distinct id by the thread that holds its first occurrence in the lists, read
+// from LDS when they fit), through the same process_entry as every other path.
+// Entry i of the concatenated history, draft and bias id lists.
+__device__ __forceinline__ int list_id(const RowCtx& c, int nh, int i) {
+    if (i < c.hist_len) return gld(c.hist + i);
+    if (i < nh) return gld(c.extra + (i - c.hist_len));
+    return gld(c.bias_ids + (i - nh));
+}
+
+// z again for each distinct id of the lists (LDS copy `ids`, or null to read
+// them from memory), with its multiplicity among the history and draft ids and
+// whether a bias entry names it.
+template <int DT>
+__device__ void patch_entries(const RowCtx& c, float* zr, int nh, int n, const int32_t* ids) {
+    for (int i = threadIdx.x; i < n; i += NTR) {
+        const int id = ids ? ids[i] : list_id(c, nh, i);
+        if (id < 0 || id >= c.V) continue;
+        bool first = true;
+        for (int j = 0; j < i; ++j)
+            if ((ids ? ids[j] : list_id(c, nh, j)) == id) {
+                first = false;
+                break;
+            }
+        if (!first) continue;
+        uint32_t cnt = 0;
+        bool hit = false;
+        for (int j = 0; j < n; ++j) {
+            const bool eq = (ids ? ids[j] : list_id(c, nh, j)) == id;
+            if (j < nh) cnt += eq ? 1u : 0u;
+            else hit |= eq;
+        }
+        const bool allowed = c.mask ? ((gld(c.mask + (id >> 5)) >> (id & 31)) & 1u) : true;
+        const float x = process_entry(c, id, read_logit<DT>(c.logits, id), cnt, hit, allowed);
+        zr[id] = x > NEG_INF ? canon_zero(x / c.T) : NEG_INF;
+    }
+}
+
+template <int DT>
+__device__ void row_z(const RowCtx& c, float* zr, SmemU& su) {
+    const int tid = threadIdx.x;
+    const int V = c.V;
+    // SU entries per thread in flight: the loop is bound by memory latency
+    for (int v0 = tid; v0 < V; v0 += NTR * SU) {
+        float x[SU];
+        uint32_t mw[SU];
+#pragma unroll
+        for (int k = 0; k < SU; ++k) {
+            const int v = v0 + k * NTR;
+            x[k] = v < V ? read_logit<DT>(c.logits, v) : NEG_INF;
+            mw[k] = (c.mask && v < V) ? gld(c.mask + (v >> 5)) : 0xFFFFFFFFu;
+        }
+#pragma unroll
+        for (int k = 0; k < SU; ++k) {
+            const int v = v0 + k * NTR;
+            if (v >= V) continue;
+            const float xv = ((mw[k] >> (v & 31)) & 1u) ? x[k] : NEG_INF;
+            zr[v] = xv > NEG_INF ? canon_zero(xv / c.T) : NEG_INF;
+        }
+    }
+    const int nh = c.hist_len + c.extra_len;
+    const int n = nh + c.bias_len;
+    if (n <= LIST_CAP) {
+        for (int i = tid; i < n; i += NTR) su.l.ids[i] = list_id(c, nh, i);
+        __syncthreads();  // also orders the raw pass before the patches
+        patch_entries<DT>(c, zr, nh, n, su.l.ids);
+    } else {
+        __syncthreads();
+        patch_entries<DT>(c, zr, nh, n, nullptr);
+    }
+    __syncthreads();
+}
+
+// Exact whole-row resolution: z for the whole row into scratch, then select by
+// count (top-k) and by mass (top-p, the draw) over bucket histograms of the
+// distance below the row maximum.
 template <int DT>
 __device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Workspace& ws,
                                            int n_tiles, const RowSummary& rs, float u, SmemU& su,
                                            SmemR& sh, RowInfo& info, const RowDbg& dbg) {
     const int tid = threadIdx.x;
     const int V = c.V;
-    const bool tl = tid < NT;
     float* zr = ws.scratch_z + (size_t)row * V;
-    const bool tables = c.hist_len + c.extra_len + c.bias_len > 0;
-    TablePrefetch f = {{-1, -1}, -1, -1, 0.0f};
-    if (tables && tl) f = prefetch_tables(c);
-    __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
-        float v[EPT];
-        uint32_t mw[Lay<DT>::NG];
-        if (tl) {
-            load_tile<DT>(c, t * TILE, v);
-            load_mask<DT>(c, t * TILE, mw);
-        }
-        if (tables) build_tables<DT>(c, t * TILE, su.t, f, tl);
-        if (tl) {
-            process_tile<DT>(c, t * TILE, v, su.t, mw, tables);
-#pragma unroll
-            for (int s = 0; s < EPT; ++s) {
-                const int id = slot_id<DT>(t * TILE, s);
-                if (id < V) zr[id] = v[s] > NEG_INF ? canon_zero(v[s] / c.T) : NEG_INF;
-            }
-        }
-        __syncthreads();
-    }
+    row_z<DT>(c, zr, su);
     const float zmax = canon_zero(rs.m / c.T);
     const int total = rs.nfinite;
     const bool topk_on = c.top_k > 0 && c.top_k < V;
     const int K_eff = topk_on ? min(c.top_k, total) : total;
+    int cnt;
+    unsigned long long ms;
     unsigned long long kK = 0;
     if (topk_on && K_eff < total)
-        kK = radix_select(zr, V, zmax, [](unsigned long long, float) { return true; }, false,
-                          (unsigned long long)K_eff, su.r, sh);
-    int nK;
-    unsigned long long WK;
-    count_and_mass(zr, V, zmax, [kK](unsigned long long k, float) { return k >= kK; }, nK, WK, sh);
+        hist_select(zr, V, zmax, [](unsigned long long, float) { return true; }, false, true,
+                    (unsigned long long)K_eff, 0.0, su, sh, cnt, ms, kK);
     unsigned long long kP = kK;
-    if (c.top_p < 1.0f) {
-        const unsigned long long tgt = (unsigned long long)((double)c.top_p * (double)WK);
-        kP = radix_select(zr, V, zmax, [kK](unsigned long long k, float) { return k >= kK; }, true,
-                          tgt, su.r, sh);
-    }
+    if (c.top_p < 1.0f)  // the first entry whose inclusive mass exceeds top_p x (top-k mass)
+        hist_select(zr, V, zmax, [kK](unsigned long long k, float) { return k >= kK; }, true,
+                    true, 0, (double)c.top_p, su, sh, cnt, ms, kP);
     const float mp = c.min_p;
     auto kept = [kP, mp](unsigned long long k, float w) { return k >= kP && (mp <= 0.0f || w >= mp); };
+    // the draw: the first kept entry whose inclusive mass exceeds u x (kept mass)
     int n_kept;
-    unsigned long long Wk;
-    count_and_mass(zr, V, zmax, kept, n_kept, Wk, sh);
-    const unsigned long long tgt = (unsigned long long)((double)u * (double)Wk);
-    const unsigned long long kt = radix_select(zr, V, zmax, kept, true, tgt, su.r, sh);
+    unsigned long long Wk, kt;
+    hist_select(zr, V, zmax, kept, true, true, 0, (double)u, su, sh, n_kept, Wk, kt);
     if (tid == 0) {
         info.kappa = kP;
         info.W = (double)Wk / MASS_SCALE;
@@ -1333,6 +1592,13 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
     // rule allows 1e-6. (A top-k set deeper than the pool is checked once the
     // pool's mass is known.)
     if (!slow && !cut_k) slow = rv.err > 5e-7 * W;
+    // An uncut row whose draw (no top-p, no min-p) or top-p cut lies deeper
+    // than all the candidates' mass cannot resolve on the pool: skip building
+    // it. (The margin covers the binary32 scaling of each tile's candidate sum.)
+    if (!slow && !cut_k && c.min_p <= 0.0f) {
+        const double need = c.top_p < 1.0f ? (double)c.top_p * W : (double)u * W;
+        slow = need > rv.Wc * (1.0 + 1e-5);
+    }
 
     if (!slow) {
         if (n <= WAVE) {
