@@ -1876,13 +1876,13 @@ __global__ __launch_bounds__(NTR) void k_spec_rows(SpecArgs a) {
     if (threadIdx.x == 0) a.ws.rowinfo[row] = info;
 }
 
-// Accepted draft count of request b: the first rejected position, or G.
+// Accepted draft count of request b: the first rejected position, or G. Lane k
+// of each wave reads position k's decision (G <= 16), so the loads overlap.
 __device__ __forceinline__ int accepted_prefix(const SpecArgs& a, int b) {
-    const int G1 = a.G + 1;
-    int n = a.G;
-    for (int k = a.G - 1; k >= 0; --k)
-        if (!a.ws.row_accept[(size_t)b * G1 + k]) n = k;
-    return n;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const bool rej = lane < a.G && !a.ws.row_accept[(size_t)b * (a.G + 1) + lane];
+    const unsigned long long m = __ballot(rej);
+    return m ? (int)__builtin_ctzll(m) : a.G;
 }
 
 // Position of request b whose token comes from the residual distribution, or -1.
@@ -1911,7 +1911,7 @@ __device__ __forceinline__ float draft_q(const float* q, int id, int d) {
 }
 
 template <int DT>
-__device__ void residual_values(const RowCtx& c, const RowInfo& ri, const float* q, int d, int tb,
+__device__ __forceinline__ void residual_values(const RowCtx& c, const RowInfo& ri, const float* q, int d, int tb,
                                 bool use_pi, SmemTile& tt, double r[EPT]) {
     float v[EPT];
     uint32_t mw[Lay<DT>::NG];
@@ -1976,43 +1976,42 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a)
 // distribution in token-id order (tile by the per-tile sums, then the entry
 // within the tile). Called by the whole workgroup.
 template <int DT>
-__device__ int residual_token(const SpecArgs& a, int b, int j, const RowInfo& ri, SmemTile& tt,
+__device__ __forceinline__ int residual_token(const SpecArgs& a, int b, int j, const RowInfo& ri, SmemTile& tt,
                               SmemS& sh, int& s_tile, int& s_usepi, double& s_rem) {
     const int n_tiles = a.ws.n_tiles;
     const RowCtx c = spec_ctx<DT>(a, b, j);
     const float* q = a.draft_probs ? a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride : nullptr;
     const int d = a.draft_tokens[(size_t)b * a.G + j];
-    if (threadIdx.x == 0) {
-        double R = 0.0, P = 0.0;
-        for (int t = 0; t < n_tiles; ++t) {
-            const double2 x = a.ws.resid_tile[(size_t)b * n_tiles + t];
-            R += x.x;
-            P += x.y;
-        }
+    if (threadIdx.x < WAVE) {
+        // lane t holds tile t's sums (n_tiles <= 32): the totals, then the
+        // tile where the running sum in tile order passes u x total
+        const int t = threadIdx.x;
+        const double2 x = t < n_tiles ? a.ws.resid_tile[(size_t)b * n_tiles + t] : make_double2(0.0, 0.0);
+        const double R = wave_sum_d(x.x);
+        const double P = wave_sum_d(x.y);
         const int use_pi = !(R > 0.0);
         const double tot = use_pi ? P : R;
         const float ur = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_RESIDUAL));
         const double tgt = (double)ur * tot;
-        double cum = 0.0;
-        int sel = -1, lastnz = -1;
-        double rem = 0.0;
-        for (int t = 0; t < n_tiles; ++t) {
-            const double2 x = a.ws.resid_tile[(size_t)b * n_tiles + t];
-            const double amt = use_pi ? x.y : x.x;
-            if (amt > 0.0) lastnz = t;
-            if (sel < 0 && cum + amt > tgt && amt > 0.0) {
-                sel = t;
-                rem = tgt - cum;
-            }
-            cum += amt;
-        }
-        if (sel < 0) {
-            sel = lastnz;
+        const double amt = use_pi ? x.y : x.x;
+        const double inc = wave_incl_scan_d(amt);
+        const double cum = inc - amt;
+        const unsigned long long hit = __ballot(t < n_tiles && amt > 0.0 && cum + amt > tgt);
+        const unsigned long long nz = __ballot(t < n_tiles && amt > 0.0);
+        int sel;
+        double rem;
+        if (hit) {
+            sel = (int)__builtin_ctzll(hit);
+            rem = tgt - __shfl(cum, sel);
+        } else {
+            sel = nz ? 63 - (int)__builtin_clzll(nz) : -1;
             rem = DBL_MAX;
         }
-        s_tile = sel;
-        s_usepi = use_pi;
-        s_rem = rem;
+        if (t == 0) {
+            s_tile = sel;
+            s_usepi = use_pi;
+            s_rem = rem;
+        }
     }
     __syncthreads();
     const int st = s_tile;
