@@ -224,3 +224,122 @@ def verify_batch(target, draft_probs, draft_tokens, params, rows=None):
             seed=params.seed, request=pr["request"], position=pr["position"],
             rows=None if rows is None else rows[b]))
     return res
+
+
+# --- tree verification ---------------------------------------------------------
+
+@dataclass
+class TreeResult:
+    tokens: np.ndarray      # [N] int32: accepted path tokens, the final token, -1 padding
+    nodes: np.ndarray       # [N] int32: tree node of each accepted token, -1 padding
+    n_acc: int              # accepted path length (nodes below the root)
+    flagged: bool           # a decision lies on a boundary
+
+
+def tree_nodes(parents):
+    """(depth, path) per node of a draft tree given as parent indices.
+
+    Node 0 is the root (the last committed token): depth 0, empty path. Node
+    n >= 1 hangs below parents[n], which must precede it (0 <= parents[n] < n);
+    a node that breaks this, or hangs below such a node, is unreachable (depth
+    -1). path[n] lists the nodes from the root's child down to n."""
+    N = len(parents)
+    depth = [-1] * N
+    path = [None] * N
+    depth[0], path[0] = 0, []
+    for n in range(1, N):
+        p = int(parents[n])
+        if 0 <= p < n and depth[p] >= 0:
+            depth[n] = depth[p] + 1
+            path[n] = path[p] + [n]
+    return depth, path
+
+
+def tree_children(parents, depth, x):
+    """Children of reachable node x in index order."""
+    return [n for n in range(1, len(parents)) if depth[n] >= 0 and int(parents[n]) == x]
+
+
+def verify_tree(target_rows, parents, tokens, *, temperature, top_k=0, top_p=1.0, min_p=0.0,
+                rep=1.0, freq=0.0, pres=0.0, hist=(), bias_ids=(), bias_vals=(), masks=None,
+                seed=0, request=0, position=0, uniform=None):
+    """Verify one request's draft tree ("Accelerating Sonar through speculation",
+    Perplexity blog, EAGLE section: draft sequences explored as a tree in which
+    each node considers its draft's top-K candidates; the longest acceptable
+    path is kept and the target adds one token).
+
+    target_rows [N, V] float32: row n holds the target's logits after the path
+    root -> n (node 0 = the root). parents [N], tokens [N]: the tree (tokens[0]
+    unused). Row n is processed with the request history followed by its path's
+    tokens as penalty history, masks[n] when given, and the request's filters.
+
+    Reading: the children of a node are deterministic candidates, so each is a
+    one-hot proposal. Walking down from the root, the children of the current
+    node are tested in index order against the residual target: child i with
+    token d is accepted iff u_i < p(d) / (1 - sum of p over the tokens of the
+    siblings already rejected), u_i = u24 of the ACCEPT word at (request,
+    position + depth, draw i) (a token equal to a rejected sibling's has
+    residual probability 0). An accepted child becomes the current node. If
+    every child is rejected, the final token is drawn from p with the rejected
+    tokens removed, by inverse CDF in token-id order (RESIDUAL word at position
+    + depth, draw 0); at a leaf it is drawn from p as the plain sampler would
+    (SAMPLE word at position + depth). Greedy rows (T = 0) accept the child
+    whose token is the greedy token and end with the greedy token. With one
+    child per node this is verify_request with a greedy draft.
+    """
+    if uniform is None:
+        def uniform(domain, pos, draw=0):
+            return philox.uniform(seed, request, pos, draw, domain)
+    N, V = target_rows.shape
+    depth, path = tree_nodes(parents)
+    hist = [int(h) for h in hist]
+    out_t = np.full(N, -1, dtype=np.int32)
+    out_n = np.full(N, -1, dtype=np.int32)
+    flagged = False
+    cur, k = 0, 0
+    while True:
+        hx = hist + [int(tokens[m]) for m in path[cur]]
+        mx = None if masks is None else masks[cur]
+        xp = process_row(target_rows[cur], hx, rep, freq, pres, bias_ids, bias_vals, mx)
+        filt = filter_row(xp, temperature, top_k, top_p, min_p)
+        flagged = flagged or filt.flag_topp or filt.flag_minp
+        dpt = depth[cur]
+        ch = tree_children(parents, depth, cur)
+        if filt.greedy or filt.n_kept == 0:
+            g = filt.argmax if filt.n_kept else -1
+            nxt = next((c for c in ch if g >= 0 and int(tokens[c]) == g), None)
+            if nxt is None:
+                out_t[k] = g
+                return TreeResult(out_t, out_n, k, flagged)
+        else:
+            nxt = None
+            rejected = []
+            remaining = 1.0
+            for i, c in enumerate(ch):
+                d = int(tokens[c])
+                p = float(filt.probs[d]) if 0 <= d < V and d not in rejected else 0.0
+                u = uniform(philox.ACCEPT, position + dpt, i)
+                ratio = p / remaining if remaining > 0.0 else 0.0
+                if abs(u - ratio) < BOUNDARY_EPS:
+                    flagged = True
+                if u < ratio:
+                    nxt = c
+                    break
+                if 0 <= d < V and d not in rejected:
+                    rejected.append(d)
+                    remaining -= p
+            if nxt is None:
+                if ch:
+                    q = np.zeros(V)
+                    for d in rejected:
+                        q[d] = 1.0
+                    tok, fl = residual_draw(filt.probs, q, uniform(philox.RESIDUAL, position + dpt))
+                else:
+                    res = draw(filt, uniform(philox.SAMPLE, position + dpt))
+                    tok, fl = res.token, res.flag_draw
+                out_t[k] = tok
+                return TreeResult(out_t, out_n, k, flagged or fl)
+        out_t[k] = int(tokens[nxt])
+        out_n[k] = nxt
+        k += 1
+        cur = nxt
