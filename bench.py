@@ -397,6 +397,37 @@ def secondary(args, dev):
         "note": "no draft rows read; emitted tokens appended on the device"}
     s.close()
     del tgs
+    # tree verification: 32 requests x 16-node draft trees x 128256 f32
+    tw = W.tree()
+    nbytes = tw.target.nbytes
+    R = max(2, -(-ROTATE_MIN // nbytes))
+    tt = torch.from_numpy(tw.target).to(dev)
+    tts = [tt] + [tt.clone() for _ in range(R - 1)]
+    tpar = torch.from_numpy(tw.parents).to(dev)
+    ttok = torch.from_numpy(tw.tokens).to(dev)
+    tp = SamplingParams(temperature=torch.from_numpy(tw.temperature).to(dev),
+                        request_ids=torch.from_numpy(tw.request_ids).to(dev),
+                        positions=torch.from_numpy(tw.positions).to(dev), seed=tw.seed)
+    s = Sampler(tw.B, tw.V, max_draft=tw.N - 1, device=0)
+    o1 = torch.empty(tw.B, tw.N, dtype=torch.int32, device=dev)
+    o2 = torch.empty(tw.B, tw.N, dtype=torch.int32, device=dev)
+    o3 = torch.empty(tw.B, dtype=torch.int32, device=dev)
+    tfns = [(lambda t=tts[r]: s.tree_verify(t, tpar, ttok, tp, o1, o2, o3)) for r in range(R)]
+    tfns[0]()
+    torch.cuda.synchronize()
+    t_emitted = int((o3 + 1).sum().item())
+    ms, _ = time_graph(tfns, steps, 5)
+    st = stage_summary(time_stages(s, tfns, steps, 5),
+                       ["k_tree_paths", "k_tree_tiles<f32>", "k_tree_rows<f32>",
+                        "k_tree_resid_tiles<f32>", "k_tree_finish<f32>"])
+    out["tree"] = {"us_per_call": ms / steps * 1e3, "stages": st,
+                   "emitted_tokens_per_call": t_emitted,
+                   "emitted_tokens_per_s": t_emitted * steps / (ms * 1e-3), "bytes": nbytes,
+                   "roofline": dict(fraction(nbytes, ms / steps * 1e-3),
+                                    kernel=dict(name="k_tree_tiles<f32>",
+                                                **fraction(nbytes, st["k_tree_tiles<f32>"]["us_mean"] * 1e-6)))}
+    s.close()
+    del tts
     # fused LM-head + Gumbel-max, hidden [64, 8192] x weight [128256, 8192] bf16
     B, K, V = 64, 8192, 128256
     gen = torch.Generator(device=dev).manual_seed(105)

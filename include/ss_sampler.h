@@ -66,7 +66,8 @@ typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
 typedef struct {
     int32_t max_batch;   /* max rows (ss_sample) / requests (spec, lmhead), >= 1 */
     int32_t vocab_size;  /* V, 1 .. 262144 */
-    int32_t max_draft;   /* max G for ss_spec_verify, 0 .. 16 (0: verify unused) */
+    int32_t max_draft;   /* max G for ss_spec_verify and N - 1 for ss_tree_verify,
+                            0 .. 63 (0: verification unused) */
     int32_t hidden_size; /* K for ss_lmhead_sample, 0 or a multiple of 64 (0: unused) */
     int32_t device;      /* HIP device ordinal */
 } ss_sampler_config;
@@ -87,7 +88,7 @@ typedef struct {
     const int32_t* history_ids;      /* [B, history_stride]; ids outside [0,V) ignored */
     const int32_t* history_len;      /* [B], each in [0, history_stride]; NULL: no history */
     int32_t history_stride;          /* >= 0, <= 65000 (multiplicities are counted in 16 bits,
-                                        with room for up to 16 draft tokens) */
+                                        with room for up to 63 draft tokens) */
     const int32_t* bias_ids;         /* [B, bias_stride]; ids outside [0,V) ignored */
     const float* bias_values;        /* [B, bias_stride]; applied in array order */
     const int32_t* bias_len;         /* [B], each in [0, bias_stride]; NULL: no bias */
@@ -135,15 +136,17 @@ int64_t ss_sampler_workspace_bytes(const ss_sampler* s);
 /* ss_sampler_set_launch_events -- measurement hook (timing of the kernels).
  *   events    array of n_events hipEvent_t handles created by the caller, or
  *             NULL to clear the hook. The library copies the handles.
- *   n_events  0 .. 8.
+ *   n_events  0 .. 16.
  * While set, every ss_sample / ss_spec_verify / ss_lmhead_sample call launches
  * its k-th kernel (k = 0, 1, ...) with events[2k] as its start and
  * events[2k + 1] as its stop event (hipExtLaunchKernel: the dispatch records
  * them when the kernel begins and ends), for every k with 2k + 1 < n_events.
  * ss_sample launches 2 kernels (tile scan, row merge), ss_spec_verify 4 (tile
- * scan, row merge, residual tile sums, per-request finish) and
- * ss_lmhead_sample 2 (fused GEMM tiles, cross-tile reduction).
- * Returns SS_ERR_INVALID_ARG for a null handle or n_events outside 0 .. 8.
+ * scan, row merge, residual tile sums, per-request finish), ss_tree_verify 5
+ * (tree paths, tile scan, row merge and child tests, residual tile sums,
+ * per-request finish) and ss_lmhead_sample 2 (fused GEMM tiles, cross-tile
+ * reduction).
+ * Returns SS_ERR_INVALID_ARG for a null handle or n_events outside 0 .. 16.
  * Not meant for graph capture. */
 ss_status ss_sampler_set_launch_events(ss_sampler* s, void* const* events, int32_t n_events);
 
@@ -235,6 +238,42 @@ ss_status ss_spec_verify_scatter(ss_sampler* s, const void* target_logits, ss_dt
                                  int32_t G, const ss_params* params, int32_t* out_tokens,
                                  int32_t* out_num_accepted, const ss_sequences* seq,
                                  void* stream);
+
+/* ss_tree_verify -- verify a draft tree per request ("Accelerating Sonar
+ * through speculation", EAGLE section: the draft explores a tree in which each
+ * node holds its draft's top-K candidates for the next token; the longest
+ * acceptable path is kept and the target adds one token).
+ *   target_logits [B, N, row_stride] of dtype: row b * N + n holds the target's
+ *                 logits after the path from the root to node n (node 0 = the
+ *                 root, the last committed token).
+ *   parents       [B, N] int32: parent node of each node (entry 0 ignored).
+ *                 Node n >= 1 hangs below parents[n] when 0 <= parents[n] < n;
+ *                 otherwise it, and everything below it, is unreachable.
+ *   tokens        [B, N] int32: draft token of each node (entry 0 ignored).
+ *   B, N          0 .. max_batch, 2 .. max_draft + 1.
+ *   params        as ss_sample; a grammar mask, when given, has one row per
+ *                 node (row b * N + n, mask_stride words apart).
+ *   out_tokens    [B, N] int32: the accepted path's tokens, then the final
+ *                 token, then -1 padding.
+ *   out_nodes     [B, N] int32: the tree node of each accepted token, then -1.
+ *   out_num_accepted [B] int32: the accepted path's length (0 .. N - 1).
+ * Node n uses the request's parameters, the request history followed by the
+ * tokens on its root path as penalty history, and position + depth(n). Walking
+ * down from the root, the children of the current node are tested in index
+ * order as one-hot proposals against the residual target: child i with token d
+ * is accepted iff u < p(d) / (1 - p of the siblings rejected before it), u from
+ * domain 1 (acceptance) at position + depth, draw i; greedy rows (T = 0) accept
+ * the child holding the greedy token. The final token is the greedy token, a
+ * draw from p without the rejected children's tokens in token-id order (domain
+ * 2) when the end node has children, or the end node's own draw as ss_sample
+ * would make it when it is a leaf. A chain (one child per node) gives exactly
+ * ss_spec_verify with a greedy draft (draft_probs NULL).
+ * Launches five kernels. Errors: as ss_sample, plus SS_ERR_INVALID_ARG for N
+ * outside 2 .. max_draft + 1 or null parents / tokens / outputs. */
+ss_status ss_tree_verify(ss_sampler* s, const void* target_logits, ss_dtype dtype,
+                         int64_t row_stride, const int32_t* parents, const int32_t* tokens,
+                         int32_t B, int32_t N, const ss_params* params, int32_t* out_tokens,
+                         int32_t* out_nodes, int32_t* out_num_accepted, void* stream);
 
 /* ss_lmhead_sample -- fused LM-head GEMM + Gumbel-max sampling.
  *   hidden        [B, K] bfloat16 bits (row-major), 16-byte aligned.

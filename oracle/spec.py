@@ -260,9 +260,29 @@ def tree_children(parents, depth, x):
     return [n for n in range(1, len(parents)) if depth[n] >= 0 and int(parents[n]) == x]
 
 
+def tree_rows(target_rows, parents, tokens, *, temperature, top_k=0, top_p=1.0, min_p=0.0,
+              rep=1.0, freq=0.0, pres=0.0, hist=(), bias_ids=(), bias_vals=(), masks=None):
+    """rows(n): node n's filtered distribution, formed on first use. Node n is
+    processed with the request history followed by the tokens on its root path
+    and masks[n] when given; it depends on neither the seed nor the position."""
+    depth, path = tree_nodes(parents)
+    hist = [int(h) for h in hist]
+    cache = {}
+
+    def rows(n):
+        if n not in cache:
+            hx = hist + [int(tokens[m]) for m in (path[n] or [])]
+            mx = None if masks is None else masks[n]
+            xp = process_row(target_rows[n], hx, rep, freq, pres, bias_ids, bias_vals, mx)
+            cache[n] = filter_row(xp, temperature, top_k, top_p, min_p)
+        return cache[n]
+
+    return rows
+
+
 def verify_tree(target_rows, parents, tokens, *, temperature, top_k=0, top_p=1.0, min_p=0.0,
                 rep=1.0, freq=0.0, pres=0.0, hist=(), bias_ids=(), bias_vals=(), masks=None,
-                seed=0, request=0, position=0, uniform=None):
+                seed=0, request=0, position=0, uniform=None, rows=None):
     """Verify one request's draft tree ("Accelerating Sonar through speculation",
     Perplexity blog, EAGLE section: draft sequences explored as a tree in which
     each node considers its draft's top-K candidates; the longest acceptable
@@ -286,22 +306,24 @@ def verify_tree(target_rows, parents, tokens, *, temperature, top_k=0, top_p=1.0
     (SAMPLE word at position + depth). Greedy rows (T = 0) accept the child
     whose token is the greedy token and end with the greedy token. With one
     child per node this is verify_request with a greedy draft.
+    rows: the request's tree_rows() (tests sweeping seeds and positions form it
+    once); by default it is formed here.
     """
     if uniform is None:
         def uniform(domain, pos, draw=0):
             return philox.uniform(seed, request, pos, draw, domain)
     N, V = target_rows.shape
     depth, path = tree_nodes(parents)
-    hist = [int(h) for h in hist]
+    if rows is None:
+        rows = tree_rows(target_rows, parents, tokens, temperature=temperature, top_k=top_k,
+                         top_p=top_p, min_p=min_p, rep=rep, freq=freq, pres=pres, hist=hist,
+                         bias_ids=bias_ids, bias_vals=bias_vals, masks=masks)
     out_t = np.full(N, -1, dtype=np.int32)
     out_n = np.full(N, -1, dtype=np.int32)
     flagged = False
     cur, k = 0, 0
     while True:
-        hx = hist + [int(tokens[m]) for m in path[cur]]
-        mx = None if masks is None else masks[cur]
-        xp = process_row(target_rows[cur], hx, rep, freq, pres, bias_ids, bias_vals, mx)
-        filt = filter_row(xp, temperature, top_k, top_p, min_p)
+        filt = rows(cur)
         flagged = flagged or filt.flag_topp or filt.flag_minp
         dpt = depth[cur]
         ch = tree_children(parents, depth, cur)
@@ -343,3 +365,21 @@ def verify_tree(target_rows, parents, tokens, *, temperature, top_k=0, top_p=1.0
         out_n[k] = nxt
         k += 1
         cur = nxt
+
+
+def verify_tree_batch(target, parents, tokens, params, rows=None):
+    """target [B, N, V] f32, parents / tokens [B, N] int. rows: per request
+    tree_rows() of the same inputs, or None."""
+    res = []
+    for b in range(target.shape[0]):
+        pr = params.row(b)
+        res.append(verify_tree(target[b], parents[b], tokens[b], **_filter_args(params, b),
+                               seed=params.seed, request=pr["request"], position=pr["position"],
+                               rows=None if rows is None else rows[b]))
+    return res
+
+
+def batch_tree_rows(target, parents, tokens, params):
+    """tree_rows() of every request of a batch."""
+    return [tree_rows(target[b], parents[b], tokens[b], **_filter_args(params, b))
+            for b in range(target.shape[0])]

@@ -238,7 +238,7 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     if (!cfg || !out) return SS_ERR_INVALID_ARG;
     *out = nullptr;
     if (cfg->max_batch < 1 || cfg->vocab_size < 1 || cfg->vocab_size > ss::MAX_VOCAB ||
-        cfg->max_draft < 0 || cfg->max_draft > 16 || cfg->hidden_size < 0 ||
+        cfg->max_draft < 0 || cfg->max_draft > 63 || cfg->hidden_size < 0 ||
         cfg->hidden_size % 64 != 0 || cfg->device < 0)
         return SS_ERR_INVALID_ARG;
     int ndev = 0;
@@ -271,6 +271,10 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     const int64_t o_acc = take(R * 4);
     const int64_t o_restile = take((int64_t)B * nt * (int64_t)sizeof(double2));
     const int64_t o_scratch = take(R * (int64_t)V * 4);
+    const int64_t dmax = cfg->max_draft > 0 ? cfg->max_draft : 1;
+    const int64_t o_tpath = take(R * dmax * 4);
+    const int64_t o_tdepth = take(R * 4);
+    const int64_t o_tnext = take(R * 4);
     const int64_t o_lmpart = cfg->hidden_size > 0 ? take(64 * (int64_t)s->n_vtiles * sizeof(float2)) : 0;
     const int64_t o_defaults = take(4 * (int64_t)B * 4);
     s->ws_bytes = off;
@@ -287,6 +291,10 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     w.row_accept = reinterpret_cast<int32_t*>(b + o_acc);
     w.resid_tile = reinterpret_cast<double2*>(b + o_restile);
     w.scratch_z = reinterpret_cast<float*>(b + o_scratch);
+    w.tree_path = reinterpret_cast<int32_t*>(b + o_tpath);
+    w.tree_depth = reinterpret_cast<int32_t*>(b + o_tdepth);
+    w.tree_next = reinterpret_cast<int32_t*>(b + o_tnext);
+    w.tree_dmax = (int)dmax;
     w.n_tiles = s->n_tiles;
     w.n_wt = s->n_wt;
     w.V = V;
@@ -332,9 +340,9 @@ void ss_sampler_destroy(ss_sampler* s) {
 int64_t ss_sampler_workspace_bytes(const ss_sampler* s) { return s ? s->ws_bytes : 0; }
 
 ss_status ss_sampler_set_launch_events(ss_sampler* s, void* const* events, int32_t n_events) {
-    if (!s || n_events < 0 || n_events > 8) return SS_ERR_INVALID_ARG;
+    if (!s || n_events < 0 || n_events > 16) return SS_ERR_INVALID_ARG;
     s->events.n = events ? n_events : 0;
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < 16; ++k)
         s->events.ev[k] = (events && k < n_events) ? static_cast<hipEvent_t>(events[k]) : nullptr;
     return SS_OK;
 }
@@ -421,6 +429,38 @@ ss_status ss_spec_verify_scatter(ss_sampler* s, const void* target_logits, ss_dt
     a.ws = s->ws;
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
     return ss::launch_spec(a, dtype, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
+                                                                                     : SS_ERR_HIP;
+}
+
+ss_status ss_tree_verify(ss_sampler* s, const void* target_logits, ss_dtype dtype,
+                         int64_t row_stride, const int32_t* parents, const int32_t* tokens,
+                         int32_t B, int32_t N, const ss_params* params, int32_t* out_tokens,
+                         int32_t* out_nodes, int32_t* out_num_accepted, void* stream) {
+    if (!s || B < 0 || B > s->cfg.max_batch) return SS_ERR_INVALID_ARG;
+    if (N < 2 || N > s->cfg.max_draft + 1) return SS_ERR_INVALID_ARG;
+    if (B == 0) return SS_OK;
+    if (!parents || !tokens || !out_tokens || !out_nodes || !out_num_accepted)
+        return SS_ERR_INVALID_ARG;
+    ss_status st = check_logits(s->cfg.vocab_size, target_logits, dtype, row_stride);
+    if (st != SS_OK) return st;
+    st = check_params(s->cfg.vocab_size, params);
+    if (st != SS_OK) return st;
+    ss::TreeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.target = target_logits;
+    a.row_stride = row_stride;
+    a.parents = parents;
+    a.tokens = tokens;
+    a.B = B;
+    a.N = N;
+    a.V = s->cfg.vocab_size;
+    a.p = to_ptrs(defaults_of(s), params);
+    a.out_tokens = out_tokens;
+    a.out_nodes = out_nodes;
+    a.out_num_accepted = out_num_accepted;
+    a.ws = s->ws;
+    if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
+    return ss::launch_tree(a, dtype, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
                                                                                      : SS_ERR_HIP;
 }
 

@@ -84,6 +84,10 @@ struct Workspace {
     int32_t* row_accept;     // [max_rows]: spec decision per draft row
     double2* resid_tile;     // [max_batch * n_tiles]: residual / target mass per tile
     float* scratch_z;        // [max_rows * V] fallback rows
+    int32_t* tree_path;      // [max_rows * tree_dmax]: tokens from the root to each tree node
+    int32_t* tree_depth;     // [max_rows]: depth of each tree node (-1: unreachable)
+    int32_t* tree_next;      // [max_rows]: accepted child of each tree node (-1: none)
+    int tree_dmax;           // path stride (the deepest path a tree of the handle can have)
     int n_tiles;             // 8192-entry workgroup tiles per row
     int n_wt;                // wave tiles per row (WPT per workgroup tile)
     int V;
@@ -124,6 +128,21 @@ struct SpecArgs {
     Workspace ws;
 };
 
+struct TreeArgs {
+    const void* target;        // [B * N] rows: row b * N + n after the path root -> n
+    int64_t row_stride;
+    const int32_t* parents;    // [B, N]
+    const int32_t* tokens;     // [B, N]
+    int B;
+    int N;
+    int V;
+    ParamPtrs p;
+    int32_t* out_tokens;       // [B, N]
+    int32_t* out_nodes;        // [B, N]
+    int32_t* out_num_accepted; // [B]
+    Workspace ws;
+};
+
 struct LmheadArgs {
     const uint16_t* hidden;
     const uint16_t* weight;
@@ -144,7 +163,7 @@ struct LmheadArgs {
 // k is bracketed by ev[2k] (its start) and ev[2k + 1] (its end), recorded by
 // the dispatch itself.
 struct LaunchEvents {
-    hipEvent_t ev[8];
+    hipEvent_t ev[16];
     int n;
     hipEvent_t start(int k) const { return 2 * k + 1 < n ? ev[2 * k] : nullptr; }
     hipEvent_t stop(int k) const { return 2 * k + 1 < n ? ev[2 * k + 1] : nullptr; }
@@ -162,6 +181,7 @@ inline void launch_k(const LaunchEvents& le, int k, F kernel, dim3 grid, dim3 bl
 
 hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le);
 hipError_t launch_spec(const SpecArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le);
+hipError_t launch_tree(const TreeArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le);
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le);
 
 }  // namespace ss

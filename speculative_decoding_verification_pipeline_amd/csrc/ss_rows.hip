@@ -1904,15 +1904,27 @@ __device__ __forceinline__ float filtered_prob(const RowCtx& c, const RowInfo& r
 
 // Residual mass of one tile of a rejected row: r = max(0, pi - q) per entry (or
 // pi itself when use_pi), in token-id order within each thread group.
-// q(id) of the draft distribution at a rejected position: the draft row, or
-// for a greedy draft (q null) one at the draft token d and zero elsewhere.
-__device__ __forceinline__ float draft_q(const float* q, int id, int d) {
-    return q ? gld(q + id) : (id == d ? 1.0f : 0.0f);
-}
+// q(id) of the draft distribution at a rejected node: a dense draft row, or
+// for deterministic drafts one at each proposed token (d0, and n more tokens in
+// `set`) and zero elsewhere.
+struct DraftQ {
+    const float* q;
+    int d0;
+    const int32_t* set;
+    int n;
+    __device__ __forceinline__ float operator()(int id) const {
+        if (q) return gld(q + id);
+        bool one = id == d0;
+        for (int k = 0; k < n; ++k) one |= set[k] == id;
+        return one ? 1.0f : 0.0f;
+    }
+};
 
+// The residual max(0, pi - q) (or pi itself when use_pi) of this thread's
+// entries of tile tb, pi being the filtered distribution described by ri.
 template <int DT>
-__device__ __forceinline__ void residual_values(const RowCtx& c, const RowInfo& ri, const float* q, int d, int tb,
-                                bool use_pi, SmemTile& tt, double r[EPT]) {
+__device__ __forceinline__ void residual_values(const RowCtx& c, const RowInfo& ri, const DraftQ& qf,
+                                                int tb, bool use_pi, SmemTile& tt, double r[EPT]) {
     float v[EPT];
     uint32_t mw[Lay<DT>::NG];
     const TablePrefetch f = prefetch_tables(c);
@@ -1927,28 +1939,17 @@ __device__ __forceinline__ void residual_values(const RowCtx& c, const RowInfo& 
         double val = 0.0;
         if (id < c.V) {
             const float pi = filtered_prob(c, ri, id, v[s]);
-            val = use_pi ? (double)pi : (double)fmaxf(0.0f, pi - draft_q(q, id, d));
+            val = use_pi ? (double)pi : (double)fmaxf(0.0f, pi - qf(id));
         }
         r[s] = val;
     }
 }
 
-// Verification, residual stage 1: per tile of each rejected row, the sums of the
-// residual max(0, pi - q) and of pi (the fallback when the residual is zero).
+// Sums over tile tb of the residual and of pi (the fallback when the residual
+// is zero), by the whole workgroup.
 template <int DT>
-__global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a) {
-    __shared__ SmemTile tt;
-    __shared__ SmemS sh;
-    const int n_tiles = a.ws.n_tiles;
-    const int b = blockIdx.x / n_tiles;
-    const int tile = blockIdx.x % n_tiles;
-    RowInfo ri;
-    const int j = residual_position(a, b, ri);
-    if (j < 0) return;
-    const RowCtx c = spec_ctx<DT>(a, b, j);
-    const float* q = a.draft_probs ? a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride : nullptr;
-    const int d = a.draft_tokens[(size_t)b * a.G + j];
-    const int tb = tile * TILE;
+__device__ __forceinline__ double2 residual_sums(const RowCtx& c, const RowInfo& ri, const DraftQ& qf,
+                                                 int tb, SmemTile& tt, SmemS& sh) {
     float v[EPT];
     uint32_t mw[Lay<DT>::NG];
     const TablePrefetch f = prefetch_tables(c);
@@ -1963,30 +1964,50 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a)
         const int id = slot_id<DT>(tb, s);
         if (id < c.V) {
             const float pi = filtered_prob(c, ri, id, v[s]);
-            sr += (double)fmaxf(0.0f, pi - draft_q(q, id, d));
+            sr += (double)fmaxf(0.0f, pi - qf(id));
             sp += (double)pi;
         }
     }
     sr = block_sum_d(sr, sh.red);
     sp = block_sum_d(sp, sh.red);
-    if (threadIdx.x == 0) a.ws.resid_tile[(size_t)b * n_tiles + tile] = make_double2(sr, sp);
+    return make_double2(sr, sp);
 }
 
-// The token of rejected position j of request b: a draw from the residual
-// distribution in token-id order (tile by the per-tile sums, then the entry
-// within the tile). Called by the whole workgroup.
+// Verification, residual stage 1: per tile of each rejected row, the sums of the
+// residual max(0, pi - q) and of pi.
 template <int DT>
-__device__ __forceinline__ int residual_token(const SpecArgs& a, int b, int j, const RowInfo& ri, SmemTile& tt,
-                              SmemS& sh, int& s_tile, int& s_usepi, double& s_rem) {
+__global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a) {
+    __shared__ SmemTile tt;
+    __shared__ SmemS sh;
     const int n_tiles = a.ws.n_tiles;
+    const int b = blockIdx.x / n_tiles;
+    const int tile = blockIdx.x % n_tiles;
+    RowInfo ri;
+    const int j = residual_position(a, b, ri);
+    if (j < 0) return;
     const RowCtx c = spec_ctx<DT>(a, b, j);
-    const float* q = a.draft_probs ? a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride : nullptr;
-    const int d = a.draft_tokens[(size_t)b * a.G + j];
+    DraftQ qf;
+    qf.q = a.draft_probs ? a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride : nullptr;
+    qf.d0 = a.draft_tokens[(size_t)b * a.G + j];
+    qf.set = nullptr;
+    qf.n = 0;
+    const double2 x = residual_sums<DT>(c, ri, qf, tile * TILE, tt, sh);
+    if (threadIdx.x == 0) a.ws.resid_tile[(size_t)b * n_tiles + tile] = x;
+}
+
+// A draw from the residual distribution of the row described by c and ri, in
+// token-id order: the tile by the per-tile sums `tiles`, then the entry within
+// the tile (u from the residual domain at c's position). Called by the whole
+// workgroup.
+template <int DT>
+__device__ __forceinline__ int residual_draw(const RowCtx& c, const RowInfo& ri, const DraftQ& qf,
+                                             const double2* tiles, int n_tiles, SmemTile& tt,
+                                             SmemS& sh, int& s_tile, int& s_usepi, double& s_rem) {
     if (threadIdx.x < WAVE) {
         // lane t holds tile t's sums (n_tiles <= 32): the totals, then the
         // tile where the running sum in tile order passes u x total
         const int t = threadIdx.x;
-        const double2 x = t < n_tiles ? a.ws.resid_tile[(size_t)b * n_tiles + t] : make_double2(0.0, 0.0);
+        const double2 x = t < n_tiles ? tiles[t] : make_double2(0.0, 0.0);
         const double R = wave_sum_d(x.x);
         const double P = wave_sum_d(x.y);
         const int use_pi = !(R > 0.0);
@@ -2018,7 +2039,7 @@ __device__ __forceinline__ int residual_token(const SpecArgs& a, int b, int j, c
     int token = -1;
     if (st >= 0) {
         double r[EPT];
-        residual_values<DT>(c, ri, q, d, st * TILE, s_usepi != 0, tt, r);
+        residual_values<DT>(c, ri, qf, st * TILE, s_usepi != 0, tt, r);
         using L = Lay<DT>;
         double carry = 0.0;
         int found = INT_MAX, lastpos = -1;
@@ -2048,6 +2069,21 @@ __device__ __forceinline__ int residual_token(const SpecArgs& a, int b, int j, c
         token = found != INT_MAX ? found : lastpos;
     }
     return token;
+}
+
+// The token of rejected position j of request b.
+template <int DT>
+__device__ __forceinline__ int residual_token(const SpecArgs& a, int b, int j, const RowInfo& ri,
+                                              SmemTile& tt, SmemS& sh, int& s_tile, int& s_usepi,
+                                              double& s_rem) {
+    const RowCtx c = spec_ctx<DT>(a, b, j);
+    DraftQ qf;
+    qf.q = a.draft_probs ? a.draft_probs + ((size_t)b * a.G + j) * a.draft_stride : nullptr;
+    qf.d0 = a.draft_tokens[(size_t)b * a.G + j];
+    qf.set = nullptr;
+    qf.n = 0;
+    return residual_draw<DT>(c, ri, qf, a.ws.resid_tile + (size_t)b * a.ws.n_tiles, a.ws.n_tiles, tt,
+                             sh, s_tile, s_usepi, s_rem);
 }
 
 // Verification, per request: the output row (accepted drafts, then the bonus
@@ -2098,6 +2134,233 @@ __global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
 
 
 // ---------------------------------------------------------------------------
+// tree verification: node n of request b is row b * N + n; its penalty history
+// is the request's followed by the tokens on the path from the root to n, and
+// its position is the request's plus the node's depth.
+
+template <int DT>
+__device__ __forceinline__ RowCtx tree_ctx(const TreeArgs& a, int b, int n, int depth) {
+    const int row = b * a.N + n;
+    const void* logits = (const char*)a.target + (size_t)row * a.row_stride * (DT == SS_F32 ? 4 : 2);
+    const uint32_t* mrow = a.p.mask ? a.p.mask + (size_t)row * a.p.mask_stride : nullptr;
+    const int d = max(depth, 0);
+    return make_ctx(a.p, b, logits, a.V, a.ws.tree_path + (size_t)row * a.ws.tree_dmax, d, mrow,
+                    (uint32_t)d);
+}
+
+// Depth and root path of every node, one wave per request (lane n = node n).
+// Node n >= 1 hangs below parents[n] when 0 <= parents[n] < n; a node that
+// breaks this, or lies below such a node, is unreachable (depth -1).
+__global__ __launch_bounds__(WAVE) void k_tree_paths(TreeArgs a) {
+    const int b = blockIdx.x;
+    const int n = threadIdx.x;
+    const int N = a.N;
+    const int par = n < N ? a.parents[(size_t)b * N + n] : -1;
+    const int tok = n < N ? a.tokens[(size_t)b * N + n] : -1;
+    const bool edge = n >= 1 && n < N && par >= 0 && par < n;
+    int d = n == 0 ? 0 : -1;
+    for (int r = 1; r < N; ++r) {  // depth r is settled after round r
+        const int pd = __shfl(d, edge ? par : 0);
+        if (d < 0 && edge && pd >= 0) d = pd + 1;
+    }
+    if (n < N) a.ws.tree_depth[(size_t)b * N + n] = d;
+    int32_t* path = a.ws.tree_path + ((size_t)b * N + min(n, N - 1)) * a.ws.tree_dmax;
+    int at = n;
+    for (int r = 0; r < N - 1; ++r) {  // path[d - 1 - r] = token of the r-th ancestor-or-self
+        const int t = __shfl(tok, at);
+        const int p = __shfl(par, at);
+        if (n < N && r < d) path[d - 1 - r] = t;
+        at = r < d ? p : at;
+    }
+}
+
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(NT) SS_TILE_OCC void k_tree_tiles(TreeArgs a) {
+    __shared__ SmemTile tt;
+    const int n_tiles = a.ws.n_tiles;
+    const int lin = xcd_linear(a.B * a.N * n_tiles);
+    const int row = lin / n_tiles;
+    const int tile = lin % n_tiles;
+    const RowCtx c = tree_ctx<DT>(a, row / a.N, row % a.N, a.ws.tree_depth[row]);
+    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt, nullptr, nullptr);
+}
+
+// Per node x: its filtered distribution, then its children tested in index
+// order against the residual target (one-hot proposals): child i with token d
+// is accepted iff u_i < p(d) / (1 - p of the siblings rejected before it), or
+// for greedy rows iff d is the greedy token. Records the accepted child.
+template <int DT>
+__global__ __launch_bounds__(NTR) void k_tree_rows(TreeArgs a) {
+    __shared__ SmemU su;
+    __shared__ SmemR sh;
+    const int row = xcd_linear(a.B * a.N);
+    const int b = row / a.N;
+    const int x = row % a.N;
+    const int depth = a.ws.tree_depth[row];
+    const RowLoad rl = row_load(a.ws, row);
+    const RowCtx c = tree_ctx<DT>(a, b, x, depth);
+    RowDbg dbg = {nullptr, 0, nullptr, nullptr, nullptr};
+    RowInfo info;
+    finalize_row<DT>(c, row, a.ws, rl, su, sh, dbg, info);
+    // every wave holds the request's tree (lane = node), so the children and
+    // their tokens are the same in every wave: the loop below is uniform
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int par = lane < a.N ? a.parents[(size_t)b * a.N + lane] : -1;
+    const int tok = lane < a.N ? a.tokens[(size_t)b * a.N + lane] : -1;
+    unsigned long long kids = __ballot(depth >= 0 && lane >= 1 && lane < a.N && par == x && x < lane);
+    int next = -1;
+    if (kids) {
+        if (c.T == 0.0f || info.n_kept == 0) {
+            const unsigned long long m = kids & __ballot(info.argmax >= 0 && tok == info.argmax);
+            next = m ? (int)__builtin_ctzll(m) : -1;
+        } else {
+            double remaining = 1.0;
+            unsigned long long rejected = 0;  // children rejected so far with a new token
+            for (int i = 0; kids; ++i) {
+                const int ch = (int)__builtin_ctzll(kids);
+                kids &= kids - 1;
+                const int d = __shfl(tok, ch);
+                const bool fresh = d >= 0 && d < a.V && (rejected & __ballot(tok == d)) == 0;
+                double pi = 0.0;
+                if (fresh) {
+                    const float xd = single_entry<DT>(c, d, sh);
+                    if (xd > NEG_INF) {
+                        const float zd = canon_zero(xd / c.T);
+                        const float w = expf(zd - info.zmax);
+                        const bool kept = key64(zd, d) >= info.kappa &&
+                                          (info.min_p <= 0.0f || w >= info.min_p);
+                        if (kept) pi = (double)w / info.W;
+                    }
+                }
+                const float ua = u24(philox_word(c.seed, c.req, c.pos, (uint32_t)i, DOM_ACCEPT));
+                const double ratio = remaining > 0.0 ? pi / remaining : 0.0;
+                if ((double)ua < ratio) {
+                    next = ch;
+                    break;
+                }
+                if (fresh) {
+                    rejected |= 1ull << ch;
+                    remaining -= pi;
+                }
+            }
+        }
+    }
+    if (threadIdx.x == 0) {
+        a.ws.tree_next[row] = next;
+        a.ws.rowinfo[row] = info;
+    }
+}
+
+// The accepted path of request b, walked in every wave from the root through
+// the accepted children (each deeper than the last, so at most N - 1 steps):
+// returns its length and the node it ends at; writer() sees each step.
+template <class F>
+__device__ __forceinline__ int tree_walk(const TreeArgs& a, int b, int& end, F writer) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int nx = lane < a.N ? a.ws.tree_next[(size_t)b * a.N + lane] : -1;
+    int cur = 0, k = 0;
+    for (int r = 0; r < a.N; ++r) {
+        const int nn = __shfl(nx, cur);
+        if (nn <= cur || nn >= a.N) break;
+        writer(k, nn);
+        cur = nn;
+        ++k;
+    }
+    end = cur;
+    return k;
+}
+
+// The tokens of node e's children (all rejected when e ends the path) into
+// set; returns their count. Whole workgroup; every wave computes the same.
+__device__ __forceinline__ int tree_kids(const TreeArgs& a, int b, int e, int32_t* set) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int par = lane < a.N ? a.parents[(size_t)b * a.N + lane] : -1;
+    const int tok = lane < a.N ? a.tokens[(size_t)b * a.N + lane] : -1;
+    const bool kid = lane >= 1 && lane < a.N && par == e && e < lane;
+    const unsigned long long m = __ballot(kid);
+    if (threadIdx.x < WAVE && kid)
+        set[__popcll(m & ((1ull << lane) - 1ull))] = tok;
+    __syncthreads();
+    return __popcll(m);
+}
+
+// Residual stage 1 of a request whose path ends at a node with children.
+template <int DT>
+__global__ __launch_bounds__(NT) SS_TILE_OCC void k_tree_resid_tiles(TreeArgs a) {
+    __shared__ SmemTile tt;
+    __shared__ SmemS sh;
+    __shared__ int32_t set[WAVE];
+    const int n_tiles = a.ws.n_tiles;
+    const int b = blockIdx.x / n_tiles;
+    const int tile = blockIdx.x % n_tiles;
+    int e;
+    tree_walk(a, b, e, [](int, int) {});
+    const int row = b * a.N + e;
+    const RowInfo ri = a.ws.rowinfo[row];
+    const int nk = tree_kids(a, b, e, set);
+    if (nk == 0 || a.p.temperature[b] == 0.0f || ri.n_kept == 0) return;
+    const RowCtx c = tree_ctx<DT>(a, b, e, a.ws.tree_depth[row]);
+    DraftQ qf;
+    qf.q = nullptr;
+    qf.d0 = -1;
+    qf.set = set;
+    qf.n = nk;
+    const double2 x = residual_sums<DT>(c, ri, qf, tile * TILE, tt, sh);
+    if (threadIdx.x == 0) a.ws.resid_tile[(size_t)b * n_tiles + tile] = x;
+}
+
+// Per request: the accepted path (tokens and nodes), then the final token: the
+// greedy token, the residual draw after the end node's children were all
+// rejected, or the end node's own draw at a leaf.
+template <int DT>
+__global__ __launch_bounds__(NT) void k_tree_finish(TreeArgs a) {
+    __shared__ SmemTile tt;
+    __shared__ SmemS sh;
+    __shared__ int32_t set[WAVE];
+    __shared__ int s_tile;
+    __shared__ int s_usepi;
+    __shared__ double s_rem;
+    const int b = blockIdx.x;
+    const int N = a.N;
+    int32_t* out_t = a.out_tokens + (size_t)b * N;
+    int32_t* out_n = a.out_nodes + (size_t)b * N;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int tok = lane < N ? a.tokens[(size_t)b * N + lane] : -1;
+    int e;
+    const int k = tree_walk(a, b, e, [&](int i, int node) {
+        const int t = __shfl(tok, node);
+        if (threadIdx.x == 0) {
+            out_t[i] = t;
+            out_n[i] = node;
+        }
+    });
+    const int row = b * N + e;
+    const RowInfo ri = a.ws.rowinfo[row];
+    const int nk = tree_kids(a, b, e, set);
+    int final_token;
+    if (a.p.temperature[b] == 0.0f || ri.n_kept == 0) {
+        final_token = ri.argmax;
+    } else if (nk == 0) {
+        final_token = ri.token;
+    } else {
+        const RowCtx c = tree_ctx<DT>(a, b, e, a.ws.tree_depth[row]);
+        DraftQ qf;
+        qf.q = nullptr;
+        qf.d0 = -1;
+        qf.set = set;
+        qf.n = nk;
+        final_token = residual_draw<DT>(c, ri, qf, a.ws.resid_tile + (size_t)b * a.ws.n_tiles,
+                                        a.ws.n_tiles, tt, sh, s_tile, s_usepi, s_rem);
+    }
+    if (threadIdx.x == 0) {
+        out_t[k] = final_token;
+        for (int i = k + 1; i < N; ++i) out_t[i] = -1;
+        for (int i = k; i < N; ++i) out_n[i] = -1;
+        a.out_num_accepted[b] = k;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 
 // Every row starts 16-byte aligned and V is a whole number of 16-byte groups:
@@ -2127,6 +2390,25 @@ static void spec_chain(const SpecArgs& a, hipStream_t st, const LaunchEvents& le
     launch_k(le, 1, k_spec_rows<DT>, dim3(rows), dim3(NTR), st, a);
     launch_k(le, 2, k_spec_resid_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
     launch_k(le, 3, k_spec_finish<DT>, dim3(a.B), dim3(NT), st, a);
+}
+
+template <int DT>
+static void tree_chain(const TreeArgs& a, hipStream_t st, const LaunchEvents& le) {
+    const int rows = a.B * a.N;
+    launch_k(le, 0, k_tree_paths, dim3(a.B), dim3(WAVE), st, a);
+    if (rows_aligned<DT>(a.target, a.row_stride, a.V))
+        launch_k(le, 1, k_tree_tiles<DT, true>, dim3(rows * a.ws.n_tiles), dim3(NT), st, a);
+    else
+        launch_k(le, 1, k_tree_tiles<DT, false>, dim3(rows * a.ws.n_tiles), dim3(NT), st, a);
+    launch_k(le, 2, k_tree_rows<DT>, dim3(rows), dim3(NTR), st, a);
+    launch_k(le, 3, k_tree_resid_tiles<DT>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
+    launch_k(le, 4, k_tree_finish<DT>, dim3(a.B), dim3(NT), st, a);
+}
+
+hipError_t launch_tree(const TreeArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le) {
+    if (dt == SS_F32) tree_chain<SS_F32>(a, st, le);
+    else tree_chain<SS_BF16>(a, st, le);
+    return hipGetLastError();
 }
 
 hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le) {

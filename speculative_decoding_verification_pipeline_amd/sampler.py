@@ -26,7 +26,8 @@ SS_BF16 = 1
 
 EXPORTED = ("ss_sampler_create", "ss_sampler_destroy", "ss_status_string",
             "ss_sampler_workspace_bytes", "ss_sampler_set_launch_events", "ss_sample",
-            "ss_spec_verify", "ss_spec_verify_scatter", "ss_lmhead_sample", "ss_sample_noalloc")
+            "ss_spec_verify", "ss_spec_verify_scatter", "ss_tree_verify", "ss_lmhead_sample",
+            "ss_sample_noalloc")
 NOALLOC_MAX_BATCH = 64
 NOALLOC_MAX_ENTRIES = 1 << 23
 
@@ -100,6 +101,9 @@ def load_library(path=None):
                                            ctypes.POINTER(CParams), vp, vp,
                                            ctypes.POINTER(CSequences), vp]
     lib.ss_spec_verify_scatter.restype = i32
+    lib.ss_tree_verify.argtypes = [vp, vp, i32, i64, vp, vp, i32, i32, ctypes.POINTER(CParams),
+                                   vp, vp, vp, vp]
+    lib.ss_tree_verify.restype = i32
     lib.ss_lmhead_sample.argtypes = [vp, vp, vp, i32, vp, vp, vp, u64, vp, vp, vp]
     lib.ss_lmhead_sample.restype = i32
     lib.ss_sample_noalloc.argtypes = [vp, i32, i64, i32, i32, ctypes.POINTER(CParams), vp, vp]
@@ -393,6 +397,42 @@ class Sampler:
             ctypes.byref(seq) if seq is not None else None, _stream(stream))
         _check("ss_spec_verify_scatter", st)
         return out_tokens, out_num_accepted
+
+    def tree_verify(self, target_logits, parents, tokens, params: SamplingParams, out_tokens=None,
+                    out_nodes=None, out_num_accepted=None, stream=None):
+        """Verify one draft tree per request: target_logits [B, N, V] (row n after
+        the root path to node n), parents / tokens [B, N] int32. Returns
+        (tokens [B, N], nodes [B, N], num_accepted [B])."""
+        _check_dev(target_logits, "target_logits", (torch.float32, torch.bfloat16), self.device)
+        _require(target_logits.dim() == 3, "target_logits must be [B, N, V]")
+        B, N, V = target_logits.shape
+        _require(V == self.vocab_size, f"target_logits have {V} columns, the sampler {self.vocab_size}")
+        _require(target_logits.stride(2) == 1 and
+                 (B <= 1 or target_logits.stride(0) == N * target_logits.stride(1)),
+                 "target_logits rows must be evenly spaced with unit stride along V")
+        for name, t in (("parents", parents), ("tokens", tokens)):
+            _check_dev(t, name, (torch.int32,), self.device)
+            _require(tuple(t.shape) == (B, N) and t.is_contiguous(),
+                     f"{name} must be a contiguous [B, N] int32 array")
+        dev = target_logits.device
+        if out_tokens is None:
+            out_tokens = torch.empty(B, N, dtype=torch.int32, device=dev)
+        if out_nodes is None:
+            out_nodes = torch.empty(B, N, dtype=torch.int32, device=dev)
+        if out_num_accepted is None:
+            out_num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+        for name, t in (("out_tokens", out_tokens), ("out_nodes", out_nodes)):
+            _check_dev(t, name, (torch.int32,), self.device)
+            _require(tuple(t.shape) == (B, N) and t.is_contiguous(),
+                     f"{name} must be a contiguous [B, N] int32 array")
+        _check_vec(out_num_accepted, "out_num_accepted", B, torch.int32, self.device)
+        cp = params.to_c(params.validate(B, V, self.device, mask_rows=N))
+        st = self.lib.ss_tree_verify(self.handle, _ptr(target_logits), self._dtype(target_logits),
+                                     int(target_logits.stride(1)), _ptr(parents), _ptr(tokens), B,
+                                     N, ctypes.byref(cp), _ptr(out_tokens), _ptr(out_nodes),
+                                     _ptr(out_num_accepted), _stream(stream))
+        _check("ss_tree_verify", st)
+        return out_tokens, out_nodes, out_num_accepted
 
     def lmhead_sample(self, hidden, weight, temperature, request_ids=None, positions=None,
                       seed=0, out=None, debug_logits=None, stream=None):

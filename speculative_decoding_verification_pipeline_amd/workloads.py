@@ -26,6 +26,11 @@ Recipes (all numpy PCG64 generators; data seeds 101..105 are fixed here):
                   (T=0), the others T=1 with no filters.
   lmhead          hidden [64, 8192] bf16 from N(0,1); weight [128256, 8192] bf16
                   from N(0, 0.02^2); T=1.0.
+  tree            B=32 requests, N=16-node static draft trees (4 children at the
+                  root, 2 below each, then chains), V=128256 f32 Zipf target
+                  rows per node; children carry the top tokens of draft logits
+                  = target row + N(0, 0.5); 16 requests greedy, the others T=1
+                  with no filters.
 """
 from __future__ import annotations
 
@@ -223,3 +228,75 @@ def lmhead(B=64, K=8192, V=128256, seed=105, chunk=4096):
         weight[v0:v0 + n] = f32_to_bf16_bits(w)
     return LMHeadWorkload(hidden, weight, np.ones(B, np.float32),
                           np.arange(B, dtype=np.int32), np.zeros(B, np.int32), seed=0)
+
+
+@dataclass
+class TreeWorkload:
+    target: np.ndarray       # [B, N, V] float32
+    parents: np.ndarray      # [B, N] int32
+    tokens: np.ndarray       # [B, N] int32
+    temperature: np.ndarray
+    top_k: np.ndarray
+    top_p: np.ndarray
+    min_p: np.ndarray
+    request_ids: np.ndarray
+    positions: np.ndarray
+    seed: int = 0
+
+    @property
+    def B(self):
+        return self.target.shape[0]
+
+    @property
+    def N(self):
+        return self.target.shape[1]
+
+    @property
+    def V(self):
+        return self.target.shape[2]
+
+
+def tree_shape(N, branching=(4, 2, 1)):
+    """Parent indices of a static draft tree of N nodes built breadth-first:
+    each node at depth k gets branching[k] children (the last entry repeats)
+    until N nodes exist."""
+    parents = [-1]
+    frontier = [0]
+    k = 0
+    while len(parents) < N and frontier:
+        nxt = []
+        for p in frontier:
+            for _ in range(branching[min(k, len(branching) - 1)]):
+                if len(parents) == N:
+                    break
+                parents.append(p)
+                nxt.append(len(parents) - 1)
+        frontier = nxt
+        k += 1
+    return np.array(parents, dtype=np.int32)
+
+
+def tree(B=32, N=16, V=128256, seed=107, n_greedy=None, branching=(4, 2, 1)):
+    """Draft trees: the same static shape for every request; each node's
+    children carry its draft's top-K tokens, the draft logits being the target
+    row plus N(0, 0.5) noise. Target rows are Zipf rows; half the requests are
+    greedy (T = 0), the others T = 1 with no filters."""
+    rng = np.random.default_rng(seed)
+    target = zipf_rows(rng, B * N, V).reshape(B, N, V)
+    parents = np.tile(tree_shape(N, branching), (B, 1))
+    tokens = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        for x in range(N):
+            kids = np.nonzero(parents[b] == x)[0]
+            kids = kids[kids > 0]
+            if kids.size == 0:
+                continue
+            draft = target[b, x].astype(np.float64) + rng.normal(0.0, 0.5, V)
+            top = np.argsort(-draft, kind="stable")[:kids.size]
+            tokens[b, kids] = top.astype(np.int32)
+    n_greedy = B // 2 if n_greedy is None else n_greedy
+    T = np.ones(B, dtype=np.float32)
+    T[rng.permutation(B)[:n_greedy]] = 0.0
+    return TreeWorkload(target, parents, tokens, T, np.zeros(B, np.int32), np.ones(B, np.float32),
+                        np.zeros(B, np.float32), np.arange(B, dtype=np.int32),
+                        np.zeros(B, np.int32), seed=0)

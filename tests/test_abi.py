@@ -26,9 +26,10 @@ def lib():
     return sampler.load_library()
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for f in ("ss_sampler_create", "ss_sample", "ss_spec_verify", "ss_lmhead_sample"):
+    for f in ("ss_sampler_create", "ss_sample", "ss_spec_verify", "ss_spec_verify_scatter",
+              "ss_tree_verify", "ss_lmhead_sample", "ss_sample_noalloc"):
         assert f in fns
 
 
@@ -53,7 +54,7 @@ def test_create_rejects_bad_limits_before_touching_hip(lib):
     from speculative_decoding_verification_pipeline_amd import sampler
     h = ctypes.c_void_p()
     bad = [sampler.Config(0, 100, 0, 0, 0), sampler.Config(4, 0, 0, 0, 0),
-           sampler.Config(4, 300000, 0, 0, 0), sampler.Config(4, 100, 17, 0, 0),
+           sampler.Config(4, 300000, 0, 0, 0), sampler.Config(4, 100, 64, 0, 0),
            sampler.Config(4, 100, 0, 100, 0), sampler.Config(4, 100, 0, 0, -1)]
     for cfg in bad:
         assert lib.ss_sampler_create(ctypes.byref(cfg), ctypes.byref(h)) == sampler.SS_ERR_INVALID_ARG
@@ -69,6 +70,10 @@ def test_calls_reject_null_handle(lib):
                               None, None) == sampler.SS_ERR_INVALID_ARG
     assert lib.ss_lmhead_sample(None, None, None, 1, None, None, None, 0, None, None,
                                 None) == sampler.SS_ERR_INVALID_ARG
+    assert lib.ss_tree_verify(None, None, 0, 0, None, None, 1, 2, ctypes.byref(p), None, None,
+                              None, None) == sampler.SS_ERR_INVALID_ARG
+    assert lib.ss_spec_verify_scatter(None, None, 0, 0, None, 0, None, 1, 1, ctypes.byref(p), None,
+                                      None, None, None) == sampler.SS_ERR_INVALID_ARG
     assert lib.ss_sampler_workspace_bytes(None) == 0
     assert lib.ss_sampler_set_launch_events(None, None, 0) == sampler.SS_ERR_INVALID_ARG
     lib.ss_sampler_destroy(None)

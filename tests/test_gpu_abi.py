@@ -161,6 +161,32 @@ def test_spec_verify_rejects_bad_arguments(live):
         SM.SS_ERR_INVALID_ARG
 
 
+def test_tree_verify_rejects_bad_arguments(live):
+    N = G + 1
+    tgt = _logits(B * N)
+    par = torch.zeros(B, N, dtype=torch.int32, device=device())
+    tok = torch.zeros(B, N, dtype=torch.int32, device=device())
+    ot = torch.empty(B, N, dtype=torch.int32, device=device())
+    on = torch.empty(B, N, dtype=torch.int32, device=device())
+    na = torch.empty(B, dtype=torch.int32, device=device())
+    p = SM.SamplingParams(temperature=_temps(1.0)).to_c()
+
+    def call(n=N, rows=B, row_stride=V, parents=True, outs=True):
+        return live.lib.ss_tree_verify(live.handle, _vp(tgt), SM.SS_F32, row_stride,
+                                       _vp(par) if parents else None, _vp(tok), rows, n,
+                                       ctypes.byref(p), _vp(ot), _vp(on) if outs else None, _vp(na),
+                                       None)
+
+    assert call() == SM.SS_OK
+    assert call(rows=0, parents=False, outs=False) == SM.SS_OK
+    bad = {"N above max_draft + 1": dict(n=N + 1), "N of one node": dict(n=1),
+           "batch above max_batch": dict(rows=B + 1), "row stride below V": dict(row_stride=V - 1),
+           "null parents": dict(parents=False), "null out_nodes": dict(outs=False)}
+    for name, kw in bad.items():
+        log(f"abi: ss_tree_verify with {name}")
+        assert call(**kw) == SM.SS_ERR_INVALID_ARG, name
+
+
 def test_lmhead_rejects_bad_arguments(live):
     g = torch.Generator().manual_seed(1)
     h = (torch.randn(B, K, generator=g) * 0.1).to(device(), torch.bfloat16)
