@@ -24,9 +24,14 @@ from __future__ import annotations
 import numpy as np
 
 from . import philox
+from . import pipeline as P
 from .pipeline import bf16_bits_to_f32
 
 GAP_EPS = 1e-5
+# A processed row's filter cuts move with the GEMM's rounding (binary32
+# accumulation over K, about 1e-5 in logit units at K = 8192): a cut whose
+# deciding quantity lies within this distance is a boundary case.
+CUT_EPS = 1e-4
 TILE = 256
 
 
@@ -95,3 +100,74 @@ def sample(z, temperature, request_ids, positions, seed):
         toks[b], gap = argmax_and_gap(s)
         flags[b] = gap < GAP_EPS
     return toks, flags
+
+
+def sample_processed(z, params: P.Params):
+    """The per-request sampling pipeline applied to LM-head logits before the
+    Gumbel step (SonicSampler abstract: penalties, bias, grammar mask,
+    temperature, top-k / top-p / min-p per request in one batched pass;
+    FlashSampling news item: Gumbel-max sampling folded into the LM-head GEMM).
+
+    Reading, row b: x = binary32(z[b]) (z is the binary64 GEMM); x' =
+    pipeline.process_row(x, ...) with the request's history, bias and mask;
+    the filtered support K = pipeline.filter_row(x', T, top_k, top_p, min_p);
+    T > 0: the token is the lowest id attaining the largest s_v = z'_v + g_v
+    over v in K, with z'_v = binary32(x'_v / T) (the sampler's z) and g_v the
+    Gumbel variate of the GUMBEL word at (seed, request, position, draw v) --
+    Gumbel-max over K samples exactly from the filtered distribution. T = 0:
+    the greedy token. Returns (tokens, flags); a row is flagged when its two
+    largest scores (largest x' for T = 0) lie within GAP_EPS, or when a cut
+    lies within CUT_EPS of its threshold: the k-th and (k+1)-th z' of a cutting
+    top-k, a top-p crossing (the exclusive masses pipeline.filter_row compares
+    with top_p), or a weight next to min_p."""
+    B, V = z.shape
+    toks = np.full(B, -1, dtype=np.int32)
+    flags = np.zeros(B, dtype=bool)
+    for b in range(B):
+        pr = params.row(b)
+        x = np.asarray(z[b], dtype=np.float64).astype(np.float32)
+        xp = P.process_row(x, pr["hist"], pr["rep"], pr["freq"], pr["pres"], pr["bias_ids"],
+                           pr["bias_vals"], pr["mask"])
+        T = float(np.float32(params.temperature[b]))
+        filt = P.filter_row(xp, T, int(params.top_k[b]), float(params.top_p[b]),
+                            float(params.min_p[b]))
+        if filt.n_kept == 0:
+            continue
+        if filt.greedy:
+            toks[b] = filt.argmax
+            fin = np.sort(xp[np.isfinite(xp)].astype(np.float64))
+            flags[b] = fin.size > 1 and fin[-1] - fin[-2] < GAP_EPS
+            continue
+        kept = filt.order[:filt.n_kept]
+        zk = (xp[kept] / np.float32(T)).astype(np.float32) + np.float32(0.0)
+        g = philox.gumbel_np(philox.words_np(params.seed, pr["request"], pr["position"], kept,
+                                             philox.GUMBEL))
+        sc = zk.astype(np.float64) + g
+        best = np.max(sc)
+        toks[b] = int(np.min(kept[sc == best]))
+        top2 = np.sort(sc)[-2:] if sc.size > 1 else None
+        flag = top2 is not None and top2[1] - top2[0] < GAP_EPS
+        flag = flag or _cut_near(filt, xp, T, params, b)
+        flags[b] = flag
+    return toks, flags
+
+
+def _cut_near(filt, xp, T, params, b):
+    """True when a filter cut of the row lies within CUT_EPS of its threshold."""
+    zo = np.log(filt.w)  # z' - max z' in key order
+    n = filt.order.size
+    if filt.topk_active and filt.n_topk < n and zo[filt.n_topk - 1] - zo[filt.n_topk] < CUT_EPS:
+        return True
+    tp = float(np.float32(params.top_p[b]))
+    if tp < 1.0:
+        pk = filt.w[:filt.n_topk] / filt.w[:filt.n_topk].sum()
+        excl = np.concatenate(([0.0], np.cumsum(pk)[:-1]))
+        near = [excl[filt.n_topp - 1]] if filt.n_topp > 1 else []
+        if filt.n_topp < filt.n_topk:
+            near.append(excl[filt.n_topp])
+        if any(abs(e - tp) < CUT_EPS for e in near):
+            return True
+    mp = float(np.float32(params.min_p[b]))
+    if mp > 0.0 and np.any(np.abs(filt.w[1:filt.n_topp] - mp) < CUT_EPS):
+        return True
+    return False

@@ -4,13 +4,20 @@ Gumbel-max theorem (textbook): argmax(z / T + Gumbel noise) is distributed as
 softmax(z / T); checked by chi-square. Partition invariance (argmax decomposes
 over any tiling of the vocabulary, the property the FlashSampling page relies
 on). The binary64 GEMM against exactly rounded sums of exact products.
+
+The per-request pipeline before the Gumbel step: it reduces to the plain
+draw without processing, top_k = 1 gives the argmax of the processed logits,
+the draws follow the filtered distribution (chi-square), and the cut flags
+fire on either side of their distance.
 """
 import math
 
 import numpy as np
+import pytest
 from scipy import stats
 
 from oracle import lmhead as L
+from oracle import lmhead as OL
 from oracle import pipeline as P
 
 
@@ -82,3 +89,81 @@ def test_greedy_and_tiled_sample_agree():
     for b in range(1, 5):
         s = L.scores_row(z[b], T[b], 11, req[b], pos[b])
         assert toks[b] == L.reduce_partials(*L.tile_partials(s))
+
+
+# --- the per-request pipeline before the Gumbel step ---------------------------
+
+def _params(B, T, **kw):
+    from oracle import pipeline as P
+    n = lambda v, dt: np.full(B, v, dt)
+    return P.Params(temperature=np.asarray(T, np.float32) if np.ndim(T) else n(T, np.float32),
+                    top_k=kw.get("top_k", n(0, np.int32)), top_p=kw.get("top_p", n(1.0, np.float32)),
+                    min_p=kw.get("min_p", n(0.0, np.float32)), rep=kw.get("rep"),
+                    freq=kw.get("freq"), pres=kw.get("pres"), hist=kw.get("hist"),
+                    bias_ids=kw.get("bias_ids"), bias_vals=kw.get("bias_vals"),
+                    mask=kw.get("mask"), request_ids=np.arange(B, dtype=np.int32) * 5 + 1,
+                    positions=np.arange(B, dtype=np.int32) % 3, seed=kw.get("seed", 9))
+
+
+def test_processed_reduces_to_plain_gumbel_max():
+    # no processing and no filter: the plain Gumbel-max draw (the two differ
+    # only by binary32 rounding of z / T, far inside the flag gap)
+    rng = np.random.default_rng(41)
+    B, V = 24, 500
+    z = rng.standard_normal((B, V)) * 2.0
+    T = rng.choice(np.array([0.0, 0.5, 1.0, 2.0], np.float32), B)
+    prm = _params(B, T)
+    got, gflags = OL.sample_processed(z, prm)
+    want, wflags = OL.sample(z, T, prm.request_ids, prm.positions, prm.seed)
+    ok = gflags | wflags | (got == want)
+    assert ok.all(), np.nonzero(~ok)
+
+
+def test_processed_top_k_one_is_the_argmax_of_processed_logits():
+    rng = np.random.default_rng(42)
+    B, V = 16, 300
+    z = rng.standard_normal((B, V)) * 3.0
+    hist = [rng.integers(0, V, 8) for _ in range(B)]
+    for b in range(B):
+        hist[b][0] = int(np.argmax(z[b]))  # penalise the raw argmax
+    prm = _params(B, 1.0, top_k=np.ones(B, np.int32), rep=np.full(B, 3.0, np.float32),
+                  freq=np.full(B, 1.0, np.float32), pres=np.full(B, 0.5, np.float32), hist=hist)
+    toks, _ = OL.sample_processed(z, prm)
+    for b in range(B):
+        xp = P.process_row(z[b].astype(np.float32), hist[b], 3.0, 1.0, 0.5, (), (), None)
+        assert toks[b] == int(np.argmax(xp))
+        assert toks[b] != int(np.argmax(z[b]))
+
+
+def test_processed_draws_follow_the_filtered_distribution():
+    from scipy import stats
+    V, n = 8, 6000
+    z = np.random.default_rng(43).standard_normal((1, V)) * 1.5
+    counts = np.zeros(V)
+    for sd in range(n):
+        prm = _params(1, 1.0, top_k=np.array([5], np.int32), top_p=np.array([0.95], np.float32),
+                      seed=sd)
+        t, _ = OL.sample_processed(z, prm)
+        counts[t[0]] += 1
+    pi = P.filter_row(z[0].astype(np.float32), 1.0, 5, 0.95, 0.0).probs
+    assert counts[pi == 0].sum() == 0
+    assert stats.chisquare(counts[pi > 0], pi[pi > 0] * n).pvalue > 1e-4
+
+
+@pytest.mark.parametrize("delta,flag", [(0.9e-4, True), (1.1e-4, False)])
+def test_processed_top_k_cut_flag(delta, flag):
+    # the 2nd and 3rd logits straddle a top-2 cut, delta apart
+    z = np.array([[2.0, 1.0, 1.0 - delta, -1.0]])
+    prm = _params(1, 1.0, top_k=np.array([2], np.int32))
+    _, flags = OL.sample_processed(z, prm)
+    assert bool(flags[0]) is flag
+
+
+@pytest.mark.parametrize("delta,flag", [(0.9e-4, True), (1.1e-4, False)])
+def test_processed_top_p_cut_flag(delta, flag):
+    # equal logits: exclusive masses 0, 1/4, 1/2, 3/4; top_p = 1/2 + delta puts
+    # the third token's exclusive mass delta below the threshold
+    z = np.zeros((1, 4))
+    prm = _params(1, 1.0, top_p=np.array([0.5 + delta], np.float32))
+    _, flags = OL.sample_processed(z, prm)
+    assert bool(flags[0]) is flag
