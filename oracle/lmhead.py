@@ -102,7 +102,22 @@ def sample(z, temperature, request_ids, positions, seed):
     return toks, flags
 
 
-def sample_processed(z, params: P.Params):
+def processed_rows(z, params: P.Params):
+    """(x', filtered row) of every row of z: the seed-independent part of
+    sample_processed, for tests that sweep seeds over fixed logits."""
+    out = []
+    for b in range(z.shape[0]):
+        pr = params.row(b)
+        x = np.asarray(z[b], dtype=np.float64).astype(np.float32)
+        xp = P.process_row(x, pr["hist"], pr["rep"], pr["freq"], pr["pres"], pr["bias_ids"],
+                           pr["bias_vals"], pr["mask"])
+        filt = P.filter_row(xp, float(np.float32(params.temperature[b])), int(params.top_k[b]),
+                            float(params.top_p[b]), float(params.min_p[b]))
+        out.append((xp, filt))
+    return out
+
+
+def sample_processed(z, params: P.Params, rows=None):
     """The per-request sampling pipeline applied to LM-head logits before the
     Gumbel step (SonicSampler abstract: penalties, bias, grammar mask,
     temperature, top-k / top-p / min-p per request in one batched pass;
@@ -116,21 +131,20 @@ def sample_processed(z, params: P.Params):
     Gumbel variate of the GUMBEL word at (seed, request, position, draw v) --
     Gumbel-max over K samples exactly from the filtered distribution. T = 0:
     the greedy token. Returns (tokens, flags); a row is flagged when its two
-    largest scores (largest x' for T = 0) lie within GAP_EPS, or when a cut
-    lies within CUT_EPS of its threshold: the k-th and (k+1)-th z' of a cutting
-    top-k, a top-p crossing (the exclusive masses pipeline.filter_row compares
-    with top_p), or a weight next to min_p."""
+    largest scores (largest x' for T = 0) lie within GAP_EPS, or when an entry
+    whose membership of the support a change of z' by CUT_EPS could flip (z'
+    near a cutting top-k's boundary, an exclusive mass near top_p, a weight
+    near min_p) is the winner or scores within GAP_EPS of it. rows:
+    processed_rows() of the same z and parameters, or None."""
     B, V = z.shape
     toks = np.full(B, -1, dtype=np.int32)
     flags = np.zeros(B, dtype=bool)
+    if rows is None:
+        rows = processed_rows(z, params)
     for b in range(B):
         pr = params.row(b)
-        x = np.asarray(z[b], dtype=np.float64).astype(np.float32)
-        xp = P.process_row(x, pr["hist"], pr["rep"], pr["freq"], pr["pres"], pr["bias_ids"],
-                           pr["bias_vals"], pr["mask"])
         T = float(np.float32(params.temperature[b]))
-        filt = P.filter_row(xp, T, int(params.top_k[b]), float(params.top_p[b]),
-                            float(params.min_p[b]))
+        xp, filt = rows[b]
         if filt.n_kept == 0:
             continue
         if filt.greedy:
@@ -139,35 +153,50 @@ def sample_processed(z, params: P.Params):
             flags[b] = fin.size > 1 and fin[-1] - fin[-2] < GAP_EPS
             continue
         kept = filt.order[:filt.n_kept]
-        zk = (xp[kept] / np.float32(T)).astype(np.float32) + np.float32(0.0)
-        g = philox.gumbel_np(philox.words_np(params.seed, pr["request"], pr["position"], kept,
-                                             philox.GUMBEL))
-        sc = zk.astype(np.float64) + g
+        req, pos = pr["request"], pr["position"]
+        sc = _scores(xp, kept, T, params.seed, req, pos)
         best = np.max(sc)
-        toks[b] = int(np.min(kept[sc == best]))
+        win = int(np.min(kept[sc == best]))
+        toks[b] = win
         top2 = np.sort(sc)[-2:] if sc.size > 1 else None
         flag = top2 is not None and top2[1] - top2[0] < GAP_EPS
-        flag = flag or _cut_near(filt, xp, T, params, b)
+        if not flag:
+            # entries a GEMM-sized change of z' could move across a cut: the
+            # draw changes only if the winner is one of them or one of them
+            # outscores it
+            amb = _ambiguous(filt, params, b)
+            if amb.size:
+                flag = win in set(amb.tolist()) or bool(
+                    np.any(_scores(xp, amb, T, params.seed, req, pos) > best - GAP_EPS))
         flags[b] = flag
     return toks, flags
 
 
-def _cut_near(filt, xp, T, params, b):
-    """True when a filter cut of the row lies within CUT_EPS of its threshold."""
+def _scores(xp, ids, T, seed, request, position):
+    """s_v = binary32(x'_v / T) + g_v for the given ids (binary64)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    zk = (xp[ids] / np.float32(T)).astype(np.float32) + np.float32(0.0)
+    g = philox.gumbel_np(philox.words_np(seed, request, position, ids, philox.GUMBEL))
+    return zk.astype(np.float64) + g
+
+
+def _ambiguous(filt, params, b):
+    """Ids whose membership of the kept support a change of z' by CUT_EPS could
+    flip: near a cutting top-k's boundary value, with an exclusive mass near
+    top_p, or with a weight near min_p (positions in key order, before the
+    respective cut's own inputs change)."""
     zo = np.log(filt.w)  # z' - max z' in key order
     n = filt.order.size
-    if filt.topk_active and filt.n_topk < n and zo[filt.n_topk - 1] - zo[filt.n_topk] < CUT_EPS:
-        return True
+    near = np.zeros(n, dtype=bool)
+    if filt.topk_active and filt.n_topk < n:
+        zc = 0.5 * (zo[filt.n_topk - 1] + zo[filt.n_topk])
+        near |= np.abs(zo - zc) < CUT_EPS
     tp = float(np.float32(params.top_p[b]))
     if tp < 1.0:
         pk = filt.w[:filt.n_topk] / filt.w[:filt.n_topk].sum()
         excl = np.concatenate(([0.0], np.cumsum(pk)[:-1]))
-        near = [excl[filt.n_topp - 1]] if filt.n_topp > 1 else []
-        if filt.n_topp < filt.n_topk:
-            near.append(excl[filt.n_topp])
-        if any(abs(e - tp) < CUT_EPS for e in near):
-            return True
+        near[1:filt.n_topk] |= np.abs(excl[1:] - tp) < CUT_EPS
     mp = float(np.float32(params.min_p[b]))
-    if mp > 0.0 and np.any(np.abs(filt.w[1:filt.n_topp] - mp) < CUT_EPS):
-        return True
-    return False
+    if mp > 0.0:
+        near[1:] |= np.abs(filt.w[1:] - mp) < CUT_EPS
+    return filt.order[near]

@@ -150,20 +150,31 @@ def test_processed_draws_follow_the_filtered_distribution():
     assert stats.chisquare(counts[pi > 0], pi[pi > 0] * n).pvalue > 1e-4
 
 
-@pytest.mark.parametrize("delta,flag", [(0.9e-4, True), (1.1e-4, False)])
+@pytest.mark.parametrize("delta,flag", [(1.9e-4, True), (2.1e-4, False)])
 def test_processed_top_k_cut_flag(delta, flag):
-    # the 2nd and 3rd logits straddle a top-2 cut, delta apart
-    z = np.array([[2.0, 1.0, 1.0 - delta, -1.0]])
-    prm = _params(1, 1.0, top_k=np.array([2], np.int32))
-    _, flags = OL.sample_processed(z, prm)
+    # top-1 between two logits delta apart: both lie within 1e-4 of the cut's
+    # midpoint when delta < 2e-4, and the winner (the only kept entry) is one
+    # of them, so the draw could change
+    z = np.array([[1.0, 1.0 - delta, -20.0]])
+    prm = _params(1, 1.0, top_k=np.array([1], np.int32))
+    toks, flags = OL.sample_processed(z, prm)
+    assert toks[0] == 0
     assert bool(flags[0]) is flag
 
 
-@pytest.mark.parametrize("delta,flag", [(0.9e-4, True), (1.1e-4, False)])
-def test_processed_top_p_cut_flag(delta, flag):
-    # equal logits: exclusive masses 0, 1/4, 1/2, 3/4; top_p = 1/2 + delta puts
-    # the third token's exclusive mass delta below the threshold
+def test_processed_top_p_cut_flag():
+    # equal logits: exclusive masses 0, 1/4, 1/2, 3/4 in id order. top_p =
+    # 1/2 + 0.9e-4 keeps tokens 0..2 with token 2's membership within the band:
+    # the row is flagged exactly when token 2 wins. At 1/2 + 1.1e-4 nothing is
+    # ambiguous and no seed is flagged.
     z = np.zeros((1, 4))
-    prm = _params(1, 1.0, top_p=np.array([0.5 + delta], np.float32))
-    _, flags = OL.sample_processed(z, prm)
-    assert bool(flags[0]) is flag
+    won_by_2 = 0
+    for sd in range(40):
+        prm = _params(1, 1.0, top_p=np.array([0.5 + 0.9e-4], np.float32), seed=sd)
+        toks, flags = OL.sample_processed(z, prm)
+        assert toks[0] in (0, 1, 2)
+        assert bool(flags[0]) == bool(toks[0] == 2)
+        won_by_2 += toks[0] == 2
+        prm = _params(1, 1.0, top_p=np.array([0.5 + 1.1e-4], np.float32), seed=sd)
+        assert not OL.sample_processed(z, prm)[1][0]
+    assert 0 < won_by_2 < 40
