@@ -28,9 +28,11 @@ from . import pipeline as P
 from .pipeline import bf16_bits_to_f32
 
 GAP_EPS = 1e-5
-# A processed row's filter cuts move with the GEMM's rounding (binary32
-# accumulation over K, about 1e-5 in logit units at K = 8192): a cut whose
-# deciding quantity lies within this distance is a boundary case.
+# A processed row's scores and filter cuts move with the GEMM's rounding:
+# binary32 accumulation over K carries a relative error of about 1e-6 of the
+# logits' magnitude at K = 8192. In sample_processed both distances below are
+# scaled by Z = max(1, largest |x'| / T of the row): the top-two score gap
+# GAP_EPS Z, and CUT_EPS Z for the cuts.
 CUT_EPS = 1e-4
 TILE = 256
 
@@ -131,10 +133,11 @@ def sample_processed(z, params: P.Params, rows=None):
     Gumbel variate of the GUMBEL word at (seed, request, position, draw v) --
     Gumbel-max over K samples exactly from the filtered distribution. T = 0:
     the greedy token. Returns (tokens, flags); a row is flagged when its two
-    largest scores (largest x' for T = 0) lie within GAP_EPS, or when an entry
-    whose membership of the support a change of z' by CUT_EPS could flip (z'
-    near a cutting top-k's boundary, an exclusive mass near top_p, a weight
-    near min_p) is the winner or scores within GAP_EPS of it. rows:
+    largest scores (largest x' for T = 0) lie within GAP_EPS Z, or when an
+    entry whose membership of the support a change of z' by CUT_EPS Z could
+    flip (z' near a cutting top-k's boundary, an exclusive mass near top_p, a
+    weight near min_p) is the winner or scores within GAP_EPS Z of it, Z =
+    max(1, largest |x'| / T of the row). rows:
     processed_rows() of the same z and parameters, or None."""
     B, V = z.shape
     toks = np.full(B, -1, dtype=np.int32)
@@ -147,10 +150,11 @@ def sample_processed(z, params: P.Params, rows=None):
         xp, filt = rows[b]
         if filt.n_kept == 0:
             continue
+        fin = np.sort(xp[np.isfinite(xp)].astype(np.float64))
+        Z = max(1.0, float(np.max(np.abs(fin))) / (T if T > 0.0 else 1.0))
         if filt.greedy:
             toks[b] = filt.argmax
-            fin = np.sort(xp[np.isfinite(xp)].astype(np.float64))
-            flags[b] = fin.size > 1 and fin[-1] - fin[-2] < GAP_EPS
+            flags[b] = fin.size > 1 and fin[-1] - fin[-2] < GAP_EPS * Z
             continue
         kept = filt.order[:filt.n_kept]
         req, pos = pr["request"], pr["position"]
@@ -159,15 +163,15 @@ def sample_processed(z, params: P.Params, rows=None):
         win = int(np.min(kept[sc == best]))
         toks[b] = win
         top2 = np.sort(sc)[-2:] if sc.size > 1 else None
-        flag = top2 is not None and top2[1] - top2[0] < GAP_EPS
+        flag = top2 is not None and top2[1] - top2[0] < GAP_EPS * Z
         if not flag:
             # entries a GEMM-sized change of z' could move across a cut: the
             # draw changes only if the winner is one of them or one of them
             # outscores it
-            amb = _ambiguous(filt, params, b)
+            amb = _ambiguous(filt, params, b, CUT_EPS * Z)
             if amb.size:
                 flag = win in set(amb.tolist()) or bool(
-                    np.any(_scores(xp, amb, T, params.seed, req, pos) > best - GAP_EPS))
+                    np.any(_scores(xp, amb, T, params.seed, req, pos) > best - GAP_EPS * Z))
         flags[b] = flag
     return toks, flags
 
@@ -180,23 +184,22 @@ def _scores(xp, ids, T, seed, request, position):
     return zk.astype(np.float64) + g
 
 
-def _ambiguous(filt, params, b):
-    """Ids whose membership of the kept support a change of z' by CUT_EPS could
-    flip: near a cutting top-k's boundary value, with an exclusive mass near
-    top_p, or with a weight near min_p (positions in key order, before the
-    respective cut's own inputs change)."""
+def _ambiguous(filt, params, b, eps):
+    """Ids whose membership of the kept support a change of z' by eps could
+    flip: z' within eps of a cutting top-k's boundary value, an exclusive mass
+    within eps of top_p, or a weight within a factor 1 +- eps of min_p."""
     zo = np.log(filt.w)  # z' - max z' in key order
     n = filt.order.size
     near = np.zeros(n, dtype=bool)
     if filt.topk_active and filt.n_topk < n:
         zc = 0.5 * (zo[filt.n_topk - 1] + zo[filt.n_topk])
-        near |= np.abs(zo - zc) < CUT_EPS
+        near |= np.abs(zo - zc) < eps
     tp = float(np.float32(params.top_p[b]))
     if tp < 1.0:
         pk = filt.w[:filt.n_topk] / filt.w[:filt.n_topk].sum()
         excl = np.concatenate(([0.0], np.cumsum(pk)[:-1]))
-        near[1:filt.n_topk] |= np.abs(excl[1:] - tp) < CUT_EPS
+        near[1:filt.n_topk] |= np.abs(excl[1:] - tp) < eps
     mp = float(np.float32(params.min_p[b]))
     if mp > 0.0:
-        near[1:] |= np.abs(filt.w[1:] - mp) < CUT_EPS
+        near[1:] |= np.abs(filt.w[1:] - mp) < eps * mp
     return filt.order[near]

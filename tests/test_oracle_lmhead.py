@@ -155,11 +155,19 @@ def test_processed_top_k_cut_flag(delta, flag):
     # top-1 between two logits delta apart: both lie within 1e-4 of the cut's
     # midpoint when delta < 2e-4, and the winner (the only kept entry) is one
     # of them, so the draw could change
-    z = np.array([[1.0, 1.0 - delta, -20.0]])
+    z = np.array([[1.0, 1.0 - delta, -1.0]])  # |x'| <= 1: the bands are unscaled
     prm = _params(1, 1.0, top_k=np.array([1], np.int32))
     toks, flags = OL.sample_processed(z, prm)
     assert toks[0] == 0
     assert bool(flags[0]) is flag
+
+
+@pytest.mark.parametrize("delta,flag", [(1.9e-3, True), (2.1e-3, False)])
+def test_processed_flag_bands_scale_with_the_logits(delta, flag):
+    # the same top-1 cut with logits of magnitude 10: the band is ten times wider
+    z = np.array([[10.0, 10.0 - delta, -10.0]])
+    prm = _params(1, 1.0, top_k=np.array([1], np.int32))
+    assert bool(OL.sample_processed(z, prm)[1][0]) is flag
 
 
 def test_processed_top_p_cut_flag():
