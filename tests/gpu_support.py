@@ -97,9 +97,10 @@ class Tally:
     2e-6 * n of the draws lie within 1e-6 of one, so the share rule cannot apply
     there; unflagged draws must still match exactly."""
 
-    def __init__(self, name, budget=True):
+    def __init__(self, name, budget=True, share=FLAG_BUDGET):
         self.name = name
         self.budget = budget
+        self.share = share
         self.draws = 0
         self.flagged = 0
         self.mismatch = []
@@ -119,7 +120,7 @@ class Tally:
             return
         # the share rule needs >= 10^4 draws to mean anything; smaller ad-hoc
         # cases may hold at most two flagged draws (all are reported above)
-        limit = FLAG_BUDGET * self.draws if self.draws >= 10_000 else 2
+        limit = self.share * self.draws if self.draws >= 10_000 else 2
         assert self.flagged < limit or (self.draws < 10_000 and self.flagged <= limit), \
             f"{self.name}: flagged share {self.flagged}/{self.draws}"
 

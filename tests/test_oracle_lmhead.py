@@ -150,10 +150,10 @@ def test_processed_draws_follow_the_filtered_distribution():
     assert stats.chisquare(counts[pi > 0], pi[pi > 0] * n).pvalue > 1e-4
 
 
-@pytest.mark.parametrize("delta,flag", [(1.9e-4, True), (2.1e-4, False)])
+@pytest.mark.parametrize("delta,flag", [(1.9e-5, True), (2.1e-5, False)])
 def test_processed_top_k_cut_flag(delta, flag):
-    # top-1 between two logits delta apart: both lie within 1e-4 of the cut's
-    # midpoint when delta < 2e-4, and the winner (the only kept entry) is one
+    # top-1 between two logits delta apart: both lie within 1e-5 of the cut's
+    # midpoint when delta < 2e-5, and the winner (the only kept entry) is one
     # of them, so the draw could change
     z = np.array([[1.0, 1.0 - delta, -1.0]])  # |x'| <= 1: the bands are unscaled
     prm = _params(1, 1.0, top_k=np.array([1], np.int32))
@@ -162,7 +162,7 @@ def test_processed_top_k_cut_flag(delta, flag):
     assert bool(flags[0]) is flag
 
 
-@pytest.mark.parametrize("delta,flag", [(1.9e-3, True), (2.1e-3, False)])
+@pytest.mark.parametrize("delta,flag", [(1.9e-4, True), (2.1e-4, False)])
 def test_processed_flag_bands_scale_with_the_logits(delta, flag):
     # the same top-1 cut with logits of magnitude 10: the band is ten times wider
     z = np.array([[10.0, 10.0 - delta, -10.0]])
@@ -172,17 +172,17 @@ def test_processed_flag_bands_scale_with_the_logits(delta, flag):
 
 def test_processed_top_p_cut_flag():
     # equal logits: exclusive masses 0, 1/4, 1/2, 3/4 in id order. top_p =
-    # 1/2 + 0.9e-4 keeps tokens 0..2 with token 2's membership within the band:
-    # the row is flagged exactly when token 2 wins. At 1/2 + 1.1e-4 nothing is
+    # 1/2 + 0.9e-5 keeps tokens 0..2 with token 2's membership within the band:
+    # the row is flagged exactly when token 2 wins. At 1/2 + 1.1e-5 nothing is
     # ambiguous and no seed is flagged.
     z = np.zeros((1, 4))
     won_by_2 = 0
     for sd in range(40):
-        prm = _params(1, 1.0, top_p=np.array([0.5 + 0.9e-4], np.float32), seed=sd)
+        prm = _params(1, 1.0, top_p=np.array([0.5 + 0.9e-5], np.float32), seed=sd)
         toks, flags = OL.sample_processed(z, prm)
         assert toks[0] in (0, 1, 2)
         assert bool(flags[0]) == bool(toks[0] == 2)
         won_by_2 += toks[0] == 2
-        prm = _params(1, 1.0, top_p=np.array([0.5 + 1.1e-4], np.float32), seed=sd)
+        prm = _params(1, 1.0, top_p=np.array([0.5 + 1.1e-5], np.float32), seed=sd)
         assert not OL.sample_processed(z, prm)[1][0]
     assert 0 < won_by_2 < 40
