@@ -443,6 +443,25 @@ def secondary(args, dev):
     st = stage_summary(time_stages(s, fn, lsteps, 2), ["k_lmhead", "k_lmhead_reduce"])
     g_us = st["k_lmhead"]["us_mean"]
     nbytes = V * K * 2 + B * K * 2
+    # the same GEMM with the per-request pipeline in its epilogue: the
+    # heterogeneous parameter recipe (penalties over 512 history ids, 16 bias
+    # ids, mixed T / top-k / top-p / min-p); rows whose cuts fall outside the
+    # tile candidates take the second pass
+    hw = W.heterogeneous(B=B, V=V)
+    hp = sampling_params(hw, dev)
+    lpath = torch.empty(B, dtype=torch.int32, device=dev)
+    s.lmhead_sample_params(Hd, Wd, hp, out=o, path=lpath)
+    torch.cuda.synchronize()
+    lp = np.bincount(lpath.cpu().numpy(), minlength=3).tolist()
+    pfn = [lambda: s.lmhead_sample_params(Hd, Wd, hp, out=o)]
+    pms, _ = time_graph(pfn, lsteps, 3)
+    pst = stage_summary(time_stages(s, pfn, lsteps, 4),
+                        ["k_lmhead_proc<stats>", "k_lm_merge", "k_lmhead_proc<second pass>",
+                         "k_lm_slow"])
+    out["lmhead_params"] = {"us_per_call": pms / lsteps * 1e3, "stages": pst,
+                            "tokens_per_s": B * lsteps / (pms * 1e-3),
+                            "rows_by_path": {"candidates": lp[0], "whole_row": lp[1],
+                                             "unfiltered_or_greedy": lp[2]}}
     out["lmhead"] = {"us_per_call": ms / lsteps * 1e3, "call_us": km * 1e3, "stages": st,
                      "tokens_per_s": B * lsteps / (ms * 1e-3),
                      "gemm_kernel_gbs": nbytes / (g_us * 1e-6) / 1e9,

@@ -327,6 +327,37 @@ ss_status ss_sample_noalloc(const void* logits, ss_dtype dtype, int64_t row_stri
                             int32_t V, const ss_params* params, int32_t* out_tokens,
                             void* stream);
 
+/* ss_lmhead_sample_params -- the fused LM-head GEMM with the whole per-request
+ * pipeline in its epilogue (SonicSampler abstract: penalties, bias, grammar
+ * mask, temperature and top-k / top-p / min-p per request in one batched pass;
+ * FlashSampling news item: Gumbel-max sampling folded into the GEMM so the
+ * logits stay on chip).
+ *   hidden, weight, B   as ss_lmhead_sample (K = hidden_size of the handle).
+ *   params              as ss_sample: temperature, filters, penalties over the
+ *                       history, logit bias, grammar mask (row b, mask_stride
+ *                       words apart), request ids, positions and seed.
+ *   out_tokens          [B] int32.
+ *   debug_path          NULL, or [B] int32: 0 = decided on the tile candidates,
+ *                       1 = decided over the whole row after the second pass,
+ *                       2 = no filter or greedy (the tiles' best scores).
+ * Each GEMM tile applies penalties, bias, mask and temperature to its logits
+ * (z' = x'/T as in ss_sample) and keeps, per batch row, its 4 largest keys, the
+ * next key, the mass below its maximum and its best Gumbel score. T = 0: the
+ * greedy token of x'. No filter: the lowest id attaining max z' + g (g from
+ * domain 3 at the token's id, as ss_lmhead_sample). With filters: the same
+ * maximum over the kept support (top-k, then top-p over the top-k mass, then
+ * min-p), which Gumbel-max samples from the filtered distribution exactly. The
+ * support is taken from the tiles' candidates whenever the cuts fall among the
+ * entries they certify (every key above the largest next key); other rows are
+ * formed again by a second GEMM pass into the workspace and selected over the
+ * whole row (that pass costs nothing when every row resolved).
+ * Launches four kernels (GEMM with summaries, row merge, the second GEMM pass,
+ * the whole-row selection). Errors: as ss_lmhead_sample, and the checks
+ * ss_sample makes on params. */
+ss_status ss_lmhead_sample_params(ss_sampler* s, const uint16_t* hidden, const uint16_t* weight,
+                                  int32_t B, const ss_params* params, int32_t* out_tokens,
+                                  int32_t* debug_path, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,8 @@ struct ss_sampler {
     int64_t ws_bytes;
     ss::Workspace ws;
     float2* lm_partials;
+    ss::LmTileStat* lm_stats;
+    int32_t* lm_unres;
     ss::LaunchEvents events;
     // defaults substituted for absent per-request parameters, [max_batch] each
     int32_t* def_zero_i;
@@ -276,6 +278,9 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     const int64_t o_tdepth = take(R * 4);
     const int64_t o_tnext = take(R * 4);
     const int64_t o_lmpart = cfg->hidden_size > 0 ? take(64 * (int64_t)s->n_vtiles * sizeof(float2)) : 0;
+    const int64_t o_lmstat =
+        cfg->hidden_size > 0 ? take(64 * (int64_t)s->n_vtiles * (int64_t)sizeof(ss::LmTileStat)) : 0;
+    const int64_t o_lmunres = cfg->hidden_size > 0 ? take(64 * 4) : 0;
     const int64_t o_defaults = take(4 * (int64_t)B * 4);
     s->ws_bytes = off;
     if (hipMalloc(&s->ws_base, (size_t)off) != hipSuccess) {
@@ -299,6 +304,8 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     w.n_wt = s->n_wt;
     w.V = V;
     s->lm_partials = cfg->hidden_size > 0 ? reinterpret_cast<float2*>(b + o_lmpart) : nullptr;
+    s->lm_stats = cfg->hidden_size > 0 ? reinterpret_cast<ss::LmTileStat*>(b + o_lmstat) : nullptr;
+    s->lm_unres = cfg->hidden_size > 0 ? reinterpret_cast<int32_t*>(b + o_lmunres) : nullptr;
     {
         int32_t* d = reinterpret_cast<int32_t*>(b + o_defaults);
         s->def_zero_i = d;
@@ -462,6 +469,38 @@ ss_status ss_tree_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
     return ss::launch_tree(a, dtype, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
                                                                                      : SS_ERR_HIP;
+}
+
+ss_status ss_lmhead_sample_params(ss_sampler* s, const uint16_t* hidden, const uint16_t* weight,
+                                  int32_t B, const ss_params* params, int32_t* out_tokens,
+                                  int32_t* debug_path, void* stream) {
+    if (!s || s->cfg.hidden_size <= 0) return SS_ERR_INVALID_ARG;
+    if (B < 1 || B > s->cfg.max_batch || B > 64) return SS_ERR_INVALID_ARG;
+    if (!hidden || !weight || !out_tokens) return SS_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(weight)) return SS_ERR_UNSUPPORTED;
+    const ss_status st = check_params(s->cfg.vocab_size, params);
+    if (st != SS_OK) return st;
+    ss::LmheadArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.hidden = hidden;
+    a.weight = weight;
+    a.B = B;
+    a.K = s->cfg.hidden_size;
+    a.V = s->cfg.vocab_size;
+    a.temperature = params->temperature;
+    a.seed = params->seed;
+    a.out_tokens = out_tokens;
+    a.partials = s->lm_partials;
+    a.n_vtiles = s->n_vtiles;
+    a.p = to_ptrs(defaults_of(s), params);
+    a.stats = s->lm_stats;
+    a.unres = s->lm_unres;
+    a.zmat = s->ws.scratch_z;
+    a.dbg_path = debug_path;
+    if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
+    return ss::launch_lmhead_params(a, static_cast<hipStream_t>(stream), s->events) == hipSuccess
+               ? SS_OK
+               : SS_ERR_HIP;
 }
 
 ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t* weight,

@@ -92,6 +92,12 @@ __device__ __forceinline__ int key64_id(unsigned long long k) {
     return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
 }
 
+// z of a key (the inverse of mono32 on its upper half).
+__device__ __forceinline__ float key_z(unsigned long long k) {
+    const uint32_t m = (uint32_t)(k >> 32);
+    return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+}
+
 // ---------------------------------------------------------------------------
 // wave64 lane exchange through DPP and the gfx950 permlane swaps (VALU, no LDS
 // round trip). Reductions pair lanes by mirrors (quad swap, half-row and row

@@ -143,6 +143,22 @@ struct TreeArgs {
     Workspace ws;
 };
 
+// Per (batch row, LM-head vocabulary tile) summary left by the processed
+// epilogue: the tile's LM_NC largest keys (z', id) in key order, the next one
+// (every other entry of the tile is at most it), the mass below the tile
+// maximum, the best Gumbel score and the count of finite entries.
+constexpr int LM_NC = 4;
+struct LmTileStat {
+    unsigned long long key[LM_NC];  // descending; 0 = none
+    unsigned long long rest;        // 0 = none
+    float mass;                     // sum of exp(z' - z'(key[0])) over the finite entries
+    float best_s;                   // the largest z' + g (T > 0) or x' (T = 0)
+    int best_i;                     // its id (the lowest among equals), INT_MAX if none
+    int nfinite;
+    int pad[2];
+};
+static_assert(sizeof(LmTileStat) == 64, "LmTileStat layout");
+
 struct LmheadArgs {
     const uint16_t* hidden;
     const uint16_t* weight;
@@ -157,6 +173,12 @@ struct LmheadArgs {
     float* debug_logits;
     float2* partials;        // [64 * n_vtiles] (score, id bits)
     int n_vtiles;
+    // the per-request pipeline in the epilogue (ss_lmhead_sample_params)
+    ParamPtrs p;
+    LmTileStat* stats;       // [64 * n_vtiles]
+    int32_t* unres;          // [64]: rows the candidates could not resolve
+    float* zmat;             // [64 * V]: z' of those rows, formed again
+    int32_t* dbg_path;       // [B] or null: 0 candidates, 1 whole row, 2 no filter or greedy
 };
 
 // Optional timing events of a call (see ss_sampler_set_launch_events): launch
@@ -183,5 +205,9 @@ hipError_t launch_sample(const SampleArgs& a, ss_dtype dt, hipStream_t st, const
 hipError_t launch_spec(const SpecArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le);
 hipError_t launch_tree(const TreeArgs& a, ss_dtype dt, hipStream_t st, const LaunchEvents& le);
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le);
+hipError_t launch_lmhead_params(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le);
+// the row kernels of ss_lmhead_sample_params (in the row-kernel source)
+void launch_lm_merge(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k);
+void launch_lm_slow(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k);
 
 }  // namespace ss

@@ -139,24 +139,12 @@ __device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
     return sa > sb || (sa == sb && ia < ib);
 }
 
-__global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t w0[LM_W_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t w1[LM_W_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t w2[LM_W_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t h0[LM_H_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t h1[LM_H_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t h2[LM_H_BYTES];
-    __shared__ float s_score[LM_NT / WAVE][LM_MAXB];
-    __shared__ int s_idx[LM_NT / WAVE][LM_MAXB];
-    const int tid = threadIdx.x;
-    const int lane = tid & (WAVE - 1);
-    const int wave = tid / WAVE;
-    const int tile = blockIdx.x;
-    const int half = lane >> 5;
-    const int r32 = lane & 31;
+// The GEMM of vocabulary tile `tile` into the two accumulators (the operand
+// stages are the six LDS buffers).
+__device__ __forceinline__ void lm_gemm(const LmheadArgs& a, int tile, floatx16 acc[2], uint8_t* w0,
+                                        uint8_t* w1, uint8_t* w2, uint8_t* h0, uint8_t* h1,
+                                        uint8_t* h2) {
     const int K = a.K;
-
-    floatx16 acc[2];
 #pragma unroll
     for (int y = 0; y < 2; ++y)
 #pragma unroll
@@ -192,6 +180,25 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
         LM_STEP(w2, h2, w1, h1, it + 2)
     }
 #undef LM_STEP
+}
+
+__global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t w0[LM_W_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t w1[LM_W_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t w2[LM_W_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t h0[LM_H_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t h1[LM_H_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t h2[LM_H_BYTES];
+    __shared__ float s_score[LM_NT / WAVE][LM_MAXB];
+    __shared__ int s_idx[LM_NT / WAVE][LM_MAXB];
+    const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    const int wave = tid / WAVE;
+    const int tile = blockIdx.x;
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+    floatx16 acc[2];
+    lm_gemm(a, tile, acc, w0, w1, w2, h0, h1, h2);
 
     // epilogue: lane holds, for batch column j = bb*32 + r32, vocabulary entries
     // tile*128 + wave*32 + 8*(r/4) + 4*half + (r%4)
@@ -257,6 +264,288 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// The per-request pipeline in the epilogue (ss_lmhead_sample_params).
+//
+// After the GEMM the stage buffers hold the tile's tables: per batch row, the
+// multiplicity of each of the tile's 128 entries in the row's history (u16)
+// and a bit per entry that some logit-bias entry names. Each entry's logit then
+// goes through penalties, bias (entries applied in array order), mask and
+// temperature as in the sampler, giving z'. MODE_STATS summarises each
+// (row, tile): its LM_NC largest keys (z', id), the next key, the mass below
+// its maximum, the best Gumbel score and the count of finite entries.
+// MODE_MAT writes z' of the rows the candidates could not resolve.
+
+constexpr int MODE_STATS = 1;
+constexpr int MODE_MAT = 2;
+constexpr int LM_NK = LM_NC + 1;  // keys kept per list: the candidates and the next one
+
+__device__ __forceinline__ float lm_penalize(float x, uint32_t count, float rep, float freq, float pres) {
+    x = (x > 0.0f) ? x / rep : x * rep;
+    const float fc = freq * (float)count;
+    x = x - fc;
+    x = x - pres;
+    return x;
+}
+
+// Inserts key k into the descending list t[0..LM_NK) (0 = empty slot).
+__device__ __forceinline__ void lm_insert(unsigned long long t[LM_NK], unsigned long long k) {
+#pragma unroll
+    for (int i = 0; i < LM_NK; ++i) {
+        const unsigned long long hi = t[i] > k ? t[i] : k;
+        const unsigned long long lo = t[i] > k ? k : t[i];
+        t[i] = hi;
+        k = lo;
+    }
+}
+
+// One list's summary while lists are merged.
+struct LmPart {
+    unsigned long long t[LM_NK];
+    float mass;      // relative to z of t[0]
+    float best_s;
+    int best_i;
+    int nfinite;
+};
+
+__device__ __forceinline__ void lm_combine(LmPart& x, const LmPart& y) {
+    const float zx = x.t[0] ? key_z(x.t[0]) : -FLT_MAX;
+    const float zy = y.t[0] ? key_z(y.t[0]) : -FLT_MAX;
+    const float zc = fmaxf(zx, zy);
+    float m = 0.0f;
+    if (x.t[0]) m += x.mass * expf(zx - zc);
+    if (y.t[0]) m += y.mass * expf(zy - zc);
+    x.mass = m;
+#pragma unroll
+    for (int i = 0; i < LM_NK; ++i)
+        if (y.t[i]) lm_insert(x.t, y.t[i]);
+    if (better(y.best_s, y.best_i, x.best_s, x.best_i)) {
+        x.best_s = y.best_s;
+        x.best_i = y.best_i;
+    }
+    x.nfinite += y.nfinite;
+}
+
+__device__ __forceinline__ LmPart lm_shfl_xor32(const LmPart& x) {
+    LmPart y;
+#pragma unroll
+    for (int i = 0; i < LM_NK; ++i) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x.t[i], 32);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x.t[i] >> 32), 32);
+        y.t[i] = ((unsigned long long)hi << 32) | lo;
+    }
+    y.mass = __shfl_xor(x.mass, 32);
+    y.best_s = __shfl_xor(x.best_s, 32);
+    y.best_i = __shfl_xor(x.best_i, 32);
+    y.nfinite = __shfl_xor(x.nfinite, 32);
+    return y;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t w0[LM_W_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t w1[LM_W_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t w2[LM_W_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t h0[LM_H_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t h1[LM_H_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t h2[LM_H_BYTES];
+    const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    const int wave = tid / WAVE;
+    const int tile = blockIdx.x;
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+    const ParamPtrs& p = a.p;
+    if (MODE == MODE_MAT) {
+        // only rows the candidates left open are formed again; none: no work
+        const bool open = lane < a.B && a.unres[lane] != 0;
+        if (__ballot(open) == 0ull) return;
+    }
+    floatx16 acc[2];
+    lm_gemm(a, tile, acc, w0, w1, w2, h0, h1, h2);
+
+    // the tables (every wave is past its last read of the stage buffers)
+    __syncthreads();
+    uint32_t* cnt = (uint32_t*)w0;       // [64][64]: two u16 multiplicities per word
+    uint32_t* bbits = (uint32_t*)w1;     // [64][4]: bias bit per entry
+    int* hl = (int*)(w1 + 1024);         // [64] history lengths
+    int* bl = hl + LM_MAXB;              // [64] bias lengths
+    for (int i = tid; i < LM_MAXB * LM_ROWS / 2; i += LM_NT) cnt[i] = 0u;
+    bbits[tid] = 0u;
+    if (tid < LM_MAXB) {
+        hl[tid] = tid < a.B ? min(p.hist_len[tid], p.hist_stride) : 0;
+        bl[tid] = tid < a.B ? min(p.bias_len[tid], p.bias_stride) : 0;
+    }
+    __syncthreads();
+    const int v0 = tile * LM_ROWS;
+    const int Hs = p.hist_stride;
+    if (Hs > 0) {
+        const int total = a.B * Hs;
+        constexpr int U = 8;  // loads in flight per thread
+        for (int f0 = tid; f0 < total; f0 += LM_NT * U) {
+            int ids[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int f = f0 + u * LM_NT;
+                const int j = f / Hs;
+                ids[u] = (f < total && f - j * Hs < hl[j]) ? p.hist_ids[f] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int f = f0 + u * LM_NT;
+                const int e = ids[u] - v0;
+                if (ids[u] >= 0 && ids[u] < a.V && e >= 0 && e < LM_ROWS)
+                    atomicAdd(&cnt[(f / Hs) * (LM_ROWS / 2) + (e >> 1)], 1u << ((e & 1) * 16));
+            }
+        }
+    }
+    const int Bs = p.bias_stride;
+    if (Bs > 0) {
+        for (int f = tid; f < a.B * Bs; f += LM_NT) {
+            const int j = f / Bs;
+            if (f - j * Bs >= bl[j]) continue;
+            const int id = p.bias_ids[f];
+            const int e = id - v0;
+            if (id >= 0 && id < a.V && e >= 0 && e < LM_ROWS) atomicOr(&bbits[j * 4 + (e >> 5)], 1u << (e & 31));
+        }
+    }
+    __syncthreads();
+
+    // each lane: for batch row j = bb*32 + r32, tile entries wave*32 + 8g + 4half + q
+    LmPart part[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        LmPart& P = part[bb];
+#pragma unroll
+        for (int i = 0; i < LM_NK; ++i) P.t[i] = 0ull;
+        P.mass = 0.0f;
+        P.best_s = -FLT_MAX;
+        P.best_i = INT_MAX;
+        P.nfinite = 0;
+        const int j = bb * 32 + r32;
+        if (j >= a.B) continue;
+        const bool mat = MODE == MODE_MAT && a.unres[j] != 0;
+        if (MODE == MODE_MAT && !mat) continue;
+        const float T = p.temperature[j];
+        const float rep = p.rep[j], freq = p.freq[j], pres = p.pres[j];
+        const uint32_t req = (uint32_t)p.request_ids[j];
+        const uint32_t pos = (uint32_t)p.positions[j];
+        const int wbase = v0 + wave * 32;
+        const uint32_t mw = (p.mask && wbase < a.V) ? p.mask[(size_t)j * p.mask_stride + (wbase >> 5)] : ~0u;
+        const int32_t* bids = p.bias_ids + (size_t)j * Bs;
+        const float* bvals = p.bias_vals + (size_t)j * Bs;
+        const int nb = bl[j];
+        float zz[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int vb = wbase + 8 * g + 4 * half;
+            uint4 wv = make_uint4(0, 0, 0, 0);
+            if (MODE == MODE_STATS && T != 0.0f && vb < a.V)
+                wv = philox4x32_10(make_uint4(req, pos, (uint32_t)vb >> 2, DOM_GUMBEL),
+                                   (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+            const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int v = vb + q;
+                const int e = v - v0;
+                float x = acc[bb][4 * g + q];
+                if (v >= a.V) {
+                    zz[4 * g + q] = -__builtin_huge_valf();
+                    continue;
+                }
+                const uint32_t c = (cnt[j * (LM_ROWS / 2) + (e >> 1)] >> ((e & 1) * 16)) & 0xFFFFu;
+                if (c) x = lm_penalize(x, c, rep, freq, pres);
+                if ((bbits[j * 4 + (e >> 5)] >> (e & 31)) & 1u)
+                    for (int k = 0; k < nb; ++k)
+                        if (bids[k] == v) x = x + bvals[k];
+                if (!((mw >> (e & 31)) & 1u)) x = -__builtin_huge_valf();
+                const bool fin = x > -__builtin_huge_valf();
+                const float zp = fin ? (T != 0.0f ? canon_zero(x / T) : canon_zero(x)) : x;
+                zz[4 * g + q] = zp;
+                if (MODE == MODE_MAT) {
+                    a.zmat[(size_t)j * a.V + v] = zp;
+                    continue;
+                }
+                if (!fin) continue;
+                lm_insert(P.t, key64(zp, v));
+                const float sc = T != 0.0f ? zp + gumbel32(ws[q]) : zp;
+                if (better(sc, v, P.best_s, P.best_i)) {
+                    P.best_s = sc;
+                    P.best_i = v;
+                }
+                ++P.nfinite;
+            }
+        }
+        if (MODE == MODE_STATS && P.t[0]) {
+            const float zt = key_z(P.t[0]);
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (zz[i] > -__builtin_huge_valf()) m += expf(zz[i] - zt);
+            P.mass = m;
+        }
+    }
+    if (MODE == MODE_MAT) return;
+    // the two halves of a column hold different entries: combine, then the
+    // four waves through LDS
+    struct alignas(16) Slot {
+        unsigned long long t[LM_NK];
+        float mass, best_s;
+        int best_i, nfinite;
+    };
+    static_assert(sizeof(Slot) * LM_MAXB * (LM_NT / WAVE) <= LM_W_BYTES, "slots fit a stage buffer");
+    Slot* slots = (Slot*)w2;  // [wave][row]
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        const LmPart y = lm_shfl_xor32(part[bb]);
+        lm_combine(part[bb], y);
+        if (half == 0) {
+            Slot& sl = slots[wave * LM_MAXB + bb * 32 + r32];
+#pragma unroll
+            for (int i = 0; i < LM_NK; ++i) sl.t[i] = part[bb].t[i];
+            sl.mass = part[bb].mass;
+            sl.best_s = part[bb].best_s;
+            sl.best_i = part[bb].best_i;
+            sl.nfinite = part[bb].nfinite;
+        }
+    }
+    __syncthreads();
+    if (tid < a.B) {
+        LmPart x;
+        {
+            const Slot& sl = slots[tid];
+#pragma unroll
+            for (int i = 0; i < LM_NK; ++i) x.t[i] = sl.t[i];
+            x.mass = sl.mass;
+            x.best_s = sl.best_s;
+            x.best_i = sl.best_i;
+            x.nfinite = sl.nfinite;
+        }
+#pragma unroll
+        for (int w = 1; w < LM_NT / WAVE; ++w) {
+            const Slot& sl = slots[w * LM_MAXB + tid];
+            LmPart y;
+#pragma unroll
+            for (int i = 0; i < LM_NK; ++i) y.t[i] = sl.t[i];
+            y.mass = sl.mass;
+            y.best_s = sl.best_s;
+            y.best_i = sl.best_i;
+            y.nfinite = sl.nfinite;
+            lm_combine(x, y);
+        }
+        LmTileStat st;
+#pragma unroll
+        for (int i = 0; i < LM_NC; ++i) st.key[i] = x.t[i];
+        st.rest = x.t[LM_NC];
+        st.mass = x.mass;
+        st.best_s = x.best_s;
+        st.best_i = x.best_i;
+        st.nfinite = x.nfinite;
+        st.pad[0] = st.pad[1] = 0;
+        a.stats[(size_t)tid * a.n_vtiles + tile] = st;
+    }
+}
+
 // Cross-tile reduction: one workgroup per batch row; each thread takes a
 // strided share of the tiles, then (max, lowest index) across the wave through
 // DPP / permlane exchanges and across the four waves through LDS.
@@ -306,6 +595,14 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_reduce(LmheadArgs a) {
             }
         a.out_tokens[j] = bi == INT_MAX ? -1 : bi;
     }
+}
+
+hipError_t launch_lmhead_params(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le) {
+    launch_k(le, 0, k_lmhead_proc<MODE_STATS>, dim3(a.n_vtiles), dim3(LM_NT), st, a);
+    launch_lm_merge(a, st, le, 1);
+    launch_k(le, 2, k_lmhead_proc<MODE_MAT>, dim3(a.n_vtiles), dim3(LM_NT), st, a);
+    launch_lm_slow(a, st, le, 3);
+    return hipGetLastError();
 }
 
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le) {

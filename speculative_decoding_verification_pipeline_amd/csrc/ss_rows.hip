@@ -1374,10 +1374,6 @@ __device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Wo
 // ---------------------------------------------------------------------------
 // the sorted pool
 
-__device__ __forceinline__ float key_z(unsigned long long k) {
-    const uint32_t m = (uint32_t)(k >> 32);
-    return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
-}
 
 // Outcome of resolving a row on its sorted pool.
 struct RowOut {
@@ -2358,6 +2354,344 @@ __global__ __launch_bounds__(NT) void k_tree_finish(TreeArgs a) {
         for (int i = k; i < N; ++i) out_n[i] = -1;
         a.out_num_accepted[b] = k;
     }
+}
+
+// ---------------------------------------------------------------------------
+// LM-head sampling with the per-request pipeline: the row stage.
+//
+// Every (row, tile) summary gives the tile's LM_NC largest keys and the next
+// one. Let R be the largest of the next keys over all tiles: every entry with a
+// key above R is among the tiles' candidates (an entry left out of its tile's
+// list is at most that tile's next key). These certified entries, sorted, are
+// an exact prefix of the row in key order; when the top-k, top-p and min-p
+// cuts all fall inside it, the kept support is known and the token is the best
+// z' + g over it. Otherwise the row is marked open: its z' are formed again by
+// a second GEMM pass and the whole-row selection below decides it.
+
+constexpr int LM_CAP = 4096;  // certified entries sorted in LDS
+
+struct SmemLm {
+    unsigned long long key[LM_CAP];
+    double pre[LM_CAP];         // inclusive prefix mass in key order
+};
+
+__device__ __forceinline__ bool lm_better(float sa, int ia, float sb, int ib) {
+    return sa > sb || (sa == sb && ia < ib);
+}
+
+// Block-wide (score, id) argmax, the lowest id among equal scores.
+__device__ __forceinline__ void lm_block_best(float& s, int& i, SmemR& sh) {
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const float os = __shfl_xor(s, o);
+        const int oi = __shfl_xor(i, o);
+        if (lm_better(os, oi, s, i)) {
+            s = os;
+            i = oi;
+        }
+    }
+    const int w = threadIdx.x / WAVE;
+    if ((threadIdx.x & (WAVE - 1)) == 0) {
+        sh.fmin[w] = s;
+        sh.imax[w] = i;
+    }
+    __syncthreads();
+    s = sh.fmin[0];
+    i = sh.imax[0];
+    for (int k = 1; k < NTR / WAVE; ++k)
+        if (lm_better(sh.fmin[k], sh.imax[k], s, i)) {
+            s = sh.fmin[k];
+            i = sh.imax[k];
+        }
+    __syncthreads();
+}
+
+__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long v, SmemR& sh) {
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
+        const unsigned long long x = ((unsigned long long)hi << 32) | lo;
+        v = x > v ? x : v;
+    }
+    const int w = threadIdx.x / WAVE;
+    if ((threadIdx.x & (WAVE - 1)) == 0) sh.hs.wsum[w] = v;
+    __syncthreads();
+    unsigned long long m = 0;
+    for (int k = 0; k < NTR / WAVE; ++k) m = sh.hs.wsum[k] > m ? sh.hs.wsum[k] : m;
+    __syncthreads();
+    return m;
+}
+
+__device__ __forceinline__ float lm_gumbel_score(const LmheadArgs& a, int j, int v, float z) {
+    const uint4 w = philox4x32_10(make_uint4((uint32_t)a.p.request_ids[j], (uint32_t)a.p.positions[j],
+                                             (uint32_t)v >> 2, DOM_GUMBEL),
+                                  (uint32_t)a.p.seed, (uint32_t)(a.p.seed >> 32));
+    const uint32_t s = (uint32_t)v & 3u;
+    return z + gumbel32(s == 0 ? w.x : s == 1 ? w.y : s == 2 ? w.z : w.w);
+}
+
+__global__ __launch_bounds__(NTR) void k_lm_merge(LmheadArgs a) {
+    __shared__ SmemLm L;
+    __shared__ SmemR sh;
+    __shared__ int s_n;
+    const int j = blockIdx.x;
+    const int tid = threadIdx.x;
+    const ParamPtrs& p = a.p;
+    const LmTileStat* st = a.stats + (size_t)j * a.n_vtiles;
+    const float T = p.temperature[j];
+    // the row's maximum, the best Gumbel score, the deepest certifying bound
+    // and the finite count
+    unsigned long long kmax = 0, rest = 0;
+    float bs = -FLT_MAX;
+    int bi = INT_MAX, nfin = 0;
+    for (int t = tid; t < a.n_vtiles; t += NTR) {
+        const LmTileStat x = st[t];
+        kmax = x.key[0] > kmax ? x.key[0] : kmax;
+        rest = x.rest > rest ? x.rest : rest;
+        if (lm_better(x.best_s, x.best_i, bs, bi)) {
+            bs = x.best_s;
+            bi = x.best_i;
+        }
+        nfin += x.nfinite;
+    }
+    kmax = block_max_u64(kmax, sh);
+    rest = block_max_u64(rest, sh);
+    lm_block_best(bs, bi, sh);
+    const int total = block_sum_i(nfin, sh.red);
+    const int V = a.V;
+    const bool topk_on = p.top_k[j] > 0 && p.top_k[j] < V;
+    const float tp = p.top_p[j];
+    const float mp = p.min_p[j];
+    const bool filtered = topk_on || tp < 1.0f || mp > 0.0f;
+    if (total == 0 || T == 0.0f || !filtered) {
+        if (tid == 0) {
+            // no finite entry: -1; greedy: the largest key; else the best score
+            a.out_tokens[j] = total == 0 ? -1 : T == 0.0f ? key64_id(kmax) : (bi == INT_MAX ? -1 : bi);
+            a.unres[j] = 0;
+            if (a.dbg_path) a.dbg_path[j] = 2;
+        }
+        return;
+    }
+    const float zmax = key_z(kmax);
+    // the row mass
+    double wsum = 0.0;
+    for (int t = tid; t < a.n_vtiles; t += NTR) {
+        const LmTileStat x = st[t];
+        if (x.key[0]) wsum += (double)x.mass * (double)expf(key_z(x.key[0]) - zmax);
+    }
+    const double W = block_sum_d(wsum, sh.red);
+    // the certified entries: keys above every tile's next key
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    for (int t = tid; t < a.n_vtiles; t += NTR) {
+        const LmTileStat x = st[t];
+#pragma unroll
+        for (int i = 0; i < LM_NC; ++i)
+            if (x.key[i] > rest) {
+                const int slot = atomicAdd(&s_n, 1);
+                if (slot < LM_CAP) L.key[slot] = x.key[i];
+            }
+    }
+    __syncthreads();
+    const int nc = s_n;
+    bool open = nc > LM_CAP;
+    int n3 = 0;
+    if (!open) {
+        // bitonic sort, descending, over the next power of two (zero keys last)
+        int P2 = WAVE;
+        while (P2 < nc) P2 <<= 1;
+        for (int i = nc + tid; i < P2; i += NTR) L.key[i] = 0ull;
+        __syncthreads();
+        for (int k = 2; k <= P2; k <<= 1) {
+            for (int h = k >> 1; h > 0; h >>= 1) {
+                for (int i = tid; i < P2 / 2; i += NTR) {
+                    const int lo = 2 * h * (i / h) + (i % h);
+                    const int hi = lo + h;
+                    const bool desc = (lo & k) == 0;
+                    const unsigned long long x = L.key[lo], y = L.key[hi];
+                    if ((x < y) == desc) {
+                        L.key[lo] = y;
+                        L.key[hi] = x;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // weights and binary64 inclusive prefix masses in key order
+        constexpr int PER = LM_CAP / NTR;
+        double run = 0.0;
+        double pre[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int i = tid * PER + q;
+            const double w = i < nc ? (double)expf(key_z(L.key[i]) - zmax) : 0.0;
+            run += w;
+            pre[q] = run;
+        }
+        double tot;
+        const double base = block_excl_scan_d(run, sh.red, tot);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int i = tid * PER + q;
+            if (i < nc) L.pre[i] = base + pre[q];
+        }
+        __syncthreads();
+        // the cuts, as the sampler makes them: top-k, top-p over the top-k
+        // mass, min-p against the maximum
+        const int K_eff = topk_on ? min(p.top_k[j], total) : total;
+        int n1 = total;
+        double Wk = W;
+        if (topk_on && K_eff < total) {
+            if (K_eff > nc) open = true;
+            else {
+                n1 = K_eff;
+                Wk = L.pre[K_eff - 1];
+            }
+        }
+        int n2 = n1;
+        if (!open && tp < 1.0f) {
+            // keep i while the mass before it is below top_p x Wk
+            const double thr = (double)tp * Wk;
+            const int lim = min(n1, nc);
+            int cnt = 0;
+            for (int i = tid; i < lim; i += NTR) cnt += (i == 0 || L.pre[i - 1] < thr) ? 1 : 0;
+            cnt = block_sum_i(cnt, sh.red);
+            if (cnt == lim && n1 > nc) open = true;  // the cut lies past the certified entries
+            else n2 = cnt;
+        }
+        if (!open) {
+            if (mp > 0.0f) {
+                if (n2 > nc) {
+                    // every uncertified entry must weigh below min_p
+                    if (rest && expf(key_z(rest) - zmax) >= mp) open = true;
+                    n2 = nc;
+                }
+                int cnt = 0;
+                for (int i = tid; i < n2; i += NTR)
+                    cnt += expf(key_z(L.key[i]) - zmax) >= mp ? 1 : 0;
+                n3 = block_sum_i(cnt, sh.red);
+            } else {
+                if (n2 > nc) open = true;
+                n3 = n2;
+            }
+        }
+    }
+    if (open) {
+        if (tid == 0) {
+            a.unres[j] = 1;
+            if (a.dbg_path) a.dbg_path[j] = 1;
+        }
+        return;
+    }
+    // Gumbel-max over the kept support
+    float s2 = -FLT_MAX;
+    int i2 = INT_MAX;
+    for (int i = tid; i < n3; i += NTR) {
+        const unsigned long long k = L.key[i];
+        const int v = key64_id(k);
+        const float sc = lm_gumbel_score(a, j, v, key_z(k));
+        if (lm_better(sc, v, s2, i2)) {
+            s2 = sc;
+            i2 = v;
+        }
+    }
+    lm_block_best(s2, i2, sh);
+    if (tid == 0) {
+        a.out_tokens[j] = i2 == INT_MAX ? -1 : i2;
+        a.unres[j] = 0;
+        if (a.dbg_path) a.dbg_path[j] = 0;
+    }
+}
+
+// Rows left open: their z' (formed again by the second GEMM pass) through the
+// whole-row selection, then the best z' + g over the kept entries.
+__global__ __launch_bounds__(NTR) void k_lm_slow(LmheadArgs a) {
+    __shared__ SmemU su;
+    __shared__ SmemR sh;
+    const int j = blockIdx.x;
+    if (!a.unres[j]) return;
+    const int tid = threadIdx.x;
+    const ParamPtrs& p = a.p;
+    const int V = a.V;
+    const float* zr = a.zmat + (size_t)j * V;
+    float m = NEG_INF;
+    int nf = 0;
+    for (int v0 = tid; v0 < V; v0 += NTR * SU) {
+        float zs[SU];
+#pragma unroll
+        for (int k = 0; k < SU; ++k) zs[k] = v0 + k * NTR < V ? zr[v0 + k * NTR] : NEG_INF;
+#pragma unroll
+        for (int k = 0; k < SU; ++k)
+            if (zs[k] > NEG_INF) {
+                m = fmaxf(m, zs[k]);
+                ++nf;
+            }
+    }
+    const float zmax = block_max(m, sh.red);
+    const int total = block_sum_i(nf, sh.red);
+    const bool topk_on = p.top_k[j] > 0 && p.top_k[j] < V;
+    const int K_eff = topk_on ? min(p.top_k[j], total) : total;
+    int cnt;
+    unsigned long long ms, kK = 0;
+    if (topk_on && K_eff < total)
+        hist_select(zr, V, zmax, [](unsigned long long, float) { return true; }, false, true,
+                    (unsigned long long)K_eff, 0.0, su, sh, cnt, ms, kK);
+    unsigned long long kP = kK;
+    if (p.top_p[j] < 1.0f)
+        hist_select(zr, V, zmax, [kK](unsigned long long k, float) { return k >= kK; }, true, true,
+                    0, (double)p.top_p[j], su, sh, cnt, ms, kP);
+    const float mp = p.min_p[j];
+    // four consecutive entries per step share one Philox block
+    float bs = -FLT_MAX;
+    int bi = INT_MAX;
+    const uint32_t req = (uint32_t)p.request_ids[j], pos = (uint32_t)p.positions[j];
+    for (int g0 = tid; g0 * 4 < V; g0 += NTR * 2) {
+        float zs[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int v = (g0 + h * NTR) * 4 + q;
+                zs[h][q] = v < V ? zr[v] : NEG_INF;
+            }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int g = g0 + h * NTR;
+            bool any = false;
+            bool keep[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float z = zs[h][q];
+                const int v = g * 4 + q;
+                keep[q] = z > NEG_INF && key64(z, v) >= kP && (mp <= 0.0f || expf(z - zmax) >= mp);
+                any |= keep[q];
+            }
+            if (!any) continue;
+            const uint4 w = philox4x32_10(make_uint4(req, pos, (uint32_t)g, DOM_GUMBEL),
+                                          (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (!keep[q]) continue;
+                const float sc = zs[h][q] + gumbel32(ws[q]);
+                if (lm_better(sc, g * 4 + q, bs, bi)) {
+                    bs = sc;
+                    bi = g * 4 + q;
+                }
+            }
+        }
+    }
+    lm_block_best(bs, bi, sh);
+    if (tid == 0) a.out_tokens[j] = bi == INT_MAX ? -1 : bi;
+}
+
+void launch_lm_merge(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k) {
+    launch_k(le, k, k_lm_merge, dim3(a.B), dim3(NTR), st, a);
+}
+
+void launch_lm_slow(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k) {
+    launch_k(le, k, k_lm_slow, dim3(a.B), dim3(NTR), st, a);
 }
 
 // ---------------------------------------------------------------------------

@@ -27,7 +27,7 @@ SS_BF16 = 1
 EXPORTED = ("ss_sampler_create", "ss_sampler_destroy", "ss_status_string",
             "ss_sampler_workspace_bytes", "ss_sampler_set_launch_events", "ss_sample",
             "ss_spec_verify", "ss_spec_verify_scatter", "ss_tree_verify", "ss_lmhead_sample",
-            "ss_sample_noalloc")
+            "ss_lmhead_sample_params", "ss_sample_noalloc")
 NOALLOC_MAX_BATCH = 64
 NOALLOC_MAX_ENTRIES = 1 << 23
 
@@ -106,6 +106,8 @@ def load_library(path=None):
     lib.ss_tree_verify.restype = i32
     lib.ss_lmhead_sample.argtypes = [vp, vp, vp, i32, vp, vp, vp, u64, vp, vp, vp]
     lib.ss_lmhead_sample.restype = i32
+    lib.ss_lmhead_sample_params.argtypes = [vp, vp, vp, i32, ctypes.POINTER(CParams), vp, vp, vp]
+    lib.ss_lmhead_sample_params.restype = i32
     lib.ss_sample_noalloc.argtypes = [vp, i32, i64, i32, i32, ctypes.POINTER(CParams), vp, vp]
     lib.ss_sample_noalloc.restype = i32
     _lib = lib
@@ -433,6 +435,29 @@ class Sampler:
                                      _ptr(out_num_accepted), _stream(stream))
         _check("ss_tree_verify", st)
         return out_tokens, out_nodes, out_num_accepted
+
+    def lmhead_sample_params(self, hidden, weight, params: SamplingParams, out=None, path=None,
+                             stream=None):
+        """LM-head GEMM with the per-request pipeline (penalties, bias, mask,
+        temperature, filters) before Gumbel-max sampling. path: optional [B]
+        int32 that receives how each row was decided."""
+        _check_dev(hidden, "hidden", (torch.bfloat16, torch.int16), self.device)
+        _check_dev(weight, "weight", (torch.bfloat16, torch.int16), self.device)
+        _require(hidden.dim() == 2 and hidden.is_contiguous(), "hidden must be a contiguous [B, K] array")
+        B, K = hidden.shape
+        _require(K == self.hidden_size, f"hidden has K = {K}, the sampler {self.hidden_size}")
+        _require(tuple(weight.shape) == (self.vocab_size, K) and weight.is_contiguous(),
+                 f"weight must be a contiguous [{self.vocab_size}, {K}] array")
+        if out is None:
+            out = torch.empty(B, dtype=torch.int32, device=hidden.device)
+        _check_vec(out, "out", B, torch.int32, self.device)
+        _check_vec(path, "path", B, torch.int32, self.device)
+        cp = params.to_c(params.validate(B, self.vocab_size, self.device))
+        st = self.lib.ss_lmhead_sample_params(self.handle, _ptr(hidden), _ptr(weight), B,
+                                              ctypes.byref(cp), _ptr(out), _ptr(path),
+                                              _stream(stream))
+        _check("ss_lmhead_sample_params", st)
+        return out
 
     def lmhead_sample(self, hidden, weight, temperature, request_ids=None, positions=None,
                       seed=0, out=None, debug_logits=None, stream=None):

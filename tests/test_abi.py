@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for f in ("ss_sampler_create", "ss_sample", "ss_spec_verify", "ss_spec_verify_scatter",
-              "ss_tree_verify", "ss_lmhead_sample", "ss_sample_noalloc"):
+              "ss_tree_verify", "ss_lmhead_sample", "ss_lmhead_sample_params",
+              "ss_sample_noalloc"):
         assert f in fns
 
 
@@ -74,6 +75,8 @@ def test_calls_reject_null_handle(lib):
                               None, None) == sampler.SS_ERR_INVALID_ARG
     assert lib.ss_spec_verify_scatter(None, None, 0, 0, None, 0, None, 1, 1, ctypes.byref(p), None,
                                       None, None, None) == sampler.SS_ERR_INVALID_ARG
+    assert lib.ss_lmhead_sample_params(None, None, None, 1, ctypes.byref(p), None, None,
+                                       None) == sampler.SS_ERR_INVALID_ARG
     assert lib.ss_sampler_workspace_bytes(None) == 0
     assert lib.ss_sampler_set_launch_events(None, None, 0) == sampler.SS_ERR_INVALID_ARG
     lib.ss_sampler_destroy(None)

@@ -204,6 +204,16 @@ def test_lmhead_rejects_bad_arguments(live):
     assert call(rows=0) == SM.SS_ERR_INVALID_ARG
     assert call(rows=B + 1) == SM.SS_ERR_INVALID_ARG
     assert call(temp=False) == SM.SS_ERR_INVALID_ARG
+    pp = SM.SamplingParams(temperature=t).to_c()
+    assert lib.ss_lmhead_sample_params(live.handle, _vp(h), _vp(w), B, ctypes.byref(pp), _vp(out),
+                                       None, None) == SM.SS_OK
+    assert lib.ss_lmhead_sample_params(live.handle, _vp(h, 2), _vp(w), B, ctypes.byref(pp),
+                                       _vp(out), None, None) == SM.SS_ERR_UNSUPPORTED
+    assert lib.ss_lmhead_sample_params(live.handle, _vp(h), _vp(w), B + 1, ctypes.byref(pp),
+                                       _vp(out), None, None) == SM.SS_ERR_INVALID_ARG
+    pp.temperature = None
+    assert lib.ss_lmhead_sample_params(live.handle, _vp(h), _vp(w), B, ctypes.byref(pp), _vp(out),
+                                       None, None) == SM.SS_ERR_INVALID_ARG
     no_k = SM.Sampler(B, V, device=0)
     try:
         assert call(handle=no_k.handle) == SM.SS_ERR_INVALID_ARG  # created with hidden_size 0

@@ -87,10 +87,14 @@ def run_sweep(wl, d, seeds, tally):
     H = torch.from_numpy(wl.hidden.view(np.int16)).to(device())
     Wt = torch.from_numpy(wl.weight.view(np.int16)).to(device())
     s = Sampler(64, V, hidden_size=K, device=0)
-    outs = [s.lmhead_sample_params(H, Wt, gpu_params(d, sd)) for sd in seeds]
+    path = torch.full((B,), -1, dtype=torch.int32, device=device())
+    outs = [s.lmhead_sample_params(H, Wt, gpu_params(d, sd), path=path if i == 0 else None)
+            for i, sd in enumerate(seeds)]
     torch.cuda.synchronize()
     got = [o.cpu().numpy() for o in outs]
-    log(f"[lmhead params {B}x{K}x{V}] {len(seeds)} GPU calls done; oracle")
+    paths = np.bincount(path.cpu().numpy(), minlength=3)
+    log(f"[lmhead params {B}x{K}x{V}] {len(seeds)} GPU calls done; rows by path "
+        f"(candidates, whole row, unfiltered): {paths.tolist()}; oracle")
     z = L.logits_fp64(wl.hidden, wl.weight)
     rows = L.processed_rows(z, oracle_params(d, 0))
     with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
@@ -98,6 +102,7 @@ def run_sweep(wl, d, seeds, tally):
     for sd, g, (want, flags) in zip(seeds, got, wants):
         for b in range(B):
             tally.add(int(g[b]) == int(want[b]), bool(flags[b]), (sd, b, int(g[b]), int(want[b])))
+    return paths
 
 
 @pytest.mark.parametrize("B,K,V,with_mask", [(16, 256, 3000, True), (33, 128, 1000, False),
@@ -134,5 +139,7 @@ def test_full_configuration():
     # change. With 64 rows of mixed filters that is a few draws in 10^4, so
     # the share is held to 1e-3 here; every unflagged draw must match.
     tally = Tally("lmhead params full", share=1e-3)
-    run_sweep(wl, d, list(range(157)), tally)
+    paths = run_sweep(wl, d, list(range(157)), tally)
     tally.check()
+    # both ways of deciding a filtered row ran
+    assert paths[0] > 0 and paths[1] > 0, paths
