@@ -1,4 +1,5 @@
-// Row kernels: the fused sampler and speculative verification (gfx950).
+// Row kernels: the fused sampler, linear and tree verification, and the row
+// stage of LM-head sampling with the per-request pipeline (gfx950).
 //
 // The pipeline and its order follow the SonicSampler abstract (arxivdaily page,
 // English abstract): per request, grammar mask, repetition / frequency /
@@ -31,8 +32,10 @@
 //    monotone in key order, followed by a rank within each bucket; top-k,
 //    top-p, min-p and the inverse-CDF draw are then wave scans over binary64
 //    prefix sums. Requests that reach past the pool run an exact whole-row
-//    fallback (radix selection by count and by mass). Results never depend on
-//    which path resolved them.
+//    path: z of the whole row into scratch, then each selection (top-k by
+//    count, top-p and the draw by mass) as one histogram pass over buckets of
+//    (zmax - z) and an exact resolve of the one bucket that holds the answer.
+//    Results never depend on which path resolved them.
 #include <float.h>
 #include <limits.h>
 
