@@ -1683,7 +1683,33 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
                 // Weights and binary64 inclusive prefix masses of the sorted pool
                 // (each thread sums EPTR consecutive entries, then the thread
                 // totals are scanned in thread order); the bucket arrays they
-                // overwrite are dead.
+                // overwrite are dead. A pool of up to EPTR waves' worth of
+                // entries is summed by wave 0 alone, which also resolves the
+                // row, so no barrier follows.
+                if (n <= EPTR * WAVE) {
+                    if (wv == 0) {
+                        float wl[EPTR];
+                        double run = 0.0, pre[EPTR];
+#pragma unroll
+                        for (int j = 0; j < EPTR; ++j) {
+                            const int i = lane * EPTR + j;
+                            wl[j] = i < n ? expf(key_z(P.F[i]) - zmax) : 0.0f;
+                            run += (double)wl[j];
+                            pre[j] = run;
+                        }
+                        const double base = wave_incl_scan_d(run) - run;
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+                        for (int j = 0; j < EPTR; ++j) {
+                            const int i = lane * EPTR + j;
+                            if (i < n) {
+                                P.w[i] = wl[j];
+                                P.P[i] = base + pre[j];
+                            }
+                        }
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    }
+                } else {
                 float wl[EPTR];
                 double pre[EPTR];
                 double run = 0.0;
@@ -1706,6 +1732,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
                     }
                 }
                 __syncthreads();
+                }
             }
         }
     }
