@@ -136,10 +136,12 @@ __device__ __forceinline__ RowCtx make_ctx(const ParamPtrs& p, int b, const void
 
 struct SmemTile {
     uint32_t cnt[TILE / 2];   // u16 history multiplicities of the tile's entries
-    uint32_t bias[TILE / 32]; // bit set: some bias entry targets this vocabulary entry
     uint32_t xw[NT];          // per thread: bit s set when its slot s is penalised or biased
-    int32_t bid[NT];          // the row's first NT bias entries, in array order
-    float bval[NT];
+    uint32_t bw[NT];          // per thread: bit s set when its slot s is biased
+    int32_t bl[NT];           // the tile's bias hits (local index, value), in no fixed order
+    float bv[NT];
+    int nbh;                  // bias hits appended (the list holds the first NT)
+    int bfull;                // 1: some entry is biased more than once, or the list overflowed
     unsigned long long wl[WPT][WCAP];  // per wave: its candidates (x' bits, id) in slot order
 };
 
@@ -415,17 +417,20 @@ __device__ __forceinline__ float process_entry(const RowCtx& c, int id, float x,
     return allowed ? x : NEG_INF;
 }
 
-__device__ __forceinline__ float process_entry_t(const RowCtx& c, int id, float x, uint32_t count,
-                                                 bool bias_hit, bool allowed, const SmemTile& t) {
-    x = penalize(c, x, count);
-    if (bias_hit) {
-        const int nl = min(c.bias_len, NT);
-        for (int k = 0; k < nl; ++k)
-            if (t.bid[k] == id) x = x + t.bval[k];
-        for (int k = NT; k < c.bias_len; ++k)
-            if (gld(c.bias_ids + k) == id) x = x + gld(c.bias_vals + k);
+// The bias of tile entry l (id tb + l), known to be biased. When each biased
+// entry of the tile has one bias entry and the tile's hits fit the list, the
+// single value comes from the LDS hit list; otherwise the row's whole list is
+// applied in array order.
+__device__ __forceinline__ float add_bias_t(const RowCtx& c, float x, int id, int l, const SmemTile& t,
+                                           int nbh, bool bfull) {
+    if (!bfull) {
+        for (int k = 0; k < nbh; ++k)
+            if (t.bl[k] == l) x = x + t.bv[k];
+        return x;
     }
-    return allowed ? x : NEG_INF;
+    for (int k = 0; k < c.bias_len; ++k)
+        if (gld(c.bias_ids + k) == id) x = x + gld(c.bias_vals + k);
+    return x;
 }
 
 // The row's history and bias lists are small and shared by all its tiles. Each
@@ -472,10 +477,10 @@ __device__ __forceinline__ TablePrefetch prefetch_tables(const RowCtx& c) {
     return f;
 }
 
-// Builds the tile's multiplicity counts, bias bitmap and bias list in LDS, and
-// for every thread a word with bit s set when its slot s holds a penalised or
-// biased entry (two barriers). Threads with active = false only take part in
-// the barriers.
+// Builds the tile's multiplicity counts in LDS, for every thread a word with
+// bit s set when its slot s holds a penalised or biased entry and a word with
+// bit s set when it is biased, and the list of the tile's bias hits (two
+// barriers). Threads with active = false only take part in the barriers.
 template <int DT>
 __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& t,
                                              const TablePrefetch& f, bool active = true) {
@@ -488,23 +493,23 @@ __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& 
 #pragma unroll
         for (int k = 0; k < TILE / 8 / NT; ++k) c4[tid + k * NT] = make_uint4(0, 0, 0, 0);
     }
-    if (has_bias) {
-        t.bias[tid] = 0;
-        t.bid[tid] = f.bias_id;
-        t.bval[tid] = f.bias_val;
+    if (active) {
+        t.xw[tid] = 0;
+        t.bw[tid] = 0;
+        if (tid == 0) {
+            t.nbh = 0;
+            t.bfull = 0;
+        }
     }
-    if (active) t.xw[tid] = 0;
     __syncthreads();
-    // owner thread and slot of local entry l (the inverse of slot_id)
-    auto flag = [&](int l) {
-        const int g = l / L::GSTRIDE, r = l % L::GSTRIDE;
-        atomicOr(&t.xw[r / L::VEC], 1u << (g * L::VEC + r % L::VEC));
-    };
+    // owner thread and slot bit of local entry l (the inverse of slot_id)
+    auto owner = [&](int l) { return (l % L::GSTRIDE) / L::VEC; };
+    auto bit = [&](int l) { return 1u << ((l / L::GSTRIDE) * L::VEC + (l % L::GSTRIDE) % L::VEC); };
     auto count = [&](int id) {
         const int l = id - tb;
         if (id >= 0 && id < c.V && l >= 0 && l < TILE) {
             atomicAdd(&t.cnt[l >> 1], 1u << ((l & 1) * 16));
-            flag(l);
+            atomicOr(&t.xw[owner(l)], bit(l));
         }
     };
     if (has_cnt) {
@@ -514,15 +519,23 @@ __device__ __forceinline__ void build_tables(const RowCtx& c, int tb, SmemTile& 
         for (int i = tid + 2 * NT; i < c.hist_len; i += NT) count(gld(c.hist + i));
         if (tid < c.extra_len) count(f.extra);
     }
-    auto mark = [&](int id) {
+    auto mark = [&](int id, float val) {
         const int l = id - tb;
         if (id >= 0 && id < c.V && l >= 0 && l < TILE) {
-            atomicOr(&t.bias[l >> 5], 1u << (l & 31));
-            flag(l);
+            const int o = owner(l);
+            const uint32_t b = bit(l);
+            atomicOr(&t.xw[o], b);
+            const uint32_t old = atomicOr(&t.bw[o], b);
+            const int p = atomicAdd(&t.nbh, 1);
+            if (p < NT) {
+                t.bl[p] = l;
+                t.bv[p] = val;
+            }
+            if ((old & b) || p >= NT) t.bfull = 1;
         }
     };
-    if (has_bias && tid < c.bias_len) mark(f.bias_id);
-    for (int i = tid + NT; has_bias && i < c.bias_len; i += NT) mark(gld(c.bias_ids + i));
+    if (has_bias && tid < c.bias_len) mark(f.bias_id, f.bias_val);
+    for (int i = tid + NT; has_bias && i < c.bias_len; i += NT) mark(gld(c.bias_ids + i), gld(c.bias_vals + i));
     __syncthreads();
 }
 
@@ -539,43 +552,82 @@ __device__ __forceinline__ void load_mask(const RowCtx& c, int tb, uint32_t mw[L
     }
 }
 
-// Penalties, bias and mask on this thread's entries. A thread whose slots hold
-// no penalised or biased entry (its exception word is zero) and that has no
-// mask does nothing; otherwise whole groups without an exception or a masked
-// entry are skipped.
+// a where the mask m is all ones, b where it is zero (a bit select)
+__device__ __forceinline__ float bsel(uint32_t m, float a, float b) {
+    return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+}
+
+// All ones when bit b of s is set (the empty asm hides that the value is 0 or
+// all ones, so the compiler keeps the bit selects instead of rewriting them
+// into an indexed access, which would move the slot array to scratch).
+__device__ __forceinline__ uint32_t bit_mask(uint32_t s, int b) {
+    uint32_t m = 0u - ((s >> b) & 1u);
+    asm volatile("" : "+v"(m));
+    return m;
+}
+
+// Slot s of this thread's entries, s held per lane (registers cannot be
+// indexed by a per-lane value): a select tree over the bits of s.
+__device__ __forceinline__ float slot_get(const float v[EPT], int s) {
+    float a[EPT / 2];
+    const uint32_t m0 = bit_mask((uint32_t)s, 0);
+#pragma unroll
+    for (int i = 0; i < EPT / 2; ++i) a[i] = bsel(m0, v[2 * i + 1], v[2 * i]);
+#pragma unroll
+    for (int w = EPT / 4, b = 1; w >= 1; w >>= 1, ++b) {
+        const uint32_t m = bit_mask((uint32_t)s, b);
+#pragma unroll
+        for (int i = 0; i < w; ++i) a[i] = bsel(m, a[2 * i + 1], a[2 * i]);
+    }
+    return a[0];
+}
+
+__device__ __forceinline__ void slot_set(float v[EPT], int s, float x) {
+    const uint32_t oh = 1u << s;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) v[i] = bsel(bit_mask(oh, i), x, v[i]);
+}
+
+// Penalties, bias and mask on this thread's entries. The mask comes first, as
+// a bit select per slot; then each lane walks the set bits of its exception
+// word (penalised or biased entries that the mask allows), one entry per
+// step, so the wave takes as many steps as its busiest lane has exceptions and
+// the code holds one copy of the per-entry work (its size matters: the whole
+// kernel competes for the instruction cache).
 template <int DT>
 __device__ __forceinline__ void process_tile(const RowCtx& c, int tb, float v[EPT], const SmemTile& t,
                                              const uint32_t mwords[Lay<DT>::NG], bool tables) {
     using L = Lay<DT>;
-    const uint32_t xw = tables ? t.xw[threadIdx.x] : 0u;
-    if (!c.mask && xw == 0u) return;
-    const bool has_cnt = (c.hist_len + c.extra_len) > 0;
-    const bool has_bias = c.bias_len > 0;
     constexpr uint32_t vm = (1u << L::VEC) - 1u;
+    uint32_t aw = 0xFFFFFFFFu;  // bit s: slot s is allowed by the mask
+    if (c.mask) {
+        aw = 0u;
 #pragma unroll
-    for (int g = 0; g < L::NG; ++g) {
-        const int l0 = g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
-        const int e0 = tb + l0;
-        const uint32_t xb = (xw >> (g * L::VEC)) & vm;
-        const uint32_t mw = mwords[g] >> (e0 & 31);
-        if ((xb | (~mw & vm)) == 0u) continue;
-#pragma unroll
-        for (int j = 0; j < L::VEC; ++j) {
-            const int id = e0 + j;
-            if (id >= c.V) continue;
-            const bool allowed = (mw >> j) & 1u;
-            float x = v[g * L::VEC + j];
-            if ((xb >> j) & 1u) {
-                const int l = l0 + j;
-                const uint32_t cnt = has_cnt ? (t.cnt[l >> 1] >> ((l & 1) * 16)) & 0xFFFFu : 0u;
-                const bool bh = has_bias && ((t.bias[l >> 5] >> (l & 31)) & 1u);
-                x = process_entry_t(c, id, x, cnt, bh, allowed, t);
-            } else if (!allowed) {
-                x = NEG_INF;
-            }
-            v[g * L::VEC + j] = x;
+        for (int g = 0; g < L::NG; ++g) {
+            const int e0 = tb + g * L::GSTRIDE + (int)threadIdx.x * L::VEC;
+            aw |= ((mwords[g] >> (e0 & 31)) & vm) << (g * L::VEC);
         }
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) v[k] = ((aw >> k) & 1u) ? v[k] : NEG_INF;
     }
+    uint32_t ex = tables ? t.xw[threadIdx.x] & aw : 0u;
+    if (ex == 0u) return;
+    const uint32_t bw = c.bias_len > 0 ? t.bw[threadIdx.x] : 0u;
+    const int nbh = bw ? t.nbh : 0;
+    const bool bfull = bw ? t.bfull != 0 : false;
+    const bool has_cnt = (c.hist_len + c.extra_len) > 0;
+    do {
+        const int sl = __builtin_ctz(ex);
+        ex &= ex - 1u;
+        const int l = (sl / L::VEC) * L::GSTRIDE + (int)threadIdx.x * L::VEC + (sl % L::VEC);
+        const int id = tb + l;
+        if (id < c.V) {
+            const uint32_t cnt = has_cnt ? (t.cnt[l >> 1] >> ((l & 1) * 16)) & 0xFFFFu : 0u;
+            float x = penalize(c, slot_get(v, sl), cnt);
+            if ((bw >> sl) & 1u) x = add_bias_t(c, x, id, l, t, nbh, bfull);
+            slot_set(v, sl, x);
+        }
+    } while (ex != 0u);
 }
 
 
