@@ -659,6 +659,11 @@ __device__ __forceinline__ int wave_max_i(int v) {
 }
 
 
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+
 // Entries of this lane above theta (strict) or at or above it, counted over the
 // wave (the ballot counts stay in scalar registers).
 __device__ __forceinline__ int wave_count_above(const float v[EPT], float theta, bool strict) {
@@ -750,45 +755,30 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
         st.argmax = m > NEG_INF ? am : -1;
     } else if (m > NEG_INF) {
         // Windows x' >= m - d T for d = DELTA, DELTA / 2, DELTA / 4: the first
-        // whose entries fit the wave's WCAP slots gives the candidates (written
-        // to the wave's LDS list in slot order while they are counted). On a
+        // whose entries fit the wave's WCAP slots gives the candidates. On a
         // low-entropy row the wave holding the row maximum keeps everything
         // within DELTA of it; a wave deep in the tail sees a locally dense
-        // region and settles for a narrower window.
+        // region and settles for a narrower window. The window is chosen on
+        // counts alone (a compare and a ballot per slot); the candidates are
+        // written once, for the chosen threshold.
         unsigned long long* wl = tt.wl[wv];
-        bool strict = false;
-        auto window = [&](float th) -> int {
-            int n = 0;
-#pragma unroll
-            for (int s = 0; s < EPT; ++s) {
-                const bool hit = v[s] >= th;
-                const unsigned long long bm = __ballot(hit);
-                if (bm) {
-                    const int p = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
-                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-                    if (hit && p < WCAP)
-                        wl[p] = ((unsigned long long)__float_as_uint(v[s]) << 32) | (uint32_t)slot_id_late<DT>(sid0, s);
-                    n += __popcll(bm);
-                }
-            }
-            return n;
-        };
         float theta = fmaxf(m - DELTA * c.T, -FLT_MAX);
-        int base = window(theta);
+        int n = wave_count_above(v, theta, false);
         // A narrower window only shortens the search: the head by count always
         // cuts lower. It is worth taking where the wide window overflowed
         // modestly (a locally dense stretch of a steep tail, whose narrower
         // cut still lies far below the row maximum); a wave with three quarters
         // of its entries inside the wide window is flat and goes to the count cut.
-        if (base > WCAP && base <= 3 * (WT / 4)) {
+        if (n > WCAP && n <= 3 * (WT / 4)) {
             theta = fmaxf(m - (0.5f * DELTA) * c.T, -FLT_MAX);
-            base = window(theta);
-            if (base > WCAP) {
+            n = wave_count_above(v, theta, false);
+            if (n > WCAP) {
                 theta = fmaxf(m - (0.25f * DELTA) * c.T, -FLT_MAX);
-                base = window(theta);
+                n = wave_count_above(v, theta, false);
             }
         }
-        if (base > WCAP) {
+        const bool strict = n > WCAP;
+        if (strict) {
             // Even the narrowest window overflows (a flat wave): keep the head by
             // count. With the lane maxima sorted descending, count(x' > sorted[L])
             // grows with L; take the largest L whose count fits (L = 0 always
@@ -802,22 +792,28 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
                 else hi = mid - 1;
             }
             theta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(srt), lo));
-            strict = true;
             st.flags |= WS_OVF;
-            base = 0;
+        }
+        // The candidates in slot order, to the wave's LDS list: at most WCAP
+        // of them, the count above having used the same comparisons.
+        auto write = [&](auto strict_c) -> int {
+            constexpr bool STRICT = decltype(strict_c)::value;
+            int k = 0;
 #pragma unroll
-            for (int s = 0; s < EPT; ++s) {
-                const bool hit = v[s] > theta;
+            for (int sl = 0; sl < EPT; ++sl) {
+                const bool hit = STRICT ? v[sl] > theta : v[sl] >= theta;
                 const unsigned long long bm = __ballot(hit);
                 if (bm) {
+                    const int p = k + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
                     if (hit)
-                        wl[base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] =
-                            ((unsigned long long)__float_as_uint(v[s]) << 32) | (uint32_t)slot_id_late<DT>(sid0, s);
-                    base += __popcll(bm);
+                        wl[p] = ((unsigned long long)__float_as_uint(v[sl]) << 32) | (uint32_t)slot_id_late<DT>(sid0, sl);
+                    k += __popcll(bm);
                 }
             }
-        }
+            return k;
+        };
+        const int base = strict ? write(BoolC<true>{}) : write(BoolC<false>{});
         st.ncand = base;
         st.zm = canon_zero(m / c.T);
         // non-candidates have x' below (or at) theta, so z at most RN(theta / T)
