@@ -36,6 +36,9 @@ constexpr int WS_SUM = 2;
 // s holds the mass of the wave tile's non-candidates, relative to RN(m / T) and
 // approximate (window-cut tiles of rows top-k may not cut).
 constexpr int WS_APX = 4;
+// Neither flag: the tile holds more finite entries than the row's top-k, so the
+// row is cut by top-k and the mass outside the candidates is not summed (the
+// merge bounds what a top-k set deeper than the pool can miss by count).
 
 // What the row finaliser knows about one row's filtered distribution.
 // kept(v) <=> key64(z_v, v) >= kappa and (min_p <= 0 or exp(z_v - zmax) >= min_p),

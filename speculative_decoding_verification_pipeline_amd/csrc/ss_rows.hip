@@ -839,16 +839,18 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
             st.zmin = wave_min_f(zc);
             st.sc = wave_sum_d((double)wcand);
         }
-        // The mass outside the candidates. A count-cut (flat) wave tile of a row
-        // top-k may leave uncut sums its whole mass exactly, z = x' / T entry by
-        // entry (the row's normaliser then rests on it). Every other wave tile
-        // sums its non-candidates with exp2 on x' log2(e) / T - m log2(e) / T,
-        // an approximation whose error the merge bounds: it serves as the
-        // normaliser's far tail, or shows that a top-k set deeper than the pool
-        // adds nothing that matters. A wave tile with more than k finite
-        // entries proves the row is cut by top-k.
+        // The mass outside the candidates. A wave tile with more than k finite
+        // entries proves the row is cut by top-k: its mass outside the
+        // candidates is not needed (the top-k set's is bounded by count in the
+        // merge). Otherwise a count-cut (flat) wave tile sums its whole mass
+        // exactly, z = x' / T entry by entry (the row's normaliser may rest on
+        // it), and every other wave tile sums its non-candidates with exp2 on
+        // x' log2(e) / T - m log2(e) / T, an approximation whose error the
+        // merge bounds: it serves as the normaliser's far tail.
         const bool certainly_cut = c.top_k > 0 && c.top_k < c.V && st.nfinite > c.top_k;
-        if (strict && !certainly_cut) {
+        if (certainly_cut) {
+            // no tail sum
+        } else if (strict) {
             const float zm = st.zm;
             double acc = 0.0;
 #pragma unroll
@@ -865,8 +867,7 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
                 for (int s = 0; s < EPT; ++s) {
                     // one fused rounding: x' c2 - m c2
                     const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(v[s], c2, -mc));
-                    const bool cand = strict ? v[s] > theta : v[s] >= theta;
-                    acc += cand ? 0.0f : t;
+                    acc += v[s] >= theta ? 0.0f : t;
                 }
             }
             st.s = wave_sum_d((double)acc);
@@ -950,6 +951,7 @@ struct RowView {
     double Wc;     // the candidates' mass: at least the pool's
     double err;    // bound on the error of the approximate part of W
     int missing;   // some tile leaves mass outside its candidates that no sum covers
+                   // (only where the row is cut by top-k)
 };
 
 // Relative error bound of a window-cut tile's approximate non-candidate mass:
@@ -1458,11 +1460,13 @@ __device__ __forceinline__ int wave_first(int lim, Pred pred) {
 // F[0, n) from the weights w_i = exp(z_i - zmax) (binary32, as everywhere on
 // this path) and their binary64 inclusive prefix sums, both already in LDS.
 // W is the row mass (used when top-k does not cut) and err a bound on its
-// error; every entry past the pool weighs at most exp(zb - zmax). slow = 1 when
-// a request needs entries past the pool.
+// error; missing: some tile's mass outside its candidates is not in W (rows
+// cut by top-k only); every entry past the pool weighs at most exp(zb - zmax).
+// slow = 1 when a request needs entries past the pool.
 __device__ __forceinline__ RowOut resolve_wave(const SmemPool& P, int n, float zmax, float zb, double W,
-                                               double err, const RowCtx& c, float u, int K_eff, bool cut_k,
-                                               int total, bool topk_on, bool want_probs, bool want_topk) {
+                                               double err, bool missing, const RowCtx& c, float u, int K_eff,
+                                               bool cut_k, int total, bool topk_on, bool want_probs,
+                                               bool want_topk) {
     RowOut o;
     o.slow = 0;
     o.kappa = 0;
@@ -1478,11 +1482,17 @@ __device__ __forceinline__ RowOut resolve_wave(const SmemPool& P, int n, float z
         WK = pool_prefix(P, min(K_eff, n) - 1);
         kK = K_eff <= n ? P.F[K_eff - 1] : 0ull;
         // A top-k set deeper than the pool takes the pool's mass as its own:
-        // the entries past the pool (all of them, approximately, and the bound
-        // of that approximation) must weigh at most TAIL_EPS of it.
-        if (K_eff > n && (W - WK) + err > TAIL_EPS * WK) {
-            o.slow = 1;
-            return o;
+        // the K_eff - n entries it holds past the pool must weigh at most
+        // TAIL_EPS of it. Each weighs at most exp(zb - zmax); where every tile
+        // summed its mass outside the candidates, all entries past the pool
+        // together weigh at most (W - WK) + err.
+        if (K_eff > n) {
+            double past = (double)(K_eff - n) * exp((double)zb - (double)zmax);
+            if (!missing) past = fmin(past, (W - WK) + err);
+            if (past > TAIL_EPS * WK) {
+                o.slow = 1;
+                return o;
+            }
         }
     }
     // top-p: the first entry whose exclusive mass reaches top_p W_K
@@ -1633,7 +1643,7 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
     const bool topk_on = c.top_k > 0 && c.top_k < V;
     const int K_eff = topk_on ? min(c.top_k, total) : total;
     const bool cut_k = topk_on && K_eff < total;
-    bool slow = n == 0 || regmax > AREG || rv.missing != 0;
+    bool slow = n == 0 || regmax > AREG || (rv.missing != 0 && !cut_k);
     // An uncut row's normaliser must be accurate: a relative error e of W moves
     // every probability and every CDF breakpoint by at most e, and the parity
     // rule allows 1e-6. (A top-k set deeper than the pool is checked once the
@@ -1788,7 +1798,8 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
         const unsigned long long* F = P.F;
         __shared__ RowOut s_out;
         if (wv == 0) {
-            const RowOut o = resolve_wave(P, n, zmax, rv.zb, W, rv.err, c, u, K_eff, cut_k, total, topk_on,
+            const RowOut o = resolve_wave(P, n, zmax, rv.zb, W, rv.err, rv.missing != 0, c, u, K_eff, cut_k,
+                                          total, topk_on,
                                           dbg.probs != nullptr, dbg.topk != nullptr);
             if (lane == 0) s_out = o;
         }
