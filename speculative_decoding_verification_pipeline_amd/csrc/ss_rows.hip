@@ -183,11 +183,15 @@ struct SmemRadix {
     unsigned long long hm[256];
 };
 
-// Whole-row selection by buckets of d = zmax - z (HB buckets of width 1/HSCALE
-// over d in [0, HB / HSCALE), one more for everything deeper): per-bucket
-// counts and fixed-point masses, then the one bucket that holds the answer.
+// Whole-row selection by buckets of d = zmax - z: HB1 buckets of width 1/HSCALE
+// over d in [0, HD1), then HB - HB1 buckets of equal width over [HD1, zmax -
+// zlo] when the row's lowest finite z, zlo, lies deeper (one more bucket, HB,
+// holds everything past HD1 when zlo is not known): per-bucket counts and
+// fixed-point masses, then the one bucket that holds the answer.
 constexpr int HB = 4096;
+constexpr int HB1 = 3072;
 constexpr float HSCALE = 128.0f;
+constexpr float HD1 = HB1 / HSCALE;  // 24
 constexpr int HCAP = 2048;  // largest bucket resolved in LDS (else the radix passes)
 
 struct SmemHist {
@@ -212,12 +216,63 @@ struct SmemHistState {
     int n;                      // entries collected from the selected bucket
 };
 
-constexpr int SU = 8;            // entries per thread in flight in the fallback's passes
+constexpr int RQ = 4;            // 16-byte loads per thread in flight in vector row passes
 constexpr int LIST_CAP = 8192;  // history + draft + bias ids staged in LDS by the fallback
 
-struct SmemList {
-    int32_t ids[LIST_CAP];
+// The workgroup visits every entry v of a float row in memory, f(v, zr[v]).
+// The passes of the whole-row path are bound by the bytes each thread keeps in
+// flight, so the 16-byte-aligned body goes four floats per load, RQ loads at a
+// time; the unaligned head and the tail take one entry per thread.
+template <class F>
+__device__ __forceinline__ void row_visit(const float* zr, int V, F f) {
+    const int tid = threadIdx.x;
+    const int head = min(V, (int)(((16u - ((uint32_t)(uintptr_t)zr & 15u)) & 15u) >> 2));
+    if (tid < head) f(tid, zr[tid]);
+    const int nq = (V - head) >> 2;
+    const uint4* q = (const uint4*)(zr + head);
+    for (int i0 = tid; i0 < nq; i0 += NTR * RQ) {
+        uint4 t[RQ];
+#pragma unroll
+        for (int k = 0; k < RQ; ++k) t[k] = i0 + k * NTR < nq ? gld(q + i0 + k * NTR) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < RQ; ++k) {
+            const int i = i0 + k * NTR;
+            if (i < nq) {
+                const int v = head + 4 * i;
+                f(v, __uint_as_float(t[k].x));
+                f(v + 1, __uint_as_float(t[k].y));
+                f(v + 2, __uint_as_float(t[k].z));
+                f(v + 3, __uint_as_float(t[k].w));
+            }
+        }
+    }
+    const int v = head + 4 * nq + tid;
+    if (v < V) f(v, zr[v]);
+}
+
+// Per-chunk tables of the whole-row path's patches: multiplicities (u16 pairs),
+// bias marks, claim flags, and which chunks any list entry touches.
+constexpr int PCH = 16384;     // vocabulary entries per chunk
+constexpr int PMASKW = 1;      // chunk mask words
+static_assert(MAX_VOCAB <= PMASKW * 32 * PCH, "patch chunk mask");
+
+struct SmemPatch {
+    uint32_t cnt[PCH / 2];
+    uint32_t bias[PCH / 32];
+    uint32_t flag[PCH / 32];
+    uint32_t touched[PMASKW];
 };
+
+constexpr int BV_CAP = 1024;  // bias values staged in LDS by the fallback
+
+struct SmemList {
+    int32_t ids[LIST_CAP];      // the history, draft and bias ids
+    uint32_t work[LIST_CAP];    // claimed entries: list index | multiplicity << 13 | bias << 27
+    float bvals[BV_CAP];        // the bias values
+    int nwork;
+    SmemPatch pt;
+};
+static_assert(LIST_CAP <= (1 << 13), "work item layout");
 
 union SmemU {
     SmemTile t;
@@ -1077,10 +1132,22 @@ __device__ unsigned long long radix_select(const float* zr, int V, float zmax, P
     return prefix;
 }
 
-__device__ __forceinline__ int hbucket(float z, float zmax) {
-    // zmax - z >= 0 rounded, then scaled exactly: monotone in z
-    const float d = (zmax - z) * HSCALE;
-    return d < (float)HB ? (int)d : HB;
+// Scale of the deep buckets for a row whose finite z lie in [zlo, zmax] (0:
+// none, zlo unknown or the row is shallower than HD1).
+__device__ __forceinline__ float hdeep_scale(float zmax, float zlo) {
+    const float r = zmax - zlo;
+    return r > HD1 ? fminf((float)(HB - HB1) / (r - HD1), 1.0e30f) : 0.0f;
+}
+
+__device__ __forceinline__ int hbucket(float z, float zmax, float s2) {
+    // d = zmax - z >= 0 rounded, then scaled exactly (near part) or shifted
+    // and scaled (deep part): every step is monotone in z, so bucket order
+    // follows key order
+    const float d = zmax - z;
+    const float dn = d * HSCALE;
+    if (dn < (float)HB1) return (int)dn;
+    if (s2 > 0.0f) return HB1 + (int)fminf((d - HD1) * s2, (float)(HB - HB1 - 1));
+    return HB;
 }
 
 __device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int d) {
@@ -1112,7 +1179,16 @@ __device__ unsigned long long block_excl_scan_u64(unsigned long long v, SmemHist
     return base + inc - v;
 }
 
-// Totals of the entries where pred holds (count, fixed-point mass) and, when
+// An entry's weight exp(z - zmax). With deep_zero, entries more than
+// HW_DEEP below the maximum weigh 0 without the exponential: their fixed-point
+// weight is 0 either way (exp(-HW_DEEP) 2^44 < 1), and the caller's predicate
+// does not tell such small weights from 0.
+constexpr float HW_DEEP = 31.0f;
+__device__ __forceinline__ float entry_w(float z, float zmax, bool deep_zero) {
+    return deep_zero && zmax - z > HW_DEEP ? 0.0f : expf(z - zmax);
+}
+
+// Totals of the entries where pred holds (count, and with by_mass the fixed-point mass) and, when
 // want_key, the key selected among them exactly as radix_select defines it:
 // by count, the key of rank `target` (1-based); by mass, the key of the first
 // entry whose inclusive mass exceeds target = frac x total mass (frac > 0) or
@@ -1121,8 +1197,8 @@ __device__ unsigned long long block_excl_scan_u64(unsigned long long v, SmemHist
 // resolved by pairwise comparison. A bucket too large for LDS, or the deepest
 // bucket, is left to radix_select.
 template <class Pred>
-__device__ void hist_select(const float* zr, int V, float zmax, Pred pred, bool by_mass,
-                            bool want_key, unsigned long long target, double frac, SmemU& su,
+__device__ void hist_select(const float* zr, int V, float zmax, float s2, bool w_deep_zero, Pred pred,
+                            bool by_mass, bool want_key, unsigned long long target, double frac, SmemU& su,
                             SmemR& sh, int& count, unsigned long long& mass,
                             unsigned long long& key) {
     const int tid = threadIdx.x;
@@ -1133,22 +1209,14 @@ __device__ void hist_select(const float* zr, int V, float zmax, Pred pred, bool 
         h.hm[b] = 0;
     }
     __syncthreads();
-    for (int v0 = tid; v0 < V; v0 += NTR * SU) {
-        float zs[SU];
-#pragma unroll
-        for (int k = 0; k < SU; ++k) zs[k] = v0 + k * NTR < V ? zr[v0 + k * NTR] : NEG_INF;
-#pragma unroll
-        for (int k = 0; k < SU; ++k) {
-            const float z = zs[k];
-            const int v = v0 + k * NTR;
-            if (!(z > NEG_INF)) continue;
-            const float w = expf(z - zmax);
-            if (!pred(key64(z, v), w)) continue;
-            const int b = hbucket(z, zmax);
-            atomicAdd(&h.hc[b], 1u);
-            atomicAdd(&h.hm[b], (unsigned long long)wq(w));
-        }
-    }
+    row_visit(zr, V, [&](int v, float z) {
+        if (!(z > NEG_INF)) return;
+        const float w = entry_w(z, zmax, w_deep_zero);
+        if (!pred(key64(z, v), w)) return;
+        const int b = hbucket(z, zmax, s2);
+        atomicAdd(&h.hc[b], 1u);
+        if (by_mass) atomicAdd(&h.hm[b], (unsigned long long)wq(w));
+    });
     __syncthreads();
     // thread t owns buckets 4t .. 4t + 3; the last thread also the deepest one
     constexpr int PER = HB / NTR;
@@ -1214,25 +1282,17 @@ __device__ void hist_select(const float* zr, int V, float zmax, Pred pred, bool 
     const unsigned long long cum = hs.cum;
     __syncthreads();  // the histogram is dead from here: its memory holds the bucket
     SmemBucket& kb = su.k;
-    for (int v0 = tid; v0 < V; v0 += NTR * SU) {
-        float zs[SU];
-#pragma unroll
-        for (int k = 0; k < SU; ++k) zs[k] = v0 + k * NTR < V ? zr[v0 + k * NTR] : NEG_INF;
-#pragma unroll
-        for (int k = 0; k < SU; ++k) {
-            const float z = zs[k];
-            const int v = v0 + k * NTR;
-            if (!(z > NEG_INF) || hbucket(z, zmax) != sel) continue;
-            const float w = expf(z - zmax);
-            const unsigned long long kk = key64(z, v);
-            if (!pred(kk, w)) continue;
-            const int slot = atomicAdd(&hs.n, 1);
-            if (slot < HCAP) {  // the histogram counted exactly these entries
-                kb.key[slot] = kk;
-                kb.wq[slot] = wq(w);
-            }
+    row_visit(zr, V, [&](int v, float z) {
+        if (!(z > NEG_INF) || hbucket(z, zmax, s2) != sel) return;
+        const float w = entry_w(z, zmax, w_deep_zero);
+        const unsigned long long kk = key64(z, v);
+        if (!pred(kk, w)) return;
+        const int slot = atomicAdd(&hs.n, 1);
+        if (slot < HCAP) {  // the histogram counted exactly these entries
+            kb.key[slot] = kk;
+            kb.wq[slot] = wq(w);
         }
-    }
+    });
     __syncthreads();
     const int n = min(hs.n, HCAP);
     if (tid == 0) hs.key = ~0ull;
@@ -1273,9 +1333,8 @@ __device__ void hist_select(const float* zr, int V, float zmax, Pred pred, bool 
 
 // z of every entry of the row into scratch, by the whole workgroup: first from
 // the raw logits and the mask alone, then the entries a history, draft or bias
-// entry touches are formed again with their multiplicity and bias (each
-// distinct id by the thread that holds its first occurrence in the lists, read
-// from LDS when they fit), through the same process_entry as every other path.
+// entry touches are formed again with their multiplicity and bias, through the
+// same process_entry as every other path.
 // Entry i of the concatenated history, draft and bias id lists.
 __device__ __forceinline__ int list_id(const RowCtx& c, int nh, int i) {
     if (i < c.hist_len) return gld(c.hist + i);
@@ -1283,67 +1342,144 @@ __device__ __forceinline__ int list_id(const RowCtx& c, int nh, int i) {
     return gld(c.bias_ids + (i - nh));
 }
 
-// z again for each distinct id of the lists (LDS copy `ids`, or null to read
-// them from memory), with its multiplicity among the history and draft ids and
-// whether a bias entry names it.
+// z again for each distinct id of the n list entries (LDS copy `ids` and the
+// bias values in `bv`, or null to read them from memory), the vocabulary taken
+// PCH entries at a time: the chunk's multiplicities and bias marks are counted
+// in LDS from the whole list, then the first thread to claim an entry's flag
+// forms its z (from memory) or, with the lists staged, appends it to a work
+// list that is formed after the last chunk, all its loads in flight together.
+// Chunks no list entry touches are skipped. Returns the least z it wrote.
 template <int DT>
-__device__ void patch_entries(const RowCtx& c, float* zr, int nh, int n, const int32_t* ids) {
-    for (int i = threadIdx.x; i < n; i += NTR) {
-        const int id = ids ? ids[i] : list_id(c, nh, i);
-        if (id < 0 || id >= c.V) continue;
-        bool first = true;
-        for (int j = 0; j < i; ++j)
-            if ((ids ? ids[j] : list_id(c, nh, j)) == id) {
-                first = false;
-                break;
-            }
-        if (!first) continue;
-        uint32_t cnt = 0;
-        bool hit = false;
-        for (int j = 0; j < n; ++j) {
-            const bool eq = (ids ? ids[j] : list_id(c, nh, j)) == id;
-            if (j < nh) cnt += eq ? 1u : 0u;
-            else hit |= eq;
-        }
-        const bool allowed = c.mask ? ((gld(c.mask + (id >> 5)) >> (id & 31)) & 1u) : true;
-        const float x = process_entry(c, id, read_logit<DT>(c.logits, id), cnt, hit, allowed);
-        zr[id] = x > NEG_INF ? canon_zero(x / c.T) : NEG_INF;
-    }
-}
-
-template <int DT>
-__device__ void row_z(const RowCtx& c, float* zr, SmemU& su) {
+__device__ float patch_entries(const RowCtx& c, float* zr, int nh, int n, SmemList& sl, bool staged) {
     const int tid = threadIdx.x;
-    const int V = c.V;
-    // SU entries per thread in flight: the loop is bound by memory latency
-    for (int v0 = tid; v0 < V; v0 += NTR * SU) {
-        float x[SU];
-        uint32_t mw[SU];
-#pragma unroll
-        for (int k = 0; k < SU; ++k) {
-            const int v = v0 + k * NTR;
-            x[k] = v < V ? read_logit<DT>(c.logits, v) : NEG_INF;
-            mw[k] = (c.mask && v < V) ? gld(c.mask + (v >> 5)) : 0xFFFFFFFFu;
+    SmemPatch& pt = sl.pt;
+    float lo = __builtin_huge_valf();
+    auto id_at = [&](int i) { return staged ? sl.ids[i] : list_id(c, nh, i); };
+    // x' of entry id from its raw logit, multiplicity and bias mark (the same
+    // steps, in the same order, as process_entry)
+    auto form = [&](int id, uint32_t cnt, bool hit) {
+        const bool allowed = c.mask ? ((gld(c.mask + (id >> 5)) >> (id & 31)) & 1u) : true;
+        float x = penalize(c, read_logit<DT>(c.logits, id), cnt);
+        if (hit) {
+            for (int k = 0; k < c.bias_len; ++k)
+                if (id_at(nh + k) == id) x = x + (staged && k < BV_CAP ? sl.bvals[k] : gld(c.bias_vals + k));
         }
-#pragma unroll
-        for (int k = 0; k < SU; ++k) {
-            const int v = v0 + k * NTR;
-            if (v >= V) continue;
-            const float xv = ((mw[k] >> (v & 31)) & 1u) ? x[k] : NEG_INF;
-            zr[v] = xv > NEG_INF ? canon_zero(xv / c.T) : NEG_INF;
-        }
-    }
-    const int nh = c.hist_len + c.extra_len;
-    const int n = nh + c.bias_len;
-    if (n <= LIST_CAP) {
-        for (int i = tid; i < n; i += NTR) su.l.ids[i] = list_id(c, nh, i);
-        __syncthreads();  // also orders the raw pass before the patches
-        patch_entries<DT>(c, zr, nh, n, su.l.ids);
-    } else {
-        __syncthreads();
-        patch_entries<DT>(c, zr, nh, n, nullptr);
+        x = allowed ? x : NEG_INF;
+        const float z = x > NEG_INF ? canon_zero(x / c.T) : NEG_INF;
+        zr[id] = z;
+        if (z > NEG_INF) lo = fminf(lo, z);
+    };
+    const int nch = (c.V + PCH - 1) / PCH;
+    if (tid < PMASKW) pt.touched[tid] = 0u;
+    if (tid == 0) sl.nwork = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += NTR) {
+        const int id = id_at(i);
+        if (id >= 0 && id < c.V) atomicOr(&pt.touched[(id / PCH) >> 5], 1u << ((id / PCH) & 31));
     }
     __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+        if (!((pt.touched[ch >> 5] >> (ch & 31)) & 1u)) continue;  // uniform
+        const int c0 = ch * PCH;
+        for (int k = tid; k < PCH / 2; k += NTR) pt.cnt[k] = 0u;
+        for (int k = tid; k < PCH / 32; k += NTR) {
+            pt.bias[k] = 0u;
+            pt.flag[k] = 0u;
+        }
+        __syncthreads();
+        for (int i = tid; i < n; i += NTR) {
+            const int l = id_at(i) - c0;
+            if (l < 0 || l >= PCH || l + c0 >= c.V) continue;
+            if (i < nh) atomicAdd(&pt.cnt[l >> 1], 1u << ((l & 1) * 16));
+            else atomicOr(&pt.bias[l >> 5], 1u << (l & 31));
+        }
+        __syncthreads();
+        for (int i = tid; i < n; i += NTR) {
+            const int id = id_at(i);
+            const int l = id - c0;
+            if (l < 0 || l >= PCH || id >= c.V) continue;
+            const uint32_t b = 1u << (l & 31);
+            if (atomicOr(&pt.flag[l >> 5], b) & b) continue;  // another thread has it
+            const uint32_t cnt = (pt.cnt[l >> 1] >> ((l & 1) * 16)) & 0xFFFFu;
+            const bool hit = (pt.bias[l >> 5] & b) != 0u;
+            if (staged) {
+                // distinct ids number at most n <= LIST_CAP: the list cannot overflow
+                sl.work[atomicAdd(&sl.nwork, 1)] = (uint32_t)i | (cnt << 13) | ((hit ? 1u : 0u) << 27);
+            } else {
+                form(id, cnt, hit);
+            }
+        }
+        __syncthreads();  // the tables are cleared for the next chunk; the work list is whole
+    }
+    if (staged) {
+        for (int w = tid; w < sl.nwork; w += NTR) {
+            const uint32_t it = sl.work[w];
+            form(sl.ids[it & 0x1FFFu], (it >> 13) & 0x3FFFu, (it >> 27) & 1u);
+        }
+    }
+    return lo;
+}
+
+// Returns a lower bound of the row's finite z (+inf: none is finite): the
+// least z written by either pass.
+template <int DT>
+__device__ float row_z(const RowCtx& c, float* zr, SmemU& su, SmemR& sh) {
+    const int tid = threadIdx.x;
+    const int V = c.V;
+    float lo = __builtin_huge_valf();
+    // the raw pass: 16-byte loads of the aligned body, RQ in flight per
+    // thread (the loop is bound by memory latency), single entries for the
+    // unaligned head and the tail
+    constexpr int VEC = Lay<DT>::VEC;
+    constexpr int ES = DT == SS_F32 ? 4 : 2;
+    auto one = [&](int v, float x, uint32_t mword) {
+        const float xv = ((mword >> (v & 31)) & 1u) ? x : NEG_INF;
+        const float z = xv > NEG_INF ? canon_zero(xv / c.T) : NEG_INF;
+        zr[v] = z;
+        if (z > NEG_INF) lo = fminf(lo, z);
+    };
+    auto mask_word = [&](int v) { return c.mask ? gld(c.mask + (v >> 5)) : 0xFFFFFFFFu; };
+    const char* row = (const char*)c.logits;
+    const int head = min(V, (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / ES));
+    if (tid < head) one(tid, read_logit<DT>(c.logits, tid), mask_word(tid));
+    const int nq = (V - head) / VEC;
+    const uint4* q = (const uint4*)(row + (size_t)head * ES);
+    for (int i0 = tid; i0 < nq; i0 += NTR * RQ) {
+        uint4 t[RQ];
+        uint32_t m0[RQ], m1[RQ];
+#pragma unroll
+        for (int k = 0; k < RQ; ++k) {
+            const int i = i0 + k * NTR;
+            const int v = head + VEC * min(i, nq - 1);
+            t[k] = i < nq ? gld(q + i) : make_uint4(0, 0, 0, 0);
+            m0[k] = mask_word(v);               // the group may straddle two mask words
+            m1[k] = mask_word(v + VEC - 1);
+        }
+#pragma unroll
+        for (int k = 0; k < RQ; ++k) {
+            const int i = i0 + k * NTR;
+            if (i >= nq) continue;
+            const int v = head + VEC * i;
+            float x[VEC];
+            unpack_group<DT>(t[k], x);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                one(v + j, x[j], ((v + j) >> 5) == (v >> 5) ? m0[k] : m1[k]);
+        }
+    }
+    for (int v = head + VEC * nq + tid; v < V; v += NTR) one(v, read_logit<DT>(c.logits, v), mask_word(v));
+    const int nh = c.hist_len + c.extra_len;
+    const int n = nh + c.bias_len;
+    if (n > 0) {
+        const bool staged = n <= LIST_CAP;
+        if (staged) {
+            for (int i = tid; i < n; i += NTR) su.l.ids[i] = list_id(c, nh, i);
+            for (int k = tid; k < min(c.bias_len, BV_CAP); k += NTR) su.l.bvals[k] = gld(c.bias_vals + k);
+        }
+        __syncthreads();  // also orders the raw pass before the patches
+        lo = fminf(lo, patch_entries<DT>(c, zr, nh, n, su.l, staged));
+    }
+    return -block_max(-lo, sh.red);  // its barriers also end the patches
 }
 
 // Exact whole-row resolution: z for the whole row into scratch, then select by
@@ -1356,8 +1492,9 @@ __device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Wo
     const int tid = threadIdx.x;
     const int V = c.V;
     float* zr = ws.scratch_z + (size_t)row * V;
-    row_z<DT>(c, zr, su);
+    const float zlo = row_z<DT>(c, zr, su, sh);
     const float zmax = canon_zero(rs.m / c.T);
+    const float s2 = hdeep_scale(zmax, zlo);
     const int total = rs.nfinite;
     const bool topk_on = c.top_k > 0 && c.top_k < V;
     const int K_eff = topk_on ? min(c.top_k, total) : total;
@@ -1365,18 +1502,20 @@ __device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Wo
     unsigned long long ms;
     unsigned long long kK = 0;
     if (topk_on && K_eff < total)
-        hist_select(zr, V, zmax, [](unsigned long long, float) { return true; }, false, true,
+        hist_select(zr, V, zmax, s2, true, [](unsigned long long, float) { return true; }, false, true,
                     (unsigned long long)K_eff, 0.0, su, sh, cnt, ms, kK);
     unsigned long long kP = kK;
     if (c.top_p < 1.0f)  // the first entry whose inclusive mass exceeds top_p x (top-k mass)
-        hist_select(zr, V, zmax, [kK](unsigned long long k, float) { return k >= kK; }, true,
+        hist_select(zr, V, zmax, s2, true, [kK](unsigned long long k, float) { return k >= kK; }, true,
                     true, 0, (double)c.top_p, su, sh, cnt, ms, kP);
     const float mp = c.min_p;
     auto kept = [kP, mp](unsigned long long k, float w) { return k >= kP && (mp <= 0.0f || w >= mp); };
     // the draw: the first kept entry whose inclusive mass exceeds u x (kept mass)
     int n_kept;
     unsigned long long Wk, kt;
-    hist_select(zr, V, zmax, kept, true, true, 0, (double)u, su, sh, n_kept, Wk, kt);
+    // min_p at or below the deepest nonzero fixed-point weight needs every w
+    const bool dz = mp <= 0.0f || mp > 1e-13f;
+    hist_select(zr, V, zmax, s2, dz, kept, true, true, 0, (double)u, su, sh, n_kept, Wk, kt);
     if (tid == 0) {
         info.kappa = kP;
         info.W = (double)Wk / MASS_SCALE;
@@ -2704,48 +2843,58 @@ __global__ __launch_bounds__(NTR) void k_lm_slow(LmheadArgs a) {
     const ParamPtrs& p = a.p;
     const int V = a.V;
     const float* zr = a.zmat + (size_t)j * V;
-    float m = NEG_INF;
+    float m = NEG_INF, lo = __builtin_huge_valf();
     int nf = 0;
-    for (int v0 = tid; v0 < V; v0 += NTR * SU) {
-        float zs[SU];
-#pragma unroll
-        for (int k = 0; k < SU; ++k) zs[k] = v0 + k * NTR < V ? zr[v0 + k * NTR] : NEG_INF;
-#pragma unroll
-        for (int k = 0; k < SU; ++k)
-            if (zs[k] > NEG_INF) {
-                m = fmaxf(m, zs[k]);
-                ++nf;
-            }
-    }
+    row_visit(zr, V, [&](int, float z) {
+        if (z > NEG_INF) {
+            m = fmaxf(m, z);
+            lo = fminf(lo, z);
+            ++nf;
+        }
+    });
     const float zmax = block_max(m, sh.red);
+    const float s2 = hdeep_scale(zmax, -block_max(-lo, sh.red));
     const int total = block_sum_i(nf, sh.red);
     const bool topk_on = p.top_k[j] > 0 && p.top_k[j] < V;
     const int K_eff = topk_on ? min(p.top_k[j], total) : total;
     int cnt;
     unsigned long long ms, kK = 0;
     if (topk_on && K_eff < total)
-        hist_select(zr, V, zmax, [](unsigned long long, float) { return true; }, false, true,
+        hist_select(zr, V, zmax, s2, true, [](unsigned long long, float) { return true; }, false, true,
                     (unsigned long long)K_eff, 0.0, su, sh, cnt, ms, kK);
     unsigned long long kP = kK;
     if (p.top_p[j] < 1.0f)
-        hist_select(zr, V, zmax, [kK](unsigned long long k, float) { return k >= kK; }, true, true,
+        hist_select(zr, V, zmax, s2, true, [kK](unsigned long long k, float) { return k >= kK; }, true, true,
                     0, (double)p.top_p[j], su, sh, cnt, ms, kP);
     const float mp = p.min_p[j];
     // four consecutive entries per step share one Philox block
     float bs = -FLT_MAX;
     int bi = INT_MAX;
     const uint32_t req = (uint32_t)p.request_ids[j], pos = (uint32_t)p.positions[j];
-    for (int g0 = tid; g0 * 4 < V; g0 += NTR * 2) {
-        float zs[2][4];
+    // RQ groups per thread in flight, each one 16-byte load where the row is
+    // aligned
+    const bool al = ((uint32_t)(uintptr_t)zr & 15u) == 0u;
+    for (int g0 = tid; g0 * 4 < V; g0 += NTR * RQ) {
+        float zs[RQ][4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < RQ; ++h) {
+            const int g = g0 + h * NTR;
+            if (al && g * 4 + 3 < V) {
+                const uint4 t = gld((const uint4*)zr + g);
+                zs[h][0] = __uint_as_float(t.x);
+                zs[h][1] = __uint_as_float(t.y);
+                zs[h][2] = __uint_as_float(t.z);
+                zs[h][3] = __uint_as_float(t.w);
+            } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int v = (g0 + h * NTR) * 4 + q;
-                zs[h][q] = v < V ? zr[v] : NEG_INF;
+                for (int q = 0; q < 4; ++q) {
+                    const int v = g * 4 + q;
+                    zs[h][q] = v < V ? zr[v] : NEG_INF;
+                }
             }
+        }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < RQ; ++h) {
             const int g = g0 + h * NTR;
             bool any = false;
             bool keep[4];
