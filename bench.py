@@ -446,7 +446,8 @@ def secondary(args, dev):
     # the same GEMM with the per-request pipeline in its epilogue: the
     # heterogeneous parameter recipe (penalties over 512 history ids, 16 bias
     # ids, mixed T / top-k / top-p / min-p); rows whose cuts fall outside the
-    # tile candidates take the second pass
+    # tile candidates are selected over their whole row of z' (which the GEMM
+    # kernel writes for rows with a filter)
     hw = W.heterogeneous(B=B, V=V)
     hp = sampling_params(hw, dev)
     lpath = torch.empty(B, dtype=torch.int32, device=dev)
@@ -455,9 +456,7 @@ def secondary(args, dev):
     lp = np.bincount(lpath.cpu().numpy(), minlength=3).tolist()
     pfn = [lambda: s.lmhead_sample_params(Hd, Wd, hp, out=o)]
     pms, _ = time_graph(pfn, lsteps, 3)
-    pst = stage_summary(time_stages(s, pfn, lsteps, 4),
-                        ["k_lmhead_proc<stats>", "k_lm_merge", "k_lmhead_proc<second pass>",
-                         "k_lm_slow"])
+    pst = stage_summary(time_stages(s, pfn, lsteps, 3), ["k_lmhead_proc", "k_lm_merge", "k_lm_slow"])
     out["lmhead_params"] = {"us_per_call": pms / lsteps * 1e3, "stages": pst,
                             "tokens_per_s": B * lsteps / (pms * 1e-3),
                             "rows_by_path": {"candidates": lp[0], "whole_row": lp[1],

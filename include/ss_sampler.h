@@ -338,7 +338,7 @@ ss_status ss_sample_noalloc(const void* logits, ss_dtype dtype, int64_t row_stri
  *                       words apart), request ids, positions and seed.
  *   out_tokens          [B] int32.
  *   debug_path          NULL, or [B] int32: 0 = decided on the tile candidates,
- *                       1 = decided over the whole row after the second pass,
+ *                       1 = decided over the whole row of z',
  *                       2 = no filter or greedy (the tiles' best scores).
  * Each GEMM tile applies penalties, bias, mask and temperature to its logits
  * (z' = x'/T as in ss_sample) and keeps, per batch row, its 4 largest keys, the
@@ -349,10 +349,11 @@ ss_status ss_sample_noalloc(const void* logits, ss_dtype dtype, int64_t row_stri
  * min-p), which Gumbel-max samples from the filtered distribution exactly. The
  * support is taken from the tiles' candidates whenever the cuts fall among the
  * entries they certify (every key above the largest next key); other rows are
- * formed again by a second GEMM pass into the workspace and selected over the
- * whole row (that pass costs nothing when every row resolved).
- * Launches four kernels (GEMM with summaries, row merge, the second GEMM pass,
- * the whole-row selection). Errors: as ss_lmhead_sample, and the checks
+ * selected over their whole row of z', which the GEMM kernel also writes to the
+ * workspace for every row with a filter (4 bytes per entry, against the 2 K of
+ * weight per vocabulary entry the GEMM reads; rows without a filter never
+ * leave the chip). Launches three kernels (GEMM with summaries, row merge, the
+ * whole-row selection, which returns at once when every row resolved). Errors: as ss_lmhead_sample, and the checks
  * ss_sample makes on params. */
 ss_status ss_lmhead_sample_params(ss_sampler* s, const uint16_t* hidden, const uint16_t* weight,
                                   int32_t B, const ss_params* params, int32_t* out_tokens,

@@ -271,13 +271,13 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead(LmheadArgs a) {
 // multiplicity of each of the tile's 128 entries in the row's history (u16)
 // and a bit per entry that some logit-bias entry names. Each entry's logit then
 // goes through penalties, bias (entries applied in array order), mask and
-// temperature as in the sampler, giving z'. MODE_STATS summarises each
+// temperature as in the sampler, giving z'. The kernel summarises each
 // (row, tile): its LM_NC largest keys (z', id), the next key, the mass below
-// its maximum, the best Gumbel score and the count of finite entries.
-// MODE_MAT writes z' of the rows the candidates could not resolve.
+// its maximum, the best Gumbel score and the count of finite entries. For rows
+// with a filter it also writes z' to the workspace (4 bytes per entry against
+// the weight's 2 K per vocabulary row): the rows the summaries cannot settle
+// are then selected over the whole row without forming the GEMM again.
 
-constexpr int MODE_STATS = 1;
-constexpr int MODE_MAT = 2;
 constexpr int LM_NK = LM_NC + 1;  // keys kept per list: the candidates and the next one
 
 __device__ __forceinline__ float lm_penalize(float x, uint32_t count, float rep, float freq, float pres) {
@@ -341,7 +341,6 @@ __device__ __forceinline__ LmPart lm_shfl_xor32(const LmPart& x) {
     return y;
 }
 
-template <int MODE>
 __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t w0[LM_W_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t w1[LM_W_BYTES];
@@ -356,11 +355,6 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
     const int half = lane >> 5;
     const int r32 = lane & 31;
     const ParamPtrs& p = a.p;
-    if (MODE == MODE_MAT) {
-        // only rows the candidates left open are formed again; none: no work
-        const bool open = lane < a.B && a.unres[lane] != 0;
-        if (__ballot(open) == 0ull) return;
-    }
     floatx16 acc[2];
     lm_gemm(a, tile, acc, w0, w1, w2, h0, h1, h2);
 
@@ -424,9 +418,10 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
         P.nfinite = 0;
         const int j = bb * 32 + r32;
         if (j >= a.B) continue;
-        const bool mat = MODE == MODE_MAT && a.unres[j] != 0;
-        if (MODE == MODE_MAT && !mat) continue;
         const float T = p.temperature[j];
+        // z' to the workspace: rows with a filter (the others never need it)
+        const bool mat = T != 0.0f && ((p.top_k[j] > 0 && p.top_k[j] < a.V) || p.top_p[j] < 1.0f ||
+                                       p.min_p[j] > 0.0f);
         const float rep = p.rep[j], freq = p.freq[j], pres = p.pres[j];
         const uint32_t req = (uint32_t)p.request_ids[j];
         const uint32_t pos = (uint32_t)p.positions[j];
@@ -440,7 +435,7 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
         for (int g = 0; g < 4; ++g) {
             const int vb = wbase + 8 * g + 4 * half;
             uint4 wv = make_uint4(0, 0, 0, 0);
-            if (MODE == MODE_STATS && T != 0.0f && vb < a.V)
+            if (T != 0.0f && vb < a.V)
                 wv = philox4x32_10(make_uint4(req, pos, (uint32_t)vb >> 2, DOM_GUMBEL),
                                    (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
             const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -462,10 +457,6 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
                 const bool fin = x > -__builtin_huge_valf();
                 const float zp = fin ? (T != 0.0f ? canon_zero(x / T) : canon_zero(x)) : x;
                 zz[4 * g + q] = zp;
-                if (MODE == MODE_MAT) {
-                    a.zmat[(size_t)j * a.V + v] = zp;
-                    continue;
-                }
                 if (!fin) continue;
                 lm_insert(P.t, key64(zp, v));
                 const float sc = T != 0.0f ? zp + gumbel32(ws[q]) : zp;
@@ -476,7 +467,21 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
                 ++P.nfinite;
             }
         }
-        if (MODE == MODE_STATS && P.t[0]) {
+        if (mat) {
+            float* zr = a.zmat + (size_t)j * a.V;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int vb = wbase + 8 * g + 4 * half;
+                if ((a.V & 3) == 0 && vb + 3 < a.V) {
+                    *(float4*)(zr + vb) = make_float4(zz[4 * g], zz[4 * g + 1], zz[4 * g + 2], zz[4 * g + 3]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (vb + q < a.V) zr[vb + q] = zz[4 * g + q];
+                }
+            }
+        }
+        if (P.t[0]) {
             const float zt = key_z(P.t[0]);
             float m = 0.0f;
 #pragma unroll
@@ -485,7 +490,6 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
             P.mass = m;
         }
     }
-    if (MODE == MODE_MAT) return;
     // the two halves of a column hold different entries: combine, then the
     // four waves through LDS
     struct alignas(16) Slot {
@@ -598,10 +602,9 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_reduce(LmheadArgs a) {
 }
 
 hipError_t launch_lmhead_params(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le) {
-    launch_k(le, 0, k_lmhead_proc<MODE_STATS>, dim3(a.n_vtiles), dim3(LM_NT), st, a);
+    launch_k(le, 0, k_lmhead_proc, dim3(a.n_vtiles), dim3(LM_NT), st, a);
     launch_lm_merge(a, st, le, 1);
-    launch_k(le, 2, k_lmhead_proc<MODE_MAT>, dim3(a.n_vtiles), dim3(LM_NT), st, a);
-    launch_lm_slow(a, st, le, 3);
+    launch_lm_slow(a, st, le, 2);
     return hipGetLastError();
 }
 

@@ -2593,8 +2593,8 @@ __global__ __launch_bounds__(NT) void k_tree_finish(TreeArgs a) {
 // list is at most that tile's next key). These certified entries, sorted, are
 // an exact prefix of the row in key order; when the top-k, top-p and min-p
 // cuts all fall inside it, the kept support is known and the token is the best
-// z' + g over it. Otherwise the row is marked open: its z' are formed again by
-// a second GEMM pass and the whole-row selection below decides it.
+// z' + g over it. Otherwise the row is marked open: its z', which the GEMM
+// kernel wrote to the workspace, go through the whole-row selection below.
 
 constexpr int LM_CAP = 4096;  // certified entries sorted in LDS
 
@@ -2832,8 +2832,8 @@ __global__ __launch_bounds__(NTR) void k_lm_merge(LmheadArgs a) {
     }
 }
 
-// Rows left open: their z' (formed again by the second GEMM pass) through the
-// whole-row selection, then the best z' + g over the kept entries.
+// Rows left open: their z' (written by the GEMM kernel) through the whole-row
+// selection, then the best z' + g over the kept entries.
 __global__ __launch_bounds__(NTR) void k_lm_slow(LmheadArgs a) {
     __shared__ SmemU su;
     __shared__ SmemR sh;
