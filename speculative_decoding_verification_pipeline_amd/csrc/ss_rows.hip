@@ -1197,7 +1197,7 @@ __device__ __forceinline__ float entry_w(float z, float zmax, bool deep_zero) {
 // resolved by pairwise comparison. A bucket too large for LDS, or the deepest
 // bucket, is left to radix_select.
 template <class Pred>
-__device__ void hist_select(const float* zr, int V, float zmax, float s2, bool w_deep_zero, Pred pred,
+__device__ __forceinline__ void hist_select(const float* zr, int V, float zmax, float s2, bool w_deep_zero, Pred pred,
                             bool by_mass, bool want_key, unsigned long long target, double frac, SmemU& su,
                             SmemR& sh, int& count, unsigned long long& mass,
                             unsigned long long& key) {
@@ -1350,7 +1350,7 @@ __device__ __forceinline__ int list_id(const RowCtx& c, int nh, int i) {
 // list that is formed after the last chunk, all its loads in flight together.
 // Chunks no list entry touches are skipped. Returns the least z it wrote.
 template <int DT>
-__device__ float patch_entries(const RowCtx& c, float* zr, int nh, int n, SmemList& sl, bool staged) {
+__device__ __forceinline__ float patch_entries(const RowCtx& c, float* zr, int nh, int n, SmemList& sl, bool staged) {
     const int tid = threadIdx.x;
     SmemPatch& pt = sl.pt;
     float lo = __builtin_huge_valf();
@@ -1423,7 +1423,7 @@ __device__ float patch_entries(const RowCtx& c, float* zr, int nh, int n, SmemLi
 // Returns a lower bound of the row's finite z (+inf: none is finite): the
 // least z written by either pass.
 template <int DT>
-__device__ float row_z(const RowCtx& c, float* zr, SmemU& su, SmemR& sh) {
+__device__ __forceinline__ float row_z(const RowCtx& c, float* zr, SmemU& su, SmemR& sh) {
     const int tid = threadIdx.x;
     const int V = c.V;
     float lo = __builtin_huge_valf();
