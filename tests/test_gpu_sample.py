@@ -143,6 +143,40 @@ def test_high_entropy_rows_take_the_exact_fallback():
     tally.check()
 
 
+def test_deep_rows_on_the_whole_row_path():
+    # Steep Zipf rows whose top-k sets reach 40-90 below the maximum in z: the
+    # whole-row selection's cut lies in its deep buckets (spread over the row's
+    # own depth). 9000 history ids per row exceed the 8192 the whole-row path
+    # stages in LDS, so its patches take the unstaged branch on rows 0-3; rows
+    # 4-7 have 3000 (staged). Row 5 names one id twice in its bias list.
+    rng = np.random.default_rng(83)
+    B, V = 8, 128256
+    x = W.zipf_rows(rng, B, V)
+    hist = rng.integers(0, V, (B, 9000), dtype=np.int64).astype(np.int32)
+    hist[4:, 3000:] = -1  # rows 4-7: 3000 ids, the rest outside the vocabulary
+    bias_ids = np.stack([rng.choice(V, 16, replace=False) for _ in range(B)]).astype(np.int32)
+    bias_ids[5, 7] = bias_ids[5, 2]
+    bias_vals = rng.uniform(-5.0, 5.0, (B, 16)).astype(np.float32)
+    w = W.SampleWorkload("deep", x, "f32", np.array([0.7, 1.0] * 4, np.float32),
+                         np.array([5000, 20000, 60000, 20000, 30000, 60000, 20000, 5000], np.int32),
+                         np.array([1.0, 1.0, 1.0, 0.95, 1.0, 1.0, 0.9, 1.0], np.float32),
+                         np.array([0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.02], np.float32),
+                         rep=np.full(B, 1.1, np.float32), freq=np.full(B, 0.2, np.float32),
+                         pres=np.full(B, 0.3, np.float32), hist=hist, bias_ids=bias_ids,
+                         bias_vals=bias_vals, request_ids=np.arange(B, dtype=np.int32),
+                         positions=np.full(B, 3, np.int32), seed=29)
+    xs, filts = oracle_filtered(w)
+    s = make_sampler(B, V)
+    tally = Tally("deep rows", budget=False)
+    toks, dbg = run_debug(s, w)
+    compare_debug(w, xs, filts, toks, dbg, w.seed, tally)
+    paths = dbg.path.cpu().numpy()
+    log(f"[deep rows] paths {paths.tolist()}")
+    assert (paths == 1).all()  # the debug outputs ask for top-k sets deeper than any pool
+    seed_sweep(s, w, filts, range(200, 300), tally)
+    tally.check()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_large_logits_at_low_temperature(dtype):
     # logits near +50 at T = 0.7 put z near 71, where a binary32 step is 2^-17:
