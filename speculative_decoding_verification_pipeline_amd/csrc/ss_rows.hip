@@ -289,6 +289,7 @@ struct SmemST {
     RedT<NB> red2;
     float fmin[NB / WAVE];
     int imax[NB / WAVE];
+    double dg[EPT / 4][NB / WAVE];  // per wave: one total per group of the tile's threads
     int sel;
     int take_last;
     unsigned long long rem;
@@ -2192,8 +2193,22 @@ __device__ __forceinline__ double2 residual_sums(const RowCtx& c, const RowInfo&
             sp += (double)pi;
         }
     }
-    sr = block_sum_d(sr, sh.red);
-    sp = block_sum_d(sp, sh.red);
+    // both sums in one exchange of the wave totals
+    sr = wave_sum_d(sr);
+    sp = wave_sum_d(sp);
+    const int wv = threadIdx.x / WAVE;
+    if ((threadIdx.x & (WAVE - 1)) == 0) {
+        sh.red.d[wv] = sr;
+        sh.red2.d[wv] = sp;
+    }
+    __syncthreads();
+    sr = 0.0;
+    sp = 0.0;
+#pragma unroll
+    for (int w = 0; w < NT / WAVE; ++w) {
+        sr += sh.red.d[w];
+        sp += sh.red2.d[w];
+    }
     return make_double2(sr, sp);
 }
 
@@ -2265,17 +2280,35 @@ __device__ __forceinline__ int residual_draw(const RowCtx& c, const RowInfo& ri,
         double r[EPT];
         residual_values<DT>(c, ri, qf, st * TILE, s_usepi != 0, tt, r);
         using L = Lay<DT>;
+        static_assert(L::NG <= EPT / 4, "group totals");
+        const int lane = threadIdx.x & (WAVE - 1);
+        const int wv = threadIdx.x / WAVE;
+        // Id order in the tile is group, then thread, then entry: every
+        // group's sums are scanned across the threads at once (one wave scan
+        // per group, one exchange of the wave totals).
+        double gs[L::NG], wex[L::NG];
+#pragma unroll
+        for (int g = 0; g < L::NG; ++g) {
+            gs[g] = 0.0;
+#pragma unroll
+            for (int k = 0; k < L::VEC; ++k) gs[g] += r[g * L::VEC + k];
+            const double inc = wave_incl_scan_d(gs[g]);
+            wex[g] = inc - gs[g];
+            if (lane == WAVE - 1) sh.dg[g][wv] = inc;
+        }
+        __syncthreads();
         double carry = 0.0;
         int found = INT_MAX, lastpos = -1;
         const double rem = s_rem;
 #pragma unroll
         for (int g = 0; g < L::NG; ++g) {
-            double gs = 0.0;
+            double run = carry + wex[g], gt = 0.0;
 #pragma unroll
-            for (int k = 0; k < L::VEC; ++k) gs += r[g * L::VEC + k];
-            double gt;
-            const double gb = block_excl_scan_d(gs, sh.red, gt);
-            double run = carry + gb;
+            for (int w = 0; w < NT / WAVE; ++w) {
+                const double t = sh.dg[g][w];
+                run += w < wv ? t : 0.0;
+                gt += t;
+            }
 #pragma unroll
             for (int k = 0; k < L::VEC; ++k) {
                 const double x = r[g * L::VEC + k];
@@ -2288,8 +2321,19 @@ __device__ __forceinline__ int residual_draw(const RowCtx& c, const RowInfo& ri,
             }
             carry += gt;
         }
-        found = block_min_i(found, sh.red);
-        lastpos = -block_min_i(-lastpos, sh.red);
+        // the smallest id that passes, else the largest id with residual mass
+        found = wave_min_i(found);
+        lastpos = wave_max_i(lastpos);
+        if (lane == 0) {
+            sh.red.i[wv] = found;
+            sh.red2.i[wv] = lastpos;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NT / WAVE; ++w) {
+            found = min(found, sh.red.i[w]);
+            lastpos = max(lastpos, sh.red2.i[w]);
+        }
         token = found != INT_MAX ? found : lastpos;
     }
     return token;
