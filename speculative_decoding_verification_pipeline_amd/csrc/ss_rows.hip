@@ -1726,7 +1726,15 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
     }
     // the draw's uniform, formed while the row's loads are in flight
     const float u = u24(philox_word(c.seed, c.req, c.pos, 0, DOM_SAMPLE));
-    const RowView rv = row_view(rl, rs.m, c.T);
+    // the row view, formed by wave 0 alone (sixteen waves forming it side by
+    // side on four SIMDs took longer than the exchange) and shared through LDS
+    __shared__ RowView s_rv;
+    if (wv == 0) {
+        const RowView r = row_view(rl, rs.m, c.T);
+        if (lane == 0) s_rv = r;
+    }
+    __syncthreads();
+    const RowView rv = s_rv;
     const float zmax = rv.zmax;
     const uint32_t mzb = mono32(rv.zb);
 
@@ -1759,23 +1767,25 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
     __syncthreads();
     // wave w's entries occupy A[w AREG, w AREG + cnt_w); entry j of the pool in
     // wave order sits in region r at j - (entries of the regions before r)
+    // off[w]: entries of the regions before region w (uniform)
     int n = 0, regmax = 0;
-    int rcnt[NWR];
+    int off[NWR];
 #pragma unroll
     for (int w = 0; w < NWR; ++w) {
-        rcnt[w] = sh.red.i[w];
-        n += rcnt[w];
-        regmax = max(regmax, rcnt[w]);
+        const int cw_w = __builtin_amdgcn_readfirstlane(sh.red.i[w]);
+        off[w] = n;
+        n += cw_w;
+        regmax = max(regmax, cw_w);
     }
     auto pool_entry = [&](int j) -> unsigned long long {
-        int r = 0;
+        int r = 0, base = 0;
 #pragma unroll
-        for (int w = 0; w < NWR - 1; ++w) {
-            const bool past = j >= rcnt[r];
-            j -= past ? rcnt[r] : 0;
+        for (int w = 1; w < NWR; ++w) {
+            const bool past = j >= off[w];
             r += past ? 1 : 0;
+            base = past ? off[w] : base;
         }
-        return A[r * AREG + j];
+        return A[r * AREG + (j - base)];
     };
     const float zlo = rv.zlo;
     const double W = rv.W;
