@@ -115,7 +115,10 @@ typedef struct {
     int32_t* path;           /* [B]: 0 = resolved from the tile candidates,
                                 1 = resolved by the exact whole-row fallback (top-k ids and
                                 probabilities asked for here can send rows there that
-                                would otherwise resolve from the candidates) */
+                                would otherwise resolve from the candidates),
+                                2 = an unfiltered row drawn from its binned tail (calls
+                                without history or bias lists; never with topk_ids or
+                                probs asked for) */
 } ss_debug;
 
 /* Creates a sampler on cfg->device and allocates its workspace (the only call
@@ -300,7 +303,11 @@ ss_status ss_lmhead_sample(ss_sampler* s, const uint16_t* hidden, const uint16_t
 /* ss_sample_noalloc -- ss_sample without a handle, for callers that cannot
  * allocate device memory: code recorded under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc. It runs the same kernels as
- * ss_sample and returns the same tokens for the same arguments.
+ * ss_sample, but for the binned tail of unfiltered rows (its scratch holds no
+ * bins: such rows take the whole-row path), and returns the same tokens for the
+ * same arguments, up to draws within rounding (1e-6 of the row's mass) of a
+ * boundary of the cumulative distribution, which the two paths sum in different
+ * orders.
  *   Device:   the current HIP device; `stream` must belong to it.
  *   Scratch:  a static device array of SS_NOALLOC_SCRATCH_BYTES per GPU,
  *             reserved with the library's code object (held until the process

@@ -135,6 +135,7 @@ constexpr int64_t sample_scratch_layout(int64_t B, int64_t V, char* base, ss::Wo
         w->row_accept = nullptr;  // verification only
         w->resid_tile = nullptr;
         w->scratch_z = reinterpret_cast<float*>(base + o_z);
+        w->bins = nullptr;  // no binned tails: such rows take the whole-row path
         w->n_tiles = (int)n_tiles;
         w->n_wt = (int)n_wt;
         w->V = (int)V;
@@ -273,6 +274,7 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     const int64_t o_acc = take(R * 4);
     const int64_t o_restile = take((int64_t)B * nt * (int64_t)sizeof(double2));
     const int64_t o_scratch = take(R * (int64_t)V * 4);
+    const int64_t o_bins = take((int64_t)B * nw * ss::NBIN * 4);
     const int64_t dmax = cfg->max_draft > 0 ? cfg->max_draft : 1;
     const int64_t o_tpath = take(R * dmax * 4);
     const int64_t o_tdepth = take(R * 4);
@@ -296,6 +298,7 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     w.row_accept = reinterpret_cast<int32_t*>(b + o_acc);
     w.resid_tile = reinterpret_cast<double2*>(b + o_restile);
     w.scratch_z = reinterpret_cast<float*>(b + o_scratch);
+    w.bins = reinterpret_cast<float*>(b + o_bins);
     w.tree_path = reinterpret_cast<int32_t*>(b + o_tpath);
     w.tree_depth = reinterpret_cast<int32_t*>(b + o_tdepth);
     w.tree_next = reinterpret_cast<int32_t*>(b + o_tnext);
@@ -382,6 +385,10 @@ ss_status ss_sample(ss_sampler* s, const void* logits, ss_dtype dtype, int64_t r
         a.dbg_path = debug->path;
     }
     a.ws = s->ws;
+    // Binned tails serve unfiltered rows without penalty or bias lists: a batch
+    // that carries such lists takes the kernels without them (their code alone
+    // slows the merge a little).
+    if (params && (params->history_ids || params->bias_ids)) a.ws.bins = nullptr;
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
     return ss::launch_sample(a, dtype, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
                                                                                        : SS_ERR_HIP;
@@ -434,6 +441,7 @@ ss_status ss_spec_verify_scatter(ss_sampler* s, const void* target_logits, ss_dt
         a.seq_len = seq->len;
     }
     a.ws = s->ws;
+    a.ws.bins = nullptr;  // verification rows draw from their candidates or the whole row
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
     return ss::launch_spec(a, dtype, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
                                                                                      : SS_ERR_HIP;
@@ -466,6 +474,7 @@ ss_status ss_tree_verify(ss_sampler* s, const void* target_logits, ss_dtype dtyp
     a.out_nodes = out_nodes;
     a.out_num_accepted = out_num_accepted;
     a.ws = s->ws;
+    a.ws.bins = nullptr;  // verification rows draw from their candidates or the whole row
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;
     return ss::launch_tree(a, dtype, static_cast<hipStream_t>(stream), s->events) == hipSuccess ? SS_OK
                                                                                      : SS_ERR_HIP;

@@ -39,6 +39,13 @@ constexpr int WS_APX = 4;
 // Neither flag: the tile holds more finite entries than the row's top-k, so the
 // row is cut by top-k and the mass outside the candidates is not summed (the
 // merge bounds what a top-k set deeper than the pool can miss by count).
+// With WS_SUM: the tile's non-candidates' mass is also binned by z (Workspace::bins).
+constexpr int WS_BIN = 8;
+// Bins of a WS_BIN tile: BIN_S per unit of z on the absolute grid floor(-z BIN_S),
+// NBIN of them from the one holding the tile's zbeta down; the last also holds
+// everything deeper.
+constexpr int BIN_S = 32;
+constexpr int NBIN = 256;
 
 // What the row finaliser knows about one row's filtered distribution.
 // kept(v) <=> key64(z_v, v) >= kappa and (min_p <= 0 or exp(z_v - zmax) >= min_p),
@@ -87,6 +94,7 @@ struct Workspace {
     int32_t* row_accept;     // [max_rows]: spec decision per draft row
     double2* resid_tile;     // [max_batch * n_tiles]: residual / target mass per tile
     float* scratch_z;        // [max_rows * V] fallback rows
+    float* bins;             // [max_batch * n_wt * NBIN] WS_BIN tiles' masses by z, or null
     int32_t* tree_path;      // [max_rows * tree_dmax]: tokens from the root to each tree node
     int32_t* tree_depth;     // [max_rows]: depth of each tree node (-1: unreachable)
     int32_t* tree_next;      // [max_rows]: accepted child of each tree node (-1: none)

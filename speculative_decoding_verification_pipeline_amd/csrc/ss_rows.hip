@@ -144,6 +144,7 @@ struct SmemTile {
     int bfull;                // 1: some entry is biased more than once, or the list overflowed
     unsigned long long wl[WPT][WCAP];  // per wave: its candidates (x' bits, id) in slot order
 };
+static_assert(WPT * NBIN * sizeof(double) <= sizeof(SmemTile::cnt), "wave bins fit the tables' LDS");
 
 // The row merge runs one 1024-thread workgroup per row (16 waves): the
 // candidate loads, the pool compaction and the sort spread over all of them.
@@ -274,6 +275,30 @@ struct SmemList {
 };
 static_assert(LIST_CAP <= (1 << 13), "work item layout");
 
+// The draw of an unfiltered row over its binned tail: the row's non-pool mass
+// by bin of z, the entries of the bin that holds the draw, and their masses by
+// sub-bin.
+constexpr int NRB = 1024;  // row bins (the last one also holds everything deeper)
+constexpr int NSB = 64;    // sub-bins of the drawn bin
+constexpr int BCAP = 8192;  // entries of the drawn bin
+constexpr int SBCAP = 512; // entries of the drawn sub-bin
+static_assert(NSB == WAVE && NRB % WAVE == 0, "one sub-bin per lane; whole bins per lane");
+constexpr int UBCAP = 8;   // wave tiles without bins that the draw bins itself
+struct SmemBins {
+    double rb[NRB];
+    double sb[NSB];
+    unsigned long long key[BCAP];
+    unsigned long long sk[SBCAP];
+    double part[NTR_MAX / WAVE];
+    int toff[MAX_WT];          // row bin of each wave tile's bin 0 (INT_MAX: no bins)
+    float tscale[MAX_WT];      // exp(zm - zmax) of each wave tile
+    int tnc[MAX_WT];           // candidates of each wave tile
+    double base, tgt;
+    float xlo, xhi;            // bin beta's entries: x in (xlo, xhi]
+    int n, beta, sub, ns, pick;
+};
+
+static_assert(sizeof(SmemBins) <= sizeof(SmemList), "the binned draw adds no LDS");
 union SmemU {
     SmemTile t;
     SmemPool p;
@@ -281,6 +306,7 @@ union SmemU {
     SmemHist h;
     SmemBucket k;
     SmemList l;
+    SmemBins b;
 };
 
 template <int NB>
@@ -729,7 +755,8 @@ __device__ __forceinline__ int wave_count_above(const float v[EPT], float theta,
     return n;
 }
 
-template <int DT, bool ALIGNED>
+// BINS: the binned tails of unfiltered rows (the SAMPLE draw only)
+template <int DT, bool ALIGNED, bool BINS>
 __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, const Workspace& ws,
                                             SmemTile& tt, float* dbg_proc_row, float* dbg_probs_row) {
     const int tid = threadIdx.x;
@@ -908,12 +935,48 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
             // no tail sum
         } else if (strict) {
             const float zm = st.zm;
-            double acc = 0.0;
+            // A count-cut wave tile of an unfiltered row without penalty or
+            // bias tables also bins its non-candidates' masses by z: the
+            // row's draw can then skip the whole-row passes. The tables' LDS,
+            // unused then, holds the wave's bins.
+            const bool bin = BINS && ws.bins != nullptr && !tables && st.zbeta > NEG_INF && c.top_p >= 1.0f &&
+                             c.min_p <= 0.0f && (c.top_k <= 0 || c.top_k >= c.V);  // uniform
+            double* wb = (double*)tt.cnt + wv * NBIN;
+            const float a0 = floorf(-st.zbeta * (float)BIN_S);
+            if (bin) {
+                for (int i = lane; i < NBIN; i += WAVE) wb[i] = 0.0;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+            // two copies of the loop: the one without bins stays free of them
+            auto sum_tile = [&](auto bin_c) {
+                constexpr bool BIN = decltype(bin_c)::value;
+                double acc = 0.0;
 #pragma unroll
-            for (int s = 0; s < EPT; ++s)
-                if (v[s] > NEG_INF) acc += (double)expf(canon_zero(v[s] / c.T) - zm);
+                for (int s = 0; s < EPT; ++s) {
+                    if (v[s] > NEG_INF) {
+                        const float z = canon_zero(v[s] / c.T);
+                        const float w = expf(z - zm);
+                        acc += (double)w;
+                        // non-candidates: x' <= theta, so z <= zbeta and the bin is >= 0
+                        if (BIN && v[s] <= theta)
+                            atomicAdd(&wb[(int)fminf(floorf(-z * (float)BIN_S) - a0, (float)(NBIN - 1))], (double)w);
+                    }
+                }
+                return acc;
+            };
+            double acc;
+            if constexpr (BINS) acc = bin ? sum_tile(BoolC<true>{}) : sum_tile(BoolC<false>{});
+            else acc = sum_tile(BoolC<false>{});
             st.s = wave_sum_d(acc);
             st.flags |= WS_SUM;
+            if (bin) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                float* gb = ws.bins + ((size_t)row * ws.n_wt + wt) * NBIN;
+                for (int i = lane; i < NBIN; i += WAVE) gb[i] = (float)wb[i];
+                st.flags |= WS_BIN;
+            }
         } else {
             float acc = 0.0f;
             if (base < st.nfinite) {
@@ -1008,6 +1071,7 @@ struct RowView {
     double err;    // bound on the error of the approximate part of W
     int missing;   // some tile leaves mass outside its candidates that no sum covers
                    // (only where the row is cut by top-k)
+    unsigned long long ub[2];  // wave tiles that leave non-candidates no WS_BIN bins cover
 };
 
 // Relative error bound of a window-cut tile's approximate non-candidate mass:
@@ -1026,11 +1090,13 @@ __device__ __forceinline__ RowView row_view(const RowLoad& l, float m, float T) 
     double sum = 0.0, err = 0.0, csum = 0.0;
     float zmin = __builtin_huge_valf();
     int missing = 0;
+    bool ub[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const WaveStat& s = h ? l.s1 : l.s0;
         const bool incomplete = s.ncand < s.nfinite;
         zb[h] = incomplete ? s.zbeta : NEG_INF;
+        ub[h] = incomplete && !(s.flags & WS_BIN);
         zmin = fminf(zmin, s.zmin);
         if (s.nfinite > 0) {
             const float zm = s.zm;
@@ -1057,6 +1123,8 @@ __device__ __forceinline__ RowView row_view(const RowLoad& l, float m, float T) 
     r.Wc = wave_sum_d(csum);
     r.err = wave_sum_d(err);
     r.missing = wave_max_i(missing);
+    r.ub[0] = __ballot(ub[0]);
+    r.ub[1] = __ballot(ub[1]);
     return r;
 }
 
@@ -1689,7 +1757,386 @@ __device__ __forceinline__ RowOut resolve_wave(const SmemPool& P, int n, float z
     return o;
 }
 
+// The largest binary32 x with RN(x / T) <= c (c finite, T > 0): x / T is
+// correctly rounded, so RN(x / T) <= c holds exactly for x up to that value.
+// A 65-way search over the ordered bit patterns of the non-NaN floats, one
+// wave: each step tests 64 points of (lo, hi) at once, P(lo) true and P(hi)
+// false throughout.
+__device__ __forceinline__ float x_at_most(float c, float T) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    auto ord = [](float x) {
+        const uint32_t b = __float_as_uint(x);
+        return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    };
+    auto unord = [](uint32_t u) { return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u); };
+    const uint32_t olo = ord(NEG_INF), ohi = ord(__builtin_huge_valf());
+    {
+        // the answer lies within a few units in the last place of c T unless
+        // that product over- or underflows: 64 consecutive floats around it
+        const uint32_t g = ord(c * T);
+        const uint32_t p = min(max(g, olo + 32u) - 32u + (uint32_t)lane, ohi);
+        const unsigned long long ok = __ballot(unord(p) / T <= c);
+        const int k = __popcll(ok);
+        if (k > 0 && k < WAVE && (ok & 1ull)) return unord(__builtin_amdgcn_readlane(p, k - 1));
+    }
+    uint32_t lo = olo, hi = ohi;
+    while (hi - lo > 1) {
+        const uint32_t p = lo + (uint32_t)(((unsigned long long)(hi - lo) * (unsigned)(lane + 1)) / (WAVE + 1));
+        const unsigned long long ok = __ballot(p == lo || unord(p) / T <= c);  // monotone in lane
+        const int k = __popcll(ok);  // lanes 0 .. k-1 hold points where P holds
+        const uint32_t nlo = __builtin_amdgcn_readlane(p, max(k - 1, 0));
+        const uint32_t nhi = k < WAVE ? __builtin_amdgcn_readlane(p, min(k, WAVE - 1)) : hi;
+        lo = k > 0 ? nlo : lo;
+        hi = nhi;
+    }
+    return unord(lo);
+}
+
+// The SAMPLE draw of an unfiltered row (no top-k, top-p or min-p) without
+// penalty or bias tables, when the draw lies past the pool's mass. Entries
+// above zb (the pool) come first in key order; every other entry has z <= zb
+// and lies in row bin floor(-z BIN_S) - floor(-zb BIN_S), which does not
+// decrease along key order. The row bins' masses come from stage 1's bins of
+// the count-cut wave tiles (scaled to zmax), the candidates at or below zb, and
+// the entries of every other wave tile that leaves entries outside its
+// candidates (at most UBCAP such tiles), formed again from the logits. The bin
+// that holds u W is then searched entry by entry: one pass over the row
+// collects its entries (by the range of x that maps into the bin's range of z),
+// their masses by sub-bin give the sub-bin, and pairwise ranks in the sub-bin
+// give the entry. Masses are binary32 weights summed in binary64, as on the
+// pool path. Returns false, leaving the row to the whole-row path, when the bin
+// also holds a tile's deepest bin (whose entries may lie deeper), when the bin
+// holds more than BCAP entries or its sub-bin more than SBCAP, or when more
+// than UBCAP wave tiles lack bins.
 template <int DT>
+__device__ __forceinline__ bool bin_draw(const RowCtx& c, int row, const Workspace& ws, const RowView& rv, float u,
+                                         int total, SmemBins& B, RowInfo& out) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (WAVE - 1);
+    const int wv = tid / WAVE;
+    if (__popcll(rv.ub[0]) + __popcll(rv.ub[1]) > UBCAP) return false;  // uniform
+    const float zmax = rv.zmax, zb = rv.zb;
+    const float atop = floorf(-zb * (float)BIN_S);
+    auto rbin = [&](float z) { return (int)fminf(floorf(-z * (float)BIN_S) - atop, (float)(NRB - 1)); };
+    auto unbinned = [&](int wt) { return (rv.ub[wt >> 6] >> (wt & 63)) & 1ull; };
+    const int n_wt = ws.n_wt;
+    const WaveStat* stats = ws.wstats + (size_t)row * n_wt;
+    // the wave tiles' bins: where each starts among the row bins, its scale
+    if (tid < n_wt) {
+        const WaveStat st = stats[tid];
+        const bool has = st.flags & WS_BIN;
+        B.toff[tid] = has ? (int)fminf(floorf(-st.zbeta * (float)BIN_S) - atop, (float)NRB) : INT_MAX;
+        B.tscale[tid] = has ? expf(st.zm - zmax) : 0.0f;
+        B.tnc[tid] = st.ncand;
+    }
+    for (int i = tid; i < NRB; i += NTR) B.rb[i] = 0.0;
+    if (tid < NSB) B.sb[tid] = 0.0;
+    if (tid == 0) B.n = 0;
+    __syncthreads();
+    // the tiles' bins, scaled to zmax, onto the row bins (the last row bin also
+    // takes everything deeper); all loads of a thread in flight at once
+    {
+        const float* bins = ws.bins + (size_t)row * n_wt * NBIN;
+        const int nb = n_wt * NBIN;
+        constexpr int UB = MAX_WT * NBIN / NTR;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            if (g == 1 && nb <= (UB / 2) * NTR) break;  // uniform
+            float m[UB / 2];
+#pragma unroll
+            for (int k = 0; k < UB / 2; ++k) {
+                const int i = tid + (g * (UB / 2) + k) * NTR;
+                m[k] = i < nb ? gld(bins + i) : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < UB / 2; ++k) {
+                const int i = tid + (g * (UB / 2) + k) * NTR;
+                if (m[k] > 0.0f) {
+                    const int off = B.toff[i / NBIN];
+                    if (off != INT_MAX)
+                        atomicAdd(&B.rb[min(off + i % NBIN, NRB - 1)], (double)m[k] * (double)B.tscale[i / NBIN]);
+                }
+            }
+        }
+    }
+    // the candidates (read again: the merge's copy is not kept this long): the
+    // pool's mass, and the bins of those at or below zb (a wave tile without
+    // bins gives all its entries below)
+    double wp = 0.0;
+    {
+        const unsigned long long* cand = ws.cand + (size_t)row * n_wt * WCAP;
+        static_assert(NTR % WCAP == 0, "a thread keeps its lane of the candidate lists");
+        unsigned long long kc[MSLOT];
+#pragma unroll
+        for (int k = 0; k < MSLOT; ++k) {
+            const int wt = wv + NWR * k;
+            kc[k] = wt < n_wt && lane < B.tnc[wt] ? gld(cand + (size_t)wt * WCAP + lane) : 0ull;
+        }
+#pragma unroll
+        for (int k = 0; k < MSLOT; ++k) {
+            const int wt = wv + NWR * k;
+            if (kc[k] != 0ull) {
+                const float z = key_z(kc[k]);
+                const double w = (double)expf(z - zmax);
+                if (z > zb) wp += w;
+                else if (!unbinned(wt)) atomicAdd(&B.rb[rbin(z)], w);
+            }
+        }
+    }
+    // wave tiles without bins: every entry at or below zb, from the logits
+    // (the wave tile's entries: WAVE VEC consecutive ids per group of the tile)
+    {
+        constexpr int VEC = Lay<DT>::VEC;
+        static_assert(WT == 2 * NTR, "two entries of a wave tile per thread");
+        for (int h = 0; h < 2; ++h) {
+            unsigned long long m = rv.ub[h];
+            while (m) {
+                const int wt = h * WAVE + (int)__builtin_ctzll(m);
+                m &= m - 1;
+                const int tb = (wt / WPT) * TILE + (wt % WPT) * (WAVE * VEC);
+#pragma unroll
+                for (int e0 = 0; e0 < 2; ++e0) {
+                    const int e = tid + e0 * NTR;
+                    const int id = tb + (e / (WAVE * VEC)) * Lay<DT>::GSTRIDE + e % (WAVE * VEC);
+                    if (id >= c.V) continue;
+                    if (c.mask && !((gld(c.mask + (id >> 5)) >> (id & 31)) & 1u)) continue;
+                    const float x = read_logit<DT>(c.logits, id);
+                    if (!(x > NEG_INF)) continue;
+                    const float z = canon_zero(x / c.T);
+                    if (z <= zb) atomicAdd(&B.rb[rbin(z)], (double)expf(z - zmax));
+                }
+            }
+        }
+    }
+    wp = wave_sum_d(wp);
+    if (lane == 0) B.part[wv] = wp;
+    __syncthreads();
+    // wave 0: the row's mass, the draw's target, the bin that holds it and
+    // the range of x that maps into that bin
+    if (wv == 0) {
+        double Wp = 0.0;
+#pragma unroll
+        for (int w = 0; w < NWR; ++w) Wp += B.part[w];
+        constexpr int PER = NRB / WAVE;
+        // lane l sums bins l PER .. l PER + PER - 1 (read in a rotated order:
+        // the lanes then meet different LDS banks)
+        double loc = 0.0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) loc += B.rb[lane * PER + ((k + lane) & (PER - 1))];
+        const double inc = wave_incl_scan_d(loc);
+        const double W = Wp + __shfl(inc, WAVE - 1);
+        const double tgt = (double)u * W;
+        const double before = Wp + inc - loc;  // mass above this lane's first bin
+        // the lane whose bins hold the target, then the bin within them
+        const unsigned long long hit = __ballot(before <= tgt && tgt < before + loc && loc > 0.0);
+        int beta = -1;
+        double base = 0.0;
+        if (hit) {
+            // that lane's bins, one per lane: the first non-empty one whose
+            // inclusive mass passes the target
+            const int l0 = (int)__builtin_ctzll(hit);
+            const double b0 = __shfl(before, l0);
+            const double m = lane < PER ? B.rb[l0 * PER + lane] : 0.0;
+            const double run = b0 + wave_incl_scan_d(m);
+            const unsigned long long h2 = __ballot(lane < PER && m > 0.0 && tgt < run);
+            if (h2) {
+                const int k = (int)__builtin_ctzll(h2);
+                beta = l0 * PER + k;
+                base = __shfl(run - m, k);
+            }
+        }
+        // row bins from the shallowest tile's deepest bin on may hold deeper entries
+        int deep = NRB - 1;
+        for (int t = lane; t < n_wt; t += WAVE) {
+            const int off = B.toff[t];
+            if (off != INT_MAX) deep = min(deep, off + NBIN - 1);
+        }
+        deep = wave_min_i(deep);
+        beta = (beta >= 0 && beta < deep && tgt >= Wp) ? beta : -1;
+        float xlo = 0.0f, xhi = 0.0f;
+        if (beta >= 0) {
+            // bin beta is z in (-(atop + beta + 1) / BIN_S, -(atop + beta) / BIN_S]
+            // (exact: integers below 2^24 over a power of two)
+            xhi = x_at_most(fminf(-(atop + (float)beta) / (float)BIN_S, zb), c.T);
+            xlo = x_at_most(-(atop + (float)(beta + 1)) / (float)BIN_S, c.T);
+        }
+        if (lane == 0) {
+            B.beta = beta;
+            B.base = base;
+            B.tgt = tgt;
+            B.part[0] = W;
+            B.xlo = xlo;
+            B.xhi = xhi;
+        }
+    }
+    __syncthreads();
+    const int beta = B.beta;
+    if (beta < 0) return false;
+    const float xlo = B.xlo, xhi = B.xhi;
+    // one pass over the row: the entries of bin beta
+    const char* rowp = (const char*)c.logits;
+    constexpr int VEC = Lay<DT>::VEC;
+    constexpr int ES = DT == SS_F32 ? 4 : 2;
+    // (ids only: their keys, and the grammar mask, come after the pass)
+    auto visit = [&](int v, float x) {
+        if (!(x > xlo && x <= xhi)) return;
+        const int slot = atomicAdd(&B.n, 1);
+        if (slot < BCAP) B.key[slot] = (unsigned long long)v;
+    };
+    const int V = c.V;
+    const int head = min(V, (int)(((16u - ((uint32_t)(uintptr_t)rowp & 15u)) & 15u) / ES));
+    if (tid < head) visit(tid, read_logit<DT>(c.logits, tid));
+    const int nq = (V - head) / VEC;
+    const uint4* q = (const uint4*)(rowp + (size_t)head * ES);
+    // One workgroup per row: 64 entries per thread in flight (16-byte loads),
+    // tested into a bit mask without branches; the few entries in range leave
+    // their ids.
+    constexpr int RC = 64 / VEC;
+    for (int i0 = tid; i0 < nq; i0 += NTR * RC) {
+        uint4 t[RC];
+#pragma unroll
+        for (int k = 0; k < RC; ++k) {
+            const int i = i0 + k * NTR;
+            t[k] = i < nq ? gld(q + i) : make_uint4(0, 0, 0, 0);
+        }
+        unsigned long long hm = 0;
+#pragma unroll
+        for (int k = 0; k < RC; ++k) {
+            float x[VEC];
+            unpack_group<DT>(t[k], x);
+            uint32_t b = 0;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) b |= (x[j] > xlo && x[j] <= xhi) ? 1u << j : 0u;
+            if (i0 + k * NTR >= nq) b = 0;
+            hm |= (unsigned long long)b << (k * VEC);
+        }
+        if (hm) {
+            int slot = atomicAdd(&B.n, __popcll(hm));
+            for (; hm; hm &= hm - 1, ++slot) {
+                const int bit = (int)__builtin_ctzll(hm);
+                if (slot < BCAP) B.key[slot] = (unsigned long long)(head + VEC * (i0 + (bit / VEC) * NTR) + bit % VEC);
+            }
+        }
+    }
+    for (int v = head + VEC * nq + tid; v < V; v += NTR) visit(v, read_logit<DT>(c.logits, v));
+    __syncthreads();
+    const int n = B.n;
+    if (n > BCAP || n == 0) return false;
+    // sub-bins of bin beta (monotone in key order), their masses, and the one
+    // that holds the target
+    const float sb0 = (atop + (float)beta) * (float)NSB;
+    auto sbin = [&](float z) {
+        return (int)fminf(fmaxf(floorf(-z * (float)(BIN_S * NSB)) - sb0, 0.0f), (float)(NSB - 1));
+    };
+    // each collected id becomes its key (0: not allowed by the grammar mask;
+    // no finite z has key 0) and adds its mass to its sub-bin
+    for (int i0 = tid; i0 < n; i0 += 4 * NTR) {
+        int v[4];
+        float x[4];
+        bool ok[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + k * NTR;
+            v[k] = i < n ? (int)B.key[i] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[k] = read_logit<DT>(c.logits, v[k]);
+            ok[k] = !c.mask || ((gld(c.mask + (v[k] >> 5)) >> (v[k] & 31)) & 1u);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + k * NTR;
+            if (i >= n) continue;
+            const float z = canon_zero(x[k] / c.T);
+            B.key[i] = ok[k] ? key64(z, v[k]) : 0ull;
+            if (ok[k]) atomicAdd(&B.sb[sbin(z)], (double)expf(z - zmax));
+        }
+    }
+    __syncthreads();
+    if (wv == 0) {
+        const double m = B.sb[lane];
+        const double inc = wave_incl_scan_d(m);
+        const double before = B.base + inc - m;
+        const double tgt = B.tgt;
+        const unsigned long long hit = __ballot(m > 0.0 && before <= tgt && tgt < before + m);
+        const unsigned long long nz = __ballot(m > 0.0);
+        // past every sub-bin (rounding of the bins' masses): the last one
+        const int sub = hit ? (int)__builtin_ctzll(hit) : nz ? 63 - (int)__builtin_clzll(nz) : -1;
+        const double sbase = __shfl(before, max(sub, 0));
+        if (lane == 0) {
+            B.sub = sub;
+            B.base = sbase;
+            B.ns = 0;
+            B.pick = -1;
+        }
+    }
+    __syncthreads();
+    const int sub = B.sub;
+    if (sub < 0) return false;
+    const double sbase = B.base, tgt = B.tgt;
+    // the sub-bin's entries, then the first of them in key order whose
+    // inclusive mass passes the target (else the last of them)
+    for (int i = tid; i < n; i += NTR) {
+        const unsigned long long ki = B.key[i];
+        if (ki != 0 && sbin(key_z(ki)) == sub) {
+            const int slot = atomicAdd(&B.ns, 1);
+            if (slot < SBCAP) B.sk[slot] = ki;
+        }
+    }
+    __syncthreads();
+    const int ns = B.ns;
+    if (ns > SBCAP) return false;
+    if (ns <= WAVE) {
+        // one entry per lane, the others' keys and weights by lane reads
+        if (wv == 0) {
+            const unsigned long long ki = lane < ns ? B.sk[lane] : 0ull;
+            const double wi = lane < ns ? (double)expf(key_z(ki) - zmax) : 0.0;
+            double before = sbase;
+            int below = 0;
+            for (int j = 0; j < ns; ++j) {
+                const unsigned long long kj = ((unsigned long long)__builtin_amdgcn_readlane((uint32_t)(ki >> 32), j) << 32) |
+                                              (uint32_t)__builtin_amdgcn_readlane((uint32_t)ki, j);
+                const double wj = __shfl(wi, j);
+                if (kj > ki) before += wj;
+                below += kj < ki ? 1 : 0;
+            }
+            const bool pass = lane < ns && before <= tgt && tgt < before + wi;
+            const bool last = lane < ns && below == 0 && !(tgt < before + wi);
+            const unsigned long long pm = __ballot(pass), lm = __ballot(last);
+            if (lane == 0) B.pick = pm ? SBCAP + 63 - (int)__builtin_clzll(pm) : lm ? (int)__builtin_ctzll(lm) : -1;
+        }
+    } else for (int i = tid; i < ns; i += NTR) {
+        const unsigned long long ki = B.sk[i];
+        double before = sbase;
+        int below = 0;
+        for (int j = 0; j < ns; ++j) {
+            const unsigned long long kj = B.sk[j];
+            if (kj > ki) before += (double)expf(key_z(kj) - zmax);
+            below += kj < ki ? 1 : 0;
+        }
+        const double wi = (double)expf(key_z(ki) - zmax);
+        // exactly one entry passes; without one the target lies past the
+        // sub-bin's mass (rounding of the bins) and the last entry is taken
+        if (before <= tgt && tgt < before + wi) atomicMax(&B.pick, SBCAP + i);
+        else if (below == 0 && !(tgt < before + wi)) atomicMax(&B.pick, i);
+    }
+    __syncthreads();
+    const int pick = B.pick;
+    if (pick < 0) return false;
+    out.token = key64_id(B.sk[pick >= SBCAP ? pick - SBCAP : pick]);
+    out.kappa = 0;
+    out.W = B.part[0];
+    out.zmax = zmax;
+    out.min_p = 0.0f;
+    out.n_kept = total;
+    out.argmax = -1;
+    out.path = 2;
+    return true;
+}
+
+// BINS: the binned tail draw of unfiltered rows (the SAMPLE draw only)
+template <int DT, bool BINS>
 __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Workspace& ws,
                                              const RowLoad& rl, SmemU& su, SmemR& sh,
                                              const RowDbg& dbg, RowInfo& info_out) {
@@ -1979,6 +2426,27 @@ __device__ __forceinline__ void finalize_row(const RowCtx& c, int row, const Wor
             return;
         }
     }
+    // an unfiltered row without penalty or bias tables whose draw lies past
+    // its pool: the binned tail
+    if (BINS && (c.top_k <= 0 || c.top_k >= V)) {
+        // (laid out apart from the hot path: most rows never come here)
+        if (__builtin_expect(c.top_p >= 1.0f && c.min_p <= 0.0f && c.hist_len + c.extra_len + c.bias_len == 0 &&
+                                 !dbg.probs && !dbg.topk && ws.bins && rv.zb > NEG_INF &&
+                                 fabsf(rv.zb) < 0x1p18f,  // bins near zb are exact integers in binary32
+                             0)) {
+            RowInfo r;
+            const bool done = bin_draw<DT>(c, row, ws, s_rv, u, rs.nfinite, su.b, r);  // the view read again from LDS
+            __syncthreads();  // every thread has read the outcome before the LDS is reused
+            if (done) {
+                if (tid == 0) {
+                    if (dbg.kept) *dbg.kept = r.n_kept;
+                    if (dbg.path) *dbg.path = 2;
+                }
+                info_out = r;
+                return;
+            }
+        }
+    }
     finalize_slow<DT>(c, row, ws, ws.n_tiles, rs, u, su, sh, info, dbg);
     __syncthreads();
     info_out = info;
@@ -2023,7 +2491,9 @@ __device__ __forceinline__ RowCtx spec_ctx(const SpecArgs& a, int b, int j) {
 // values per lane and the window passes in registers without spilling.
 #define SS_TILE_OCC __attribute__((amdgpu_waves_per_eu(6)))
 
-template <int DT, bool ALIGNED>
+// BINS: kernels that keep binned tails for unfiltered rows (batches without
+// penalty or bias lists: rows with lists never use them)
+template <int DT, bool ALIGNED, bool BINS>
 __global__ __launch_bounds__(NT) SS_TILE_OCC void k_sample_tiles(SampleArgs a) {
     __shared__ SmemTile tt;
     const int n_tiles = a.ws.n_tiles;
@@ -2031,12 +2501,12 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_sample_tiles(SampleArgs a) {
     const int row = lin / n_tiles;
     const int tile = lin % n_tiles;
     const RowCtx c = sample_ctx<DT>(a, row);
-    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt,
+    tile_stage1<DT, ALIGNED, BINS>(c, row, tile, a.ws, tt,
                     a.dbg_processed ? a.dbg_processed + (size_t)row * a.V : nullptr,
                     a.dbg_probs ? a.dbg_probs + (size_t)row * a.V : nullptr);
 }
 
-template <int DT>
+template <int DT, bool BINS>
 __global__ __launch_bounds__(NTR) void k_sample_rows(SampleArgs a) {
     __shared__ SmemU su;
     __shared__ SmemR sh;
@@ -2050,7 +2520,7 @@ __global__ __launch_bounds__(NTR) void k_sample_rows(SampleArgs a) {
     dbg.probs = a.dbg_probs ? a.dbg_probs + (size_t)row * a.V : nullptr;
     dbg.path = a.dbg_path ? a.dbg_path + row : nullptr;
     RowInfo info;
-    finalize_row<DT>(c, row, a.ws, rl, su, sh, dbg, info);
+    finalize_row<DT, BINS>(c, row, a.ws, rl, su, sh, dbg, info);
     if (threadIdx.x == 0) a.out_tokens[row] = info.token;
 }
 
@@ -2064,7 +2534,7 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_tiles(SpecArgs a) {
     const int row = lin / n_tiles;
     const int tile = lin % n_tiles;
     const RowCtx c = spec_ctx<DT>(a, row / G1, row % G1);
-    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt, nullptr, nullptr);
+    tile_stage1<DT, ALIGNED, false>(c, row, tile, a.ws, tt, nullptr, nullptr);
 }
 
 // Verification, per target row: the filtered distribution, then the accept
@@ -2082,7 +2552,7 @@ __global__ __launch_bounds__(NTR) void k_spec_rows(SpecArgs a) {
     const RowCtx c = spec_ctx<DT>(a, b, j);
     RowDbg dbg = {nullptr, 0, nullptr, nullptr, nullptr};
     RowInfo info;
-    finalize_row<DT>(c, row, a.ws, rl, su, sh, dbg, info);
+    finalize_row<DT, false>(c, row, a.ws, rl, su, sh, dbg, info);
     if (j < a.G) {
         const int d = a.draft_tokens[(size_t)b * a.G + j];
         int acc;
@@ -2460,7 +2930,7 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_tree_tiles(TreeArgs a) {
     const int row = lin / n_tiles;
     const int tile = lin % n_tiles;
     const RowCtx c = tree_ctx<DT>(a, row / a.N, row % a.N, a.ws.tree_depth[row]);
-    tile_stage1<DT, ALIGNED>(c, row, tile, a.ws, tt, nullptr, nullptr);
+    tile_stage1<DT, ALIGNED, false>(c, row, tile, a.ws, tt, nullptr, nullptr);
 }
 
 // Per node x: its filtered distribution, then its children tested in index
@@ -2479,7 +2949,7 @@ __global__ __launch_bounds__(NTR) void k_tree_rows(TreeArgs a) {
     const RowCtx c = tree_ctx<DT>(a, b, x, depth);
     RowDbg dbg = {nullptr, 0, nullptr, nullptr, nullptr};
     RowInfo info;
-    finalize_row<DT>(c, row, a.ws, rl, su, sh, dbg, info);
+    finalize_row<DT, false>(c, row, a.ws, rl, su, sh, dbg, info);
     // every wave holds the request's tree (lane = node), so the children and
     // their tokens are the same in every wave: the loop below is uniform
     const int lane = threadIdx.x & (WAVE - 1);
@@ -2999,11 +3469,17 @@ static bool rows_aligned(const void* base, int64_t row_stride, int V) {
 
 template <int DT>
 static void sample_chain(const SampleArgs& a, hipStream_t st, const LaunchEvents& le) {
-    if (rows_aligned<DT>(a.logits, a.row_stride, a.V))
-        launch_k(le, 0, k_sample_tiles<DT, true>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
-    else
-        launch_k(le, 0, k_sample_tiles<DT, false>, dim3(a.B * a.ws.n_tiles), dim3(NT), st, a);
-    launch_k(le, 1, k_sample_rows<DT>, dim3(a.B), dim3(NTR), st, a);
+    const dim3 g(a.B * a.ws.n_tiles);
+    const bool al = rows_aligned<DT>(a.logits, a.row_stride, a.V);
+    if (a.ws.bins) {
+        if (al) launch_k(le, 0, k_sample_tiles<DT, true, true>, g, dim3(NT), st, a);
+        else launch_k(le, 0, k_sample_tiles<DT, false, true>, g, dim3(NT), st, a);
+        launch_k(le, 1, k_sample_rows<DT, true>, dim3(a.B), dim3(NTR), st, a);
+    } else {
+        if (al) launch_k(le, 0, k_sample_tiles<DT, true, false>, g, dim3(NT), st, a);
+        else launch_k(le, 0, k_sample_tiles<DT, false, false>, g, dim3(NT), st, a);
+        launch_k(le, 1, k_sample_rows<DT, false>, dim3(a.B), dim3(NTR), st, a);
+    }
 }
 
 template <int DT>
