@@ -456,7 +456,8 @@ def secondary(args, dev):
     lp = np.bincount(lpath.cpu().numpy(), minlength=3).tolist()
     pfn = [lambda: s.lmhead_sample_params(Hd, Wd, hp, out=o)]
     pms, _ = time_graph(pfn, lsteps, 3)
-    pst = stage_summary(time_stages(s, pfn, lsteps, 3), ["k_lmhead_proc", "k_lm_merge", "k_lm_slow"])
+    pst = stage_summary(time_stages(s, pfn, lsteps, 5),
+                        ["k_lmhead_proc", "k_lm_merge", "k_lm_slow", "k_lm_gumbel", "k_lm_pick"])
     out["lmhead_params"] = {"us_per_call": pms / lsteps * 1e3, "stages": pst,
                             "tokens_per_s": B * lsteps / (pms * 1e-3),
                             "rows_by_path": {"candidates": lp[0], "whole_row": lp[1],

@@ -147,8 +147,8 @@ int64_t ss_sampler_workspace_bytes(const ss_sampler* s);
  * ss_sample launches 2 kernels (tile scan, row merge), ss_spec_verify 4 (tile
  * scan, row merge, residual tile sums, per-request finish), ss_tree_verify 5
  * (tree paths, tile scan, row merge and child tests, residual tile sums,
- * per-request finish) and ss_lmhead_sample 2 (fused GEMM tiles, cross-tile
- * reduction).
+ * per-request finish), ss_lmhead_sample 2 (fused GEMM tiles, cross-tile
+ * reduction) and ss_lmhead_sample_params 5 (as listed there).
  * Returns SS_ERR_INVALID_ARG for a null handle or n_events outside 0 .. 16.
  * Not meant for graph capture. */
 ss_status ss_sampler_set_launch_events(ss_sampler* s, void* const* events, int32_t n_events);
@@ -359,8 +359,10 @@ ss_status ss_sample_noalloc(const void* logits, ss_dtype dtype, int64_t row_stri
  * selected over their whole row of z', which the GEMM kernel also writes to the
  * workspace for every row with a filter (4 bytes per entry, against the 2 K of
  * weight per vocabulary entry the GEMM reads; rows without a filter never
- * leave the chip). Launches three kernels (GEMM with summaries, row merge, the
- * whole-row selection, which returns at once when every row resolved). Errors: as ss_lmhead_sample, and the checks
+ * leave the chip). Launches five kernels: GEMM with summaries, row merge, the
+ * whole-row selection of the kept set, the Gumbel pass over the kept set (32
+ * workgroups per row) and the token write; the last three return at once for
+ * rows the candidates resolved. Errors: as ss_lmhead_sample, and the checks
  * ss_sample makes on params. */
 ss_status ss_lmhead_sample_params(ss_sampler* s, const uint16_t* hidden, const uint16_t* weight,
                                   int32_t B, const ss_params* params, int32_t* out_tokens,

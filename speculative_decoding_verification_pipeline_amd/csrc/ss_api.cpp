@@ -25,6 +25,7 @@ struct ss_sampler {
     float2* lm_partials;
     ss::LmTileStat* lm_stats;
     int32_t* lm_unres;
+    ss::LmCut* lm_cut;
     ss::LaunchEvents events;
     // defaults substituted for absent per-request parameters, [max_batch] each
     int32_t* def_zero_i;
@@ -283,6 +284,7 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     const int64_t o_lmstat =
         cfg->hidden_size > 0 ? take(64 * (int64_t)s->n_vtiles * (int64_t)sizeof(ss::LmTileStat)) : 0;
     const int64_t o_lmunres = cfg->hidden_size > 0 ? take(64 * 4) : 0;
+    const int64_t o_lmcut = cfg->hidden_size > 0 ? take(64 * (int64_t)sizeof(ss::LmCut)) : 0;
     const int64_t o_defaults = take(4 * (int64_t)B * 4);
     s->ws_bytes = off;
     if (hipMalloc(&s->ws_base, (size_t)off) != hipSuccess) {
@@ -309,6 +311,7 @@ ss_status ss_sampler_create(const ss_sampler_config* cfg, ss_sampler** out) {
     s->lm_partials = cfg->hidden_size > 0 ? reinterpret_cast<float2*>(b + o_lmpart) : nullptr;
     s->lm_stats = cfg->hidden_size > 0 ? reinterpret_cast<ss::LmTileStat*>(b + o_lmstat) : nullptr;
     s->lm_unres = cfg->hidden_size > 0 ? reinterpret_cast<int32_t*>(b + o_lmunres) : nullptr;
+    s->lm_cut = cfg->hidden_size > 0 ? reinterpret_cast<ss::LmCut*>(b + o_lmcut) : nullptr;
     {
         int32_t* d = reinterpret_cast<int32_t*>(b + o_defaults);
         s->def_zero_i = d;
@@ -504,6 +507,7 @@ ss_status ss_lmhead_sample_params(ss_sampler* s, const uint16_t* hidden, const u
     a.p = to_ptrs(defaults_of(s), params);
     a.stats = s->lm_stats;
     a.unres = s->lm_unres;
+    a.cut = s->lm_cut;
     a.zmat = s->ws.scratch_z;
     a.dbg_path = debug_path;
     if (hipSetDevice(s->cfg.device) != hipSuccess) return SS_ERR_HIP;

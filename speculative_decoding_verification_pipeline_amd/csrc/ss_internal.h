@@ -170,6 +170,17 @@ struct LmTileStat {
 };
 static_assert(sizeof(LmTileStat) == 64, "LmTileStat layout");
 
+// The kept set of an open LM-head row, fixed by the whole-row selection, and
+// the best (z' + g, id) key its chunks have found (0 = none yet).
+struct LmCut {
+    unsigned long long kP;    // kept: key64(z', v) >= kP ...
+    unsigned long long best;  // mono32(z' + g) << 32 | ~id, the maximum over the chunks
+    float zmax;               // ... and, with min_p > 0, exp(z' - zmax) >= min_p
+    float mp;
+    int pad[2];
+};
+static_assert(sizeof(LmCut) == 32, "LmCut layout");
+
 struct LmheadArgs {
     const uint16_t* hidden;
     const uint16_t* weight;
@@ -188,6 +199,7 @@ struct LmheadArgs {
     ParamPtrs p;
     LmTileStat* stats;       // [64 * n_vtiles]
     int32_t* unres;          // [64]: rows the candidates could not resolve
+    LmCut* cut;              // [64]: their kept sets and best keys
     float* zmat;             // [64 * V]: z' of those rows, formed again
     int32_t* dbg_path;       // [B] or null: 0 candidates, 1 whole row, 2 no filter or greedy
 };
@@ -220,5 +232,6 @@ hipError_t launch_lmhead_params(const LmheadArgs& a, hipStream_t st, const Launc
 // the row kernels of ss_lmhead_sample_params (in the row-kernel source)
 void launch_lm_merge(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k);
 void launch_lm_slow(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k);
+void launch_lm_gumbel(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k);
 
 }  // namespace ss

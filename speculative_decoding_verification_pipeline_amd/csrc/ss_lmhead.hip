@@ -605,6 +605,7 @@ hipError_t launch_lmhead_params(const LmheadArgs& a, hipStream_t st, const Launc
     launch_k(le, 0, k_lmhead_proc, dim3(a.n_vtiles), dim3(LM_NT), st, a);
     launch_lm_merge(a, st, le, 1);
     launch_lm_slow(a, st, le, 2);
+    launch_lm_gumbel(a, st, le, 3);
     return hipGetLastError();
 }
 

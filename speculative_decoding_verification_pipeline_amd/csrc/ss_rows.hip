@@ -223,20 +223,21 @@ constexpr int LIST_CAP = 8192;  // history + draft + bias ids staged in LDS by t
 // The workgroup visits every entry v of a float row in memory, f(v, zr[v]).
 // The passes of the whole-row path are bound by the bytes each thread keeps in
 // flight, so the 16-byte-aligned body goes four floats per load, RQ loads at a
-// time; the unaligned head and the tail take one entry per thread.
-template <class F>
+// time (NQ of them; a pass with little work per entry takes more); the
+// unaligned head and the tail take one entry per thread.
+template <int NQ = RQ, class F>
 __device__ __forceinline__ void row_visit(const float* zr, int V, F f) {
     const int tid = threadIdx.x;
     const int head = min(V, (int)(((16u - ((uint32_t)(uintptr_t)zr & 15u)) & 15u) >> 2));
     if (tid < head) f(tid, zr[tid]);
     const int nq = (V - head) >> 2;
     const uint4* q = (const uint4*)(zr + head);
-    for (int i0 = tid; i0 < nq; i0 += NTR * RQ) {
-        uint4 t[RQ];
+    for (int i0 = tid; i0 < nq; i0 += NTR * NQ) {
+        uint4 t[NQ];
 #pragma unroll
-        for (int k = 0; k < RQ; ++k) t[k] = i0 + k * NTR < nq ? gld(q + i0 + k * NTR) : make_uint4(0, 0, 0, 0);
+        for (int k = 0; k < NQ; ++k) t[k] = i0 + k * NTR < nq ? gld(q + i0 + k * NTR) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int k = 0; k < RQ; ++k) {
+        for (int k = 0; k < NQ; ++k) {
             const int i = i0 + k * NTR;
             if (i < nq) {
                 const int v = head + 4 * i;
@@ -1257,20 +1258,33 @@ __device__ __forceinline__ float entry_w(float z, float zmax, bool deep_zero) {
     return deep_zero && zmax - z > HW_DEEP ? 0.0f : expf(z - zmax);
 }
 
-// Totals of the entries where pred holds (count, and with by_mass the fixed-point mass) and, when
-// want_key, the key selected among them exactly as radix_select defines it:
+// Totals of the entries that pass (key >= kmin, and w >= wmin when wmin > 0: the
+// predicate of every selection here) (count, and with by_mass the fixed-point
+// mass) and, when want_key, the key selected among them exactly as radix_select
+// defines it (an entry's weight is formed only where the mass or wmin needs it):
 // by count, the key of rank `target` (1-based); by mass, the key of the first
 // entry whose inclusive mass exceeds target = frac x total mass (frac > 0) or
 // `target` (frac = 0); the smallest such key if none does. One pass builds the
 // bucket histogram; a second collects the selected bucket's entries, which are
 // resolved by pairwise comparison. A bucket too large for LDS, or the deepest
 // bucket, is left to radix_select.
-template <class Pred>
-__device__ __forceinline__ void hist_select(const float* zr, int V, float zmax, float s2, bool w_deep_zero, Pred pred,
-                            bool by_mass, bool want_key, unsigned long long target, double frac, SmemU& su,
-                            SmemR& sh, int& count, unsigned long long& mass,
-                            unsigned long long& key) {
+__device__ __forceinline__ void hist_select(const float* zr, int V, float zmax, float s2, bool w_deep_zero,
+                                            unsigned long long kmin, float wmin, bool by_mass, bool want_key,
+                                            unsigned long long target, double frac, SmemU& su, SmemR& sh,
+                                            int& count, unsigned long long& mass, unsigned long long& key) {
     const int tid = threadIdx.x;
+    const bool need_w = by_mass || wmin > 0.0f;  // uniform
+    // the entry's key when it passes (0 otherwise: no finite z has key 0), and its weight
+    auto pass = [&](int v, float z, float& w) -> unsigned long long {
+        const unsigned long long kk = key64(z, v);
+        if (kk < kmin) return 0ull;
+        w = 0.0f;
+        if (need_w) {
+            w = entry_w(z, zmax, w_deep_zero);
+            if (wmin > 0.0f && !(w >= wmin)) return 0ull;
+        }
+        return kk;
+    };
     SmemHist& h = su.h;
     SmemHistState& hs = sh.hs;
     for (int b = tid; b <= HB; b += NTR) {
@@ -1280,8 +1294,8 @@ __device__ __forceinline__ void hist_select(const float* zr, int V, float zmax, 
     __syncthreads();
     row_visit(zr, V, [&](int v, float z) {
         if (!(z > NEG_INF)) return;
-        const float w = entry_w(z, zmax, w_deep_zero);
-        if (!pred(key64(z, v), w)) return;
+        float w;
+        if (!pass(v, z, w)) return;
         const int b = hbucket(z, zmax, s2);
         atomicAdd(&h.hc[b], 1u);
         if (by_mass) atomicAdd(&h.hm[b], (unsigned long long)wq(w));
@@ -1345,7 +1359,9 @@ __device__ __forceinline__ void hist_select(const float* zr, int V, float zmax, 
     __syncthreads();
     const int csel = hs.total_count;
     if (sel == HB || csel > HCAP) {
-        key = radix_select(zr, V, zmax, pred, by_mass, tgt, su.r, sh);
+        key = radix_select(zr, V, zmax,
+                           [kmin, wmin](unsigned long long k, float w) { return k >= kmin && (wmin <= 0.0f || w >= wmin); },
+                           by_mass, tgt, su.r, sh);
         return;
     }
     const unsigned long long cum = hs.cum;
@@ -1353,9 +1369,9 @@ __device__ __forceinline__ void hist_select(const float* zr, int V, float zmax, 
     SmemBucket& kb = su.k;
     row_visit(zr, V, [&](int v, float z) {
         if (!(z > NEG_INF) || hbucket(z, zmax, s2) != sel) return;
-        const float w = entry_w(z, zmax, w_deep_zero);
-        const unsigned long long kk = key64(z, v);
-        if (!pred(kk, w)) return;
+        float w;
+        const unsigned long long kk = pass(v, z, w);
+        if (!kk) return;
         const int slot = atomicAdd(&hs.n, 1);
         if (slot < HCAP) {  // the histogram counted exactly these entries
             kb.key[slot] = kk;
@@ -1571,12 +1587,11 @@ __device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Wo
     unsigned long long ms;
     unsigned long long kK = 0;
     if (topk_on && K_eff < total)
-        hist_select(zr, V, zmax, s2, true, [](unsigned long long, float) { return true; }, false, true,
-                    (unsigned long long)K_eff, 0.0, su, sh, cnt, ms, kK);
+        hist_select(zr, V, zmax, s2, true, 0ull, 0.0f, false, true, (unsigned long long)K_eff, 0.0, su, sh, cnt,
+                    ms, kK);
     unsigned long long kP = kK;
     if (c.top_p < 1.0f)  // the first entry whose inclusive mass exceeds top_p x (top-k mass)
-        hist_select(zr, V, zmax, s2, true, [kK](unsigned long long k, float) { return k >= kK; }, true,
-                    true, 0, (double)c.top_p, su, sh, cnt, ms, kP);
+        hist_select(zr, V, zmax, s2, true, kK, 0.0f, true, true, 0, (double)c.top_p, su, sh, cnt, ms, kP);
     const float mp = c.min_p;
     auto kept = [kP, mp](unsigned long long k, float w) { return k >= kP && (mp <= 0.0f || w >= mp); };
     // the draw: the first kept entry whose inclusive mass exceeds u x (kept mass)
@@ -1584,7 +1599,7 @@ __device__ __forceinline__ void finalize_slow(const RowCtx& c, int row, const Wo
     unsigned long long Wk, kt;
     // min_p at or below the deepest nonzero fixed-point weight needs every w
     const bool dz = mp <= 0.0f || mp > 1e-13f;
-    hist_select(zr, V, zmax, s2, dz, kept, true, true, 0, (double)u, su, sh, n_kept, Wk, kt);
+    hist_select(zr, V, zmax, s2, dz, kP, mp, true, true, 0, (double)u, su, sh, n_kept, Wk, kt);
     if (tid == 0) {
         info.kappa = kP;
         info.W = (double)Wk / MASS_SCALE;
@@ -3357,7 +3372,8 @@ __global__ __launch_bounds__(NTR) void k_lm_merge(LmheadArgs a) {
 }
 
 // Rows left open: their z' (written by the GEMM kernel) through the whole-row
-// selection, then the best z' + g over the kept entries.
+// selection of the kept set (top-k, then top-p; min-p is tested entry by entry
+// in the Gumbel pass that follows).
 __global__ __launch_bounds__(NTR) void k_lm_slow(LmheadArgs a) {
     __shared__ SmemU su;
     __shared__ SmemR sh;
@@ -3369,7 +3385,7 @@ __global__ __launch_bounds__(NTR) void k_lm_slow(LmheadArgs a) {
     const float* zr = a.zmat + (size_t)j * V;
     float m = NEG_INF, lo = __builtin_huge_valf();
     int nf = 0;
-    row_visit(zr, V, [&](int, float z) {
+    row_visit<16>(zr, V, [&](int, float z) {
         if (z > NEG_INF) {
             m = fmaxf(m, z);
             lo = fminf(lo, z);
@@ -3384,26 +3400,52 @@ __global__ __launch_bounds__(NTR) void k_lm_slow(LmheadArgs a) {
     int cnt;
     unsigned long long ms, kK = 0;
     if (topk_on && K_eff < total)
-        hist_select(zr, V, zmax, s2, true, [](unsigned long long, float) { return true; }, false, true,
+        hist_select(zr, V, zmax, s2, true, 0ull, 0.0f, false, true,
                     (unsigned long long)K_eff, 0.0, su, sh, cnt, ms, kK);
     unsigned long long kP = kK;
     if (p.top_p[j] < 1.0f)
-        hist_select(zr, V, zmax, s2, true, [kK](unsigned long long k, float) { return k >= kK; }, true, true,
+        hist_select(zr, V, zmax, s2, true, kK, 0.0f, true, true,
                     0, (double)p.top_p[j], su, sh, cnt, ms, kP);
-    const float mp = p.min_p[j];
-    // four consecutive entries per step share one Philox block
+    // the kept set; the Gumbel pass over it runs over the whole GPU (k_lm_gumbel)
+    if (tid == 0) {
+        LmCut q;
+        q.kP = kP;
+        q.best = 0;
+        q.zmax = zmax;
+        q.mp = p.min_p[j];
+        q.pad[0] = q.pad[1] = 0;
+        a.cut[j] = q;
+    }
+}
+
+// The Gumbel-max over an open row's kept set, LM_GCH chunks of the row per row
+// (one workgroup each): every workgroup takes the best (z' + g, id) of its
+// chunk and folds it into the row's key with a 64-bit atomic maximum (higher
+// score first, then the lower id: the order the candidate paths use).
+constexpr int LM_GCH = 32;
+constexpr int LM_GNT = 256;
+
+__global__ __launch_bounds__(LM_GNT) void k_lm_gumbel(LmheadArgs a) {
+    const int j = blockIdx.y;
+    if (!a.unres[j]) return;
+    const int tid = threadIdx.x;
+    const ParamPtrs& p = a.p;
+    const int V = a.V;
+    const LmCut q = a.cut[j];
+    const float* zr = a.zmat + (size_t)j * V;
+    const int ng = (V + 3) / 4;  // groups of four entries, one Philox block each
+    const int per = (ng + LM_GCH - 1) / LM_GCH;
+    const int gb = blockIdx.x * per, ge = min(ng, gb + per);
     float bs = -FLT_MAX;
     int bi = INT_MAX;
     const uint32_t req = (uint32_t)p.request_ids[j], pos = (uint32_t)p.positions[j];
-    // RQ groups per thread in flight, each one 16-byte load where the row is
-    // aligned
     const bool al = ((uint32_t)(uintptr_t)zr & 15u) == 0u;
-    for (int g0 = tid; g0 * 4 < V; g0 += NTR * RQ) {
+    for (int g0 = gb + tid; g0 < ge; g0 += LM_GNT * RQ) {
         float zs[RQ][4];
 #pragma unroll
         for (int h = 0; h < RQ; ++h) {
-            const int g = g0 + h * NTR;
-            if (al && g * 4 + 3 < V) {
+            const int g = g0 + h * LM_GNT;
+            if (g < ge && al && g * 4 + 3 < V) {
                 const uint4 t = gld((const uint4*)zr + g);
                 zs[h][0] = __uint_as_float(t.x);
                 zs[h][1] = __uint_as_float(t.y);
@@ -3411,41 +3453,74 @@ __global__ __launch_bounds__(NTR) void k_lm_slow(LmheadArgs a) {
                 zs[h][3] = __uint_as_float(t.w);
             } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int v = g * 4 + q;
-                    zs[h][q] = v < V ? zr[v] : NEG_INF;
+                for (int k = 0; k < 4; ++k) {
+                    const int v = g * 4 + k;
+                    zs[h][k] = g < ge && v < V ? zr[v] : NEG_INF;
                 }
             }
         }
 #pragma unroll
         for (int h = 0; h < RQ; ++h) {
-            const int g = g0 + h * NTR;
+            const int g = g0 + h * LM_GNT;
             bool any = false;
             bool keep[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float z = zs[h][q];
-                const int v = g * 4 + q;
-                keep[q] = z > NEG_INF && key64(z, v) >= kP && (mp <= 0.0f || expf(z - zmax) >= mp);
-                any |= keep[q];
+            for (int k = 0; k < 4; ++k) {
+                const float z = zs[h][k];
+                const int v = g * 4 + k;
+                keep[k] = z > NEG_INF && key64(z, v) >= q.kP && (q.mp <= 0.0f || expf(z - q.zmax) >= q.mp);
+                any |= keep[k];
             }
             if (!any) continue;
             const uint4 w = philox4x32_10(make_uint4(req, pos, (uint32_t)g, DOM_GUMBEL),
                                           (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (!keep[q]) continue;
-                const float sc = zs[h][q] + gumbel32(ws[q]);
-                if (lm_better(sc, g * 4 + q, bs, bi)) {
+            for (int k = 0; k < 4; ++k) {
+                if (!keep[k]) continue;
+                const float sc = zs[h][k] + gumbel32(ws[k]);
+                if (lm_better(sc, g * 4 + k, bs, bi)) {
                     bs = sc;
-                    bi = g * 4 + q;
+                    bi = g * 4 + k;
                 }
             }
         }
     }
-    lm_block_best(bs, bi, sh);
-    if (tid == 0) a.out_tokens[j] = bi == INT_MAX ? -1 : bi;
+    // the workgroup's best, then the row's
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const float os = __shfl_xor(bs, o);
+        const int oi = __shfl_xor(bi, o);
+        if (lm_better(os, oi, bs, bi)) {
+            bs = os;
+            bi = oi;
+        }
+    }
+    __shared__ float s_s[LM_GNT / WAVE];
+    __shared__ int s_i[LM_GNT / WAVE];
+    if ((tid & (WAVE - 1)) == 0) {
+        s_s[tid / WAVE] = bs;
+        s_i[tid / WAVE] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < LM_GNT / WAVE; ++w)
+            if (lm_better(s_s[w], s_i[w], bs, bi)) {
+                bs = s_s[w];
+                bi = s_i[w];
+            }
+        if (bi != INT_MAX)
+            atomicMax(&a.cut[j].best, key64(bs, bi));
+    }
+}
+
+// The open rows' tokens from their best keys (-1: an empty kept set).
+__global__ __launch_bounds__(WAVE) void k_lm_pick(LmheadArgs a) {
+    for (int j = threadIdx.x; j < a.B; j += WAVE) {
+        if (!a.unres[j]) continue;
+        const unsigned long long k = a.cut[j].best;
+        a.out_tokens[j] = k ? key64_id(k) : -1;
+    }
 }
 
 void launch_lm_merge(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k) {
@@ -3454,6 +3529,11 @@ void launch_lm_merge(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le
 
 void launch_lm_slow(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k) {
     launch_k(le, k, k_lm_slow, dim3(a.B), dim3(NTR), st, a);
+}
+
+void launch_lm_gumbel(const LmheadArgs& a, hipStream_t st, const LaunchEvents& le, int k) {
+    launch_k(le, k, k_lm_gumbel, dim3(LM_GCH, a.B), dim3(LM_GNT), st, a);
+    launch_k(le, k + 1, k_lm_pick, dim3(1), dim3(WAVE), st, a);
 }
 
 // ---------------------------------------------------------------------------
