@@ -166,7 +166,8 @@ struct LmTileStat {
     float best_s;                   // the largest z' + g (T > 0) or x' (T = 0)
     int best_i;                     // its id (the lowest among equals), INT_MAX if none
     int nfinite;
-    int pad[2];
+    float zmin;                     // the least finite z' (+inf if none)
+    int pad;
 };
 static_assert(sizeof(LmTileStat) == 64, "LmTileStat layout");
 
@@ -177,7 +178,8 @@ struct LmCut {
     unsigned long long best;  // mono32(z' + g) << 32 | ~id, the maximum over the chunks
     float zmax;               // ... and, with min_p > 0, exp(z' - zmax) >= min_p
     float mp;
-    int pad[2];
+    float zlo;                // the row's least finite z'
+    int total;                // its finite entries
 };
 static_assert(sizeof(LmCut) == 32, "LmCut layout");
 

@@ -306,6 +306,7 @@ struct LmPart {
     float best_s;
     int best_i;
     int nfinite;
+    float zmin;      // the least finite z'
 };
 
 __device__ __forceinline__ void lm_combine(LmPart& x, const LmPart& y) {
@@ -324,6 +325,7 @@ __device__ __forceinline__ void lm_combine(LmPart& x, const LmPart& y) {
         x.best_i = y.best_i;
     }
     x.nfinite += y.nfinite;
+    x.zmin = fminf(x.zmin, y.zmin);
 }
 
 __device__ __forceinline__ LmPart lm_shfl_xor32(const LmPart& x) {
@@ -338,6 +340,7 @@ __device__ __forceinline__ LmPart lm_shfl_xor32(const LmPart& x) {
     y.best_s = __shfl_xor(x.best_s, 32);
     y.best_i = __shfl_xor(x.best_i, 32);
     y.nfinite = __shfl_xor(x.nfinite, 32);
+    y.zmin = __shfl_xor(x.zmin, 32);
     return y;
 }
 
@@ -416,6 +419,7 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
         P.best_s = -FLT_MAX;
         P.best_i = INT_MAX;
         P.nfinite = 0;
+        P.zmin = __builtin_huge_valf();
         const int j = bb * 32 + r32;
         if (j >= a.B) continue;
         const float T = p.temperature[j];
@@ -483,11 +487,15 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
         }
         if (P.t[0]) {
             const float zt = key_z(P.t[0]);
-            float m = 0.0f;
+            float m = 0.0f, lo = __builtin_huge_valf();
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (zz[i] > -__builtin_huge_valf()) m += expf(zz[i] - zt);
+                if (zz[i] > -__builtin_huge_valf()) {
+                    m += expf(zz[i] - zt);
+                    lo = fminf(lo, zz[i]);
+                }
             P.mass = m;
+            P.zmin = lo;
         }
     }
     // the two halves of a column hold different entries: combine, then the
@@ -496,6 +504,7 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
         unsigned long long t[LM_NK];
         float mass, best_s;
         int best_i, nfinite;
+        float zmin;
     };
     static_assert(sizeof(Slot) * LM_MAXB * (LM_NT / WAVE) <= LM_W_BYTES, "slots fit a stage buffer");
     Slot* slots = (Slot*)w2;  // [wave][row]
@@ -511,6 +520,7 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
             sl.best_s = part[bb].best_s;
             sl.best_i = part[bb].best_i;
             sl.nfinite = part[bb].nfinite;
+            sl.zmin = part[bb].zmin;
         }
     }
     __syncthreads();
@@ -524,6 +534,7 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
             x.best_s = sl.best_s;
             x.best_i = sl.best_i;
             x.nfinite = sl.nfinite;
+            x.zmin = sl.zmin;
         }
 #pragma unroll
         for (int w = 1; w < LM_NT / WAVE; ++w) {
@@ -535,6 +546,7 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
             y.best_s = sl.best_s;
             y.best_i = sl.best_i;
             y.nfinite = sl.nfinite;
+            y.zmin = sl.zmin;
             lm_combine(x, y);
         }
         LmTileStat st;
@@ -545,7 +557,8 @@ __global__ __launch_bounds__(LM_NT) void k_lmhead_proc(LmheadArgs a) {
         st.best_s = x.best_s;
         st.best_i = x.best_i;
         st.nfinite = x.nfinite;
-        st.pad[0] = st.pad[1] = 0;
+        st.zmin = x.zmin;
+        st.pad = 0;
         a.stats[(size_t)tid * a.n_vtiles + tile] = st;
     }
 }

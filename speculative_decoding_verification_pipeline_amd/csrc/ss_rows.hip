@@ -3345,9 +3345,21 @@ __global__ __launch_bounds__(NTR) void k_lm_merge(LmheadArgs a) {
         }
     }
     if (open) {
+        // what the whole-row selection needs of the row: its extent and count
+        float lo = __builtin_huge_valf();
+        for (int t = tid; t < a.n_vtiles; t += NTR) lo = fminf(lo, st[t].zmin);
+        lo = -block_max(-lo, sh.red);
         if (tid == 0) {
             a.unres[j] = 1;
             if (a.dbg_path) a.dbg_path[j] = 1;
+            LmCut q;
+            q.kP = 0;
+            q.best = 0;
+            q.zmax = zmax;
+            q.mp = mp;
+            q.zlo = lo;
+            q.total = total;
+            a.cut[j] = q;
         }
         return;
     }
@@ -3383,18 +3395,11 @@ __global__ __launch_bounds__(NTR) void k_lm_slow(LmheadArgs a) {
     const ParamPtrs& p = a.p;
     const int V = a.V;
     const float* zr = a.zmat + (size_t)j * V;
-    float m = NEG_INF, lo = __builtin_huge_valf();
-    int nf = 0;
-    row_visit<16>(zr, V, [&](int, float z) {
-        if (z > NEG_INF) {
-            m = fmaxf(m, z);
-            lo = fminf(lo, z);
-            ++nf;
-        }
-    });
-    const float zmax = block_max(m, sh.red);
-    const float s2 = hdeep_scale(zmax, -block_max(-lo, sh.red));
-    const int total = block_sum_i(nf, sh.red);
+    // the row's maximum, least entry and count, from the tiles' summaries
+    const LmCut c0 = a.cut[j];
+    const float zmax = c0.zmax;
+    const float s2 = hdeep_scale(zmax, c0.zlo);
+    const int total = c0.total;
     const bool topk_on = p.top_k[j] > 0 && p.top_k[j] < V;
     const int K_eff = topk_on ? min(p.top_k[j], total) : total;
     int cnt;
@@ -3408,12 +3413,9 @@ __global__ __launch_bounds__(NTR) void k_lm_slow(LmheadArgs a) {
                     0, (double)p.top_p[j], su, sh, cnt, ms, kP);
     // the kept set; the Gumbel pass over it runs over the whole GPU (k_lm_gumbel)
     if (tid == 0) {
-        LmCut q;
+        LmCut q = c0;
         q.kP = kP;
         q.best = 0;
-        q.zmax = zmax;
-        q.mp = p.min_p[j];
-        q.pad[0] = q.pad[1] = 0;
         a.cut[j] = q;
     }
 }
