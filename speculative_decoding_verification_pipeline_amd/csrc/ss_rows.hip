@@ -2666,10 +2666,12 @@ __device__ __forceinline__ void residual_values(const RowCtx& c, const RowInfo& 
 }
 
 // Sums over tile tb of the residual and of pi (the fallback when the residual
-// is zero), by the whole workgroup.
+// is zero), by the whole workgroup. With `keep`, each entry's residual (a
+// binary32 value) also goes to keep[id], so that the draw within the tile
+// reads it instead of forming the tile again.
 template <int DT>
 __device__ __forceinline__ double2 residual_sums(const RowCtx& c, const RowInfo& ri, const DraftQ& qf,
-                                                 int tb, SmemTile& tt, SmemS& sh) {
+                                                 int tb, SmemTile& tt, SmemS& sh, float* keep) {
     float v[EPT];
     uint32_t mw[Lay<DT>::NG];
     const TablePrefetch f = prefetch_tables(c);
@@ -2684,7 +2686,9 @@ __device__ __forceinline__ double2 residual_sums(const RowCtx& c, const RowInfo&
         const int id = slot_id<DT>(tb, s);
         if (id < c.V) {
             const float pi = filtered_prob(c, ri, id, v[s]);
-            sr += (double)fmaxf(0.0f, pi - qf(id));
+            const float rv = fmaxf(0.0f, pi - qf(id));
+            if (keep) keep[id] = rv;
+            sr += (double)rv;
             sp += (double)pi;
         }
     }
@@ -2725,23 +2729,26 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_spec_resid_tiles(SpecArgs a)
     qf.d0 = a.draft_tokens[(size_t)b * a.G + j];
     qf.set = nullptr;
     qf.n = 0;
-    const double2 x = residual_sums<DT>(c, ri, qf, tile * TILE, tt, sh);
+    const double2 x = residual_sums<DT>(c, ri, qf, tile * TILE, tt, sh,
+                                        a.ws.scratch_z + ((size_t)b * (a.G + 1) + j) * a.V);
     if (threadIdx.x == 0) a.ws.resid_tile[(size_t)b * n_tiles + tile] = x;
 }
 
 // A draw from the residual distribution of the row described by c and ri, in
 // token-id order: the tile by the per-tile sums `tiles`, then the entry within
-// the tile (u from the residual domain at c's position). Called by the whole
-// workgroup.
+// the tile (u from the residual domain at c's position). The entries'
+// residuals come from `kept` (written with the sums) when the draw uses the
+// residual, else they are formed again. Called by the whole workgroup; lane t
+// of wave 0 brings tile t's sums in `x` (loaded early by the caller: they do
+// not depend on which row is drawn).
 template <int DT>
 __device__ __forceinline__ int residual_draw(const RowCtx& c, const RowInfo& ri, const DraftQ& qf,
-                                             const double2* tiles, int n_tiles, SmemTile& tt,
+                                             double2 x, int n_tiles, const float* kept, SmemTile& tt,
                                              SmemS& sh, int& s_tile, int& s_usepi, double& s_rem) {
     if (threadIdx.x < WAVE) {
         // lane t holds tile t's sums (n_tiles <= 32): the totals, then the
         // tile where the running sum in tile order passes u x total
         const int t = threadIdx.x;
-        const double2 x = t < n_tiles ? tiles[t] : make_double2(0.0, 0.0);
         const double R = wave_sum_d(x.x);
         const double P = wave_sum_d(x.y);
         const int use_pi = !(R > 0.0);
@@ -2773,7 +2780,15 @@ __device__ __forceinline__ int residual_draw(const RowCtx& c, const RowInfo& ri,
     int token = -1;
     if (st >= 0) {
         double r[EPT];
-        residual_values<DT>(c, ri, qf, st * TILE, s_usepi != 0, tt, r);
+        if (kept && s_usepi == 0) {
+#pragma unroll
+            for (int s = 0; s < EPT; ++s) {
+                const int id = slot_id<DT>(st * TILE, s);
+                r[s] = id < c.V ? (double)gld(kept + id) : 0.0;
+            }
+        } else {
+            residual_values<DT>(c, ri, qf, st * TILE, s_usepi != 0, tt, r);
+        }
         using L = Lay<DT>;
         static_assert(L::NG <= EPT / 4, "group totals");
         const int lane = threadIdx.x & (WAVE - 1);
@@ -2836,7 +2851,7 @@ __device__ __forceinline__ int residual_draw(const RowCtx& c, const RowInfo& ri,
 
 // The token of rejected position j of request b.
 template <int DT>
-__device__ __forceinline__ int residual_token(const SpecArgs& a, int b, int j, const RowInfo& ri,
+__device__ __forceinline__ int residual_token(const SpecArgs& a, int b, int j, const RowInfo& ri, double2 xt,
                                               SmemTile& tt, SmemS& sh, int& s_tile, int& s_usepi,
                                               double& s_rem) {
     const RowCtx c = spec_ctx<DT>(a, b, j);
@@ -2845,7 +2860,7 @@ __device__ __forceinline__ int residual_token(const SpecArgs& a, int b, int j, c
     qf.d0 = a.draft_tokens[(size_t)b * a.G + j];
     qf.set = nullptr;
     qf.n = 0;
-    return residual_draw<DT>(c, ri, qf, a.ws.resid_tile + (size_t)b * a.ws.n_tiles, a.ws.n_tiles, tt,
+    return residual_draw<DT>(c, ri, qf, xt, a.ws.n_tiles, a.ws.scratch_z + ((size_t)b * (a.G + 1) + j) * a.V, tt,
                              sh, s_tile, s_usepi, s_rem);
 }
 
@@ -2863,6 +2878,9 @@ __global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
     __shared__ double s_rem;
     const int b = blockIdx.x;
     const int G1 = a.G + 1;
+    // the residual tile sums, issued first (used only if a position is rejected)
+    const double2 xt = threadIdx.x < a.ws.n_tiles ? a.ws.resid_tile[(size_t)b * a.ws.n_tiles + threadIdx.x]
+                                                  : make_double2(0.0, 0.0);
     const int n = accepted_prefix(a, b);
     RowInfo ri;
     const int j = residual_position(a, b, ri);
@@ -2875,7 +2893,7 @@ __global__ __launch_bounds__(NT) void k_spec_finish(SpecArgs a) {
         if (j < 0) out[n] = final_token;
     }
     if (j >= 0) {  // uniform over the workgroup
-        final_token = residual_token<DT>(a, b, j, ri, tt, sh, s_tile, s_usepi, s_rem);
+        final_token = residual_token<DT>(a, b, j, ri, xt, tt, sh, s_tile, s_usepi, s_rem);
         if (threadIdx.x == 0) out[j] = final_token;
     }
     if (a.seq_tokens) {
@@ -3068,7 +3086,7 @@ __global__ __launch_bounds__(NT) SS_TILE_OCC void k_tree_resid_tiles(TreeArgs a)
     qf.d0 = -1;
     qf.set = set;
     qf.n = nk;
-    const double2 x = residual_sums<DT>(c, ri, qf, tile * TILE, tt, sh);
+    const double2 x = residual_sums<DT>(c, ri, qf, tile * TILE, tt, sh, a.ws.scratch_z + (size_t)row * a.V);
     if (threadIdx.x == 0) a.ws.resid_tile[(size_t)b * n_tiles + tile] = x;
 }
 
@@ -3089,6 +3107,9 @@ __global__ __launch_bounds__(NT) void k_tree_finish(TreeArgs a) {
     int32_t* out_n = a.out_nodes + (size_t)b * N;
     const int lane = threadIdx.x & (WAVE - 1);
     const int tok = lane < N ? a.tokens[(size_t)b * N + lane] : -1;
+    // the residual tile sums, issued first (used only if the end node's children were rejected)
+    const double2 xt = threadIdx.x < a.ws.n_tiles ? a.ws.resid_tile[(size_t)b * a.ws.n_tiles + threadIdx.x]
+                                                  : make_double2(0.0, 0.0);
     int e;
     const int k = tree_walk(a, b, e, [&](int i, int node) {
         const int t = __shfl(tok, node);
@@ -3112,8 +3133,8 @@ __global__ __launch_bounds__(NT) void k_tree_finish(TreeArgs a) {
         qf.d0 = -1;
         qf.set = set;
         qf.n = nk;
-        final_token = residual_draw<DT>(c, ri, qf, a.ws.resid_tile + (size_t)b * a.ws.n_tiles,
-                                        a.ws.n_tiles, tt, sh, s_tile, s_usepi, s_rem);
+        final_token = residual_draw<DT>(c, ri, qf, xt, a.ws.n_tiles, a.ws.scratch_z + (size_t)row * a.V, tt, sh,
+                                        s_tile, s_usepi, s_rem);
     }
     if (threadIdx.x == 0) {
         out_t[k] = final_token;
