@@ -3160,7 +3160,12 @@ constexpr int LM_CAP = 4096;  // certified entries sorted in LDS
 
 struct SmemLm {
     unsigned long long key[LM_CAP];
-    double pre[LM_CAP];         // inclusive prefix mass in key order
+    union {
+        unsigned long long sorted[LM_CAP];  // the keys in bucket order, while they are ranked
+        double pre[LM_CAP];                 // inclusive prefix mass in key order
+    };
+    uint32_t cnt[NBK];                      // bucket sizes
+    uint32_t start[NBK];                    // bucket offsets
 };
 
 __device__ __forceinline__ bool lm_better(float sa, int ia, float sb, int ib) {
@@ -3285,7 +3290,70 @@ __global__ __launch_bounds__(NTR) void k_lm_merge(LmheadArgs a) {
     const int nc = s_n;
     bool open = nc > LM_CAP;
     int n3 = 0;
-    if (!open) {
+    // Counting sort of the certified keys by bucket b = (zmax - z) S, which
+    // does not decrease along key order, then each key's rank among its
+    // bucket's keys (a bitonic network when a bucket is too large).
+    bool bitonic = false;
+    if (!open && nc > 1) {
+        float zl = __builtin_huge_valf();
+        for (int i = tid; i < nc; i += NTR) zl = fminf(zl, key_z(L.key[i]));
+        zl = -block_max(-zl, sh.red);
+        const float R = zmax - zl;
+        const float S = R > 0.0f ? fminf((float)NBK / R, 3.0e38f) : 0.0f;
+        for (int i = tid; i < NBK; i += NTR) L.cnt[i] = 0u;
+        __syncthreads();
+        constexpr int PE = LM_CAP / NTR;
+        unsigned long long kk[PE];
+        int bk[PE], ar[PE];
+#pragma unroll
+        for (int q = 0; q < PE; ++q) {
+            const int e = tid + q * NTR;
+            kk[q] = 0ull;
+            bk[q] = 0;
+            ar[q] = 0;
+            if (e < nc) {
+                kk[q] = L.key[e];
+                bk[q] = (int)fminf((zmax - key_z(kk[q])) * S, (float)(NBK - 1));
+                ar[q] = (int)atomicAdd(&L.cnt[bk[q]], 1u);
+            }
+        }
+        __syncthreads();
+        uint32_t cb[BKPT];
+        unsigned long long mine = 0, mx = 0;
+#pragma unroll
+        for (int q = 0; q < BKPT; ++q) {
+            cb[q] = L.cnt[tid * BKPT + q];
+            mine += cb[q];
+            mx = cb[q] > mx ? cb[q] : mx;
+        }
+        unsigned long long all;
+        unsigned long long base = block_excl_scan_u64(mine, sh.hs, all);
+        mx = block_max_u64(mx, sh);
+#pragma unroll
+        for (int q = 0; q < BKPT; ++q) {
+            L.start[tid * BKPT + q] = (uint32_t)base;
+            base += cb[q];
+        }
+        bitonic = mx > BK_MAX;  // uniform
+        __syncthreads();
+        if (!bitonic) {
+#pragma unroll
+            for (int q = 0; q < PE; ++q)
+                if (tid + q * NTR < nc) L.sorted[L.start[bk[q]] + ar[q]] = kk[q];
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < PE; ++q) {
+                if (tid + q * NTR < nc) {
+                    const int s0 = (int)L.start[bk[q]], cq = (int)L.cnt[bk[q]];
+                    int r = 0;
+                    for (int i = 0; i < cq; ++i) r += L.sorted[s0 + i] > kk[q] ? 1 : 0;
+                    L.key[s0 + r] = kk[q];
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (!open && bitonic) {
         // bitonic sort, descending, over the next power of two (zero keys last)
         int P2 = WAVE;
         while (P2 < nc) P2 <<= 1;
@@ -3306,6 +3374,8 @@ __global__ __launch_bounds__(NTR) void k_lm_merge(LmheadArgs a) {
                 __syncthreads();
             }
         }
+    }
+    if (!open) {
         // weights and binary64 inclusive prefix masses in key order
         constexpr int PER = LM_CAP / NTR;
         double run = 0.0;
