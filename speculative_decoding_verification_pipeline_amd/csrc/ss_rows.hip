@@ -35,7 +35,16 @@
 //    path: z of the whole row into scratch, then each selection (top-k by
 //    count, top-p and the draw by mass) as one histogram pass over buckets of
 //    (zmax - z) and an exact resolve of the one bucket that holds the answer.
-//    Results never depend on which path resolved them.
+//    Between the two, an unfiltered row without penalty or bias lists whose
+//    draw lies past its pool is drawn from binned tails: its count-cut waves
+//    also bin their other entries' masses by z in stage 1, and stage 2 finds
+//    the bin that holds the draw, then that bin's entries in one pass over the
+//    row. Results never depend on which path resolved them.
+//  * Verification reuses both stages over every target row; its residual stage
+//    keeps each entry's residual with the per-tile sums so that the draw reads
+//    the chosen tile's residuals. The LM-head rows left open by the GEMM's
+//    tile candidates fix their kept set on one workgroup per row, then run the
+//    Gumbel pass over it on the whole GPU.
 #include <float.h>
 #include <limits.h>
 
