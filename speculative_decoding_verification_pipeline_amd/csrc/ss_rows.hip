@@ -2622,13 +2622,16 @@ __device__ __forceinline__ int residual_position(const SpecArgs& a, int b, RowIn
     return n;
 }
 
-// pi(v) of the filtered distribution described by ri, for processed logit x.
-__device__ __forceinline__ float filtered_prob(const RowCtx& c, const RowInfo& ri, int id, float x) {
+// pi(v) of the filtered distribution described by ri, for processed logit x
+// (invW = 1 / ri.W: the binary64 product differs from the quotient by at most
+// one unit in its last place, far below the binary32 rounding of pi).
+__device__ __forceinline__ float filtered_prob(const RowCtx& c, const RowInfo& ri, double invW, int id,
+                                               float x) {
     if (!(x > NEG_INF)) return 0.0f;
     const float z = canon_zero(x / c.T);
     const float w = expf(z - ri.zmax);
     const bool kept = key64(z, id) >= ri.kappa && (ri.min_p <= 0.0f || w >= ri.min_p);
-    return kept ? (float)((double)w / ri.W) : 0.0f;
+    return kept ? (float)((double)w * invW) : 0.0f;
 }
 
 // Residual mass of one tile of a rejected row: r = max(0, pi - q) per entry (or
@@ -2662,12 +2665,13 @@ __device__ __forceinline__ void residual_values(const RowCtx& c, const RowInfo& 
     const bool tables = c.hist_len + c.extra_len + c.bias_len > 0;
     if (tables) build_tables<DT>(c, tb, tt, f);
     process_tile<DT>(c, tb, v, tt, mw, tables);
+    const double invW = 1.0 / ri.W;
 #pragma unroll
     for (int s = 0; s < EPT; ++s) {
         const int id = slot_id<DT>(tb, s);
         double val = 0.0;
         if (id < c.V) {
-            const float pi = filtered_prob(c, ri, id, v[s]);
+            const float pi = filtered_prob(c, ri, invW, id, v[s]);
             val = use_pi ? (double)pi : (double)fmaxf(0.0f, pi - qf(id));
         }
         r[s] = val;
@@ -2690,11 +2694,12 @@ __device__ __forceinline__ double2 residual_sums(const RowCtx& c, const RowInfo&
     if (tables) build_tables<DT>(c, tb, tt, f);
     process_tile<DT>(c, tb, v, tt, mw, tables);
     double sr = 0.0, sp = 0.0;
+    const double invW = 1.0 / ri.W;
 #pragma unroll
     for (int s = 0; s < EPT; ++s) {
         const int id = slot_id<DT>(tb, s);
         if (id < c.V) {
-            const float pi = filtered_prob(c, ri, id, v[s]);
+            const float pi = filtered_prob(c, ri, invW, id, v[s]);
             const float rv = fmaxf(0.0f, pi - qf(id));
             if (keep) keep[id] = rv;
             sr += (double)rv;
