@@ -1144,7 +1144,18 @@ __device__ __forceinline__ int row_argmax(const RowLoad& l, float m) {
     return wave_min_i(min(a, b));
 }
 
-__device__ __forceinline__ uint64_t wq(float w) { return (uint64_t)((double)w * MASS_SCALE); }
+// floor(w 2^44) for a binary32 weight w in [0, 1], by integer shifts of its
+// significand: the same value as truncating the binary64 product w * 2^44
+// (exact: 24 bits), without the binary64-to-integer conversion sequence.
+__device__ __forceinline__ uint64_t wq(float w) {
+    static_assert(MASS_SCALE == 0x1p44, "the shift below assumes 2^44");
+    const uint32_t b = __float_as_uint(w);
+    const int e = (int)(b >> 23);  // biased exponent (w >= 0)
+    const uint64_t m = (uint64_t)((b & 0x7FFFFFu) | 0x800000u);
+    const int sh = e - 106;        // w 2^44 = m 2^(e - 127 - 23 + 44)
+    if (e == 0) return 0;          // zero or subnormal: below 2^-82
+    return sh >= 0 ? m << sh : (sh > -64 ? m >> -sh : 0);
+}
 
 
 // Radix selection over the row's z (scratch), 8 passes of 8-bit digits on key64.
@@ -1303,8 +1314,13 @@ __device__ __forceinline__ void hist_select(const float* zr, int V, float zmax, 
     __syncthreads();
     row_visit(zr, V, [&](int v, float z) {
         if (!(z > NEG_INF)) return;
-        float w;
-        if (!pass(v, z, w)) return;
+        // the key only where kmin can exclude the entry
+        if (kmin != 0ull && key64(z, v) < kmin) return;
+        float w = 0.0f;
+        if (need_w) {
+            w = entry_w(z, zmax, w_deep_zero);
+            if (wmin > 0.0f && !(w >= wmin)) return;
+        }
         const int b = hbucket(z, zmax, s2);
         atomicAdd(&h.hc[b], 1u);
         if (by_mass) atomicAdd(&h.hm[b], (unsigned long long)wq(w));
