@@ -121,6 +121,25 @@ def test_ragged_and_degenerate(V, dtype, mask, entropy):
     tally.check()
 
 
+@pytest.mark.parametrize("V,dtype,mask,entropy", [
+    (37, "f32", True, "mixed"), (4099, "bf16", False, "mixed"), (20001, "f32", True, "normal"),
+    (65537, "bf16", True, "mixed"), (128256, "f32", False, "flat")])
+def test_batches_without_lists(V, dtype, mask, entropy):
+    # no history or bias lists: the kernels that keep binned tails, over rows
+    # with and without filters (debug outputs, then 40 seeds without them)
+    rng = np.random.default_rng(V * 11 + len(dtype))
+    B = 8
+    w = random_workload(rng, B, V, dtype, entropy, mask, extras=False)
+    log(f"[no lists] V={V} {dtype} mask={mask} {entropy}")
+    xs, filts = oracle_filtered(w)
+    s = make_sampler(B, V)
+    tally = Tally(f"no lists V={V}", budget=False)
+    toks, dbg = run_debug(s, w)
+    compare_debug(w, xs, filts, toks, dbg, w.seed, tally)
+    seed_sweep(s, w, filts, range(700, 740), tally)
+    tally.check()
+
+
 def test_high_entropy_rows_take_the_exact_fallback():
     rng = np.random.default_rng(5)
     B, V = 4, 128256
