@@ -294,6 +294,25 @@ __device__ __forceinline__ double wave_incl_scan_d(double v) {
     return v;
 }
 
+template <int C, int ROWMASK, bool BZ>
+__device__ __forceinline__ unsigned long long dpp_u64_masked(unsigned long long u) {
+    const uint32_t lo = dpp_u32<C, ROWMASK, BZ>(0u, (uint32_t)u);
+    const uint32_t hi = dpp_u32<C, ROWMASK, BZ>(0u, (uint32_t)(u >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Inclusive prefix sum of a u64 over the wave (lane order), by the same DPP
+// steps as wave_incl_scan_d.
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v) {
+    v += dpp_u64_masked<DPP_ROW_SHR1, 0xF, true>(v);
+    v += dpp_u64_masked<DPP_ROW_SHR2, 0xF, true>(v);
+    v += dpp_u64_masked<DPP_ROW_SHR4, 0xF, true>(v);
+    v += dpp_u64_masked<DPP_ROW_SHR8, 0xF, true>(v);
+    v += dpp_u64_masked<DPP_BCAST15, 0xA, false>(v);
+    v += dpp_u64_masked<DPP_BCAST31, 0xC, false>(v);
+    return v;
+}
+
 // Scratch for workgroup-level reductions over NB threads (NB / WAVE waves).
 template <int NB>
 struct RedT {

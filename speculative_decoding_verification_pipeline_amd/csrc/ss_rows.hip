@@ -216,6 +216,7 @@ struct SmemBucket {
 
 struct SmemHistState {
     unsigned long long wsum[NTR_MAX / WAVE];
+    unsigned long long wsum2[NTR_MAX / WAVE];
     unsigned long long cum;     // count or mass of the buckets before the selected one
     unsigned long long target;
     unsigned long long key;
@@ -1240,23 +1241,12 @@ __device__ __forceinline__ int hbucket(float z, float zmax, float s2) {
     return HB;
 }
 
-__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int d) {
-    const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, d);
-    const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), d);
-    return ((unsigned long long)hi << 32) | lo;
-}
-
 // Exclusive prefix of one u64 per thread in thread order (exact); total too.
 __device__ unsigned long long block_excl_scan_u64(unsigned long long v, SmemHistState& hs,
                                                   unsigned long long& total) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int w = threadIdx.x / WAVE;
-    unsigned long long inc = v;
-#pragma unroll
-    for (int d = 1; d < WAVE; d <<= 1) {
-        const unsigned long long o = shfl_up_u64(inc, d);
-        if (lane >= d) inc += o;
-    }
+    const unsigned long long inc = wave_incl_scan_u64(v);
     if (lane == WAVE - 1) hs.wsum[w] = inc;
     __syncthreads();
     unsigned long long base = 0, tot = 0;
@@ -1267,6 +1257,35 @@ __device__ unsigned long long block_excl_scan_u64(unsigned long long v, SmemHist
     __syncthreads();
     total = tot;
     return base + inc - v;
+}
+
+// The same for two values at once (one pair of barriers).
+__device__ void block_excl_scan2_u64(unsigned long long a, unsigned long long b, SmemHistState& hs,
+                                     unsigned long long& pre_a, unsigned long long& pre_b,
+                                     unsigned long long& tot_a, unsigned long long& tot_b) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int w = threadIdx.x / WAVE;
+    const unsigned long long ia = wave_incl_scan_u64(a), ib = wave_incl_scan_u64(b);
+    if (lane == WAVE - 1) {
+        hs.wsum[w] = ia;
+        hs.wsum2[w] = ib;
+    }
+    __syncthreads();
+    unsigned long long ba = 0, bb = 0, ta = 0, tb = 0;
+    for (int k = 0; k < NTR / WAVE; ++k) {
+        const unsigned long long x = hs.wsum[k], y = hs.wsum2[k];
+        if (k < w) {
+            ba += x;
+            bb += y;
+        }
+        ta += x;
+        tb += y;
+    }
+    __syncthreads();
+    pre_a = ba + ia - a;
+    pre_b = bb + ib - b;
+    tot_a = ta;
+    tot_b = tb;
 }
 
 // An entry's weight exp(z - zmax). With deep_zero, entries more than
@@ -1338,9 +1357,8 @@ __device__ __forceinline__ void hist_select(const float* zr, int V, float zmax, 
         mine_m += h.hm[b0 + i];
         if (h.hc[b0 + i]) lastnz = b0 + i;
     }
-    unsigned long long tot_c, tot_m;
-    const unsigned long long pre_c = block_excl_scan_u64(mine_c, hs, tot_c);
-    const unsigned long long pre_m = block_excl_scan_u64(mine_m, hs, tot_m);
+    unsigned long long tot_c, tot_m, pre_c, pre_m;
+    block_excl_scan2_u64(mine_c, mine_m, hs, pre_c, pre_m, tot_c, tot_m);
     count = (int)tot_c;
     mass = tot_m;
     if (!want_key) return;
