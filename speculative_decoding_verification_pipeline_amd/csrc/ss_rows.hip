@@ -2990,12 +2990,15 @@ __global__ __launch_bounds__(WAVE) void k_tree_paths(TreeArgs a) {
     int d = n == 0 ? 0 : -1;
     for (int r = 1; r < N; ++r) {  // depth r is settled after round r
         const int pd = __shfl(d, edge ? par : 0);
-        if (d < 0 && edge && pd >= 0) d = pd + 1;
+        const bool set = d < 0 && edge && pd >= 0;
+        if (set) d = pd + 1;
+        if (!__ballot(set)) break;  // a round that settles nothing ends the walk (uniform)
     }
     if (n < N) a.ws.tree_depth[(size_t)b * N + n] = d;
     int32_t* path = a.ws.tree_path + ((size_t)b * N + min(n, N - 1)) * a.ws.tree_dmax;
     int at = n;
-    for (int r = 0; r < N - 1; ++r) {  // path[d - 1 - r] = token of the r-th ancestor-or-self
+    const int dmax = wave_max_i(n < N ? d : 0);
+    for (int r = 0; r < dmax; ++r) {  // path[d - 1 - r] = token of the r-th ancestor-or-self
         const int t = __shfl(tok, at);
         const int p = __shfl(par, at);
         if (n < N && r < d) path[d - 1 - r] = t;
