@@ -959,14 +959,19 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
-            // two copies of the loop: the one without bins stays free of them
-            auto sum_tile = [&](auto bin_c) {
+            // separate copies of the loop: the one without bins stays free of
+            // them, and where T is a power of two (T = 1 above all) x' / T is
+            // the exact product x' (1 / T), without a division per entry
+            const float rT = 1.0f / c.T;
+            const bool pow2 = (__float_as_uint(c.T) & 0x7FFFFFu) == 0u && c.T >= FLT_MIN;  // uniform
+            auto sum_tile = [&](auto bin_c, auto p2_c) {
                 constexpr bool BIN = decltype(bin_c)::value;
+                constexpr bool P2 = decltype(p2_c)::value;
                 double acc = 0.0;
 #pragma unroll
                 for (int s = 0; s < EPT; ++s) {
                     if (v[s] > NEG_INF) {
-                        const float z = canon_zero(v[s] / c.T);
+                        const float z = canon_zero(P2 ? v[s] * rT : v[s] / c.T);
                         const float w = expf(z - zm);
                         acc += (double)w;
                         // non-candidates: x' <= theta, so z <= zbeta and the bin is >= 0
@@ -977,8 +982,12 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
                 return acc;
             };
             double acc;
-            if constexpr (BINS) acc = bin ? sum_tile(BoolC<true>{}) : sum_tile(BoolC<false>{});
-            else acc = sum_tile(BoolC<false>{});
+            if constexpr (BINS) {
+                if (bin) acc = pow2 ? sum_tile(BoolC<true>{}, BoolC<true>{}) : sum_tile(BoolC<true>{}, BoolC<false>{});
+                else acc = pow2 ? sum_tile(BoolC<false>{}, BoolC<true>{}) : sum_tile(BoolC<false>{}, BoolC<false>{});
+            } else {
+                acc = pow2 ? sum_tile(BoolC<false>{}, BoolC<true>{}) : sum_tile(BoolC<false>{}, BoolC<false>{});
+            }
             st.s = wave_sum_d(acc);
             st.flags |= WS_SUM;
             if (bin) {
