@@ -140,6 +140,12 @@ __device__ __forceinline__ RowCtx make_ctx(const ParamPtrs& p, int b, const void
     return c;
 }
 
+// T > 0 a (normal) power of two: then x / T is exactly x (1 / T), with no
+// rounding step of its own, and a product replaces the division.
+__device__ __forceinline__ bool pow2_temp(float T) {
+    return (__float_as_uint(T) & 0x7FFFFFu) == 0u && T >= FLT_MIN;
+}
+
 // ---------------------------------------------------------------------------
 // LDS layouts (one union per workgroup; phases are separated by barriers)
 
@@ -963,7 +969,7 @@ __device__ __forceinline__ void tile_stage1(const RowCtx& c, int row, int tile, 
             // them, and where T is a power of two (T = 1 above all) x' / T is
             // the exact product x' (1 / T), without a division per entry
             const float rT = 1.0f / c.T;
-            const bool pow2 = (__float_as_uint(c.T) & 0x7FFFFFu) == 0u && c.T >= FLT_MIN;  // uniform
+            const bool pow2 = pow2_temp(c.T);  // uniform
             auto sum_tile = [&](auto bin_c, auto p2_c) {
                 constexpr bool BIN = decltype(bin_c)::value;
                 constexpr bool P2 = decltype(p2_c)::value;
@@ -2668,10 +2674,12 @@ __device__ __forceinline__ int residual_position(const SpecArgs& a, int b, RowIn
 // pi(v) of the filtered distribution described by ri, for processed logit x
 // (invW = 1 / ri.W: the binary64 product differs from the quotient by at most
 // one unit in its last place, far below the binary32 rounding of pi).
-__device__ __forceinline__ float filtered_prob(const RowCtx& c, const RowInfo& ri, double invW, int id,
+// (P2: T is a power of two, and x' / T the exact product x' rT.)
+template <bool P2>
+__device__ __forceinline__ float filtered_prob(const RowCtx& c, const RowInfo& ri, double invW, float rT, int id,
                                                float x) {
     if (!(x > NEG_INF)) return 0.0f;
-    const float z = canon_zero(x / c.T);
+    const float z = canon_zero(P2 ? x * rT : x / c.T);
     const float w = expf(z - ri.zmax);
     const bool kept = key64(z, id) >= ri.kappa && (ri.min_p <= 0.0f || w >= ri.min_p);
     return kept ? (float)((double)w * invW) : 0.0f;
@@ -2709,16 +2717,22 @@ __device__ __forceinline__ void residual_values(const RowCtx& c, const RowInfo& 
     if (tables) build_tables<DT>(c, tb, tt, f);
     process_tile<DT>(c, tb, v, tt, mw, tables);
     const double invW = 1.0 / ri.W;
+    const float rT = 1.0f / c.T;
+    auto fill = [&](auto p2_c) {
+        constexpr bool P2 = decltype(p2_c)::value;
 #pragma unroll
-    for (int s = 0; s < EPT; ++s) {
-        const int id = slot_id<DT>(tb, s);
-        double val = 0.0;
-        if (id < c.V) {
-            const float pi = filtered_prob(c, ri, invW, id, v[s]);
-            val = use_pi ? (double)pi : (double)fmaxf(0.0f, pi - qf(id));
+        for (int s = 0; s < EPT; ++s) {
+            const int id = slot_id<DT>(tb, s);
+            double val = 0.0;
+            if (id < c.V) {
+                const float pi = filtered_prob<P2>(c, ri, invW, rT, id, v[s]);
+                val = use_pi ? (double)pi : (double)fmaxf(0.0f, pi - qf(id));
+            }
+            r[s] = val;
         }
-        r[s] = val;
-    }
+    };
+    if (pow2_temp(c.T)) fill(BoolC<true>{});
+    else fill(BoolC<false>{});
 }
 
 // Sums over tile tb of the residual and of pi (the fallback when the residual
@@ -2738,17 +2752,23 @@ __device__ __forceinline__ double2 residual_sums(const RowCtx& c, const RowInfo&
     process_tile<DT>(c, tb, v, tt, mw, tables);
     double sr = 0.0, sp = 0.0;
     const double invW = 1.0 / ri.W;
+    const float rT = 1.0f / c.T;
+    auto sum = [&](auto p2_c) {
+        constexpr bool P2 = decltype(p2_c)::value;
 #pragma unroll
-    for (int s = 0; s < EPT; ++s) {
-        const int id = slot_id<DT>(tb, s);
-        if (id < c.V) {
-            const float pi = filtered_prob(c, ri, invW, id, v[s]);
-            const float rv = fmaxf(0.0f, pi - qf(id));
-            if (keep) keep[id] = rv;
-            sr += (double)rv;
-            sp += (double)pi;
+        for (int s = 0; s < EPT; ++s) {
+            const int id = slot_id<DT>(tb, s);
+            if (id < c.V) {
+                const float pi = filtered_prob<P2>(c, ri, invW, rT, id, v[s]);
+                const float rv = fmaxf(0.0f, pi - qf(id));
+                if (keep) keep[id] = rv;
+                sr += (double)rv;
+                sp += (double)pi;
+            }
         }
-    }
+    };
+    if (pow2_temp(c.T)) sum(BoolC<true>{});
+    else sum(BoolC<false>{});
     // both sums in one exchange of the wave totals
     sr = wave_sum_d(sr);
     sp = wave_sum_d(sp);
